@@ -1,0 +1,305 @@
+"""Seeded synthetic inputs for the five MoE-layer workloads.
+
+Every tensor is drawn from its own NumPy PCG64 substream,
+``SeedSequence(0, spawn_key=(workload, kind, a, b))``, so any single expert
+of any layer can be regenerated on its own and in parallel.  Nothing here
+computes the layer: the only arithmetic is the *quantiser* that turns fp32
+draws into ggml Q8_0 / Q4_0 blocks (the weight format the pages name for
+expert banks, "FreeToken" GitHub README, sections "Quant types" and "Known
+limits") and the bias / trace recipes that describe the workloads.
+
+Block formats (ggml array-of-structs, little endian), one block per 32
+consecutive weights along the input dimension of a weight row:
+
+* Q8_0: fp16 scale ``d`` (2 B) then 32 x int8 ``q``  -> 34 B.
+  Quantiser: ``d = max|w| / 127``; ``q = round_half_away(w / d)``.
+* Q4_0: fp16 scale ``d`` (2 B) then 16 B of nibbles  -> 18 B.  Byte ``j``
+  holds element ``j`` in its low nibble and element ``j + 16`` in its high
+  nibble.  Quantiser: ``m`` = signed element of largest magnitude (first on
+  ties), ``d = m / -8``, ``q = min(15, floor(w / d + 8.5))``.
+
+Matrix orientation: every weight matrix is ``[out_rows][in_cols / 32]``
+blocks; per expert the tensors are gate ``[I][H]``, up ``[I][H]`` and
+down ``[H][I]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "QK", "BLOCK_BYTES", "KIND", "Workload", "WORKLOADS", "workload",
+    "rng_for", "quantize_q8_0", "quantize_q4_0", "expert_weights_f32",
+    "expert_blocks", "router_weight", "router_bias", "activations",
+    "given_logits", "slot_permutation", "zipf_cdf", "cache_trace",
+    "cache_trace_logits", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "generate_blocks_parallel", "weights_per_expert", "bytes_per_expert",
+]
+
+QK = 32
+BLOCK_BYTES = {"q8_0": 34, "q4_0": 18}
+
+# substream "kind" field
+KIND = {
+    "x": 1, "router": 2, "gate": 3, "up": 4, "down": 5, "logits": 6,
+    "slots": 7, "trace": 8, "trace_logits": 9,
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: sizes, weight format and routing source."""
+    index: int            # substream id (1..5)
+    name: str
+    H: int                # hidden size
+    E: int                # routed experts per layer
+    k: int                # experts per token
+    I: int                # expert FFN intermediate size
+    qtype: str            # "q8_0" | "q4_0"
+    batches: Tuple[int, ...]  # token counts T
+    layers: int = 1
+    x_dtype: str = "f32"  # "f32" | "bf16"
+    router: str = "matrix"  # "matrix" | "logits" | "trace"
+    zipf_bias_s: Optional[float] = None  # router bias -s*ln(e+1)
+    cache_fraction: Optional[float] = None
+    steps: Optional[int] = None
+    trace_keep_p: Optional[float] = None
+    trace_zipf_s: Optional[float] = None
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in [
+        Workload(1, "tiny_q8_0", H=256, E=8, k=2, I=512, qtype="q8_0",
+                 batches=(4,)),
+        Workload(2, "decode_q8_0_h2048_e128", H=2048, E=128, k=8, I=768,
+                 qtype="q8_0", batches=(1, 4, 16), layers=48),
+        Workload(3, "prefill_q4_0_h2048_e128", H=2048, E=128, k=8, I=768,
+                 qtype="q4_0", batches=(4096,), x_dtype="bf16",
+                 router="logits"),
+        Workload(4, "wide_q4_0_h2048_e512", H=2048, E=512, k=10, I=512,
+                 qtype="q4_0", batches=(1, 64), zipf_bias_s=1.1),
+        Workload(5, "cache_q4_0_h4096_e256", H=4096, E=256, k=8, I=2048,
+                 qtype="q4_0", batches=(1,), layers=8, router="trace",
+                 cache_fraction=0.4, steps=2048, trace_keep_p=0.7,
+                 trace_zipf_s=1.0),
+    ]
+}
+
+
+def workload(name_or_index) -> Workload:
+    if isinstance(name_or_index, int):
+        for w in WORKLOADS.values():
+            if w.index == name_or_index:
+                return w
+        raise KeyError(name_or_index)
+    return WORKLOADS[name_or_index]
+
+
+def weights_per_expert(wl: Workload) -> int:
+    return 3 * wl.H * wl.I
+
+
+def bytes_per_expert(wl: Workload) -> int:
+    return weights_per_expert(wl) // QK * BLOCK_BYTES[wl.qtype]
+
+
+def rng_for(wl_index: int, kind: str, a: int = 0, b: int = 0) -> np.random.Generator:
+    """Independent PCG64 stream for (workload, tensor kind, a, b), root seed 0."""
+    ss = np.random.SeedSequence(0, spawn_key=(wl_index, KIND[kind], a, b))
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers (NumPy has no bf16 dtype: bf16 travels as uint16 bit patterns)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# quantisers (input preparation only)
+# --------------------------------------------------------------------------
+def _round_half_away(x32: np.ndarray) -> np.ndarray:
+    x = x32.astype(np.float64)
+    return np.trunc(x + np.copysign(0.5, x))
+
+
+def quantize_q8_0(w: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K] -> uint8 [rows, K/32, 34] ggml Q8_0 blocks."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    assert K % QK == 0
+    b = w.reshape(rows, K // QK, QK)
+    amax = np.abs(b).max(axis=2)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    nz = d != 0
+    inv = np.zeros_like(d)
+    inv[nz] = np.float32(1.0) / d[nz]
+    q = _round_half_away(b * inv[..., None]).astype(np.int8)
+    out = np.empty((rows, K // QK, 34), dtype=np.uint8)
+    out[..., 0:2] = d.astype(np.float16).view(np.uint8).reshape(rows, K // QK, 2)
+    out[..., 2:] = q.view(np.uint8)
+    return out
+
+
+def quantize_q4_0(w: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K] -> uint8 [rows, K/32, 18] ggml Q4_0 blocks."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    assert K % QK == 0
+    b = w.reshape(rows, K // QK, QK)
+    idx = np.abs(b).argmax(axis=2)  # first occurrence on ties
+    m = np.take_along_axis(b, idx[..., None], axis=2)[..., 0]
+    d = (m / np.float32(-8.0)).astype(np.float32)
+    nz = d != 0
+    inv = np.zeros_like(d)
+    inv[nz] = np.float32(1.0) / d[nz]
+    t = (b * inv[..., None] + np.float32(8.5)).astype(np.float32)
+    q = np.minimum(np.trunc(t), 15).astype(np.uint8)
+    out = np.empty((rows, K // QK, 18), dtype=np.uint8)
+    out[..., 0:2] = d.astype(np.float16).view(np.uint8).reshape(rows, K // QK, 2)
+    out[..., 2:] = q[..., :16] | (q[..., 16:] << 4)
+    return out
+
+
+_QUANT = {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0}
+
+
+# --------------------------------------------------------------------------
+# weights, router, activations
+# --------------------------------------------------------------------------
+def expert_weights_f32(wl: Workload, layer: int, expert: int):
+    """fp32 N(0, 0.02) draws (gate [I,H], up [I,H], down [H,I]) before quantisation."""
+    sigma = np.float32(0.02)
+    out = []
+    for kind, shape in (("gate", (wl.I, wl.H)), ("up", (wl.I, wl.H)), ("down", (wl.H, wl.I))):
+        g = rng_for(wl.index, kind, layer, expert)
+        out.append(g.standard_normal(shape, dtype=np.float32) * sigma)
+    return tuple(out)
+
+
+def expert_blocks(wl: Workload, layer: int, expert: int):
+    """ggml blocks (gate, up, down) of one expert: uint8 [rows, cols/32, bpb]."""
+    q = _QUANT[wl.qtype]
+    return tuple(q(m) for m in expert_weights_f32(wl, layer, expert))
+
+
+def generate_blocks_parallel(wl: Workload, pairs: Sequence[Tuple[int, int]],
+                             consume, threads: Optional[int] = None) -> None:
+    """Generate expert_blocks for many (layer, expert) pairs on a thread pool.
+
+    ``consume(layer, expert, (gate, up, down))`` is called from the worker
+    threads; NumPy releases the GIL inside the heavy loops.
+    """
+    threads = threads or min(16, os.cpu_count() or 1)
+
+    def job(le):
+        l, e = le
+        consume(l, e, expert_blocks(wl, l, e))
+
+    with ThreadPoolExecutor(threads) as ex:
+        for _ in ex.map(job, pairs):
+            pass
+
+
+def router_weight(wl: Workload, layer: int = 0) -> np.ndarray:
+    """Router matrix Wr [E, H] fp32, N(0, 0.02) (row e maps hidden -> logit e)."""
+    g = rng_for(wl.index, "router", layer)
+    return g.standard_normal((wl.E, wl.H), dtype=np.float32) * np.float32(0.02)
+
+
+def router_bias(wl: Workload) -> Optional[np.ndarray]:
+    """Zipf-shaped logit bias b[e] = -s * ln(e + 1) (expert e has rank e + 1)."""
+    if wl.zipf_bias_s is None:
+        return None
+    e = np.arange(wl.E, dtype=np.float64)
+    return (-wl.zipf_bias_s * np.log(e + 1.0)).astype(np.float32)
+
+
+def activations(wl: Workload, T: int, step: int = 0) -> np.ndarray:
+    """Token activations [T, H] N(0, 1): fp32, or bf16 bit patterns (uint16)."""
+    g = rng_for(wl.index, "x", T, step)
+    x = g.standard_normal((T, wl.H), dtype=np.float32)
+    if wl.x_dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x
+
+
+def given_logits(wl: Workload, T: int) -> np.ndarray:
+    """Router logits supplied directly: i.i.d. N(0, 1) fp32 [T, E]."""
+    g = rng_for(wl.index, "logits", T)
+    return g.standard_normal((T, wl.E), dtype=np.float32)
+
+
+def slot_permutation(wl: Workload, layer: int = 0, n_slots: Optional[int] = None) -> np.ndarray:
+    """Seeded expert -> VRAM slot map (int32 [E]) for fully resident pools."""
+    g = rng_for(wl.index, "slots", layer)
+    n = n_slots or wl.E
+    return g.permutation(n)[: wl.E].astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# expert-cache routing trace
+# --------------------------------------------------------------------------
+def zipf_cdf(n: int, s: float) -> np.ndarray:
+    r = np.arange(1, n + 1, dtype=np.float64)
+    p = r ** (-s)
+    c = np.cumsum(p)
+    return c / c[-1]
+
+
+def cache_trace(wl: Workload, steps: Optional[int] = None) -> np.ndarray:
+    """Expert ids int32 [steps, layers, k] with temporal locality.
+
+    Per layer, independently: step 0 takes k distinct Zipf(s) draws over
+    ranks 1..E (rank r is expert r-1, repeats rejected).  Each later step
+    keeps every id of the previous step with probability p (in order), then
+    fills up with Zipf draws, rejecting ids already chosen.
+    """
+    steps = steps or wl.steps
+    L, E, k = wl.layers, wl.E, wl.k
+    cdf = zipf_cdf(E, wl.trace_zipf_s)
+    out = np.empty((steps, L, k), dtype=np.int32)
+    for l in range(L):
+        g = rng_for(wl.index, "trace", l)
+        prev: List[int] = []
+        for s in range(steps):
+            if s == 0:
+                chosen: List[int] = []
+            else:
+                keep = g.random(len(prev)) < wl.trace_keep_p
+                chosen = [e for e, kp in zip(prev, keep) if kp]
+            while len(chosen) < k:
+                e = int(np.searchsorted(cdf, g.random(), side="right"))
+                e = min(e, E - 1)
+                if e not in chosen:
+                    chosen.append(e)
+            out[s, l] = chosen
+            prev = chosen
+    return out
+
+
+def cache_trace_logits(wl: Workload, trace: np.ndarray, step: int) -> np.ndarray:
+    """Router logits [layers, E] fp32 for one step of the trace.
+
+    The step's chosen ids get i.i.d. N(0, 1) logits; every other expert gets
+    -1e4, so a top-k selection picks exactly the chosen set.
+    """
+    L, E = wl.layers, wl.E
+    out = np.full((L, E), -1.0e4, dtype=np.float32)
+    for l in range(L):
+        g = rng_for(wl.index, "trace_logits", l, step)
+        out[l, trace[step, l]] = g.standard_normal(trace.shape[2], dtype=np.float32)
+    return out

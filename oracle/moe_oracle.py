@@ -1,0 +1,264 @@
+"""CPU oracle for the routed-expert MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it, and it shares no code with the GPU library: it reads the logical
+ggml block bytes produced by ``gen`` and computes everything in float64 with
+plain NumPy steps that can be checked against the definitions by eye.
+
+Sources.  The pages describe FreeToken, an engine that keeps the full expert
+pool in host memory and uses VRAM as an expert cache
+("FreeToken github moe: Setup Guide & MoE Runtime Comparison", introduction;
+"FreeToken Inference Engine: 3x Speed Boost for MoE Models", section "From
+Static Allocation to Dynamic Scheduling").  The expert banks are ggml
+Q4_0 / Q8_0 blocks held in one slot pool of one type (FreeToken fork README,
+sections "Quant types" and "Known limits").  Each token activates only a
+subset of the experts (setup guide, introduction).  The steps below are the
+plainest reading of that layer: softmax over expert logits, keep the k
+largest (ties to the lower expert id), renormalise the kept probabilities,
+group token/expert pairs by expert, run a SwiGLU expert FFN per pair, and
+sum the FFN outputs weighted by the renormalised probabilities.
+
+Decision precision.  Top-k selection is an integer decision taken on fp32
+logits, the precision the GPU kernel decides in: ``topk_select`` casts its
+input to float32 before ordering.  Everything else is float64.
+
+Parity pins.  Every function here is pinned by ``tests/test_oracle_pins.py``
+against closed forms, brute force or independent simulations.  The full
+layer output at large sizes has no external values to compare against; it is
+pinned only through its pinned parts ("parity unpinned" beyond them).
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+QK = 32  # weights per block, both formats
+
+
+# --------------------------------------------------------------------------
+# 1. block dequantisation (ggml Q8_0 / Q4_0; FreeToken fork README, "Quant types")
+# --------------------------------------------------------------------------
+def _block_scale(blocks: np.ndarray) -> np.ndarray:
+    """fp16 little-endian scale in bytes 0..1 of every block, as float64."""
+    return np.ascontiguousarray(blocks[..., 0:2]).view(np.float16)[..., 0].astype(np.float64)
+
+
+def dequant_q8_0(blocks: np.ndarray) -> np.ndarray:
+    """uint8 [..., nblk, 34] -> float64 [..., nblk*32]; w_i = d * q_i (q int8)."""
+    d = _block_scale(blocks)
+    q = np.ascontiguousarray(blocks[..., 2:34]).view(np.int8).astype(np.float64)
+    w = d[..., None] * q
+    return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK)
+
+
+def dequant_q4_0(blocks: np.ndarray) -> np.ndarray:
+    """uint8 [..., nblk, 18] -> float64 [..., nblk*32]; w = d * (q - 8).
+
+    Byte j of the 16 nibble bytes carries element j (low nibble) and
+    element j + 16 (high nibble).
+    """
+    d = _block_scale(blocks)
+    nib = blocks[..., 2:18]
+    q = np.concatenate([nib & 0x0F, nib >> 4], axis=-1).astype(np.float64)
+    w = d[..., None] * (q - 8.0)
+    return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK)
+
+
+def dequant(qtype: str, blocks: np.ndarray) -> np.ndarray:
+    if qtype == "q8_0":
+        return dequant_q8_0(blocks)
+    if qtype == "q4_0":
+        return dequant_q4_0(blocks)
+    raise ValueError(f"unsupported block type {qtype!r}")
+
+
+# --------------------------------------------------------------------------
+# 2-5. router: logits, softmax, top-k, renormalisation
+# --------------------------------------------------------------------------
+def router_logits(x: np.ndarray, router_w: np.ndarray,
+                  bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """l[t, e] = sum_h x[t, h] * Wr[e, h] (+ b[e]); Wr is [E, H]."""
+    l = np.asarray(x, dtype=np.float64) @ np.asarray(router_w, dtype=np.float64).T
+    if bias is not None:
+        l = l + np.asarray(bias, dtype=np.float64)[None, :]
+    return l
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    """Row softmax, max-shifted for range."""
+    l = np.asarray(l, dtype=np.float64)
+    z = np.exp(l - l.max(axis=-1, keepdims=True))
+    return z / z.sum(axis=-1, keepdims=True)
+
+
+def topk_select(l: np.ndarray, k: int) -> np.ndarray:
+    """Ids of the k largest fp32 logits per row, ordered (logit desc, id asc).
+
+    Selecting on logits equals selecting on their softmax (a monotone map)
+    and avoids false ties where exp() rounds two logits to one value.
+    """
+    l32 = np.asarray(l, dtype=np.float32)
+    order = np.argsort(-l32, axis=-1, kind="stable")  # equal keys keep id order
+    return order[..., :k].astype(np.int32)
+
+
+def renormalize(p: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """w[t, j] = p[t, ids[t, j]] / sum_j' p[t, ids[t, j']]."""
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=-1)
+    return sel / sel.sum(axis=-1, keepdims=True)
+
+
+def route(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """softmax -> top-k -> renormalise.  Returns (ids int32 [T,k], w float64 [T,k])."""
+    ids = topk_select(logits, k)
+    w = renormalize(softmax(logits), ids)
+    return ids, w
+
+
+def topk_gap(l: np.ndarray, k: int) -> np.ndarray:
+    """Per row: k-th largest minus (k+1)-th largest logit (inf when k == E)."""
+    s = -np.sort(-np.asarray(l, dtype=np.float64), axis=-1)
+    if k >= s.shape[-1]:
+        return np.full(s.shape[:-1], np.inf)
+    return s[..., k - 1] - s[..., k]
+
+
+# --------------------------------------------------------------------------
+# 6. permutation: group pairs p = t*k + j by expert (stable)
+# --------------------------------------------------------------------------
+def permute(ids: np.ndarray, E: int):
+    """Stable counting sort of pairs by expert id.
+
+    Returns (offsets [E+1], sorted_pairs [P], pair_pos [P], active ids).
+    ``sorted_pairs[offsets[e]:offsets[e+1]]`` lists the pairs routed to
+    expert e in ascending pair order; ``pair_pos`` is the inverse map;
+    ``active`` lists the experts with at least one pair, ascending.
+    """
+    flat = np.asarray(ids, dtype=np.int64).ravel()
+    P = flat.size
+    counts = np.zeros(E, dtype=np.int64)
+    for e in flat:
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:-1].copy()
+    sorted_pairs = np.empty(P, dtype=np.int64)
+    pair_pos = np.empty(P, dtype=np.int64)
+    for p in range(P):
+        e = flat[p]
+        sorted_pairs[cursor[e]] = p
+        pair_pos[p] = cursor[e]
+        cursor[e] += 1
+    active = np.array([e for e in range(E) if counts[e] > 0], dtype=np.int64)
+    return (offsets.astype(np.int32), sorted_pairs.astype(np.int32),
+            pair_pos.astype(np.int32), active.astype(np.int32))
+
+
+# --------------------------------------------------------------------------
+# 7. expert FFN (SwiGLU) and 8. combine
+# --------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x_rows: np.ndarray, wg: np.ndarray, wu: np.ndarray,
+               wd: np.ndarray) -> np.ndarray:
+    """SwiGLU FFN of one expert on rows x [n, H]: Wd (silu(Wg x) * (Wu x)).
+
+    wg, wu: [I, H]; wd: [H, I] (float64 dequantised weights).
+    """
+    x = np.asarray(x_rows, dtype=np.float64)
+    g = x @ wg.T
+    u = x @ wu.T
+    return (silu(g) * u) @ wd.T
+
+
+def moe_ffn_pairs(x: np.ndarray, ids: np.ndarray, E: int, qtype: str,
+                  get_blocks) -> np.ndarray:
+    """y_pairs [T*k, H]: FFN output of every pair p = t*k + j in pair order.
+
+    ``get_blocks(e)`` returns the ggml blocks (gate, up, down) of expert e.
+    """
+    T, k = ids.shape
+    x = np.asarray(x, dtype=np.float64)
+    offsets, sorted_pairs, _, active = permute(ids, E)
+    y = np.zeros((T * k, x.shape[1]), dtype=np.float64)
+    for e in active:
+        pairs = sorted_pairs[offsets[e]:offsets[e + 1]]
+        gb, ub, db = get_blocks(int(e))
+        wg, wu, wd = dequant(qtype, gb), dequant(qtype, ub), dequant(qtype, db)
+        y[pairs] = expert_ffn(x[pairs // k], wg, wu, wd)
+    return y
+
+
+def combine(y_pairs: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """out[t] = sum over j ascending of w[t, j] * y[t*k + j]."""
+    T, k = w.shape
+    y = np.asarray(y_pairs, dtype=np.float64).reshape(T, k, -1)
+    out = np.zeros((T, y.shape[2]), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * y[:, j, :]
+    return out
+
+
+def moe_layer(x: np.ndarray, qtype: str, get_blocks, k: int, *,
+              router_w: Optional[np.ndarray] = None,
+              bias: Optional[np.ndarray] = None,
+              logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Whole layer: route -> permute -> expert FFN -> combine.
+
+    Router logits are computed from x and Wr, or taken as given.  Returns
+    a dict with logits, ids, w, y_pairs, out and the top-k logit gap.
+    """
+    if logits is None:
+        logits = router_logits(x, router_w, bias)
+    logits = np.asarray(logits, dtype=np.float64)
+    ids, w = route(logits, k)
+    y = moe_ffn_pairs(x, ids, logits.shape[1], qtype, get_blocks)
+    return {"logits": logits, "ids": ids, "w": w, "y_pairs": y,
+            "out": combine(y, w), "gap": topk_gap(logits, k)}
+
+
+# --------------------------------------------------------------------------
+# 9. expert cache: global LRU over (layer, expert) keys
+#    (FreeToken fork README, "About": global LRU expert caching; setup guide:
+#    a shared LRU follows token-level routing locality; 3x-speed article,
+#    "From Static Allocation to Dynamic Scheduling": VRAM is a cache over the
+#    host-resident pool and only missing experts move over PCIe)
+# --------------------------------------------------------------------------
+def lru_simulate(trace: np.ndarray, capacity: int):
+    """Replay lookups in order; returns (hit bool [steps, L, n], evicted keys).
+
+    For every step, every layer and every id of that (step, layer) in
+    order, the key (layer, id) is looked up.  A resident key is a hit and
+    becomes most recently used.  A missing key is inserted; when the cache
+    is full the least recently used key is evicted first, never one looked
+    up earlier in the same (step, layer).  The cache starts empty.
+    """
+    steps, L, n = trace.shape
+    last_use: Dict[Tuple[int, int], int] = {}
+    clock = 0
+    hit = np.zeros(trace.shape, dtype=bool)
+    evicted: List[Tuple[int, int, Tuple[int, int]]] = []
+    for s in range(steps):
+        for l in range(L):
+            current = set()
+            for j in range(n):
+                key = (l, int(trace[s, l, j]))
+                clock += 1
+                if key in last_use:
+                    hit[s, l, j] = True
+                else:
+                    if len(last_use) >= capacity:
+                        candidates = [kk for kk in last_use if kk not in current]
+                        if not candidates:
+                            raise ValueError("cache capacity below the keys of one layer")
+                        victim = min(candidates, key=lambda kk: last_use[kk])
+                        del last_use[victim]
+                        evicted.append((s, l, victim))
+                last_use[key] = clock
+                current.add(key)
+    return hit, evicted

@@ -1,0 +1,349 @@
+"""Pins of the CPU oracle against closed forms, brute force and independent
+simulations (no GPU).  Each pin is chosen so that a plausible slip in the
+oracle (wrong byte or nibble order, dropped -8 offset, transposed router,
+wrong tie rule, missing renormalisation, unstable grouping, swapped SwiGLU
+operands, wrong combine index, wrong LRU victim) fails at least one test.
+"""
+import collections
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from gen import inputs as gi
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_blocks.txt")
+
+
+# ---------------------------------------------------------------- helpers
+def fp16_bits_to_float(bits: int) -> float:
+    """IEEE binary16 decoded from its fields (independent of NumPy's float16)."""
+    sign = -1.0 if bits & 0x8000 else 1.0
+    exp = (bits >> 10) & 0x1F
+    man = bits & 0x3FF
+    if exp == 0:
+        return sign * man * 2.0 ** -24
+    assert exp != 31, "inf/nan scales are outside the format's use"
+    return sign * (1.0 + man / 1024.0) * 2.0 ** (exp - 15)
+
+
+def build_block(qtype: str, d_bits: int, codes) -> np.ndarray:
+    """Pack one block by hand from the format description."""
+    codes = list(codes)
+    assert len(codes) == 32
+    if qtype == "q8_0":
+        body = [c & 0xFF for c in codes]
+    else:
+        body = [(codes[j] & 0xF) | ((codes[j + 16] & 0xF) << 4) for j in range(16)]
+    return np.array([d_bits & 0xFF, d_bits >> 8] + body, dtype=np.uint8)
+
+
+def load_golden():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        qt, dh, dv, codes = [f.strip() for f in line.split(";")]
+        rows.append((qt, int(dh, 16), float(dv), [int(c) for c in codes.split()]))
+    return rows
+
+
+# ---------------------------------------------------------------- dequant
+@pytest.mark.parametrize("row", load_golden(), ids=lambda r: f"{r[0]}-{r[1]:04X}")
+def test_dequant_hand_blocks(row):
+    qt, d_bits, d_val, codes = row
+    assert fp16_bits_to_float(d_bits) == d_val  # the fixture's hand-derived d
+    blk = build_block(qt, d_bits, codes)[None, None, :]
+    got = oracle.dequant(qt, blk)[0]
+    off = 0 if qt == "q8_0" else 8
+    want = np.array([d_val * (c - off) for c in codes], dtype=np.float64)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+def test_dequant_brute_force_all_codes(qt):
+    """Every code value times a set of scales, element position varied."""
+    codes_all = list(range(-128, 128)) if qt == "q8_0" else list(range(16))
+    d_bits_set = [0x3C00, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0xFBFF, 0xB555, 0x2E66]
+    for d_bits in d_bits_set:
+        dv = fp16_bits_to_float(d_bits)
+        for start in range(0, len(codes_all), 32):
+            chunk = (codes_all[start:start + 32] + codes_all)[:32]
+            chunk = chunk[::-1] if (start // 32) % 2 else chunk
+            blk = build_block(qt, d_bits, chunk)[None, None, :]
+            got = oracle.dequant(qt, blk)[0]
+            off = 0 if qt == "q8_0" else 8
+            for i, c in enumerate(chunk):
+                exact = Fraction(dv) * (c - off)
+                assert Fraction(float(got[i])) == exact
+
+
+def test_dequant_layout_rows_and_blocks():
+    """Blocks run along the input dimension; rows stack (shape [rows, nblk*32])."""
+    rng = np.random.default_rng(3)
+    blocks = gi.quantize_q8_0(rng.standard_normal((3, 96)).astype(np.float32))
+    w = oracle.dequant_q8_0(blocks)
+    assert w.shape == (3, 96)
+    for r in range(3):
+        for b in range(3):
+            d = fp16_bits_to_float(int(blocks[r, b, 0]) | (int(blocks[r, b, 1]) << 8))
+            q = blocks[r, b, 2:].view(np.int8).astype(np.float64)
+            np.testing.assert_array_equal(w[r, 32 * b:32 * b + 32], d * q)
+
+
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+def test_round_trip_extreme_code(qt):
+    """quantise(dequant(b)) == b for blocks holding the extreme code."""
+    rng = np.random.default_rng(7)
+    quant = gi.quantize_q8_0 if qt == "q8_0" else gi.quantize_q4_0
+    for trial in range(200):
+        d_bits = int(rng.integers(0x0400, 0x5800))  # positive normal fp16 scales
+        if qt == "q4_0" and trial % 2:
+            d_bits |= 0x8000  # negative scales are legal in q4_0
+        if qt == "q8_0":
+            codes = rng.integers(-127, 128, 32)
+            codes[rng.integers(32)] = 127 if trial % 2 else -127
+        else:
+            codes = rng.integers(1, 16, 32)
+            codes[rng.integers(32)] = 0
+        blk = build_block(qt, d_bits, codes.tolist())[None, None, :]
+        w = oracle.dequant(qt, blk).astype(np.float32)
+        again = quant(w)
+        np.testing.assert_array_equal(again, blk)
+
+
+# ---------------------------------------------------------------- router
+def test_router_logits_loop():
+    rng = np.random.default_rng(11)
+    T, H, E = 3, 7, 5
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = rng.standard_normal((E, H)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    got = oracle.router_logits(x, wr, b)
+    assert got.shape == (T, E)
+    for t in range(T):
+        for e in range(E):
+            want = math.fsum(float(x[t, h]) * float(wr[e, h]) for h in range(H)) + float(b[e])
+            assert abs(got[t, e] - want) <= 1e-12 * (1 + abs(want))
+
+
+def test_softmax_properties():
+    rng = np.random.default_rng(5)
+    l = rng.standard_normal((6, 9)) * 4
+    p = oracle.softmax(l)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(oracle.softmax(l + 123.0), p, rtol=1e-13)
+    # closed form on a 2-vector: logistic function
+    a = oracle.softmax(np.array([[0.3, -1.2]]))[0, 0]
+    assert abs(a - 1.0 / (1.0 + math.exp(-1.5))) < 1e-15
+
+
+def _brute_topk(row, k):
+    """Best k-subset by lexicographic (logit desc, id asc) order, by enumeration."""
+    E = len(row)
+    keyed = sorted(range(E), key=lambda e: (-float(row[e]), e))
+    best = None
+    for sub in itertools.combinations(range(E), k):
+        # a subset is the top-k iff no outside element beats an inside one
+        ok = all((-float(row[o]), o) > (-float(row[i]), i)
+                 for o in range(E) if o not in sub for i in sub)
+        if ok:
+            assert best is None
+            best = sub
+    assert best is not None
+    return sorted(best, key=lambda e: (-float(row[e]), e)), keyed[:k]
+
+
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(17)
+    for trial in range(60):
+        E = int(rng.integers(2, 8))
+        k = int(rng.integers(1, E + 1))
+        row = rng.integers(-2, 3, E).astype(np.float32)  # many exact ties
+        if trial % 3 == 0:
+            row = rng.standard_normal(E).astype(np.float32)
+        got = oracle.topk_select(row[None, :], k)[0].tolist()
+        want, _ = _brute_topk(row, k)
+        assert got == want, (row, k)
+
+
+def test_topk_planted_ties_lower_id_wins():
+    l = np.array([[0.5, 2.0, 2.0, -1.0, 2.0, 0.5]], dtype=np.float32)
+    assert oracle.topk_select(l, 2)[0].tolist() == [1, 2]
+    assert oracle.topk_select(l, 4)[0].tolist() == [1, 2, 4, 0]
+    # -0.0 and +0.0 compare equal: lower id first
+    z = np.array([[0.0, -0.0, -1.0]], dtype=np.float32)
+    z[0, 0] = -0.0
+    z[0, 1] = 0.0
+    assert oracle.topk_select(z, 2)[0].tolist() == [0, 1]
+
+
+def test_topk_decides_in_fp32():
+    """Two float64 logits that round to one fp32 value tie -> lower id."""
+    a = 1.0
+    b = 1.0 + 2.0 ** -30  # larger in float64, equal in fp32
+    assert np.float32(a) == np.float32(b)
+    assert oracle.topk_select(np.array([[a, b]]), 1)[0].tolist() == [0]
+
+
+def test_renormalised_weights():
+    rng = np.random.default_rng(19)
+    l = rng.standard_normal((50, 16)) * 3
+    for k in (1, 3, 8, 16):
+        ids, w = oracle.route(l, k)
+        np.testing.assert_allclose(w.sum(-1), 1.0, rtol=0, atol=k * 2.0 ** -52 * 4)
+        assert np.all(w > 0)
+        # weights follow the ids' order: non-increasing
+        assert np.all(np.diff(w, axis=-1) <= 1e-15)
+    ids, w = oracle.route(l, 16)  # k == E: renormalisation is the softmax itself
+    p = oracle.softmax(l)
+    np.testing.assert_allclose(w, np.take_along_axis(p, ids.astype(int), -1), rtol=1e-14)
+    ids, w = oracle.route(l, 1)
+    np.testing.assert_array_equal(w, 1.0)
+    # closed form for k = 2: w0 = 1 / (1 + exp(l1 - l0))
+    ids, w = oracle.route(l, 2)
+    r = np.take_along_axis(l, ids.astype(int), -1)
+    np.testing.assert_allclose(w[:, 0], 1.0 / (1.0 + np.exp(r[:, 1] - r[:, 0])), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- permute
+def test_permute_matches_stable_argsort():
+    rng = np.random.default_rng(23)
+    for T, k, E in [(1, 1, 1), (4, 2, 8), (16, 8, 128), (7, 3, 5), (33, 10, 512)]:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        off, sp, pos, active = oracle.permute(ids, E)
+        flat = ids.ravel()
+        np.testing.assert_array_equal(sp, np.argsort(flat, kind="stable"))
+        np.testing.assert_array_equal(np.bincount(flat, minlength=E), np.diff(off))
+        assert off[0] == 0 and off[-1] == T * k
+        np.testing.assert_array_equal(sp[pos], np.arange(T * k))  # inverse map
+        np.testing.assert_array_equal(active, np.flatnonzero(np.bincount(flat, minlength=E)))
+        data = rng.standard_normal(T * k)
+        np.testing.assert_array_equal(data[sp][pos], data)  # gather then scatter
+
+
+def test_permute_duplicates_stable():
+    ids = np.array([[2, 0], [2, 1], [0, 2]], dtype=np.int32)
+    off, sp, pos, active = oracle.permute(ids, 3)
+    assert off.tolist() == [0, 2, 3, 6]
+    assert sp.tolist() == [1, 4, 3, 0, 2, 5]  # p -> e: 0->2 1->0 2->2 3->1 4->0 5->2
+    assert active.tolist() == [0, 1, 2]
+
+
+# ---------------------------------------------------------------- FFN and combine
+def _dense_ffn_loops(x, wg, wu, wd):
+    """SwiGLU FFN by explicit loops: silu on the gate projection, times up."""
+    H, I = wd.shape
+    g = [math.fsum(wg[i, h] * x[h] for h in range(H)) for i in range(I)]
+    u = [math.fsum(wu[i, h] * x[h] for h in range(H)) for i in range(I)]
+    a = [gi_ / (1.0 + math.exp(-gi_)) * ui for gi_, ui in zip(g, u)]
+    return np.array([math.fsum(wd[h, i] * a[i] for i in range(I)) for h in range(H)])
+
+
+def test_silu_special_values():
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(oracle.silu(np.array([40.0])), 40.0, rtol=1e-15)
+    assert abs(oracle.silu(np.array([-40.0]))[0]) < 1e-15
+    z = 0.7
+    assert abs(oracle.silu(np.array([z]))[0] - z / (1 + math.exp(-z))) < 1e-16
+
+
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+def test_single_expert_k1_is_dense_ffn(qt):
+    """E = 1, k = 1: the layer is the dense SwiGLU FFN of that expert (w = 1)."""
+    rng = np.random.default_rng(29)
+    H, I, T = 64, 96, 3
+    quant = gi.quantize_q8_0 if qt == "q8_0" else gi.quantize_q4_0
+    blocks = (quant((rng.standard_normal((I, H)) * 0.1).astype(np.float32)),
+              quant((rng.standard_normal((I, H)) * 0.1).astype(np.float32)),
+              quant((rng.standard_normal((H, I)) * 0.1).astype(np.float32)))
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    res = oracle.moe_layer(x, qt, lambda e: blocks, 1,
+                           logits=rng.standard_normal((T, 1)))
+    np.testing.assert_array_equal(res["w"], 1.0)
+    wg, wu, wd = (oracle.dequant(qt, b) for b in blocks)
+    for t in range(T):
+        want = _dense_ffn_loops(x[t].astype(np.float64), wg, wu, wd)
+        np.testing.assert_allclose(res["out"][t], want, rtol=1e-12, atol=1e-12)
+
+
+def test_combine_one_hot_is_gather():
+    rng = np.random.default_rng(31)
+    T, k, H = 5, 3, 4  # T != k so a transposed index fails
+    y = rng.standard_normal((T * k, H))
+    w = np.zeros((T, k))
+    pick = rng.integers(0, k, T)
+    w[np.arange(T), pick] = 1.0
+    out = oracle.combine(y, w)
+    np.testing.assert_array_equal(out, y[np.arange(T) * k + pick])
+    w2 = rng.random((T, k))
+    want = np.stack([sum(w2[t, j] * y[t * k + j] for j in range(k)) for t in range(T)])
+    np.testing.assert_allclose(oracle.combine(y, w2), want, rtol=1e-15)
+
+
+def test_layer_permutation_invariance_of_expert_labels():
+    """Relabelling experts (permuting router rows and banks) leaves out unchanged."""
+    rng = np.random.default_rng(37)
+    H, I, E, k, T = 32, 64, 6, 2, 5
+    banks = [tuple(gi.quantize_q8_0((rng.standard_normal(s) * 0.05).astype(np.float32))
+                   for s in ((I, H), (I, H), (H, I))) for _ in range(E)]
+    wr = rng.standard_normal((E, H)).astype(np.float32)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    a = oracle.moe_layer(x, "q8_0", lambda e: banks[e], k, router_w=wr)
+    perm = rng.permutation(E)
+    b = oracle.moe_layer(x, "q8_0", lambda e: banks[perm[e]], k, router_w=wr[perm])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- LRU
+def _ordered_dict_lru(trace, capacity):
+    cache = collections.OrderedDict()
+    hits = np.zeros(trace.shape, dtype=bool)
+    for s in range(trace.shape[0]):
+        for l in range(trace.shape[1]):
+            protect = set()
+            for j in range(trace.shape[2]):
+                key = (l, int(trace[s, l, j]))
+                if key in cache:
+                    hits[s, l, j] = True
+                    cache.move_to_end(key)
+                else:
+                    if len(cache) >= capacity:
+                        for victim in cache:  # oldest first
+                            if victim not in protect:
+                                break
+                        del cache[victim]
+                    cache[key] = True
+                protect.add(key)
+    return hits
+
+
+def test_lru_hand_trace():
+    # capacity 3, one layer, two lookups per step
+    trace = np.array([[[0, 1]], [[2, 0]], [[3, 1]], [[0, 2]]], dtype=np.int32)
+    hit, ev = oracle.lru_simulate(trace, 3)
+    assert hit.reshape(-1).tolist() == [False, False, False, True, False, False, True, False]
+    # step 2: 3 evicts key 1 (LRU), then 1 evicts 2; step 3: 0 hit, 2 evicts 3
+    assert [e[2] for e in ev] == [(0, 1), (0, 2), (0, 3)]
+
+
+def test_lru_matches_ordered_dict_simulation():
+    wl = gi.workload(5)
+    trace = gi.cache_trace(wl, steps=96)
+    for cap in (8, 20, 100, 816):
+        hit, _ = oracle.lru_simulate(trace, cap)
+        np.testing.assert_array_equal(hit, _ordered_dict_lru(trace, cap))
+
+
+def test_lru_protects_current_layer_keys():
+    trace = np.array([[[0, 1, 2]], [[3, 4, 5]]], dtype=np.int32)
+    hit, ev = oracle.lru_simulate(trace, 3)
+    assert not hit.any()
+    assert [e[2] for e in ev] == [(0, 0), (0, 1), (0, 2)]
+    with pytest.raises(ValueError):
+        oracle.lru_simulate(trace, 2)
