@@ -1,0 +1,87 @@
+"""Build libmoe.so in-tree for gfx950.
+
+Every source under ``csrc/`` is compiled with ``hipcc --offload-arch=gfx950``
+and the objects are linked against the HIP runtime that PyTorch ships
+(``torch/lib/libamdhip64.so``), so that the library and PyTorch share one
+HIP runtime, one device context and one set of streams in the process.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+CLANGXX = os.path.join(ROCM, "llvm", "bin", "clang++")
+
+COMMON_FLAGS = [
+    "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    # keep the compiler from forming packed fp32 VALU ops
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics",
+]
+
+
+def _torch_lib_dir() -> str:
+    import torch  # noqa: WPS433 (build-time only)
+    return os.path.join(os.path.dirname(torch.__file__), "lib")
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if p.returncode != 0:
+        raise RuntimeError("command failed:\n  " + " ".join(cmd) + "\n" + p.stdout)
+    return p.stdout
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source and link libmoe.so.  Returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+
+    def compile_one(src):
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        if src.endswith(".hip"):
+            cmd = [HIPCC, "-c", "-x", "hip", src, "-o", obj] + COMMON_FLAGS + HIP_FLAGS
+        else:
+            cmd = [HIPCC, "-c", src, "-o", obj] + COMMON_FLAGS
+        out = _run(cmd)
+        if verbose and out.strip():
+            print(out)
+        return obj
+
+    with ThreadPoolExecutor(max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    tlib = _torch_lib_dir()
+    tmp = LIB_PATH + ".tmp"
+    cmd = [CLANGXX, "-shared", "-fPIC", "-o", tmp] + objs + [
+        "-L", tlib, "-l:libamdhip64.so", "-Wl,-rpath," + tlib, "-Wl,--no-undefined",
+        "-lstdc++", "-lm", "-lpthread",
+    ]
+    out = _run(cmd)
+    if verbose and out.strip():
+        print(out)
+    shutil.move(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,300 @@
+// Expert cache: a global LRU over (layer, expert) keys backed by a device
+// slot pool, with the full expert pool in pinned host memory.
+//
+// FreeToken treats VRAM as a cache over the host-resident pool and streams
+// only missing experts over PCIe ("FreeToken Inference Engine: 3x Speed
+// Boost for MoE Models", sections "From Static Allocation to Dynamic
+// Scheduling" and "RTX 5090 Benchmark"); the cache is one global LRU
+// (FreeToken fork README, "About"; setup guide: a shared LRU follows
+// token-level routing locality).
+//
+// Slots.  The device pool has n_slots + 2 slots.  At most n_slots keys are
+// resident; free slots wait in a FIFO, so the slot a miss is copied into was
+// released at least two evictions earlier (ping-pong staging): its last
+// reader has normally long finished, and the copy still waits on that
+// reader's event before overwriting it.
+//
+// Order of LRU updates.  cache_slot_table_lookup applies the layer's ids in
+// order: a hit refreshes the key; a miss evicts the least recently used key
+// not looked up earlier in this (step, layer) and inserts the new key at
+// once, with its destination slot.  prefetch_expert then moves the bytes
+// and installs the slot in the device table in stream order.
+#include <algorithm>
+#include <set>
+#include <unordered_map>
+#include <vector>
+
+#include "device_common.h"
+
+namespace moe {
+
+constexpr int kTableUpdates = 16;
+struct TableUpdate {
+  int n;
+  int idx[kTableUpdates];
+  int val[kTableUpdates];
+};
+
+__global__ void table_update_kernel(int32_t* table, TableUpdate u) {
+  const int i = threadIdx.x;
+  if (i < u.n) table[u.idx[i]] = u.val[i];
+}
+
+constexpr int kEventRing = 256;
+
+}  // namespace moe
+
+using namespace moe;
+
+struct moe_cache {
+  int device = 0;
+  int L = 0, E = 0, n_slots = 0, qtype = 0, H = 0, I = 0;
+  size_t slot_bytes = 0;
+  uint8_t* d_pool = nullptr;
+  const uint8_t* h_pool = nullptr;
+  int32_t* d_table = nullptr;            // [L][E]
+  std::vector<int32_t> table;            // host shadow: key -> slot or -1
+  std::vector<int> slot_key;             // slot -> key or -1
+  std::vector<uint64_t> stamp;           // key -> recency stamp
+  std::vector<uint64_t> protect;         // key -> lookup epoch
+  std::set<std::pair<uint64_t, int>> lru;  // (stamp, key) of resident keys
+  std::vector<int> free_fifo;            // free slots, oldest release first
+  size_t free_head = 0;
+  struct Pending { int slot; int victim_key; };
+  std::unordered_map<int, Pending> pending;  // key -> destination (copy not issued)
+  std::vector<int> slot_event;           // slot -> index into events or -1
+  std::vector<int> layer_slots;          // slots touched by the current lookup
+  hipEvent_t events[kEventRing] = {};       // layer-done events (compute stream)
+  hipEvent_t copy_events[kEventRing] = {};  // copy-done events (copy streams)
+  int next_event = 0, next_copy_event = 0;
+  uint64_t clock = 0, epoch = 0;
+  int64_t hits = 0, misses = 0;
+};
+
+static int pop_free(moe_cache* c) {
+  if (c->free_head >= c->free_fifo.size()) return -1;
+  const int s = c->free_fifo[c->free_head++];
+  if (c->free_head > 4096 && c->free_head * 2 > c->free_fifo.size()) {
+    c->free_fifo.erase(c->free_fifo.begin(), c->free_fifo.begin() + (long)c->free_head);
+    c->free_head = 0;
+  }
+  return s;
+}
+
+extern "C" {
+
+int cache_slot_table_destroy(moe_cache* c);
+
+int cache_slot_table_create(int L, int E, int n_slots, int qtype, int H, int I, void* d_pool,
+                            const void* h_pool, moe_cache** out) {
+  clear_error();
+  if (!out) return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_create: out is NULL");
+  if (!qtype_supported(qtype))
+    return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "cache_slot_table_create: block type %d is not supported", qtype);
+  if (L < 1 || E < 1 || E > kMaxE || n_slots < 1)
+    return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_create: L=%d E=%d n_slots=%d", L, E, n_slots);
+  if (H <= 0 || I <= 0 || H % kGroupWeights || I % kGroupWeights)
+    return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_create: H=%d I=%d must be multiples of %d", H, I,
+                     kGroupWeights);
+  if (!d_pool || !h_pool) return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_create: NULL pool");
+  if (!aligned(d_pool, 16)) return set_error(MOE_ERR_ALIGNMENT, "cache_slot_table_create: d_pool not 16-byte aligned");
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, h_pool);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return set_error(MOE_ERR_NOT_PINNED,
+                     "cache_slot_table_create: the host expert pool is not pinned (allocate it with hipHostMalloc)");
+  }
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_error(e, "hipGetDevice");
+  moe_cache* c = new moe_cache;
+  c->device = dev;
+  c->L = L; c->E = E; c->n_slots = n_slots; c->qtype = qtype; c->H = H; c->I = I;
+  c->slot_bytes = slot_bytes_of(qtype, H, I);
+  c->d_pool = (uint8_t*)d_pool;
+  c->h_pool = (const uint8_t*)h_pool;
+  const int keys = L * E;
+  c->table.assign(keys, -1);
+  c->stamp.assign(keys, 0);
+  c->protect.assign(keys, 0);
+  c->slot_key.assign(n_slots + 2, -1);
+  c->slot_event.assign(n_slots + 2, -1);
+  for (int s = 0; s < n_slots + 2; ++s) c->free_fifo.push_back(s);
+  if ((e = hipMalloc(&c->d_table, sizeof(int32_t) * keys)) != hipSuccess) {
+    delete c;
+    return hip_error(e, "hipMalloc(slot table)");
+  }
+  if ((e = hipMemcpy(c->d_table, c->table.data(), sizeof(int32_t) * keys, hipMemcpyHostToDevice)) != hipSuccess) {
+    (void)hipFree(c->d_table);
+    delete c;
+    return hip_error(e, "hipMemcpy(slot table)");
+  }
+  for (int i = 0; i < 2 * kEventRing; ++i) {
+    hipEvent_t* ev = i < kEventRing ? &c->events[i] : &c->copy_events[i - kEventRing];
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) {
+      cache_slot_table_destroy(c);
+      return hip_error(e, "hipEventCreate");
+    }
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+int cache_slot_table_destroy(moe_cache* c) {
+  clear_error();
+  if (!c) return MOE_OK;
+  (void)hipDeviceSynchronize();
+  for (int i = 0; i < kEventRing; ++i) {
+    if (c->events[i]) (void)hipEventDestroy(c->events[i]);
+    if (c->copy_events[i]) (void)hipEventDestroy(c->copy_events[i]);
+  }
+  if (c->d_table) (void)hipFree(c->d_table);
+  delete c;
+  return MOE_OK;
+}
+
+const int32_t* cache_slot_table_device(moe_cache* c) { return c ? c->d_table : nullptr; }
+
+int cache_slot_table_stats(moe_cache* c, int64_t* hits, int64_t* misses) {
+  clear_error();
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_stats: cache is NULL");
+  if (hits) *hits = c->hits;
+  if (misses) *misses = c->misses;
+  return MOE_OK;
+}
+
+int cache_slot_table_lookup(moe_cache* c, int layer, const int32_t* ids, int n, int32_t* slots_out,
+                            int32_t* miss_ids, int* n_miss) {
+  clear_error();
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_lookup: cache is NULL");
+  if (layer < 0 || layer >= c->L || n < 0 || (n > 0 && (!ids || !slots_out)) || !n_miss)
+    return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_lookup: layer=%d n=%d", layer, n);
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= c->E)
+      return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_lookup: expert id %d of layer %d not in [0, %d)",
+                       ids[i], layer, c->E);
+  {
+    std::vector<int32_t> distinct(ids, ids + n);
+    std::sort(distinct.begin(), distinct.end());
+    const long nd = std::unique(distinct.begin(), distinct.end()) - distinct.begin();
+    if (nd > c->n_slots)
+      return set_error(MOE_ERR_CAPACITY, "cache_slot_table_lookup: layer %d needs %ld distinct experts, cache holds %d",
+                       layer, nd, c->n_slots);
+  }
+  if (!c->layer_slots.empty())
+    return set_error(MOE_ERR_INVALID_ARG,
+                     "cache_slot_table_lookup: the previous lookup's layer was not marked done "
+                     "(cache_mark_layer_done) so its slots could be overwritten while in use");
+  ++c->epoch;
+  int nm = 0;
+  for (int i = 0; i < n; ++i) {
+    const int key = layer * c->E + ids[i];
+    ++c->clock;
+    if (c->table[key] >= 0) {
+      ++c->hits;
+      c->lru.erase({c->stamp[key], key});
+    } else {
+      ++c->misses;
+      int victim = -1;
+      if ((int)c->lru.size() >= c->n_slots) {
+        for (auto it = c->lru.begin(); it != c->lru.end(); ++it) {
+          if (c->protect[it->second] != c->epoch) {
+            victim = it->second;
+            break;
+          }
+        }
+        if (victim < 0)
+          return set_error(MOE_ERR_CAPACITY,
+                           "cache_slot_table_lookup: all %d slots hold experts of layer %d's current lookup",
+                           c->n_slots, layer);
+        const int vs = c->table[victim];
+        c->lru.erase({c->stamp[victim], victim});
+        c->table[victim] = -1;
+        c->slot_key[vs] = -1;
+        c->free_fifo.push_back(vs);
+        auto pv = c->pending.find(victim);
+        if (pv != c->pending.end()) c->pending.erase(pv);  // evicted before its copy was issued
+      }
+      const int s = pop_free(c);
+      c->table[key] = s;
+      c->slot_key[s] = key;
+      c->pending[key] = moe_cache::Pending{s, victim};
+      if (miss_ids) {
+        bool seen = false;
+        for (int m = 0; m < nm; ++m) seen |= miss_ids[m] == ids[i];
+        if (!seen) miss_ids[nm++] = ids[i];
+      } else {
+        ++nm;
+      }
+    }
+    c->stamp[key] = c->clock;
+    c->protect[key] = c->epoch;
+    c->lru.insert({c->clock, key});
+    slots_out[i] = c->table[key];
+    c->layer_slots.push_back(c->table[key]);
+  }
+  *n_miss = nm;
+  return MOE_OK;
+}
+
+int prefetch_expert(moe_cache* c, int layer, int expert, void* copy_stream, void* compute_stream,
+                    int32_t* slot_out) {
+  clear_error();
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "prefetch_expert: cache is NULL");
+  if (layer < 0 || layer >= c->L || expert < 0 || expert >= c->E)
+    return set_error(MOE_ERR_INVALID_ARG, "prefetch_expert: layer=%d expert=%d", layer, expert);
+  const int key = layer * c->E + expert;
+  auto it = c->pending.find(key);
+  if (it == c->pending.end()) {
+    if (c->table[key] < 0)
+      return set_error(MOE_ERR_NOT_RESIDENT,
+                       "prefetch_expert: layer %d expert %d was not looked up (no destination slot)", layer, expert);
+    if (slot_out) *slot_out = c->table[key];
+    return MOE_OK;  // resident already
+  }
+  const moe_cache::Pending pd = it->second;
+  c->pending.erase(it);
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_error(e, "hipSetDevice");
+  hipStream_t cs = (hipStream_t)copy_stream, ks = (hipStream_t)compute_stream;
+  // the slot's previous reader must be done before the copy overwrites it
+  if (c->slot_event[pd.slot] >= 0) {
+    if ((e = hipStreamWaitEvent(cs, c->events[c->slot_event[pd.slot]], 0)) != hipSuccess)
+      return hip_error(e, "hipStreamWaitEvent(copy)");
+  }
+  if ((e = hipMemcpyAsync(c->d_pool + (size_t)pd.slot * c->slot_bytes, c->h_pool + (size_t)key * c->slot_bytes,
+                          c->slot_bytes, hipMemcpyHostToDevice, cs)) != hipSuccess)
+    return hip_error(e, "hipMemcpyAsync(expert)");
+  hipEvent_t done = c->copy_events[c->next_copy_event];
+  c->next_copy_event = (c->next_copy_event + 1) % kEventRing;
+  if ((e = hipEventRecord(done, cs)) != hipSuccess) return hip_error(e, "hipEventRecord(copy)");
+  if ((e = hipStreamWaitEvent(ks, done, 0)) != hipSuccess) return hip_error(e, "hipStreamWaitEvent(compute)");
+  TableUpdate u{};
+  u.idx[u.n] = key; u.val[u.n] = pd.slot; ++u.n;
+  if (pd.victim_key >= 0 && c->table[pd.victim_key] < 0) {
+    u.idx[u.n] = pd.victim_key; u.val[u.n] = -1; ++u.n;
+  }
+  table_update_kernel<<<1, 64, 0, ks>>>(c->d_table, u);
+  int rc = check_launch("table_update_kernel");
+  if (rc) return rc;
+  if (slot_out) *slot_out = pd.slot;
+  return MOE_OK;
+}
+
+int cache_mark_layer_done(moe_cache* c, int layer, void* compute_stream) {
+  clear_error();
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "cache_mark_layer_done: cache is NULL");
+  if (layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID_ARG, "cache_mark_layer_done: layer=%d", layer);
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_error(e, "hipSetDevice");
+  const int ev = c->next_event;
+  c->next_event = (c->next_event + 1) % kEventRing;
+  if ((e = hipEventRecord(c->events[ev], (hipStream_t)compute_stream)) != hipSuccess)
+    return hip_error(e, "hipEventRecord(layer done)");
+  for (int s : c->layer_slots) c->slot_event[s] = ev;
+  c->layer_slots.clear();
+  ++c->epoch;  // the layer's keys are no longer protected
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Weighted combine of the per-pair expert outputs back to token order, and
+// the block dequantisation entry point used by the exact-parity checks.
+#include "device_common.h"
+
+namespace moe {
+
+// out[t][h] = sum over j ascending of w[t][j] * y[t*k + j][h].
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const float* __restrict__ w, int k, int H,
+                                                      float* __restrict__ out) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.y;
+  if (h >= H) return;
+  float acc = 0.0f;
+  for (int j = 0; j < k; ++j) acc = fmaf(w[(size_t)t * k + j], y[((size_t)t * k + j) * H + h], acc);
+  out[(size_t)t * H + h] = acc;
+}
+
+// One thread per block of 32 weights: exact d*q (or d*(q-8)) in fp32.
+template <int QT, bool BF16>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ packed, int rows,
+                                                      int cols, void* __restrict__ out) {
+  const int nblk = cols / kQK;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)rows * nblk) return;
+  const int r = (int)(idx / nblk), b = (int)(idx % nblk);
+  const uint8_t* row = packed + (size_t)r * row_bytes(QT, cols);
+  float q[32];
+  block_codes<QT>(row, b, q);
+  const float d = block_scale<QT>(row, b);
+  if constexpr (BF16) {
+    uint16_t* o = (uint16_t*)out + (size_t)r * cols + b * kQK;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) o[i] = f32_to_bf16_rne(d * q[i]);
+  } else {
+    float* o = (float*)out + (size_t)r * cols + b * kQK;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) o[i] = d * q[i];
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_combine(moe_ctx* ctx, const float* y_pairs, const float* topk_w, int T, int k,
+                           int H, float* out, void* stream) {
+  clear_error();
+  if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_combine: ctx is NULL");
+  if (T < 0 || k < 1 || H < 1)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_combine: need T >= 0, k >= 1, H >= 1 (T=%d k=%d H=%d)", T, k, H);
+  if (T == 0) return MOE_OK;
+  if (T > 65535) return set_error(MOE_ERR_INVALID_ARG, "moe_combine: T=%d above 65535", T);
+  if (!y_pairs || !topk_w || !out) return set_error(MOE_ERR_INVALID_ARG, "moe_combine: NULL buffer");
+  int rc = ensure_device(ctx);
+  if (rc) return rc;
+  dim3 grid((H + 255) / 256, T);
+  combine_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(y_pairs, topk_w, k, H, out);
+  return check_launch("combine_kernel");
+}
+
+extern "C" int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int rows, int cols,
+                              int out_dtype, void* out, void* stream) {
+  clear_error();
+  if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_dequantize: ctx is NULL");
+  if (!qtype_supported(qtype))
+    return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "moe_dequantize: block type %d is not supported", qtype);
+  if (rows < 0 || cols <= 0 || cols % kGroupWeights)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_dequantize: rows=%d cols=%d (cols a multiple of %d)", rows,
+                     cols, kGroupWeights);
+  if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_dequantize: out_dtype %d unknown", out_dtype);
+  if (rows == 0) return MOE_OK;
+  if (!packed || !out) return set_error(MOE_ERR_INVALID_ARG, "moe_dequantize: NULL buffer");
+  if (!aligned(packed, 16)) return set_error(MOE_ERR_ALIGNMENT, "moe_dequantize: packed must be 16-byte aligned");
+  int rc = ensure_device(ctx);
+  if (rc) return rc;
+  const long long n = (long long)rows * (cols / kQK);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  hipStream_t s = (hipStream_t)stream;
+  if (qtype == MOE_QTYPE_Q8_0) {
+    if (out_dtype == MOE_DTYPE_F32) dequant_kernel<MOE_QTYPE_Q8_0, false><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
+    else dequant_kernel<MOE_QTYPE_Q8_0, true><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
+  } else {
+    if (out_dtype == MOE_DTYPE_F32) dequant_kernel<MOE_QTYPE_Q4_0, false><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
+    else dequant_kernel<MOE_QTYPE_Q4_0, true><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
+  }
+  return check_launch("dequant_kernel");
+}

@@ -1,0 +1,84 @@
+// moe_expert_ffn: validation and dispatch of the expert-FFN kernels.
+#include <algorithm>
+
+#include "ffn.h"
+
+namespace moe {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static size_t ffn_ws_bytes(const moe_ffn_args* a) {
+  return align_up((size_t)a->T * a->k * a->I * sizeof(float), 256);
+}
+
+static int validate_ffn(const moe_ffn_args* a, bool need_buffers) {
+  if (!a) return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: args is NULL");
+  if (!qtype_supported(a->qtype))
+    return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "moe_expert_ffn: block type %d is not supported", a->qtype);
+  if (a->H <= 0 || a->I <= 0 || a->H % kGroupWeights || a->I % kGroupWeights)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: H=%d and I=%d must be positive multiples of %d",
+                     a->H, a->I, kGroupWeights);
+  if (a->T < 0 || a->E < 1 || a->E > kMaxE || a->k < 1 || a->k > a->E)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: need T >= 0, 1 <= k <= E <= %d (T=%d k=%d E=%d)",
+                     kMaxE, a->T, a->k, a->E);
+  if (a->mode != MOE_MODE_DECODE && a->mode != MOE_MODE_PREFILL)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: mode %d unknown", a->mode);
+  if (a->x_dtype != MOE_DTYPE_F32 && a->x_dtype != MOE_DTYPE_BF16)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: x_dtype %d unknown", a->x_dtype);
+  if (a->mode == MOE_MODE_DECODE && a->x_dtype != MOE_DTYPE_F32)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: decode mode takes fp32 activations");
+  if (a->slot_bytes < slot_bytes_of(a->qtype, a->H, a->I))
+    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: slot_bytes %zu below one %s expert (%zu)",
+                     a->slot_bytes, qtype_name(a->qtype), slot_bytes_of(a->qtype, a->H, a->I));
+  if (a->n_slots < 1) return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_slots=%d", a->n_slots);
+  if (a->slot_bytes % 16)
+    return set_error(MOE_ERR_ALIGNMENT, "moe_expert_ffn: slot_bytes must be a multiple of 16");
+  if (!need_buffers || a->T == 0) return MOE_OK;
+  if (!a->pool_base || !a->slot_table || !a->x || !a->expert_offsets || !a->sorted_pairs ||
+      !a->active || !a->y_pairs)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: NULL buffer in args");
+  if (!aligned(a->pool_base, 16) || !aligned(a->x, 16) || !aligned(a->y_pairs, 16))
+    return set_error(MOE_ERR_ALIGNMENT, "moe_expert_ffn: pool_base, x and y_pairs must be 16-byte aligned");
+  if (a->ws_bytes < ffn_ws_bytes(a) || (ffn_ws_bytes(a) && !a->ws))
+    return set_error(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace holds %zu bytes, needs %zu",
+                     a->ws_bytes, ffn_ws_bytes(a));
+  if (!aligned(a->ws, 256)) return set_error(MOE_ERR_ALIGNMENT, "moe_expert_ffn: ws must be 256-byte aligned");
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_expert_ffn_workspace_size(const moe_ffn_args* args, size_t* bytes) {
+  clear_error();
+  int rc = validate_ffn(args, false);
+  if (rc) return rc;
+  if (!bytes) return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn_workspace_size: bytes is NULL");
+  *bytes = ffn_ws_bytes(args);
+  return MOE_OK;
+}
+
+extern "C" int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* a, void* stream) {
+  clear_error();
+  if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: ctx is NULL");
+  int rc = validate_ffn(a, true);
+  if (rc) return rc;
+  if (a->T == 0) return MOE_OK;
+  if ((rc = ensure_device(ctx))) return rc;
+  FfnParams p;
+  p.pool = (const uint8_t*)a->pool_base;
+  p.slot_bytes = a->slot_bytes;
+  p.n_slots = a->n_slots;
+  p.qtype = a->qtype;
+  p.H = a->H; p.I = a->I; p.T = a->T; p.k = a->k; p.E = a->E;
+  p.slot_table = a->slot_table;
+  p.offsets = a->expert_offsets;
+  p.sorted_pairs = a->sorted_pairs;
+  p.active = a->active;
+  p.mask = a->expert_mask;
+  p.y = a->y_pairs;
+  p.hbuf = (float*)a->ws;
+  p.err = ctx->d_err;
+  return launch_ffn_valu(p, a->x, a->x_dtype, 8 * ctx->num_cus, (hipStream_t)stream);
+}

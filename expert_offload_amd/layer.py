@@ -1,0 +1,88 @@
+"""Run one MoE layer forward through libmoe's entry points.
+
+``LayerBuffers`` owns the device buffers of one batch size; ``forward``
+issues moe_route -> moe_permute -> moe_expert_ffn -> moe_combine on one
+stream.  ``pack_expert`` / ``SlotPool`` move ggml blocks (host) into the
+device slot layout (libmoe's packer) and into a device slot pool.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def pack_expert(qtype: str, H: int, I: int, gate, up, down) -> np.ndarray:
+    """ggml blocks (host) -> one slot in the device layout (host uint8)."""
+    q = L.QTYPE[qtype]
+    out = np.empty(L.moe_slot_bytes(q, H, I), dtype=np.uint8)
+    L.moe_pack_expert(q, H, I, np.ascontiguousarray(gate), np.ascontiguousarray(up),
+                      np.ascontiguousarray(down), out)
+    return out
+
+
+class SlotPool:
+    """A device slot pool of ``n_slots`` experts of one block type."""
+
+    def __init__(self, qtype: str, H: int, I: int, n_slots: int, device="cuda"):
+        self.qtype, self.H, self.I, self.n_slots = qtype, H, I, n_slots
+        self.q = L.QTYPE[qtype]
+        self.slot_bytes = L.moe_slot_bytes(self.q, H, I)
+        self.data = torch.empty(n_slots * self.slot_bytes, dtype=torch.uint8, device=device)
+
+    def base(self, first_slot: int = 0) -> int:
+        return self.data.data_ptr() + first_slot * self.slot_bytes
+
+    def put(self, slot: int, packed: np.ndarray) -> None:
+        dst = self.data[slot * self.slot_bytes:(slot + 1) * self.slot_bytes]
+        dst.copy_(torch.from_numpy(packed))
+
+
+class LayerBuffers:
+    """Device buffers for one layer forward over T tokens."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, qtype: str, device="cuda",
+                 mode: int = L.MODE_DECODE, x_dtype: int = L.DTYPE_F32):
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.q = L.QTYPE[qtype]
+        self.mode, self.x_dtype = mode, x_dtype
+        P = max(T * k, 1)
+        i32, f32 = torch.int32, torch.float32
+        self.logits = torch.empty((max(T, 1), E), dtype=f32, device=device)
+        self.ids = torch.empty((max(T, 1), k), dtype=i32, device=device)
+        self.w = torch.empty((max(T, 1), k), dtype=f32, device=device)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=device)
+        self.sorted_pairs = torch.empty(P, dtype=i32, device=device)
+        self.pair_pos = torch.empty(P, dtype=i32, device=device)
+        self.active = torch.empty(E + 1, dtype=i32, device=device)
+        self.y = torch.empty((P, H), dtype=f32, device=device)
+        self.out = torch.empty((max(T, 1), H), dtype=f32, device=device)
+        probe = L.moe_ffn_args(qtype=self.q, H=H, I=I, T=T, k=k, E=E, mode=mode, x_dtype=x_dtype, n_slots=1,
+                               slot_bytes=L.moe_slot_bytes(self.q, H, I))
+        self.ws_bytes = L.moe_expert_ffn_workspace_size(probe)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+
+
+def forward(ctx: L.Ctx, buf: LayerBuffers, pool_base: int, slot_bytes: int, n_slots: int, slot_table, x,
+            router_w=None, bias=None, logits_in=None, expert_mask=None, stream=None,
+            steps=("route", "permute", "ffn", "combine")) -> torch.Tensor:
+    """One layer forward; returns ``buf.out`` (valid in stream order)."""
+    T, H, I, E, k = buf.T, buf.H, buf.I, buf.E, buf.k
+    if "route" in steps:
+        L.moe_route(ctx, x, router_w, bias, logits_in, T, H, E, k, buf.logits, buf.ids, buf.w,
+                    stream=stream, x_dtype=buf.x_dtype)
+    if "permute" in steps:
+        L.moe_permute(ctx, buf.ids, T, k, E, buf.offsets, buf.sorted_pairs, buf.pair_pos,
+                      buf.active, stream=stream)
+    if "ffn" in steps:
+        args = L.make_ffn_args(pool_base, slot_bytes, n_slots, buf.q, H, I, T, k, E, slot_table, x,
+                               buf.offsets, buf.sorted_pairs, buf.active, buf.y, buf.mode,
+                               ws=buf.ws, ws_bytes=buf.ws.numel(), expert_mask=expert_mask,
+                               x_dtype=buf.x_dtype)
+        L.moe_expert_ffn(ctx, args, stream=stream)
+    if "combine" in steps:
+        L.moe_combine(ctx, buf.y, buf.w, T, k, H, buf.out, stream=stream)
+    return buf.out

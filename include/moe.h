@@ -1,0 +1,263 @@
+/*
+ * moe.h -- C ABI of libmoe: the routed-expert MoE layer forward for MI355X
+ * (gfx950), with a VRAM expert cache over a pinned host expert pool.
+ *
+ * The operation.  FreeToken keeps the full expert pool in host memory and
+ * treats VRAM as a cache of experts ("FreeToken github moe: Setup Guide &
+ * MoE Runtime Comparison", introduction; "FreeToken Inference Engine: 3x
+ * Speed Boost for MoE Models", section "From Static Allocation to Dynamic
+ * Scheduling").  Expert banks are ggml Q4_0 / Q8_0 blocks in one GPU slot
+ * pool of a single type (FreeToken fork README, "Quant types" and "Known
+ * limits"); decode and prefill use different kernel families there (matrix
+ * x vector for decode, matrix x matrix for prefill, same section).  One
+ * layer forward is:
+ *   logits -> softmax -> top-k (ties to the lower expert id) -> renormalise
+ *   -> expert id to slot -> group (token, expert) pairs by expert
+ *   -> per pair: h = silu(Wg x) * (Wu x), y = Wd h  -> out[t] = sum_j w_tj y_tj
+ *
+ * Conventions (all entry points).
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  An unsupported
+ *    block type is an error, never a silently empty result (the fork README,
+ *    "What else changed", describes the bug where an unknown type returned
+ *    uninitialised memory and a block-size query returned 0).
+ *    moe_last_error() returns a thread-local message naming the offending
+ *    argument, layer, expert or type.
+ *  - Pointers: "device" pointers are HIP device memory of the context's
+ *    device (for example torch tensors' data_ptr()); "host" pointers are
+ *    ordinary process memory.  The caller owns every buffer and every
+ *    stream; the library never allocates device memory in a compute call.
+ *    Streams are hipStream_t values passed as void* (NULL = default stream).
+ *  - All shape, type and alignment checks run on the host before any
+ *    launch.  Compute calls are stream ordered and do not synchronise, so
+ *    on success outputs are valid once the stream reaches the call.
+ *  - A fault that only the device can see (an expert whose slot is -1, that
+ *    is not resident) sets the context's sticky device error word and
+ *    writes NaN to that expert's outputs; moe_ctx_check() reports it.
+ *  - Shapes: H and I must be multiples of 256 (eight 32-weight blocks);
+ *    1 <= k <= E <= 1024.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ codes */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,
+  MOE_ERR_UNSUPPORTED_QTYPE = -2,
+  MOE_ERR_MIXED_QTYPE = -3,
+  MOE_ERR_ALIGNMENT = -4,
+  MOE_ERR_WORKSPACE = -5,
+  MOE_ERR_NOT_RESIDENT = -6,
+  MOE_ERR_NOT_PINNED = -7,
+  MOE_ERR_CAPACITY = -8,
+  MOE_ERR_HIP = -9
+};
+
+/* Block types, numbered as in ggml's type enum. */
+enum { MOE_QTYPE_Q4_0 = 2, MOE_QTYPE_Q8_0 = 8 };
+
+/* Activation dtypes. */
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+/* Expert FFN kernel families: matrix x vector decode with fp32 activations
+ * and fp32 accumulation, or grouped matrix x matrix prefill with bf16
+ * operands on the matrix cores and fp32 accumulation (fork README, "Quant
+ * types": separate decode and prefill kernels per block type). */
+enum { MOE_MODE_DECODE = 0, MOE_MODE_PREFILL = 1 };
+
+typedef struct moe_ctx moe_ctx;
+typedef struct moe_cache moe_cache;
+
+/* Thread-local description of the last error of this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ---------------------------------------------------------------- context
+ * moe_ctx_create: binds device `device`, allocates the 4-byte device error
+ * word.  moe_ctx_check: waits for `stream`, reads and clears the error word;
+ * returns MOE_ERR_NOT_RESIDENT if a kernel met a slot of -1 since the last
+ * check (the message names the expert).  moe_ctx_destroy frees the word. */
+int moe_ctx_create(int device, moe_ctx** out);
+int moe_ctx_destroy(moe_ctx* ctx);
+int moe_ctx_check(moe_ctx* ctx, void* stream);
+
+/* ------------------------------------------------------------ block types
+ * Q8_0: 32 weights, fp16 scale d + 32 int8 q (34 B), w = d*q.
+ * Q4_0: 32 weights, fp16 scale d + 16 nibble bytes (18 B), w = d*(q-8);
+ *       byte j holds element j (low nibble) and element j+16 (high nibble).
+ * Unknown qtype -> MOE_ERR_UNSUPPORTED_QTYPE and the outputs untouched. */
+int moe_qtype_info(int qtype, int* block_elems, int* block_bytes);
+
+/* -------------------------------------------------------------- packing
+ * Device layout of one expert slot (same byte count as the ggml blocks):
+ * gate [I rows][H], up [I rows][H], down [H rows][I], each matrix row-major
+ * by rows, each row a sequence of groups of 8 blocks; a group is the 8
+ * blocks' quant bytes (ggml order, 8*32 B for Q8_0, 8*16 B for Q4_0)
+ * followed by their 8 fp16 scales (16 B), so every group is 16-B aligned.
+ * The pinned host pool holds experts in this same layout, so staging an
+ * expert into VRAM is one verbatim copy ("FreeToken Inference Engine",
+ * FTW paragraph: load straight into the engine's layout, no repacking).
+ *
+ * moe_slot_bytes: bytes of one expert slot.
+ * moe_pack_expert (host): ggml blocks of gate [I][H/32], up [I][H/32],
+ * down [H][I/32] (host memory) -> `dst` (host memory, dst_bytes >= slot).
+ * moe_pack_matrix (host): one [rows][cols/32] block matrix -> device layout. */
+int moe_slot_bytes(int qtype, int H, int I, size_t* out_bytes);
+int moe_pack_expert(int qtype, int H, int I, const void* gate_blocks,
+                    const void* up_blocks, const void* down_blocks, void* dst,
+                    size_t dst_bytes);
+int moe_pack_matrix(int qtype, int rows, int cols, const void* blocks,
+                    void* dst, size_t dst_bytes);
+
+/* ----------------------------------------------------------------- route
+ * Router softmax and top-k with renormalisation, for T tokens.
+ *   x          device, [T][H] in x_dtype (ignored when logits_in != NULL)
+ *   router_w   device fp32 [E][H] (row e maps hidden -> logit e)
+ *   bias       device fp32 [E] added to the logits, or NULL
+ *   logits_in  device fp32 [T][E] given logits, or NULL to compute x.Wr^T
+ *   logits_out device fp32 [T][E]: the logits the selection used (bias
+ *              included); required when the logits are computed from x,
+ *              optional (may be NULL) with logits_in
+ *   topk_ids   device int32 [T][k]: the k largest logits, ordered by
+ *              (logit desc, id asc); equal logits go to the lower id
+ *   topk_w     device fp32 [T][k]: softmax probabilities of the chosen
+ *              experts renormalised to sum 1
+ * Selection is decided on the fp32 logits. */
+int moe_route(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w,
+              const float* bias, const float* logits_in, int T, int H, int E,
+              int k, float* logits_out, int32_t* topk_ids, float* topk_w,
+              void* stream);
+
+/* --------------------------------------------------------------- permute
+ * Groups the P = T*k pairs p = t*k + j by expert, stably (pair order kept
+ * inside an expert).  All device int32:
+ *   expert_offsets [E+1]: exclusive prefix sum of per-expert pair counts
+ *   sorted_pairs   [P]  : pairs of expert e at [offsets[e], offsets[e+1])
+ *   pair_pos       [P]  : inverse: sorted_pairs[pair_pos[p]] == p
+ *   active         [E+1]: active[0] = number of experts with pairs, then
+ *                         those expert ids ascending
+ * ws: device workspace of moe_permute_workspace_size() bytes (may be NULL
+ * when that size is 0). */
+int moe_permute_workspace_size(int T, int k, int E, size_t* bytes);
+int moe_permute(moe_ctx* ctx, const int32_t* topk_ids, int T, int k, int E,
+                int32_t* expert_offsets, int32_t* sorted_pairs,
+                int32_t* pair_pos, int32_t* active, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* ------------------------------------------------------------ expert FFN
+ * For every active expert e (or only those with expert_mask[e] != 0) and
+ * every pair p of e: y_pairs[p] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t)),
+ * t = p / k, with the expert's weights at pool_base + slot*slot_bytes,
+ * slot = slot_table[e] (the expert-id -> slot indirection over one slot
+ * pool, fork README "Known limits").  A slot of -1 (or outside the pool)
+ * sets the device error word and fills that expert's y rows with NaN.
+ * Experts masked out are skipped and their y rows left as they were. */
+typedef struct moe_ffn_args {
+  const void* pool_base;          /* device: slot pool */
+  size_t slot_bytes;              /* bytes per slot (moe_slot_bytes) */
+  int n_slots;                    /* slots in the pool; a slot outside
+                                     [0, n_slots) counts as not resident */
+  int qtype;                      /* MOE_QTYPE_* of every slot */
+  int H, I;                       /* hidden, intermediate */
+  int T, k, E;                    /* tokens, experts per token, experts */
+  const int32_t* slot_table;      /* device [E]: slot of expert e or -1 */
+  const void* x;                  /* device [T][H] in x_dtype */
+  int x_dtype;                    /* MOE_DTYPE_F32 (decode) or _BF16 */
+  const int32_t* expert_offsets;  /* device [E+1] from moe_permute */
+  const int32_t* sorted_pairs;    /* device [T*k] from moe_permute */
+  const int32_t* active;          /* device [E+1] from moe_permute */
+  const int32_t* expert_mask;     /* device [E] or NULL (= all) */
+  float* y_pairs;                 /* device fp32 [T*k][H], pair order */
+  int mode;                       /* MOE_MODE_DECODE or MOE_MODE_PREFILL */
+  void* ws;                       /* device workspace */
+  size_t ws_bytes;
+} moe_ffn_args;
+
+int moe_expert_ffn_workspace_size(const moe_ffn_args* args, size_t* bytes);
+int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* args, void* stream);
+
+/* --------------------------------------------------------------- combine
+ * out[t][:] = sum over j ascending of topk_w[t][j] * y_pairs[t*k + j][:]
+ * (device fp32; out [T][H]). */
+int moe_combine(moe_ctx* ctx, const float* y_pairs, const float* topk_w,
+                int T, int k, int H, float* out, void* stream);
+
+/* ------------------------------------------------------------ dequantise
+ * One packed matrix (device layout above, rows x cols) -> device `out`
+ * [rows][cols] as fp32 (exact d*q) or bf16 (round to nearest even of that
+ * fp32), through the same block decoding the FFN kernels use. */
+int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int rows,
+                   int cols, int out_dtype, void* out, void* stream);
+
+/* ---------------------------------------------------------- expert cache
+ * A global LRU over (layer, expert) keys (fork README, "About": global LRU
+ * expert caching; setup guide: a shared LRU follows token-level routing
+ * locality) backed by a device slot pool, with the full pool in pinned host
+ * memory.  Only missing experts move over PCIe ("FreeToken Inference
+ * Engine: 3x Speed Boost for MoE Models", "RTX 5090 Benchmark").
+ *   d_pool   device, (n_slots + 2) * slot_bytes, caller-owned.  At most
+ *            n_slots keys are resident; free slots are reused oldest-first,
+ *            so a copy lands in a slot released two evictions earlier
+ *            (ping-pong staging) after that slot's last reader finished.
+ *   h_pool   host pinned memory (hipHostMalloc / torch pin_memory),
+ *            experts [L][E] in the device slot layout, caller-owned;
+ *            memory that is not pinned -> MOE_ERR_NOT_PINNED.
+ * The device slot table (int32 [L][E], -1 = absent) is owned by the cache;
+ * cache_slot_table_device() returns it (row `layer` is the slot_table of
+ * moe_expert_ffn).  The cache starts empty.
+ *
+ * cache_slot_table_lookup (host): applies n ids of one layer in order.  A
+ * resident key is a hit and becomes most recently used.  A missing key is
+ * inserted at once, evicting the least recently used key that was not
+ * looked up earlier in this call; it gets a destination slot but its bytes
+ * are not there yet: call prefetch_expert for every listed miss before the
+ * FFN.  slots_out[i] = slot of ids[i]; miss_ids lists the misses in order
+ * without repeats (may be NULL); *n_miss = their number.
+ * MOE_ERR_CAPACITY if the call names more distinct experts than n_slots
+ * (the cache is then unchanged).  Every lookup must be followed by
+ * cache_mark_layer_done before the next lookup.
+ *
+ * prefetch_expert: for a key listed as a miss, copies its bytes from the
+ * pinned pool into its slot with hipMemcpyAsync on copy_stream (after the
+ * slot's previous reader, recorded by cache_mark_layer_done, has finished),
+ * makes compute_stream wait for the copy, and writes the key's slot (and
+ * -1 for the key it evicted) into the device table in compute_stream
+ * order.  A key already resident returns its slot with no copy.
+ * *slot_out (may be NULL) = the slot.
+ *
+ * cache_mark_layer_done: records on compute_stream the point after which the
+ * slots of the last lookup are no longer read (enqueue it after the layer's
+ * FFN), and ends that lookup. */
+int cache_slot_table_create(int L, int E, int n_slots, int qtype, int H, int I,
+                            void* d_pool, const void* h_pool, moe_cache** out);
+int cache_slot_table_lookup(moe_cache* c, int layer, const int32_t* ids,
+                            int n, int32_t* slots_out, int32_t* miss_ids,
+                            int* n_miss);
+const int32_t* cache_slot_table_device(moe_cache* c);
+int cache_slot_table_stats(moe_cache* c, int64_t* hits, int64_t* misses);
+int cache_slot_table_destroy(moe_cache* c);
+int prefetch_expert(moe_cache* c, int layer, int expert, void* copy_stream,
+                    void* compute_stream, int32_t* slot_out);
+int cache_mark_layer_done(moe_cache* c, int layer, void* compute_stream);
+
+/* ------------------------------------------------------- bank type check
+ * One block type for every expert bank: the slot pool is one allocation
+ * indexed with a single row stride, so mixed types would read every block
+ * at the wrong offset and must be refused, naming the layers (fork README,
+ * "Known limits").  qtypes: host int [L][n_per_layer] (e.g. gate, up, down
+ * per layer).  On success *out_qtype is the common type; otherwise
+ * MOE_ERR_MIXED_QTYPE (message lists the layers that differ from layer 0)
+ * or MOE_ERR_UNSUPPORTED_QTYPE. */
+int moe_check_bank_types(int L, int n_per_layer, const int* qtypes,
+                         int* out_qtype);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

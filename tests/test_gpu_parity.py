@@ -1,0 +1,231 @@
+"""GPU parity of libmoe against the CPU oracle: exact dequantisation, exact
+top-k ids and grouping, and layer outputs within tolerance (max relative
+error <= 1e-3 for fp32-accumulated decode)."""
+import numpy as np
+import pytest
+import torch
+
+import expert_offload_amd as moe
+from expert_offload_amd import _lib as L
+from expert_offload_amd import layer
+from gen import inputs as gi
+import oracle
+
+from gpu_util import DEV, ResidentLayer, dev, max_rel_err, note
+
+pytestmark = pytest.mark.gpu
+
+DECODE_TOL = 1e-3
+WEIGHT_TOL = 1e-5
+NEAR_TIE = 1e-5  # oracle logit gap below which fp32 rounding may reorder experts
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = moe.Ctx(0)
+    yield c
+    c.close()
+
+
+# ------------------------------------------------------------------ dequant
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("rows,cols", [(3, 256), (17, 768), (64, 2048)])
+def test_dequantize_exact(ctx, qt, rows, cols):
+    note(f"dequant {qt} {rows}x{cols}")
+    rng = np.random.default_rng(rows * cols)
+    quant = gi.quantize_q8_0 if qt == "q8_0" else gi.quantize_q4_0
+    w = (rng.standard_normal((rows, cols)) * rng.choice([1e-3, 0.02, 3.0, 500.0], (rows, 1)))
+    blocks = quant(w.astype(np.float32))
+    blocks[0, 0, 0:2] = [0, 0]              # d = 0
+    blocks[-1, -1, 0:2] = [0x01, 0x00]      # subnormal d
+    packed = np.empty(blocks.size, dtype=np.uint8)
+    moe.moe_pack_matrix(L.QTYPE[qt], rows, cols, blocks, packed)
+    pd = dev(packed)
+    out32 = torch.full((rows, cols), float("nan"), dtype=torch.float32, device=DEV)
+    out16 = torch.zeros((rows, cols), dtype=torch.bfloat16, device=DEV)
+    moe.moe_dequantize(ctx, L.QTYPE[qt], pd, rows, cols, out32)
+    moe.moe_dequantize(ctx, L.QTYPE[qt], pd, rows, cols, out16)
+    torch.cuda.synchronize()
+    ref = oracle.dequant(qt, blocks)
+    ref32 = ref.astype(np.float32)
+    assert np.array_equal(ref32.astype(np.float64), ref)  # d*q is exact in fp32
+    got32 = out32.cpu().numpy()
+    np.testing.assert_array_equal(got32.view(np.uint32), ref32.view(np.uint32))
+    got16 = out16.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got16, gi.f32_to_bf16_bits(ref32))
+
+
+# -------------------------------------------------------------------- route
+def _route_given(ctx, logits, k, bias=None):
+    T, E = logits.shape
+    ids = torch.full((T, k), -5, dtype=torch.int32, device=DEV)
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    lo = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    moe.moe_route(ctx, None, None, None if bias is None else dev(bias), dev(logits), T, 0, E, k,
+                  lo, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy(), lo.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (7, 128, 8), (33, 512, 10), (5, 1024, 64),
+                                   (4096, 128, 8), (3, 64, 64), (2, 1, 1)])
+def test_topk_exact_given_logits(ctx, T, E, k):
+    note(f"topk given logits T={T} E={E} k={k}")
+    rng = np.random.default_rng(T * 1000 + E)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    # planted exact ties, including ties straddling the k-th place
+    l[0, : min(E, 5)] = 0.75
+    if T > 1:
+        l[1] = np.round(l[1] * 2) / 2
+    ids, w, lo = _route_given(ctx, l, k)
+    ref_ids = oracle.topk_select(l, k)
+    np.testing.assert_array_equal(ids, ref_ids)
+    np.testing.assert_array_equal(lo, l)
+    ref_w = oracle.renormalize(oracle.softmax(l.astype(np.float64)), ref_ids)
+    assert np.abs(w - ref_w).max() <= WEIGHT_TOL * np.abs(ref_w).max()
+
+
+def test_topk_bias_and_nan(ctx):
+    E, k = 16, 4
+    l = np.zeros((2, E), dtype=np.float32)
+    l[0, 3] = np.nan
+    bias = -np.log(np.arange(E) + 1.0).astype(np.float32)
+    ids, w, lo = _route_given(ctx, l, k, bias=bias)
+    # NaN is never chosen over a finite logit; with the bias, lower ids win
+    assert ids[0].tolist() == [0, 1, 2, 4]
+    assert ids[1].tolist() == [0, 1, 2, 3]
+    np.testing.assert_array_equal(lo[1], bias)
+
+
+@pytest.mark.parametrize("name,T", [("tiny_q8_0", 4), ("decode_q8_0_h2048_e128", 16),
+                                    ("wide_q4_0_h2048_e512", 64)])
+def test_router_computed(ctx, name, T):
+    note(f"router computed {name} T={T}")
+    wl = gi.workload(name)
+    x = gi.activations(wl, T)
+    wr = gi.router_weight(wl)
+    b = gi.router_bias(wl)
+    ids = torch.empty((T, wl.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, wl.k), dtype=torch.float32, device=DEV)
+    lo = torch.empty((T, wl.E), dtype=torch.float32, device=DEV)
+    moe.moe_route(ctx, dev(x), dev(wr), None if b is None else dev(b), None, T, wl.H, wl.E, wl.k,
+                  lo, ids, w)
+    torch.cuda.synchronize()
+    ref_l = oracle.router_logits(x, wr, b)
+    assert np.abs(lo.cpu().numpy() - ref_l).max() <= 1e-5 * max(1.0, np.abs(ref_l).max())
+    ref_ids, ref_w = oracle.route(ref_l, wl.k)
+    gap = oracle.topk_gap(ref_l, wl.k)
+    ok = gap >= NEAR_TIE
+    got_ids = ids.cpu().numpy()
+    np.testing.assert_array_equal(got_ids[ok], ref_ids[ok])
+    assert (~ok).sum() <= max(1, T // 100), f"{(~ok).sum()} near-tie tokens"
+    assert np.abs(w.cpu().numpy()[ok] - ref_w[ok]).max() <= WEIGHT_TOL
+
+
+# ------------------------------------------------------------------ permute
+@pytest.mark.parametrize("T,k,E", [(0, 2, 8), (1, 1, 1), (4, 2, 8), (16, 8, 128), (64, 10, 512),
+                                   (100, 7, 1024), (4096, 8, 128), (513, 3, 5)])
+def test_permute_exact(ctx, T, k, E):
+    note(f"permute T={T} k={k} E={E}")
+    rng = np.random.default_rng(T + 7 * k + E)
+    if T == 0:
+        ids = np.zeros((0, k), dtype=np.int32)
+    elif E >= k:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32).reshape(T, k)
+    else:
+        ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    if T > 3:
+        ids[: T // 2, 0] = 0  # a hot expert (repeats within a token are allowed)
+    P = max(T * k, 1)
+    off = torch.full((E + 1,), -9, dtype=torch.int32, device=DEV)
+    sp = torch.full((P,), -9, dtype=torch.int32, device=DEV)
+    pos = torch.full((P,), -9, dtype=torch.int32, device=DEV)
+    act = torch.full((E + 1,), -9, dtype=torch.int32, device=DEV)
+    moe.moe_permute(ctx, dev(ids) if T else sp, T, k, E, off, sp, pos, act)
+    torch.cuda.synchronize()
+    r_off, r_sp, r_pos, r_act = oracle.permute(ids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), r_off)
+    if T:
+        np.testing.assert_array_equal(sp.cpu().numpy(), r_sp)
+        np.testing.assert_array_equal(pos.cpu().numpy(), r_pos)
+    a = act.cpu().numpy()
+    assert a[0] == len(r_act)
+    np.testing.assert_array_equal(a[1:1 + a[0]], r_act)
+
+
+# ------------------------------------------------------------- whole layers
+def _run_layer(ctx, rl, T, x, wr=None, b=None, logits=None, mode=L.MODE_DECODE, x_dtype=L.DTYPE_F32,
+               xd=None):
+    wl = rl.wl
+    buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV, mode=mode,
+                             x_dtype=x_dtype)
+    buf.y.fill_(float("nan"))
+    buf.out.fill_(float("nan"))
+    out = layer.forward(ctx, buf, rl.pool.base(), rl.pool.slot_bytes, rl.pool.n_slots, rl.slot_table,
+                        dev(x) if xd is None else xd,
+                        router_w=None if wr is None else dev(wr), bias=None if b is None else dev(b),
+                        logits_in=None if logits is None else dev(logits))
+    torch.cuda.synchronize()
+    moe.moe_ctx_check(ctx)
+    return buf, out.cpu().numpy()
+
+
+def _check_layer(buf, got_out, ref, tol, T):
+    ids = buf.ids.cpu().numpy()
+    ok = ref["gap"] >= NEAR_TIE
+    np.testing.assert_array_equal(ids[ok], ref["ids"][ok])
+    assert (~ok).sum() <= max(1, T // 100)
+    y = buf.y.cpu().numpy().reshape(T, -1, got_out.shape[1])[ok]
+    ry = ref["y_pairs"].reshape(T, -1, got_out.shape[1])[ok]
+    e_y = max_rel_err(y, ry)
+    e_out = max_rel_err(got_out[ok], ref["out"][ok])
+    note(f"   y max rel err {e_y:.2e}, out max rel err {e_out:.2e}")
+    assert np.isfinite(got_out).all()
+    assert e_y <= tol and e_out <= tol
+
+
+def test_tiny_layer(ctx):
+    wl = gi.workload("tiny_q8_0")
+    T = wl.batches[0]
+    rl = ResidentLayer(wl)
+    x, wr = gi.activations(wl, T), gi.router_weight(wl)
+    buf, out = _run_layer(ctx, rl, T, x, wr)
+    ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, router_w=wr)
+    _check_layer(buf, out, ref, DECODE_TOL, T)
+
+
+@pytest.fixture(scope="module")
+def decode_layer():
+    return ResidentLayer(gi.workload("decode_q8_0_h2048_e128"), layer_idx=0)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_decode_q8_0_layer(ctx, decode_layer, T):
+    note(f"decode q8_0 layer T={T}")
+    wl = decode_layer.wl
+    x, wr = gi.activations(wl, T), gi.router_weight(wl, 0)
+    buf, out = _run_layer(ctx, decode_layer, T, x, wr)
+    ref = oracle.moe_layer(x, wl.qtype, decode_layer.get_blocks, wl.k, router_w=wr)
+    _check_layer(buf, out, ref, DECODE_TOL, T)
+
+
+def test_not_resident_expert_gives_nan_and_error(ctx):
+    wl = gi.workload("tiny_q8_0")
+    T = wl.batches[0]
+    rl = ResidentLayer(wl)
+    x, wr = gi.activations(wl, T), gi.router_weight(wl)
+    ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, router_w=wr)
+    victim = int(ref["ids"][0, 0])
+    table = rl.perm.copy()
+    table[victim] = -1
+    rl.slot_table = dev(table)
+    buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV)
+    out = layer.forward(ctx, buf, rl.pool.base(), rl.pool.slot_bytes, rl.pool.n_slots, rl.slot_table, dev(x),
+                        router_w=dev(wr)).cpu().numpy()
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_ctx_check(ctx)
+    assert ei.value.name == "MOE_ERR_NOT_RESIDENT" and f"expert {victim}" in str(ei.value)
+    moe.moe_ctx_check(ctx)  # the word was cleared
+    uses = (ref["ids"] == victim).any(axis=1)
+    assert np.isnan(out[uses]).all(axis=1).all()
+    assert np.isfinite(out[~uses]).all()

@@ -1,0 +1,139 @@
+"""libmoe on the host (no GPU): the library loads, exports every symbol the
+header declares, and its host-only entry points (block-type table, slot
+sizes, the ggml -> device layout packer, the bank-type rule, workspace
+queries, argument errors) behave as documented."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import expert_offload_amd as moe
+from expert_offload_amd import _lib as L
+from gen import inputs as gi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_]+)\s*\(", src)) - {"defined"})
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 20
+    lib = moe.lib()
+    for n in names:
+        assert hasattr(lib, n), f"libmoe does not export {n}"
+    assert sorted(moe.EXPORTS) == names
+
+
+def test_qtype_table():
+    assert moe.moe_qtype_info(L.QTYPE["q8_0"]) == (32, 34)
+    assert moe.moe_qtype_info(L.QTYPE["q4_0"]) == (32, 18)
+    for bad in (0, 1, 3, 6, 7, 12, -1, 99):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_qtype_info(bad)
+        assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"
+        assert str(bad) in str(ei.value)
+
+
+def test_unsupported_qtype_leaves_outputs_untouched():
+    a, b = ctypes.c_int(-7), ctypes.c_int(-7)
+    rc = moe.lib().moe_qtype_info(14, ctypes.byref(a), ctypes.byref(b))
+    assert rc == -2 and a.value == -7 and b.value == -7
+
+
+@pytest.mark.parametrize("qt,H,I", [("q8_0", 256, 512), ("q8_0", 2048, 768), ("q4_0", 2048, 768),
+                                    ("q4_0", 2048, 512), ("q4_0", 4096, 2048)])
+def test_slot_bytes_equal_ggml_bytes(qt, H, I):
+    per_block = {"q8_0": 34, "q4_0": 18}[qt]
+    assert moe.moe_slot_bytes(L.QTYPE[qt], H, I) == 3 * H * I // 32 * per_block
+
+
+def test_slot_bytes_errors():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_slot_bytes(L.QTYPE["q8_0"], 300, 512)
+    assert ei.value.name == "MOE_ERR_INVALID_ARG"
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_slot_bytes(16, 256, 256)
+    assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"
+
+
+def _unpack_doc_layout(qt, rows, cols, packed):
+    """Read the documented device layout back into ggml blocks."""
+    qb = 32 if qt == "q8_0" else 16
+    gbytes = 8 * qb + 16
+    out = np.empty((rows, cols // 32, qb + 2), dtype=np.uint8)
+    rb = cols // 256 * gbytes
+    for r in range(rows):
+        for g in range(cols // 256):
+            grp = packed[r * rb + g * gbytes: r * rb + (g + 1) * gbytes]
+            for b in range(8):
+                out[r, 8 * g + b, 2:] = grp[b * qb:(b + 1) * qb]
+                out[r, 8 * g + b, :2] = grp[8 * qb + 2 * b: 8 * qb + 2 * b + 2]
+    return out
+
+
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+def test_pack_expert_layout(qt):
+    H, I = 512, 256
+    rng = np.random.default_rng(1)
+    quant = gi.quantize_q8_0 if qt == "q8_0" else gi.quantize_q4_0
+    g = quant(rng.standard_normal((I, H)).astype(np.float32))
+    u = quant(rng.standard_normal((I, H)).astype(np.float32))
+    d = quant(rng.standard_normal((H, I)).astype(np.float32))
+    from expert_offload_amd.layer import pack_expert
+    packed = pack_expert(qt, H, I, g, u, d)
+    n1 = g.size
+    assert packed.size == g.size + u.size + d.size
+    np.testing.assert_array_equal(_unpack_doc_layout(qt, I, H, packed[:n1]), g)
+    np.testing.assert_array_equal(_unpack_doc_layout(qt, I, H, packed[n1:2 * n1]), u)
+    np.testing.assert_array_equal(_unpack_doc_layout(qt, H, I, packed[2 * n1:]), d)
+
+
+def test_pack_expert_small_destination():
+    H, I = 256, 256
+    g = np.zeros((I, H // 32, 34), np.uint8)
+    dst = np.zeros(10, np.uint8)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_pack_expert(8, H, I, g, g, g, dst)
+    assert ei.value.name == "MOE_ERR_WORKSPACE"
+
+
+def test_bank_type_rule():
+    q4, q8 = L.QTYPE["q4_0"], L.QTYPE["q8_0"]
+    assert moe.moe_check_bank_types([[q4, q4, q4]] * 5) == q4
+    mixed = [[q4, q4, q4]] * 5
+    mixed[1] = [q4, q4, q8]
+    mixed[3] = [q8, q8, q8]
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_check_bank_types(mixed)
+    assert ei.value.name == "MOE_ERR_MIXED_QTYPE"
+    assert "1, 3" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_check_bank_types([[14, 14, 14]])
+    assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"
+
+
+def test_workspace_queries():
+    assert moe.moe_permute_workspace_size(16, 8, 128) == 0
+    args = L.moe_ffn_args(qtype=8, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, n_slots=128,
+                          slot_bytes=moe.moe_slot_bytes(8, 2048, 768))
+    assert moe.moe_expert_ffn_workspace_size(args) >= 16 * 8 * 768 * 4
+    bad = L.moe_ffn_args(qtype=3, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, slot_bytes=1)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_expert_ffn_workspace_size(bad)
+    assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"
+
+
+def test_null_context_is_an_error():
+    lib = moe.lib()
+    assert lib.moe_route(None, None, 0, None, None, None, 1, 256, 8, 2, None, None, None, None) == -1
+    assert lib.moe_permute(None, None, 1, 2, 8, None, None, None, None, None, 0, None) == -1
+    assert lib.moe_combine(None, None, None, 1, 2, 256, None, None) == -1
+    assert lib.moe_ctx_check(None, None) == -1
+    assert "ctx is NULL" in moe.moe_last_error()
