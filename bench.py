@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer forward on one MI355X.
+
+Default workload: decode through 48 stacked, independently weighted MoE
+layers (hidden 2048, 128 experts, top-8, intermediate 768, Q8_0 experts,
+fp32 activations, every expert resident in HBM), one step = one token batch
+through all 48 layers (route -> permute -> expert FFN -> combine per layer),
+captured once as a HIP graph and replayed.  `value` is tokens per second
+through the stack.
+
+Also reported on the same line:
+  roofline      the dominant kernel's algorithmic bytes per launch over its
+                average duration, timed with HIP events on its stream
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  batches       the same stack at the other batch sizes
+  prefill       4096-token grouped-GEMM layer (hidden 2048, 128 experts,
+                top-8, intermediate 768, Q4_0, bf16 activations)
+Progress goes to stderr; the JSON line is the only stdout output.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s as % of peak"
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--batch", type=int, default=1, help="tokens per step of the decode stack")
+    p.add_argument("--layers", type=int, default=48)
+    p.add_argument("--no-extras", action="store_true", help="skip the other batch sizes and prefill")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--unfused", action="store_true",
+                   help="run each layer as the four separate entry points instead of the two fused calls")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------- decode
+class DecodeStack:
+    def __init__(self, ctx, wl, n_layers: int, fused: bool = True):
+        import numpy as np
+        import torch
+        from expert_offload_amd import layer
+        from gen import inputs as gi
+
+        self.ctx, self.wl, self.L, self.fused = ctx, wl, n_layers, fused
+        self.pool = layer.SlotPool(wl.qtype, wl.H, wl.I, n_layers * wl.E, device="cuda")
+        self.perm = [gi.slot_permutation(wl, l) for l in range(n_layers)]
+        t0 = time.time()
+
+        def put(l, e, b):
+            self.pool.put(l * wl.E + int(self.perm[l][e]), layer.pack_expert(wl.qtype, wl.H, wl.I, *b))
+
+        gi.generate_blocks_parallel(wl, [(l, e) for l in range(n_layers) for e in range(wl.E)], put)
+        torch.cuda.synchronize()
+        log(f"generated and packed {n_layers}x{wl.E} experts "
+            f"({self.pool.data.numel() / 1e9:.1f} GB) in {time.time() - t0:.1f}s")
+        self.tables = [torch.from_numpy(p).cuda() for p in self.perm]
+        self.router = [torch.from_numpy(gi.router_weight(wl, l)).cuda() for l in range(n_layers)]
+        self.np = np
+
+    def buffers(self, T):
+        from expert_offload_amd import layer
+        wl = self.wl
+        return [layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device="cuda")
+                for _ in range(self.L)]
+
+    def run(self, bufs, x, stream=None):
+        from expert_offload_amd import layer
+        wl = self.wl
+        for l in range(self.L):
+            layer.forward(self.ctx, bufs[l], self.pool.base(l * wl.E), self.pool.slot_bytes, wl.E,
+                          self.tables[l], x, router_w=self.router[l], stream=stream, fused=self.fused)
+
+    def n_active(self, bufs):
+        return [int(b.active[0].item()) for b in bufs]
+
+
+def time_graph(stack, T, steps, warmup):
+    import torch
+    from gen import inputs as gi
+    x = torch.from_numpy(gi.activations(stack.wl, T)).cuda()
+    bufs = stack.buffers(T)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        stack.run(bufs, x)  # eager warm-up outside the capture
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        stack.run(bufs, x)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    return x, bufs, wall, gpu_ms
+
+
+def kernel_profile(stack, x, bufs, reps=5):
+    """Per-kernel average durations from the library's event timing (eager)."""
+    import torch
+    import expert_offload_amd as moe
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        stack.run(bufs, x)
+    s.synchronize()
+    moe.moe_ctx_set_timing(stack.ctx, True)
+    with torch.cuda.stream(s):
+        for _ in range(reps):
+            stack.run(bufs, x)
+    s.synchronize()
+    out = {}
+    for name in ("router_logits", "topk_permute", "topk", "permute", "ffn_gateup", "ffn_down", "combine"):
+        n, ms = moe.moe_ctx_kernel_time(stack.ctx, name)
+        if n:
+            out[name] = (n, ms)
+    moe.moe_ctx_set_timing(stack.ctx, False)
+    return out
+
+
+def decode_kernel_bytes(wl, T, n_active_per_layer):
+    """Algorithmic bytes per launch (averaged over layers) of the FFN kernels."""
+    from gen import inputs as gi
+    qb = gi.BLOCK_BYTES[wl.qtype] / 32.0
+    gate_up = 2 * wl.I * wl.H * qb
+    down = wl.H * wl.I * qb
+    na = sum(n_active_per_layer) / len(n_active_per_layer)
+    return {
+        "ffn_gateup": na * gate_up + T * wl.H * 4,
+        "ffn_down": na * down + T * wl.H * 4,
+    }
+
+
+def decode_layer_bytes(wl, T, n_active):
+    from gen import inputs as gi
+    return n_active * gi.bytes_per_expert(wl) + wl.E * wl.H * 4 + 2 * T * wl.H * 4
+
+
+# ---------------------------------------------------------------- prefill
+def prefill_extra(ctx, steps=10, warmup=3):
+    import numpy as np
+    import torch
+    import expert_offload_amd as moe
+    from expert_offload_amd import _lib as L
+    from expert_offload_amd import layer
+    from gen import inputs as gi
+
+    wl = gi.workload("prefill_q4_0_h2048_e128")
+    T = wl.batches[0]
+    pool = layer.SlotPool(wl.qtype, wl.H, wl.I, wl.E, device="cuda")
+    perm = gi.slot_permutation(wl, 0)
+
+    def put(l, e, b):
+        pool.put(int(perm[e]), layer.pack_expert(wl.qtype, wl.H, wl.I, *b))
+
+    gi.generate_blocks_parallel(wl, [(0, e) for e in range(wl.E)], put)
+    table = torch.from_numpy(perm).cuda()
+    xbits = gi.activations(wl, T)
+    x = torch.from_numpy(xbits.view(np.int16)).view(torch.bfloat16).cuda()
+    logits = torch.from_numpy(gi.given_logits(wl, T)).cuda()
+    buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device="cuda",
+                             mode=L.MODE_PREFILL, x_dtype=L.DTYPE_BF16)
+
+    def run():
+        layer.forward(ctx, buf, pool.base(), pool.slot_bytes, wl.E, table, x, logits_in=logits)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        run()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    moe.moe_ctx_set_timing(ctx, True)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    kt = {}
+    for name in ("topk", "permute", "ffn_gateup", "ffn_down", "combine"):
+        n, t = moe.moe_ctx_kernel_time(ctx, name)
+        if n:
+            kt[name] = t / n
+    moe.moe_ctx_set_timing(ctx, False)
+    flops = 2.0 * T * wl.k * 3 * wl.H * wl.I
+    ffn_ms = kt.get("ffn_gateup", 0) + kt.get("ffn_down", 0)
+    tflops = flops / (ffn_ms * 1e-3) / 1e12 if ffn_ms else None
+    gate_up_flops = 2.0 * T * wl.k * 2 * wl.H * wl.I
+    gu_tflops = gate_up_flops / (kt["ffn_gateup"] * 1e-3) / 1e12 if kt.get("ffn_gateup") else None
+    return {
+        "workload": wl.name, "tokens": T, "layer_ms": ms, "tokens_per_s": T / (ms * 1e-3),
+        "kernel_ms": kt, "ffn_tflops": tflops, "ffn_frac_bf16_peak": tflops / BF16_PEAK_TFLOPS if tflops else None,
+        "gateup_tflops": gu_tflops,
+        "flops_per_layer": flops,
+    }
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_baseline(wl, T, budget_s):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from gen import inputs as gi
+    import oracle
+
+    x = gi.activations(wl, T)
+    done, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        for l in range(wl.layers):
+            wr = gi.router_weight(wl, l)
+            ids = oracle.topk_select(oracle.router_logits(x, wr), wl.k)
+            blocks = {}
+            gi.generate_blocks_parallel(
+                wl, [(l, int(e)) for e in np.unique(ids)],
+                lambda ll, e, b: blocks.__setitem__(e, b))
+            t0 = time.perf_counter()
+            oracle.moe_layer(x, wl.qtype, lambda e: blocks[e], wl.k, router_w=wr)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            if elapsed >= budget_s:
+                break
+    per_layer = elapsed / done
+    return {
+        "value": T / (per_layer * wl.layers), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": f"NumPy fp64 oracle, 1 BLAS thread, {done} of {wl.layers} layers at T={T} "
+                  f"({elapsed:.1f}s), scaled to the {wl.layers}-layer stack",
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported on this build "
+              "(multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import expert_offload_amd as moe
+    from gen import inputs as gi
+
+    moe.lib()
+    wl = gi.workload("decode_q8_0_h2048_e128")
+    if args.layers != wl.layers:
+        log(f"NOTE: {args.layers} layers instead of {wl.layers} (profiling run)")
+    ctx = moe.Ctx(0)
+    stack = DecodeStack(ctx, wl, args.layers, fused=not args.unfused)
+
+    T = args.batch
+    x, bufs, wall, gpu_ms = time_graph(stack, T, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    n_active = stack.n_active(bufs)
+    moe.moe_ctx_check(ctx)
+    log(f"T={T}: {ms_per_step:.3f} ms/step wall, {gpu_ms / args.steps:.3f} ms/step GPU, "
+        f"{T / (ms_per_step * 1e-3):.1f} tok/s, mean active experts {sum(n_active) / len(n_active):.1f}")
+
+    prof = kernel_profile(stack, x, bufs)
+    kbytes = decode_kernel_bytes(wl, T, n_active)
+    ffn = {k: v for k, v in prof.items() if k in kbytes}
+    dom = max(ffn, key=lambda k: ffn[k][1])
+    n, tot = ffn[dom]
+    avg_ms = tot / n
+    achieved = kbytes[dom] / (avg_ms * 1e-3) / 1e9
+    for name, (cnt, ms) in sorted(prof.items()):
+        log(f"   kernel {name:14s} launches {cnt:5d} avg {ms / cnt * 1e3:8.2f} us")
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "avg_us": avg_ms * 1e3,
+                "bytes_per_launch": kbytes[dom]}
+    stack_bytes = sum(decode_layer_bytes(wl, T, a) for a in n_active)
+    result = {
+        "metric": METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": args.layers, "tokens_per_step": T, "hidden": wl.H,
+                   "experts": wl.E, "top_k": wl.k, "intermediate": wl.I, "weights": "Q8_0",
+                   "activations": "fp32", "graph": "hip graph of the whole stack",
+                   "calls_per_layer": "moe_route_permute + moe_expert_ffn(fused combine)" if not args.unfused
+                   else "moe_route, moe_permute, moe_expert_ffn, moe_combine"},
+        "roofline": roofline,
+        "stack_hbm_gbs": stack_bytes / (ms_per_step * 1e-3) / 1e9,
+    }
+    if not args.no_extras:
+        extra = {}
+        for tb in wl.batches:
+            if tb == T:
+                continue
+            _, bb, w2, _ = time_graph(stack, tb, max(10, args.steps // 2), args.warmup)
+            ms2 = w2 * 1e3 / max(10, args.steps // 2)
+            na2 = stack.n_active(bb)
+            extra[str(tb)] = {"tokens_per_s": tb / (ms2 * 1e-3), "ms_per_step": ms2,
+                              "mean_active_experts": sum(na2) / len(na2),
+                              "stack_hbm_gbs": sum(decode_layer_bytes(wl, tb, a) for a in na2) / (ms2 * 1e-3) / 1e9}
+            log(f"T={tb}: {ms2:.3f} ms/step, {tb / (ms2 * 1e-3):.1f} tok/s")
+        result["batches"] = extra
+        del stack
+        torch.cuda.empty_cache()
+        try:
+            result["prefill"] = prefill_extra(ctx)
+            log(f"prefill: {result['prefill']['tokens_per_s']:.0f} tok/s, FFN "
+                f"{result['prefill']['ffn_tflops']:.1f} TFLOP/s")
+        except Exception as e:  # reported, never silently dropped
+            result["prefill"] = {"error": repr(e)}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(wl, T, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,7 +33,8 @@ EXPORTS = (
     "moe_expert_ffn", "moe_combine", "moe_dequantize", "cache_slot_table_create",
     "cache_slot_table_lookup", "cache_slot_table_device", "cache_slot_table_stats",
     "cache_slot_table_destroy", "prefetch_expert", "cache_mark_layer_done",
-    "moe_check_bank_types",
+    "moe_check_bank_types", "moe_ctx_set_timing", "moe_ctx_kernel_time",
+    "moe_route_permute_workspace_size", "moe_route_permute",
 )
 
 
@@ -54,6 +55,7 @@ class moe_ffn_args(ctypes.Structure):
         ("sorted_pairs", ctypes.c_void_p), ("active", ctypes.c_void_p),
         ("expert_mask", ctypes.c_void_p), ("y_pairs", ctypes.c_void_p), ("mode", ctypes.c_int),
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+        ("topk_w", ctypes.c_void_p), ("out", ctypes.c_void_p),
     ]
 
 
@@ -97,6 +99,10 @@ def lib() -> ctypes.CDLL:
         "prefetch_expert": (i, [vp, i, i, vp, vp, i32p]),
         "cache_mark_layer_done": (i, [vp, i, vp]),
         "moe_check_bank_types": (i, [i, i, ip, ip]),
+        "moe_ctx_set_timing": (i, [vp, i]),
+        "moe_route_permute_workspace_size": (i, [i, i, i, szp]),
+        "moe_route_permute": (i, [vp, vp, i, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_ctx_kernel_time": (i, [vp, ctypes.c_char_p, ip, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -165,6 +171,18 @@ def moe_ctx_check(ctx: Ctx, stream=None) -> None:
     _check(lib().moe_ctx_check(ctx.handle, _stream(stream)), "moe_ctx_check")
 
 
+def moe_ctx_set_timing(ctx: Ctx, enable: bool) -> None:
+    _check(lib().moe_ctx_set_timing(ctx.handle, int(bool(enable))), "moe_ctx_set_timing")
+
+
+def moe_ctx_kernel_time(ctx: Ctx, kernel: str) -> Tuple[int, float]:
+    """(number of timed launches, summed milliseconds) of one kernel."""
+    n, ms = ctypes.c_int(), ctypes.c_double()
+    _check(lib().moe_ctx_kernel_time(ctx.handle, kernel.encode(), ctypes.byref(n), ctypes.byref(ms)),
+           "moe_ctx_kernel_time")
+    return n.value, ms.value
+
+
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
 
@@ -217,6 +235,25 @@ def moe_route(ctx: Ctx, x, router_w, bias, logits_in, T: int, H: int, E: int, k:
                            _dev_ptr(topk_w), _stream(stream)), "moe_route")
 
 
+def moe_route_permute_workspace_size(T: int, k: int, E: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_route_permute_workspace_size(T, k, E, ctypes.byref(n)),
+           "moe_route_permute_workspace_size")
+    return n.value
+
+
+def moe_route_permute(ctx: Ctx, x, router_w, bias, logits_in, T: int, H: int, E: int, k: int,
+                      logits_out, topk_ids, topk_w, expert_offsets, sorted_pairs, pair_pos, active,
+                      ws, ws_bytes: int, stream=None, x_dtype: Optional[int] = None) -> None:
+    if x_dtype is None:
+        x_dtype = DTYPE_BF16 if (isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16) else DTYPE_F32
+    _check(lib().moe_route_permute(ctx.handle, _dev_ptr(x), x_dtype, _dev_ptr(router_w), _dev_ptr(bias),
+                                   _dev_ptr(logits_in), T, H, E, k, _dev_ptr(logits_out),
+                                   _dev_ptr(topk_ids), _dev_ptr(topk_w), _dev_ptr(expert_offsets),
+                                   _dev_ptr(sorted_pairs), _dev_ptr(pair_pos), _dev_ptr(active),
+                                   _dev_ptr(ws), ws_bytes, _stream(stream)), "moe_route_permute")
+
+
 def moe_permute_workspace_size(T: int, k: int, E: int) -> int:
     n = ctypes.c_size_t()
     _check(lib().moe_permute_workspace_size(T, k, E, ctypes.byref(n)), "moe_permute_workspace_size")
@@ -232,7 +269,7 @@ def moe_permute(ctx: Ctx, topk_ids, T: int, k: int, E: int, expert_offsets, sort
 
 def make_ffn_args(pool, slot_bytes, n_slots, qtype, H, I, T, k, E, slot_table, x, expert_offsets,
                   sorted_pairs, active, y_pairs, mode, ws=None, ws_bytes=0, expert_mask=None,
-                  x_dtype=None) -> moe_ffn_args:
+                  x_dtype=None, topk_w=None, out=None) -> moe_ffn_args:
     if x_dtype is None:
         x_dtype = DTYPE_BF16 if (isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16) else DTYPE_F32
     return moe_ffn_args(
@@ -240,7 +277,7 @@ def make_ffn_args(pool, slot_bytes, n_slots, qtype, H, I, T, k, E, slot_table, x
         slot_table=_dev_ptr(slot_table), x=_dev_ptr(x), x_dtype=x_dtype,
         expert_offsets=_dev_ptr(expert_offsets), sorted_pairs=_dev_ptr(sorted_pairs),
         active=_dev_ptr(active), expert_mask=_dev_ptr(expert_mask), y_pairs=_dev_ptr(y_pairs),
-        mode=mode, ws=_dev_ptr(ws), ws_bytes=ws_bytes)
+        mode=mode, ws=_dev_ptr(ws), ws_bytes=ws_bytes, topk_w=_dev_ptr(topk_w), out=_dev_ptr(out))
 
 
 def moe_expert_ffn_workspace_size(args: moe_ffn_args) -> int:

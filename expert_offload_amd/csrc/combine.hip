@@ -39,6 +39,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   }
 }
 
+int launch_combine(moe_ctx* ctx, const float* y, const float* w, int T, int k, int H, float* out, hipStream_t s) {
+  dim3 grid((H + 255) / 256, T);
+  KernelTimer timer(ctx, "combine", s);
+  combine_kernel<<<grid, 256, 0, s>>>(y, w, k, H, out);
+  return check_launch("combine_kernel");
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -54,9 +61,7 @@ extern "C" int moe_combine(moe_ctx* ctx, const float* y_pairs, const float* topk
   if (!y_pairs || !topk_w || !out) return set_error(MOE_ERR_INVALID_ARG, "moe_combine: NULL buffer");
   int rc = ensure_device(ctx);
   if (rc) return rc;
-  dim3 grid((H + 255) / 256, T);
-  combine_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(y_pairs, topk_w, k, H, out);
-  return check_launch("combine_kernel");
+  return launch_combine(ctx, y_pairs, topk_w, T, k, H, out, (hipStream_t)stream);
 }
 
 extern "C" int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int rows, int cols,
@@ -78,6 +83,7 @@ extern "C" int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int r
   const long long n = (long long)rows * (cols / kQK);
   const unsigned grid = (unsigned)((n + 255) / 256);
   hipStream_t s = (hipStream_t)stream;
+  KernelTimer timer(ctx, "dequant", s);
   if (qtype == MOE_QTYPE_Q8_0) {
     if (out_dtype == MOE_DTYPE_F32) dequant_kernel<MOE_QTYPE_Q8_0, false><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
     else dequant_kernel<MOE_QTYPE_Q8_0, true><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);

@@ -1,0 +1,537 @@
+// Decode-path kernels: fused router + top-k + grouping, and the expert FFN
+// as HBM-streaming dequant-GEMVs (gate/up + SwiGLU, then down + combine).
+//
+// GEMV layout.  A wavefront owns RW = (64 / LPR) * RPL weight rows: lanes
+// form 64/LPR groups of LPR lanes, each group covers RPL rows, and every
+// lane owns the same BPL column blocks of all its rows.  The lane issues
+// all of its rows' 16-byte quant loads before any arithmetic (enough bytes
+// in flight to cover HBM latency), reuses each activation block for RPL
+// rows, and the RPL partial sums are folded across the LPR lanes with a
+// transposed butterfly (RPL - 1 + log2(LPR / RPL) shuffles instead of
+// RPL * log2(LPR)).
+//
+// Block arithmetic.  With u the stored byte (Q8_0: q + 128 after flipping
+// the sign bit; Q4_0: the nibble q), sum_k w_k x_k = d * (sum_k u_k x_k -
+// OFF * sum_k x_k), OFF = 128 or 8; sum_k x_k is formed once per block and
+// token and shared by the lane's RPL rows.
+#include <climits>
+
+#include "device_common.h"
+#include "ffn.h"
+
+namespace moe {
+
+// --------------------------------------------------------------- helpers
+template <int QT>
+struct QTraits;
+template <>
+struct QTraits<MOE_QTYPE_Q8_0> {
+  static constexpr int kWords = 8;  // 32 bytes of codes
+  static constexpr float kOff = 128.0f;
+};
+template <>
+struct QTraits<MOE_QTYPE_Q4_0> {
+  static constexpr int kWords = 4;  // 16 bytes of nibbles
+  static constexpr float kOff = 8.0f;
+};
+
+template <int QT>
+__device__ __forceinline__ void load_block_raw(const uint8_t* row, int b, uint32_t (&w)[QTraits<QT>::kWords],
+                                               float& d) {
+  const uint8_t* q = block_quants<QT>(row, b);
+  const uint4 v0 = *reinterpret_cast<const uint4*>(q);
+  w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+  if constexpr (QT == MOE_QTYPE_Q8_0) {
+    const uint4 v1 = *reinterpret_cast<const uint4*>(q + 16);
+    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+  }
+  d = block_scale<QT>(row, b);
+}
+
+// sum_k u_k * x_k over one block, u the unsigned stored code.
+template <int QT>
+__device__ __forceinline__ float block_udot(const uint32_t (&w)[QTraits<QT>::kWords], const float (&xv)[32]) {
+  float s = 0.0f;
+  if constexpr (QT == MOE_QTYPE_Q8_0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = w[i] ^ 0x80808080u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = fmaf((float)((u >> (8 * j)) & 0xFFu), xv[4 * i + j], s);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s = fmaf((float)((lo >> (8 * j)) & 0xFFu), xv[4 * i + j], s);
+        s = fmaf((float)((hi >> (8 * j)) & 0xFFu), xv[16 + 4 * i + j], s);
+      }
+    }
+  }
+  return s;
+}
+
+__device__ __forceinline__ void load_f32x32(const float* p, float (&xv)[32]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(p + 4 * i);
+    xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ float sum32(const float (&xv)[32]) {
+  float a = 0.0f, b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) {
+    a += xv[i];
+    b += xv[i + 1];
+  }
+  return a + b;
+}
+
+// Transposed butterfly over aligned groups of LPR lanes: on entry lane l
+// holds partial sums v[0..N) of N rows; on exit v[0] of every lane holds the
+// full sum of row (l % LPR) / (LPR / N) of its group.
+template <int OFF, int N, int M>
+__device__ __forceinline__ void fold_rows(float (&v)[M], int lane) {
+  if constexpr (OFF >= 1) {
+    if constexpr (N > 1) {
+      const bool hi = (lane & OFF) != 0;
+#pragma unroll
+      for (int r = 0; r < N / 2; ++r) {
+        const float keep = hi ? v[r + N / 2] : v[r];
+        const float send = hi ? v[r] : v[r + N / 2];
+        v[r] = keep + __shfl_xor(send, OFF, kWave);
+      }
+      fold_rows<OFF / 2, N / 2, M>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], OFF, kWave);
+      fold_rows<OFF / 2, 1, M>(v, lane);
+    }
+  }
+}
+
+// Rows of one lane's GEMV: RPL rows x BPL blocks of raw codes and scales.
+template <int QT, int LPR, int BPL, int RPL>
+struct RowTile {
+  uint32_t w[RPL][BPL][QTraits<QT>::kWords];
+  float d[RPL][BPL];
+
+  __device__ __forceinline__ void load(const uint8_t* const (&rows)[RPL], int lg) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) load_block_raw<QT>(rows[r], lg + LPR * i, w[r][i], d[r][i]);
+  }
+
+  // acc[r] = sum over the lane's blocks of d * (u . x - OFF * sum x), with
+  // the lane's activation blocks already in xv.  Rows are finished one at a
+  // time in load order, so the wait before row r covers only the loads up to
+  // row r and row r's math overlaps the later rows' transfers.  Each row's
+  // codes pass through an empty asm right before use so the compiler widens
+  // them here, inside the token loop, instead of keeping RPL*BPL*32 widened
+  // floats live; four partial sums per row break the FMA dependency chain.
+  __device__ __forceinline__ void dot(const float (&xv)[BPL][32], float (&acc)[RPL]) {
+    float sx[BPL];
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) sx[i] = sum32(xv[i]) * QTraits<QT>::kOff;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      acc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+#pragma unroll
+        for (int q = 0; q < QTraits<QT>::kWords; ++q) asm volatile("" : "+v"(w[r][i][q]));
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (QT == MOE_QTYPE_Q8_0) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t u = w[r][i][q] ^ 0x80808080u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part[j] = fmaf((float)((u >> (8 * j)) & 0xFFu), xv[i][4 * q + j], part[j]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = w[r][i][q] & 0x0F0F0F0Fu, hi = (w[r][i][q] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              part[j] = fmaf((float)((lo >> (8 * j)) & 0xFFu), xv[i][4 * q + j], part[j]);
+              part[j] = fmaf((float)((hi >> (8 * j)) & 0xFFu), xv[i][16 + 4 * q + j], part[j]);
+            }
+          }
+        }
+        acc[r] = fmaf(d[r][i], (part[0] + part[1]) + (part[2] + part[3]) - sx[i], acc[r]);
+      }
+    }
+  }
+};
+
+// The lane's BPL activation blocks of one token row.
+template <int LPR, int BPL>
+__device__ __forceinline__ void load_act(const float* act, int lg, float (&xv)[BPL][32]) {
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) load_f32x32(act + (size_t)(lg + LPR * i) * kQK, xv[i]);
+}
+
+// --------------------------------------------------- control-data staging
+// The grouping written by the routing launch (active list, offsets, the
+// grouped pair list) and the slot table are read by every wavefront.  The
+// workgroup copies them into LDS with independent loads (one memory round
+// trip) instead of chasing them one dependent load at a time.
+constexpr int kCtlMaxPairs = 1024;
+
+struct CtlLds {
+  int active[kMaxE + 1];
+  int offsets[kMaxE + 1];
+  int slots[kMaxE];
+  int pairs[kCtlMaxPairs];
+  float w[kCtlMaxPairs];
+};
+
+// The decode kernels run only when T*k <= kCtlMaxPairs.
+template <int NT>
+__device__ __forceinline__ void stage_ctl(const FfnParams& p, CtlLds& s, bool want_w) {
+  const int E = p.E, P = p.T * p.k;
+  for (int i = threadIdx.x; i <= E; i += NT) {
+    s.active[i] = p.active[i];
+    s.offsets[i] = p.offsets[i];
+    if (i < E) s.slots[i] = p.slot_table[i];
+  }
+  for (int i = threadIdx.x; i < P; i += NT) {
+    s.pairs[i] = p.sorted_pairs[i];
+    if (want_w) s.w[i] = p.topk_w[i];
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------ gate/up + SwiGLU
+// A work item is one wavefront: (active expert, RW/2 intermediate indices);
+// its rows interleave gate and up: row 2m = gate(i0 + m), 2m + 1 = up(i0 + m).
+template <int QT, int LPR, int BPL, int RPL>
+__global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const float* __restrict__ x) {
+  constexpr int RPP = kWave / LPR, RW = RPP * RPL, NI = RW / 2;
+  __shared__ CtlLds ctl;
+  stage_ctl<256>(p, ctl, false);
+  const int* pairs = ctl.pairs;
+  constexpr int STRIDE = RPL >= 2 ? LPR / RPL : LPR;  // lane distance gate row -> up row
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane / LPR, lg = lane % LPR;
+  const int rr = g * RPL + lg / (LPR / RPL);  // row this lane holds after the fold
+  const bool writer = (lg % (LPR / RPL)) == 0 && (rr & 1) == 0;
+  const int n_chunks = p.I / NI;
+  const int items = ctl.active[0] * n_chunks;
+  const size_t gate_off = slot_gate_off(QT, p.H, p.I), up_off = slot_up_off(QT, p.H, p.I);
+  const size_t rbytes = row_bytes(QT, p.H);
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
+    const int a = item / n_chunks, c = item - a * n_chunks;
+    const int e = ctl.active[1 + a];
+    if (p.mask && !p.mask[e]) continue;
+    const int slot = ctl.slots[e];
+    const int pbeg = ctl.offsets[e], n_e = ctl.offsets[e + 1] - pbeg;
+    const int i0 = c * NI;
+    if (slot < 0 || slot >= p.n_slots) {
+      if (lane == 0) atomicCAS(p.err, 0, e + 1);
+      for (int s = lane; s < n_e * NI; s += kWave) p.hbuf[(size_t)(pbeg + s / NI) * p.I + i0 + s % NI] = NAN;
+      continue;
+    }
+    const uint8_t* base = p.pool + (size_t)slot * p.slot_bytes;
+    const uint8_t* rows[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int rw = g * RPL + r;
+      rows[r] = base + ((rw & 1) ? up_off : gate_off) + (size_t)(i0 + rw / 2) * rbytes;
+    }
+    // first token's activations go out before the weights (they are L2
+    // hits), so the per-row waits do not wait for the whole tile
+    // the first token's activations go out before the weights (L2 hits), and
+    // the first token is peeled out of the loop so its row-by-row waits cover
+    // only the weight loads issued so far
+    float xv[BPL][32];
+    load_act<LPR, BPL>(x + (size_t)(pairs[pbeg] / p.k) * p.H, lg, xv);
+    RowTile<QT, LPR, BPL, RPL> tile;
+    tile.load(rows, lg);
+    auto finish = [&](int s, float (&acc)[RPL]) {
+      fold_rows<LPR / 2, RPL, RPL>(acc, lane);
+      const float u = __shfl_down(acc[0], STRIDE, kWave);
+      if (writer) {
+        const float gv = acc[0];
+        p.hbuf[(size_t)(pbeg + s) * p.I + i0 + rr / 2] = gv / (1.0f + expf(-gv)) * u;
+      }
+    };
+    {
+      float acc[RPL];
+      tile.dot(xv, acc);
+      finish(0, acc);
+    }
+    for (int s = 1; s < n_e; ++s) {
+      load_act<LPR, BPL>(x + (size_t)(pairs[pbeg + s] / p.k) * p.H, lg, xv);
+      float acc[RPL];
+      tile.dot(xv, acc);
+      finish(s, acc);
+    }
+  }
+}
+
+// ------------------------------------------------------ down (+ combine)
+// A workgroup owns RW output rows of every active expert; its wavefronts
+// take the experts in turn (expert a -> wave a mod waves), write y for their
+// pairs, and after a barrier the workgroup forms out[t] = sum_j w[t][j] *
+// y[t*k + j] over those rows (j ascending, as moe_combine does).  No data
+// crosses workgroups, so no device-wide fences are needed.
+constexpr int kDownWaves = 8;
+constexpr int kDownLdsFloats = 2048;    // y tile kept in LDS for the combine when T*k*RW fits
+constexpr int kDownStageFloats = 1024;  // per-wave staging of one h row when I fits
+constexpr int kStageVec = kDownStageFloats / (4 * kWave);  // float4 per lane
+
+// One h row (I <= kDownStageFloats floats) in registers, on its way to LDS.
+struct HRowRegs {
+  float4 v[kStageVec];
+  // Lanes past the row end re-read its last 4 floats (in bounds) and skip
+  // the store, so every element is written unconditionally here.
+  __device__ __forceinline__ void load(const float* src, int I, int lane) {
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const int c = min((lane + kWave * i) * 4, I - 4);
+      v[i] = *reinterpret_cast<const float4*>(src + c);
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int I, int lane) const {
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const int c = (lane + kWave * i) * 4;
+      if (c < I) *reinterpret_cast<float4*>(dst + c) = v[i];
+    }
+  }
+};
+
+template <int QT, int LPR, int BPL, int RPL>
+__global__ __launch_bounds__(kDownWaves * kWave) void ffn_down_decode(FfnParams p) {
+  constexpr int RPP = kWave / LPR, RW = RPP * RPL;
+  __shared__ float s_y[kDownLdsFloats];
+  __shared__ float s_h[kDownWaves][kDownStageFloats];
+  __shared__ CtlLds ctl;
+  stage_ctl<kDownWaves * kWave>(p, ctl, p.out != nullptr);
+  const int* pairs = ctl.pairs;
+  const float* topk_w = ctl.w;
+  const bool lds_y = p.T * p.k * RW <= kDownLdsFloats;
+  // With LPR < 64 the 64/LPR lane groups own the same columns of h: each h
+  // row is read from memory once (issued before the weights) into the
+  // wavefront's LDS row, and the groups read their blocks from there.
+  const bool stage_h = RPP > 1 && p.I <= kDownStageFloats;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  float* hrow = s_h[wave];
+  const int g = lane / LPR, lg = lane % LPR;
+  const int rr = g * RPL + lg / (LPR / RPL);
+  const bool writer = (lg % (LPR / RPL)) == 0;
+  const int n_tiles = p.H / RW;
+  const int n_active = ctl.active[0];
+  const size_t down_off = slot_down_off(QT, p.H, p.I);
+  const size_t rbytes = row_bytes(QT, p.I);
+  for (int tile_i = blockIdx.x; tile_i < n_tiles; tile_i += gridDim.x) {
+    const int h0 = tile_i * RW;
+    for (int a = wave; a < n_active; a += kDownWaves) {
+      const int e = ctl.active[1 + a];
+      if (p.mask && !p.mask[e]) continue;
+      const int slot = ctl.slots[e];
+      const int pbeg = ctl.offsets[e], n_e = ctl.offsets[e + 1] - pbeg;
+      if (slot < 0 || slot >= p.n_slots) {
+        if (lane == 0) atomicCAS(p.err, 0, e + 1);
+        for (int s = lane; s < n_e * RW; s += kWave) {
+          const int pair = pairs[pbeg + s / RW];
+          p.y[(size_t)pair * p.H + h0 + s % RW] = NAN;
+          if (lds_y) s_y[pair * RW + s % RW] = NAN;
+        }
+        continue;
+      }
+      const uint8_t* base = p.pool + (size_t)slot * p.slot_bytes + down_off;
+      const uint8_t* rows[RPL];
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) rows[r] = base + (size_t)(h0 + g * RPL + r) * rbytes;
+#define MOE_DOWN_FINISH(S)                                  \
+  do {                                                      \
+    const int pair_ = pairs[pbeg + (S)];                    \
+    fold_rows<LPR / 2, RPL, RPL>(acc, lane);                \
+    if (writer) {                                           \
+      p.y[(size_t)pair_ * p.H + h0 + rr] = acc[0];          \
+      if (lds_y) s_y[pair_ * RW + rr] = acc[0];             \
+    }                                                       \
+  } while (0)
+      RowTile<QT, LPR, BPL, RPL> tile;
+      float xv[BPL][32];
+      if (stage_h) {
+        HRowRegs hr;
+        hr.load(p.hbuf + (size_t)pbeg * p.I, p.I, lane);
+        tile.load(rows, lg);
+        hr.store(hrow, p.I, lane);
+        load_act<LPR, BPL>(hrow, lg, xv);
+        float acc[RPL];
+        tile.dot(xv, acc);
+        MOE_DOWN_FINISH(0);
+        for (int s = 1; s < n_e; ++s) {
+          hr.load(p.hbuf + (size_t)(pbeg + s) * p.I, p.I, lane);
+          hr.store(hrow, p.I, lane);
+          load_act<LPR, BPL>(hrow, lg, xv);
+          tile.dot(xv, acc);
+          MOE_DOWN_FINISH(s);
+        }
+      } else {
+        load_act<LPR, BPL>(p.hbuf + (size_t)pbeg * p.I, lg, xv);
+        tile.load(rows, lg);
+        float acc[RPL];
+        tile.dot(xv, acc);
+        MOE_DOWN_FINISH(0);
+        for (int s = 1; s < n_e; ++s) {
+          load_act<LPR, BPL>(p.hbuf + (size_t)(pbeg + s) * p.I, lg, xv);
+          tile.dot(xv, acc);
+          MOE_DOWN_FINISH(s);
+        }
+      }
+#undef MOE_DOWN_FINISH
+    }
+    if (p.out) {
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < p.T * RW; idx += kDownWaves * kWave) {
+        const int t = idx / RW, r = idx - t * RW;
+        float acc = 0.0f;
+        for (int j = 0; j < p.k; ++j) {
+          const float yv = lds_y ? s_y[(t * p.k + j) * RW + r] : p.y[((size_t)t * p.k + j) * p.H + h0 + r];
+          acc = fmaf(topk_w[(size_t)t * p.k + j], yv, acc);
+        }
+        p.out[(size_t)t * p.H + h0 + r] = acc;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------ dispatch
+struct GemvShape {
+  int lpr, bpl;
+};
+
+// Lanes per row: every block of a row is owned by one of LPR lanes, each
+// holding BPL blocks.  Returns false for column counts without a kernel.
+static bool gemv_shape(int cols, GemvShape* s) {
+  const int nblk = cols / kQK;
+  for (int lpr = 64; lpr >= 8; lpr >>= 1) {
+    if (nblk % lpr == 0 && nblk / lpr <= 3) {
+      *s = {lpr, nblk / lpr};
+      return true;
+    }
+  }
+  return false;
+}
+
+template <int QT, int BPL>
+constexpr int rows_per_lane() {
+  constexpr int budget = 64 / (BPL * QTraits<QT>::kWords);  // <= 64 registers of raw codes
+  return budget >= 8 ? 8 : budget >= 4 ? 4 : budget >= 2 ? 2 : 1;
+}
+
+template <int QT, int LPR, int BPL>
+static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStream_t s) {
+  constexpr int RPL0 = rows_per_lane<QT, BPL>();
+  constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
+  ffn_gateup_decode<QT, LPR, BPL, RPL><<<grid, 256, 0, s>>>(p, x);
+}
+// Down tiles aim at 8 rows (H/8 workgroups): RPL = 8 / (64 / LPR) within
+// the register budget.
+template <int QT, int LPR, int BPL>
+constexpr int down_rows_per_lane() {
+  constexpr int want = 8 / (kWave / LPR) > 0 ? 8 / (kWave / LPR) : 1;
+  constexpr int budget = rows_per_lane<QT, BPL>();
+  return want < budget ? want : budget;
+}
+template <int QT, int LPR, int BPL>
+static void launch_down(const FfnParams& p, int grid, hipStream_t s) {
+  ffn_down_decode<QT, LPR, BPL, down_rows_per_lane<QT, LPR, BPL>()><<<grid, kDownWaves * kWave, 0, s>>>(p);
+}
+template <int QT, int LPR, int BPL>
+static constexpr int down_rows_per_tile() {
+  return (kWave / LPR) * down_rows_per_lane<QT, LPR, BPL>();
+}
+template <int QT, int LPR, int BPL>
+static constexpr int rows_per_wave() {
+  constexpr int RPL0 = rows_per_lane<QT, BPL>();
+  constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
+  return (kWave / LPR) * RPL;
+}
+
+template <int QT>
+static int down_rows_rt(GemvShape sh) {
+#define MOE_RPT(L, B) \
+  if (sh.lpr == L && sh.bpl == B) return down_rows_per_tile<QT, L, B>();
+  MOE_RPT(64, 1) MOE_RPT(64, 2) MOE_RPT(64, 3) MOE_RPT(32, 1) MOE_RPT(32, 2) MOE_RPT(32, 3)
+  MOE_RPT(16, 1) MOE_RPT(16, 2) MOE_RPT(16, 3) MOE_RPT(8, 1) MOE_RPT(8, 2) MOE_RPT(8, 3)
+#undef MOE_RPT
+  return 0;
+}
+
+template <int QT>
+static int rows_per_wave_rt(GemvShape sh) {
+#define MOE_RPW(L, B) \
+  if (sh.lpr == L && sh.bpl == B) return rows_per_wave<QT, L, B>();
+  MOE_RPW(64, 1) MOE_RPW(64, 2) MOE_RPW(64, 3) MOE_RPW(32, 1) MOE_RPW(32, 2) MOE_RPW(32, 3)
+  MOE_RPW(16, 1) MOE_RPW(16, 2) MOE_RPW(16, 3) MOE_RPW(8, 1) MOE_RPW(8, 2) MOE_RPW(8, 3)
+#undef MOE_RPW
+  return 0;
+}
+
+template <int QT>
+static void dispatch_gateup(GemvShape sh, const FfnParams& p, const float* x, int grid, hipStream_t s) {
+#define MOE_GU(L, B) \
+  if (sh.lpr == L && sh.bpl == B) return launch_gateup<QT, L, B>(p, x, grid, s);
+  MOE_GU(64, 1) MOE_GU(64, 2) MOE_GU(64, 3) MOE_GU(32, 1) MOE_GU(32, 2) MOE_GU(32, 3)
+  MOE_GU(16, 1) MOE_GU(16, 2) MOE_GU(16, 3) MOE_GU(8, 1) MOE_GU(8, 2) MOE_GU(8, 3)
+#undef MOE_GU
+}
+template <int QT>
+static void dispatch_down(GemvShape sh, const FfnParams& p, int grid, hipStream_t s) {
+#define MOE_DN(L, B) \
+  if (sh.lpr == L && sh.bpl == B) return launch_down<QT, L, B>(p, grid, s);
+  MOE_DN(64, 1) MOE_DN(64, 2) MOE_DN(64, 3) MOE_DN(32, 1) MOE_DN(32, 2) MOE_DN(32, 3)
+  MOE_DN(16, 1) MOE_DN(16, 2) MOE_DN(16, 3) MOE_DN(8, 1) MOE_DN(8, 2) MOE_DN(8, 3)
+#undef MOE_DN
+}
+
+bool decode_gemv_supported(int H, int I, int T, int k) {
+  GemvShape a, b;
+  return (long long)T * k <= kCtlMaxPairs && gemv_shape(H, &a) && gemv_shape(I, &b);
+}
+
+int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s) {
+  GemvShape gu, dn;
+  gemv_shape(p.H, &gu);
+  gemv_shape(p.I, &dn);
+  const int max_active = std::min(p.E, p.T * p.k);
+  const int cap = 16 * ctx->num_cus;
+  int rw_gu, rt_dn;
+  if (p.qtype == MOE_QTYPE_Q8_0) {
+    rw_gu = rows_per_wave_rt<MOE_QTYPE_Q8_0>(gu);
+    rt_dn = down_rows_rt<MOE_QTYPE_Q8_0>(dn);
+  } else {
+    rw_gu = rows_per_wave_rt<MOE_QTYPE_Q4_0>(gu);
+    rt_dn = down_rows_rt<MOE_QTYPE_Q4_0>(dn);
+  }
+  const long long items_gu = (long long)max_active * (p.I / (rw_gu / 2));
+  const int grid_gu = (int)std::max(1LL, std::min<long long>(cap, (items_gu + 3) / 4));
+  const int grid_dn = std::max(1, p.H / rt_dn);
+  {
+    KernelTimer timer(ctx, "ffn_gateup", s);
+    if (p.qtype == MOE_QTYPE_Q8_0) dispatch_gateup<MOE_QTYPE_Q8_0>(gu, p, x, grid_gu, s);
+    else dispatch_gateup<MOE_QTYPE_Q4_0>(gu, p, x, grid_gu, s);
+  }
+  int rc = check_launch("ffn_gateup_decode");
+  if (rc) return rc;
+  {
+    KernelTimer timer(ctx, "ffn_down", s);
+    if (p.qtype == MOE_QTYPE_Q8_0) dispatch_down<MOE_QTYPE_Q8_0>(dn, p, grid_dn, s);
+    else dispatch_down<MOE_QTYPE_Q4_0>(dn, p, grid_dn, s);
+  }
+  return check_launch("ffn_down_decode");
+}
+
+}  // namespace moe

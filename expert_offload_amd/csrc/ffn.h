@@ -19,8 +19,13 @@ struct FfnParams {
   float* y;     // [T*k][H] fp32, pair order
   float* hbuf;  // [T*k][I] fp32, grouped (sorted) order
   int* err;
+  const float* topk_w;  // [T][k] (fused combine only)
+  float* out;           // [T][H] or NULL: fused combine target
 };
 
-int launch_ffn_valu(const FfnParams& p, const void* x, int x_dtype, int grid_cap, hipStream_t s);
+int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype, hipStream_t s);
+bool decode_gemv_supported(int H, int I, int T, int k);
+int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s);
+int launch_combine(moe_ctx* ctx, const float* y, const float* w, int T, int k, int H, float* out, hipStream_t s);
 
 }  // namespace moe

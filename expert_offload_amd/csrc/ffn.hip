@@ -7,6 +7,7 @@ namespace moe {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Workspace: h, T*k x I fp32 in grouped (sorted) pair order.
 static size_t ffn_ws_bytes(const moe_ffn_args* a) {
   return align_up((size_t)a->T * a->k * a->I * sizeof(float), 256);
 }
@@ -43,6 +44,13 @@ static int validate_ffn(const moe_ffn_args* a, bool need_buffers) {
     return set_error(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace holds %zu bytes, needs %zu",
                      a->ws_bytes, ffn_ws_bytes(a));
   if (!aligned(a->ws, 256)) return set_error(MOE_ERR_ALIGNMENT, "moe_expert_ffn: ws must be 256-byte aligned");
+  if (a->out) {
+    if (!a->topk_w) return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: out needs topk_w");
+    if (a->expert_mask)
+      return set_error(MOE_ERR_INVALID_ARG,
+                       "moe_expert_ffn: the fused combine (out) needs every expert in one call (no expert_mask)");
+    if (!aligned(a->out, 16)) return set_error(MOE_ERR_ALIGNMENT, "moe_expert_ffn: out must be 16-byte aligned");
+  }
   return MOE_OK;
 }
 
@@ -80,5 +88,13 @@ extern "C" int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* a, void* stream)
   p.y = a->y_pairs;
   p.hbuf = (float*)a->ws;
   p.err = ctx->d_err;
-  return launch_ffn_valu(p, a->x, a->x_dtype, 8 * ctx->num_cus, (hipStream_t)stream);
+  p.topk_w = a->topk_w;
+  p.out = a->out;
+  hipStream_t s = (hipStream_t)stream;
+  if (a->mode == MOE_MODE_DECODE && decode_gemv_supported(a->H, a->I, a->T, a->k))
+    return launch_ffn_decode(ctx, p, (const float*)a->x, s);
+  p.out = nullptr;
+  rc = launch_ffn_valu(ctx, p, a->x, a->x_dtype, s);
+  if (rc || !a->out) return rc;
+  return launch_combine(ctx, a->y_pairs, a->topk_w, a->T, a->k, a->H, a->out, s);
 }

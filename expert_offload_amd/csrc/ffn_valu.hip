@@ -157,26 +157,33 @@ __global__ __launch_bounds__(256) void ffn_down_valu(FfnParams p) {
   }
 }
 
-int launch_ffn_valu(const FfnParams& p, const void* x, int x_dtype, int grid_cap, hipStream_t s) {
+int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype, hipStream_t s) {
+  const int grid_cap = 8 * ctx->num_cus;
   const int max_active = std::min(p.E, p.T * p.k);
   const int g1 = std::max(1, std::min(grid_cap, max_active * (p.I / 8)));
   const int g2 = std::max(1, std::min(grid_cap, max_active * (p.H / 16)));
-  if (p.qtype == MOE_QTYPE_Q8_0) {
-    if (x_dtype == MOE_DTYPE_F32)
-      ffn_gateup_valu<MOE_QTYPE_Q8_0, float><<<g1, 256, 0, s>>>(p, (const float*)x);
+  {
+    KernelTimer timer(ctx, "ffn_gateup", s);
+    if (p.qtype == MOE_QTYPE_Q8_0) {
+      if (x_dtype == MOE_DTYPE_F32)
+        ffn_gateup_valu<MOE_QTYPE_Q8_0, float><<<g1, 256, 0, s>>>(p, (const float*)x);
+      else
+        ffn_gateup_valu<MOE_QTYPE_Q8_0, uint16_t><<<g1, 256, 0, s>>>(p, (const uint16_t*)x);
+    } else {
+      if (x_dtype == MOE_DTYPE_F32)
+        ffn_gateup_valu<MOE_QTYPE_Q4_0, float><<<g1, 256, 0, s>>>(p, (const float*)x);
+      else
+        ffn_gateup_valu<MOE_QTYPE_Q4_0, uint16_t><<<g1, 256, 0, s>>>(p, (const uint16_t*)x);
+    }
+  }
+  int rc = check_launch("ffn_gateup_valu");
+  if (rc) return rc;
+  {
+    KernelTimer timer(ctx, "ffn_down", s);
+    if (p.qtype == MOE_QTYPE_Q8_0)
+      ffn_down_valu<MOE_QTYPE_Q8_0><<<g2, 256, 0, s>>>(p);
     else
-      ffn_gateup_valu<MOE_QTYPE_Q8_0, uint16_t><<<g1, 256, 0, s>>>(p, (const uint16_t*)x);
-    int rc = check_launch("ffn_gateup_valu");
-    if (rc) return rc;
-    ffn_down_valu<MOE_QTYPE_Q8_0><<<g2, 256, 0, s>>>(p);
-  } else {
-    if (x_dtype == MOE_DTYPE_F32)
-      ffn_gateup_valu<MOE_QTYPE_Q4_0, float><<<g1, 256, 0, s>>>(p, (const float*)x);
-    else
-      ffn_gateup_valu<MOE_QTYPE_Q4_0, uint16_t><<<g1, 256, 0, s>>>(p, (const uint16_t*)x);
-    int rc = check_launch("ffn_gateup_valu");
-    if (rc) return rc;
-    ffn_down_valu<MOE_QTYPE_Q4_0><<<g2, 256, 0, s>>>(p);
+      ffn_down_valu<MOE_QTYPE_Q4_0><<<g2, 256, 0, s>>>(p);
   }
   return check_launch("ffn_down_valu");
 }

@@ -43,6 +43,33 @@ int check_launch(const char* kernel) {
   return MOE_OK;
 }
 
+static hipEvent_t take_event(moe_ctx* ctx) {
+  if (!ctx->spare_events.empty()) {
+    hipEvent_t e = ctx->spare_events.back();
+    ctx->spare_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+KernelTimer::KernelTimer(moe_ctx* ctx, const char* kernel, hipStream_t s) : ctx_(ctx), s_(s) {
+  if (!ctx || !ctx->timing) return;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return;
+  rec_.kernel = kernel;
+  rec_.start = take_event(ctx);
+  rec_.stop = take_event(ctx);
+  if (!rec_.start || !rec_.stop) return;
+  on_ = hipEventRecord(rec_.start, s) == hipSuccess;
+}
+
+KernelTimer::~KernelTimer() {
+  if (!on_) return;
+  if (hipEventRecord(rec_.stop, s_) == hipSuccess) ctx_->recs.push_back(rec_);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -63,7 +90,10 @@ int moe_ctx_create(int device, moe_ctx** out) {
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return hip_error(e, "hipDeviceGetAttribute");
-  moe_ctx* c = new moe_ctx{device, cus, nullptr};
+  moe_ctx* c = new moe_ctx;
+  c->device = device;
+  c->num_cus = cus;
+  c->d_err = nullptr;
   if ((e = hipMalloc(&c->d_err, sizeof(int))) != hipSuccess) {
     delete c;
     return hip_error(e, "hipMalloc(error word)");
@@ -77,9 +107,47 @@ int moe_ctx_create(int device, moe_ctx** out) {
   return MOE_OK;
 }
 
+int moe_ctx_set_timing(moe_ctx* ctx, int enable) {
+  clear_error();
+  if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_ctx_set_timing: ctx is NULL");
+  for (auto& r : ctx->recs) {
+    ctx->spare_events.push_back(r.start);
+    ctx->spare_events.push_back(r.stop);
+  }
+  ctx->recs.clear();
+  ctx->timing = enable != 0;
+  return MOE_OK;
+}
+
+int moe_ctx_kernel_time(moe_ctx* ctx, const char* kernel, int* count, double* total_ms) {
+  clear_error();
+  if (!ctx || !kernel || !count || !total_ms)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_ctx_kernel_time: NULL argument");
+  int n = 0;
+  double tot = 0.0;
+  for (auto& r : ctx->recs) {
+    if (std::strcmp(r.kernel, kernel) != 0) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_error(e, "hipEventSynchronize");
+    float ms = 0.0f;
+    if ((e = hipEventElapsedTime(&ms, r.start, r.stop)) != hipSuccess) return hip_error(e, "hipEventElapsedTime");
+    tot += ms;
+    ++n;
+  }
+  *count = n;
+  *total_ms = tot;
+  return MOE_OK;
+}
+
 int moe_ctx_destroy(moe_ctx* ctx) {
   clear_error();
   if (!ctx) return MOE_OK;
+  (void)hipDeviceSynchronize();
+  for (auto& r : ctx->recs) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  for (auto e : ctx->spare_events) (void)hipEventDestroy(e);
   if (ctx->d_err) (void)hipFree(ctx->d_err);
   delete ctx;
   return MOE_OK;

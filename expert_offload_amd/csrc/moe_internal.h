@@ -6,16 +6,41 @@
 #include <cstddef>
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "../../include/moe.h"
+
+struct moe_timing_rec {
+  const char* kernel;
+  hipEvent_t start, stop;
+};
 
 struct moe_ctx {
   int device;
   int num_cus;
-  int* d_err;  // sticky device error word: 0 or (expert id + 1)
+  int* d_err;  // sticky device error word: 0, (expert id + 1), or INT_MIN
+  bool timing = false;
+  std::vector<moe_timing_rec> recs;
+  std::vector<hipEvent_t> spare_events;
 };
 
 namespace moe {
+
+// Brackets one kernel launch with HIP events on its stream while the
+// context's timing is on (never inside a stream capture).
+class KernelTimer {
+ public:
+  KernelTimer(moe_ctx* ctx, const char* kernel, hipStream_t s);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  moe_ctx* ctx_;
+  hipStream_t s_;
+  moe_timing_rec rec_{};
+  bool on_ = false;
+};
 
 // ---------------------------------------------------------------- errors
 int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -1,0 +1,290 @@
+// Device routines shared by the routing kernels: the wavefront top-k and
+// the single-workgroup stable grouping of pairs by expert.
+#pragma once
+
+#include <climits>
+
+#include "device_common.h"
+
+namespace moe {
+
+// One wavefront selects the top k of token t's E logits (src row, plus
+// bias when given); NS = ceil(E / 64) logits per lane, slot i of lane l
+// holding id l + 64 i.  Each round takes the wave-wide maximum of the values
+// still free (a 32-bit max reduction), then the lowest id holding that value
+// (ballots over the slots): equal values go to the lower id.  Then w_j =
+// exp(l_j - l_max) / sum_j' exp(l_j' - l_max), which equals the softmax
+// probabilities renormalised over the kept experts.  NaN logits count as
+// -inf.  Writes ids/w (and the logits used, when logits_out is set); ids
+// also go to ids_copy if set.
+template <int NS>
+__device__ __forceinline__ void wave_topk_ns(const float* __restrict__ src, const float* __restrict__ bias,
+                                             int E, int k, float* __restrict__ logits_out,
+                                             int32_t* __restrict__ ids, float* __restrict__ w,
+                                             int32_t* ids_copy) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float v[NS];
+  bool ok[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int e = lane + kWave * i;
+    ok[i] = e < E;
+    v[i] = ok[i] ? src[e] : -INFINITY;
+  }
+  if (bias) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (ok[i]) v[i] += bias[lane + kWave * i];
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (ok[i] && logits_out) logits_out[lane + kWave * i] = v[i];
+    if (v[i] != v[i]) v[i] = -INFINITY;
+  }
+  float my_val = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (ok[i]) m = fmaxf(m, v[i]);
+    m = wave_max_dpp(m);
+    int bi = -1;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const uint64_t mask = __ballot(ok[i] && v[i] == m);
+      if (bi < 0 && mask) bi = (int)__builtin_ctzll(mask) + kWave * i;
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (lane + kWave * i == bi) ok[i] = false;  // taken
+    if (lane == j) my_val = m;
+    if (lane == 0) {
+      ids[j] = bi;
+      if (ids_copy) ids_copy[j] = bi;
+    }
+  }
+  const float m0 = __shfl(my_val, 0, kWave);
+  const float ex = lane < k ? expf(my_val - m0) : 0.0f;
+  const float s = wave_sum_dpp(ex);
+  if (lane < k) w[lane] = ex / s;
+}
+
+__device__ __forceinline__ void wave_topk(const float* __restrict__ src, const float* __restrict__ bias,
+                                          int E, int k, float* __restrict__ logits_out,
+                                          int32_t* __restrict__ ids, float* __restrict__ w,
+                                          int32_t* ids_copy) {
+  if (E <= 64) wave_topk_ns<1>(src, bias, E, k, logits_out, ids, w, ids_copy);
+  else if (E <= 128) wave_topk_ns<2>(src, bias, E, k, logits_out, ids, w, ids_copy);
+  else if (E <= 256) wave_topk_ns<4>(src, bias, E, k, logits_out, ids, w, ids_copy);
+  else if (E <= 512) wave_topk_ns<8>(src, bias, E, k, logits_out, ids, w, ids_copy);
+  else wave_topk_ns<16>(src, bias, E, k, logits_out, ids, w, ids_copy);
+}
+
+// Exclusive scan of n <= kMaxE ints in LDS `a` into LDS `out` by a block of
+// NT threads; returns the total.  Uses s_wave[NT / 64].
+template <int NT>
+__device__ int block_exclusive_scan(const int* a, int* out, int n, int* s_wave) {
+  constexpr int per = kMaxE / NT;
+  constexpr int waves = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  int v[per];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    const int idx = tid * per + i;
+    v[i] = idx < n ? a[idx] : 0;
+    local += v[i];
+  }
+  int inc = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += o;
+  }
+  if (lane == kWave - 1) s_wave[wave] = inc;
+  __syncthreads();
+  int wave_base = 0, total = 0;
+  for (int w = 0; w < waves; ++w) {
+    if (w < wave) wave_base += s_wave[w];
+    total += s_wave[w];
+  }
+  int run = wave_base + inc - local;
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    const int idx = tid * per + i;
+    if (idx < n) out[idx] = run;
+    run += v[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// LDS scratch of block_permute for NT threads.
+template <int NT>
+struct PermuteLds {
+  int cnt[kMaxE];
+  int cur[kMaxE];
+  int wcnt[NT / kWave][kMaxE];
+  int wave[NT / kWave];
+};
+
+// Stable grouping of the P pairs (ids[p] = expert of pair p) by one block of
+// NT threads: LDS histogram, exclusive scan, then rounds of NT pairs whose
+// ranks among equal ids come from wavefront ballots over the id bits plus
+// per-wave counts.  Ids outside [0, E) are left out (err set to INT_MIN,
+// pair_pos = -1, trailing sorted_pairs = -1).
+template <int NT>
+__device__ void block_permute(const int32_t* ids, int P, int E, int32_t* __restrict__ offsets,
+                              int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+                              int32_t* __restrict__ active, int* __restrict__ err, PermuteLds<NT>& s) {
+  constexpr int waves = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  for (int i = tid; i < E; i += NT) s.cnt[i] = 0;
+  for (int i = tid; i < waves * E; i += NT) s.wcnt[i / E][i % E] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += NT) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) {
+      atomicAdd(&s.cnt[e], 1);
+    } else {
+      atomicCAS(err, 0, INT_MIN);
+      pair_pos[p] = -1;
+    }
+  }
+  __syncthreads();
+  const int n_valid = block_exclusive_scan<NT>(s.cnt, s.cur, E, s.wave);
+  for (int e = tid; e < E; e += NT) offsets[e] = s.cur[e];
+  if (tid == 0) offsets[E] = n_valid;
+  for (int i = n_valid + tid; i < P; i += NT) sorted_pairs[i] = -1;
+  // active experts via a scan of (count > 0); wcnt rows 0 and 1 are scratch here
+  static_assert(waves >= 2, "block_permute needs at least two wavefronts");
+  int* flags = &s.wcnt[0][0];
+  int* fpos = &s.wcnt[1][0];
+  for (int e = tid; e < E; e += NT) flags[e] = s.cnt[e] > 0;
+  __syncthreads();
+  const int n_active = block_exclusive_scan<NT>(flags, fpos, E, s.wave);
+  for (int e = tid; e < E; e += NT)
+    if (s.cnt[e] > 0) active[1 + fpos[e]] = e;
+  if (tid == 0) active[0] = n_active;
+  __syncthreads();
+  for (int i = tid; i < 2 * E; i += NT) s.wcnt[i / E][i % E] = 0;
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int r0 = 0; r0 < P; r0 += NT) {
+    const int p = r0 + tid;
+    const int id = p < P ? ids[p] : E;
+    const bool valid = (unsigned)id < (unsigned)E;
+    const int e = valid ? id : E;
+    uint64_t match = __ballot(1);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool b = (e >> bit) & 1;
+      const uint64_t m = __ballot(b);
+      match &= b ? m : ~m;
+    }
+    const int rank = __popcll(match & lt_mask);
+    if (valid && rank == 0) s.wcnt[wave][e] = __popcll(match);
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int w = 0; w < wave; ++w) pre += s.wcnt[w][e];
+      const int pos = s.cur[e] + pre + rank;
+      sorted_pairs[pos] = p;
+      pair_pos[p] = pos;
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&s.cur[e], s.wcnt[wave][e]);
+      s.wcnt[wave][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// Stable grouping by the first wavefront of the block alone (no barriers),
+// for P <= 1024 pairs: LDS histogram, a wave-level exclusive scan over the
+// experts (each lane owns ceil(E/64) consecutive ids), then rounds of 64
+// pairs ranked by ballots over the id bits and a per-expert LDS cursor.
+// cnt and cur are LDS arrays of >= E ints.  Same outputs as block_permute.
+__device__ void wave_permute(const int32_t* ids, int P, int E, int32_t* __restrict__ offsets,
+                             int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+                             int32_t* __restrict__ active, int* __restrict__ err, int* cnt, int* cur) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int p = lane; p < P; p += kWave) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) {
+      atomicAdd(&cnt[e], 1);
+    } else {
+      atomicCAS(err, 0, INT_MIN);
+      pair_pos[p] = -1;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int per = (E + kWave - 1) / kWave;
+  const int e0 = lane * per;
+  int tot = 0, nz = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      tot += cnt[e];
+      nz += cnt[e] > 0;
+    }
+  }
+  int inc_t = tot, inc_n = nz;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int a = __shfl_up(inc_t, off, kWave), b = __shfl_up(inc_n, off, kWave);
+    if (lane >= off) {
+      inc_t += a;
+      inc_n += b;
+    }
+  }
+  int run = inc_t - tot, arun = inc_n - nz;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int c = cnt[e];
+      offsets[e] = run;
+      cur[e] = run;
+      if (c > 0) active[1 + arun++] = e;
+      run += c;
+    }
+  }
+  const int n_valid = __shfl(inc_t, kWave - 1, kWave);
+  const int n_act = __shfl(inc_n, kWave - 1, kWave);
+  if (lane == 0) {
+    offsets[E] = n_valid;
+    active[0] = n_act;
+  }
+  for (int i = n_valid + lane; i < P; i += kWave) sorted_pairs[i] = -1;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int r0 = 0; r0 < P; r0 += kWave) {
+    const int p = r0 + lane;
+    const int id = p < P ? ids[p] : E;
+    const bool valid = (unsigned)id < (unsigned)E;
+    const int e = valid ? id : E;
+    uint64_t match = __ballot(1);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool b = (e >> bit) & 1;
+      const uint64_t m = __ballot(b);
+      match &= b ? m : ~m;
+    }
+    const int rank = __popcll(match & lt_mask);
+    if (valid) {
+      const int pos = cur[e] + rank;
+      sorted_pairs[pos] = p;
+      pair_pos[p] = pos;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (valid && rank == 0) cur[e] += __popcll(match);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+}
+
+}  // namespace moe

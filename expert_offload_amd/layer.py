@@ -63,14 +63,31 @@ class LayerBuffers:
         probe = L.moe_ffn_args(qtype=self.q, H=H, I=I, T=T, k=k, E=E, mode=mode, x_dtype=x_dtype, n_slots=1,
                                slot_bytes=L.moe_slot_bytes(self.q, H, I))
         self.ws_bytes = L.moe_expert_ffn_workspace_size(probe)
-        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        # workspaces start zeroed; the library leaves their counters zero
+        self.ws = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.route_ws = torch.zeros(max(L.moe_route_permute_workspace_size(T, k, E), 256),
+                                    dtype=torch.uint8, device=device)
 
 
 def forward(ctx: L.Ctx, buf: LayerBuffers, pool_base: int, slot_bytes: int, n_slots: int, slot_table, x,
             router_w=None, bias=None, logits_in=None, expert_mask=None, stream=None,
-            steps=("route", "permute", "ffn", "combine")) -> torch.Tensor:
-    """One layer forward; returns ``buf.out`` (valid in stream order)."""
+            steps=("route", "permute", "ffn", "combine"), fused: bool = False) -> torch.Tensor:
+    """One layer forward; returns ``buf.out`` (valid in stream order).
+
+    ``fused``: moe_route_permute, then moe_expert_ffn with the combine folded
+    in (two calls); otherwise the four entry points one after another.
+    """
     T, H, I, E, k = buf.T, buf.H, buf.I, buf.E, buf.k
+    if fused and expert_mask is None:
+        L.moe_route_permute(ctx, x, router_w, bias, logits_in, T, H, E, k, buf.logits, buf.ids, buf.w,
+                            buf.offsets, buf.sorted_pairs, buf.pair_pos, buf.active, buf.route_ws,
+                            buf.route_ws.numel(), stream=stream, x_dtype=buf.x_dtype)
+        args = L.make_ffn_args(pool_base, slot_bytes, n_slots, buf.q, H, I, T, k, E, slot_table, x,
+                               buf.offsets, buf.sorted_pairs, buf.active, buf.y, buf.mode,
+                               ws=buf.ws, ws_bytes=buf.ws.numel(), x_dtype=buf.x_dtype,
+                               topk_w=buf.w, out=buf.out)
+        L.moe_expert_ffn(ctx, args, stream=stream)
+        return buf.out
     if "route" in steps:
         L.moe_route(ctx, x, router_w, bias, logits_in, T, H, E, k, buf.logits, buf.ids, buf.w,
                     stream=stream, x_dtype=buf.x_dtype)

@@ -87,6 +87,18 @@ int moe_ctx_create(int device, moe_ctx** out);
 int moe_ctx_destroy(moe_ctx* ctx);
 int moe_ctx_check(moe_ctx* ctx, void* stream);
 
+/* Per-kernel timing for profiling.  moe_ctx_set_timing(ctx, 1) makes every
+ * later launch of this context record a HIP event pair around the kernel on
+ * its stream (launches inside a stream capture are not timed); enabling or
+ * disabling discards earlier records.  moe_ctx_kernel_time waits for the
+ * recorded launches of `kernel` (names: "router_logits", "topk", "permute",
+ * "ffn_gateup", "ffn_down", "combine", "dequant", "topk_permute") and
+ * returns their number
+ * and summed duration in milliseconds. */
+int moe_ctx_set_timing(moe_ctx* ctx, int enable);
+int moe_ctx_kernel_time(moe_ctx* ctx, const char* kernel, int* count,
+                        double* total_ms);
+
 /* ------------------------------------------------------------ block types
  * Q8_0: 32 weights, fp16 scale d + 32 int8 q (34 B), w = d*q.
  * Q4_0: 32 weights, fp16 scale d + 16 nibble bytes (18 B), w = d*(q-8);
@@ -145,6 +157,18 @@ int moe_route(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w,
  * ws: device workspace of moe_permute_workspace_size() bytes (may be NULL
  * when that size is 0). */
 int moe_permute_workspace_size(int T, int k, int E, size_t* bytes);
+/* moe_route_permute: moe_route followed by moe_permute with the top-k and
+ * the grouping in one launch, for decode-sized batches (T*k <= 4096;
+ * larger batches run the separate kernels).  Same arguments and results;
+ * the workspace size is 0 (ws may be NULL). */
+int moe_route_permute_workspace_size(int T, int k, int E, size_t* bytes);
+int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype,
+                      const float* router_w, const float* bias,
+                      const float* logits_in, int T, int H, int E, int k,
+                      float* logits_out, int32_t* topk_ids, float* topk_w,
+                      int32_t* expert_offsets, int32_t* sorted_pairs,
+                      int32_t* pair_pos, int32_t* active, void* ws,
+                      size_t ws_bytes, void* stream);
 int moe_permute(moe_ctx* ctx, const int32_t* topk_ids, int T, int k, int E,
                 int32_t* expert_offsets, int32_t* sorted_pairs,
                 int32_t* pair_pos, int32_t* active, void* ws, size_t ws_bytes,
@@ -175,8 +199,12 @@ typedef struct moe_ffn_args {
   const int32_t* expert_mask;     /* device [E] or NULL (= all) */
   float* y_pairs;                 /* device fp32 [T*k][H], pair order */
   int mode;                       /* MOE_MODE_DECODE or MOE_MODE_PREFILL */
-  void* ws;                       /* device workspace */
+  void* ws;                       /* device workspace (256-B aligned) */
   size_t ws_bytes;
+  const float* topk_w;            /* device [T][k]; with out: fused combine */
+  float* out;                     /* device fp32 [T][H] or NULL: when set,
+                                     the call also writes out as
+                                     moe_combine would (needs no mask) */
 } moe_ffn_args;
 
 int moe_expert_ffn_workspace_size(const moe_ffn_args* args, size_t* bytes);

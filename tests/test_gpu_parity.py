@@ -155,19 +155,24 @@ def test_permute_exact(ctx, T, k, E):
 
 # ------------------------------------------------------------- whole layers
 def _run_layer(ctx, rl, T, x, wr=None, b=None, logits=None, mode=L.MODE_DECODE, x_dtype=L.DTYPE_F32,
-               xd=None):
+               xd=None, fused=False, repeat=1):
     wl = rl.wl
     buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV, mode=mode,
                              x_dtype=x_dtype)
-    buf.y.fill_(float("nan"))
-    buf.out.fill_(float("nan"))
-    out = layer.forward(ctx, buf, rl.pool.base(), rl.pool.slot_bytes, rl.pool.n_slots, rl.slot_table,
-                        dev(x) if xd is None else xd,
-                        router_w=None if wr is None else dev(wr), bias=None if b is None else dev(b),
-                        logits_in=None if logits is None else dev(logits))
-    torch.cuda.synchronize()
-    moe.moe_ctx_check(ctx)
-    return buf, out.cpu().numpy()
+    outs = []
+    for _ in range(repeat):
+        buf.y.fill_(float("nan"))
+        buf.out.fill_(float("nan"))
+        out = layer.forward(ctx, buf, rl.pool.base(), rl.pool.slot_bytes, rl.pool.n_slots, rl.slot_table,
+                            dev(x) if xd is None else xd,
+                            router_w=None if wr is None else dev(wr), bias=None if b is None else dev(b),
+                            logits_in=None if logits is None else dev(logits), fused=fused)
+        torch.cuda.synchronize()
+        moe.moe_ctx_check(ctx)
+        outs.append(out.cpu().numpy())
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])  # counters were reset between calls
+    return buf, outs[0]
 
 
 def _check_layer(buf, got_out, ref, tol, T):
@@ -199,14 +204,91 @@ def decode_layer():
     return ResidentLayer(gi.workload("decode_q8_0_h2048_e128"), layer_idx=0)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("T", [1, 4, 16])
-def test_decode_q8_0_layer(ctx, decode_layer, T):
-    note(f"decode q8_0 layer T={T}")
+def test_decode_q8_0_layer(ctx, decode_layer, T, fused):
+    note(f"decode q8_0 layer T={T} fused={fused}")
     wl = decode_layer.wl
     x, wr = gi.activations(wl, T), gi.router_weight(wl, 0)
-    buf, out = _run_layer(ctx, decode_layer, T, x, wr)
+    buf, out = _run_layer(ctx, decode_layer, T, x, wr, fused=fused, repeat=2)
     ref = oracle.moe_layer(x, wl.qtype, decode_layer.get_blocks, wl.k, router_w=wr)
     _check_layer(buf, out, ref, DECODE_TOL, T)
+
+
+def test_tiny_layer_fused(ctx):
+    wl = gi.workload("tiny_q8_0")
+    T = wl.batches[0]
+    rl = ResidentLayer(wl)
+    x, wr = gi.activations(wl, T), gi.router_weight(wl)
+    buf, out = _run_layer(ctx, rl, T, x, wr, fused=True, repeat=3)
+    ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, router_w=wr)
+    _check_layer(buf, out, ref, DECODE_TOL, T)
+
+
+@pytest.fixture(scope="module")
+def wide_layer():
+    return ResidentLayer(gi.workload("wide_q4_0_h2048_e512"), layer_idx=0)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("T", [1, 64])
+def test_wide_q4_0_layer_zipf(ctx, wide_layer, T, fused):
+    note(f"wide q4_0 layer T={T} fused={fused}")
+    wl = wide_layer.wl
+    x, wr, b = gi.activations(wl, T), gi.router_weight(wl, 0), gi.router_bias(wl)
+    buf, out = _run_layer(ctx, wide_layer, T, x, wr, b, fused=fused, repeat=2)
+    ref = oracle.moe_layer(x, wl.qtype, wide_layer.get_blocks, wl.k, router_w=wr, bias=b)
+    _check_layer(buf, out, ref, DECODE_TOL, T)
+    counts = np.diff(buf.offsets.cpu().numpy())
+    note(f"   active experts {int((counts > 0).sum())}, max tokens per expert {int(counts.max())}")
+
+
+def test_cache_shaped_q4_0_layer(ctx):
+    """H=4096, I=2048, 256 experts, top-8 (one layer, all resident)."""
+    wl = gi.workload("cache_q4_0_h4096_e256")
+    T = 1
+    trace = gi.cache_trace(wl, steps=3)
+    ids_needed = sorted(set(int(e) for e in trace[:, 0].ravel()))
+    rl = ResidentLayer(wl, layer_idx=0, experts=ids_needed)
+    for step in range(3):
+        logits = gi.cache_trace_logits(wl, trace, step)[0:1]
+        x = gi.activations(wl, T, step)
+        for fused in (False, True):
+            buf, out = _run_layer(ctx, rl, T, x, logits=logits, fused=fused)
+            ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, logits=logits)
+            assert sorted(buf.ids.cpu().numpy()[0].tolist()) == sorted(trace[step, 0].tolist())
+            _check_layer(buf, out, ref, DECODE_TOL, T)
+
+
+@pytest.mark.parametrize("T,E,k,H,given", [(1, 128, 8, 2048, False), (16, 128, 8, 2048, False),
+                                           (64, 512, 10, 2048, False), (4, 8, 2, 256, False),
+                                           (3, 1024, 64, 256, False), (7, 256, 8, 4096, True),
+                                           (500, 128, 8, 2048, True)])
+def test_route_permute_fused_equals_separate(ctx, T, E, k, H, given):
+    note(f"route_permute T={T} E={E} k={k} given={given}")
+    rng = np.random.default_rng(T + E + k)
+    x = dev(rng.standard_normal((T, H)).astype(np.float32))
+    wr = dev((rng.standard_normal((E, H)) * 0.02).astype(np.float32))
+    lg = dev(rng.standard_normal((T, E)).astype(np.float32)) if given else None
+    bias = dev(rng.standard_normal(E).astype(np.float32) * 0.1)
+
+    def bufs():
+        return dict(lo=torch.full((T, E), np.nan, device=DEV), ids=torch.full((T, k), -7, dtype=torch.int32, device=DEV),
+                    w=torch.full((T, k), np.nan, device=DEV), off=torch.full((E + 1,), -7, dtype=torch.int32, device=DEV),
+                    sp=torch.full((T * k,), -7, dtype=torch.int32, device=DEV),
+                    pos=torch.full((T * k,), -7, dtype=torch.int32, device=DEV),
+                    act=torch.full((E + 1,), -7, dtype=torch.int32, device=DEV))
+    a, f = bufs(), bufs()
+    moe.moe_route(ctx, x, wr, bias, lg, T, H, E, k, a["lo"], a["ids"], a["w"])
+    moe.moe_permute(ctx, a["ids"], T, k, E, a["off"], a["sp"], a["pos"], a["act"])
+    assert moe.moe_route_permute_workspace_size(T, k, E) == 0
+    for _ in range(2):
+        moe.moe_route_permute(ctx, x, wr, bias, lg, T, H, E, k, f["lo"], f["ids"], f["w"], f["off"], f["sp"],
+                              f["pos"], f["act"], None, 0)
+    torch.cuda.synchronize()
+    moe.moe_ctx_check(ctx)
+    for key in a:
+        np.testing.assert_array_equal(a[key].cpu().numpy(), f[key].cpu().numpy(), err_msg=key)
 
 
 def test_not_resident_expert_gives_nan_and_error(ctx):
