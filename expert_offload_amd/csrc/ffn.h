@@ -26,6 +26,9 @@ struct FfnParams {
 int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype, hipStream_t s);
 bool decode_gemv_supported(int H, int I, int T, int k);
 int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s);
+bool prefill_mfma_supported(int H, int I);
+size_t prefill_ws_bytes(int T, int k, int I, int E);
+int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws, hipStream_t s);
 int launch_combine(moe_ctx* ctx, const float* y, const float* w, int T, int k, int H, float* out, hipStream_t s);
 
 }  // namespace moe

@@ -7,9 +7,12 @@ namespace moe {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace: h, T*k x I fp32 in grouped (sorted) pair order.
+// Workspace: decode keeps h as T*k x I fp32 in grouped (sorted) pair order;
+// prefill keeps a tile list and h as bf16.  One size covers both.
 static size_t ffn_ws_bytes(const moe_ffn_args* a) {
-  return align_up((size_t)a->T * a->k * a->I * sizeof(float), 256);
+  const size_t dec = align_up((size_t)a->T * a->k * a->I * sizeof(float), 256);
+  const size_t pre = align_up(prefill_ws_bytes(a->T, a->k, a->I, a->E), 256);
+  return dec > pre ? dec : pre;
 }
 
 static int validate_ffn(const moe_ffn_args* a, bool need_buffers) {
@@ -94,7 +97,10 @@ extern "C" int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* a, void* stream)
   if (a->mode == MOE_MODE_DECODE && decode_gemv_supported(a->H, a->I, a->T, a->k))
     return launch_ffn_decode(ctx, p, (const float*)a->x, s);
   p.out = nullptr;
-  rc = launch_ffn_valu(ctx, p, a->x, a->x_dtype, s);
+  if (a->mode == MOE_MODE_PREFILL && a->x_dtype == MOE_DTYPE_BF16 && prefill_mfma_supported(a->H, a->I))
+    rc = launch_ffn_prefill(ctx, p, a->x, a->ws, s);
+  else
+    rc = launch_ffn_valu(ctx, p, a->x, a->x_dtype, s);
   if (rc || !a->out) return rc;
   return launch_combine(ctx, a->y_pairs, a->topk_w, a->T, a->k, a->H, a->out, s);
 }

@@ -311,3 +311,56 @@ def test_not_resident_expert_gives_nan_and_error(ctx):
     uses = (ref["ids"] == victim).any(axis=1)
     assert np.isnan(out[uses]).all(axis=1).all()
     assert np.isfinite(out[~uses]).all()
+
+
+# ---------------------------------------------------------------- prefill
+PREFILL_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def prefill_layer():
+    return ResidentLayer(gi.workload("prefill_q4_0_h2048_e128"), layer_idx=0)
+
+
+def _prefill_inputs(wl, T):
+    logits = gi.given_logits(wl, T)
+    xbits = gi.activations(wl, T)
+    return logits, xbits, gi.bf16_bits_to_f32(xbits)
+
+
+@pytest.mark.parametrize("T", [1, 37, 300, 1000])
+def test_prefill_layer(ctx, prefill_layer, T):
+    """Grouped-GEMM path (bf16 MFMA) against the oracle, ragged expert tiles."""
+    note(f"prefill q4_0 layer T={T}")
+    wl = prefill_layer.wl
+    logits, xbits, x32 = _prefill_inputs(wl, T)
+    from gpu_util import bf16_tensor
+    buf, out = _run_layer(ctx, prefill_layer, T, x32, logits=logits, mode=L.MODE_PREFILL,
+                          x_dtype=L.DTYPE_BF16, xd=bf16_tensor(xbits), repeat=2)
+    ref = oracle.moe_layer(x32, wl.qtype, prefill_layer.get_blocks, wl.k, logits=logits)
+    np.testing.assert_array_equal(buf.ids.cpu().numpy(), ref["ids"])
+    _check_layer(buf, out, ref, PREFILL_TOL, T)
+
+
+def test_prefill_full_size_sampled(ctx, prefill_layer):
+    """4096 tokens, ~256 pairs per expert; 64 sampled tokens checked against the oracle."""
+    wl = prefill_layer.wl
+    T = wl.batches[0]
+    note(f"prefill full size T={T}")
+    logits, xbits, x32 = _prefill_inputs(wl, T)
+    from gpu_util import bf16_tensor
+    buf, out = _run_layer(ctx, prefill_layer, T, x32, logits=logits, mode=L.MODE_PREFILL,
+                          x_dtype=L.DTYPE_BF16, xd=bf16_tensor(xbits))
+    counts = np.diff(buf.offsets.cpu().numpy())
+    note(f"   pairs per expert: min {counts.min()} max {counts.max()}")
+    rng = np.random.default_rng(5)
+    sample = np.sort(rng.choice(T, 64, replace=False))
+    sample[0], sample[-1] = 0, T - 1
+    ref = oracle.moe_layer(x32[sample], wl.qtype, prefill_layer.get_blocks, wl.k, logits=logits[sample])
+    np.testing.assert_array_equal(buf.ids.cpu().numpy()[sample], ref["ids"])
+    err = max_rel_err(out[sample], ref["out"])
+    y = buf.y.cpu().numpy().reshape(T, wl.k, wl.H)[sample]
+    e_y = max_rel_err(y, ref["y_pairs"].reshape(len(sample), wl.k, wl.H))
+    note(f"   sampled out max rel err {err:.2e}, y {e_y:.2e}")
+    assert err <= PREFILL_TOL and e_y <= PREFILL_TOL
+    assert np.isfinite(out).all()
