@@ -103,3 +103,74 @@ def forward(ctx: L.Ctx, buf: LayerBuffers, pool_base: int, slot_bytes: int, n_sl
     if "combine" in steps:
         L.moe_combine(ctx, buf.y, buf.w, T, k, H, buf.out, stream=stream)
     return buf.out
+
+
+class CachedLayers:
+    """Decode through L layers whose experts live in a pinned host pool,
+    with a VRAM expert cache (cache_slot_table_* / prefetch_expert).
+
+    Per layer: route on the GPU; the ids come back to the host (the host
+    cannot know them earlier, since a layer's routing depends on that
+    layer's input); the host looks them up in the global LRU; the FFN runs
+    on the hits while the misses are copied on a side stream; then the FFN
+    runs on the misses and the combine forms the output.
+    """
+
+    def __init__(self, ctx: L.Ctx, qtype: str, H: int, I: int, E: int, k: int, L_layers: int,
+                 n_slots: int, host_pool: torch.Tensor, device="cuda"):
+        self.ctx, self.qtype, self.H, self.I, self.E, self.k, self.L = ctx, qtype, H, I, E, k, L_layers
+        self.q = L.QTYPE[qtype]
+        self.slot_bytes = L.moe_slot_bytes(self.q, H, I)
+        self.n_slots = n_slots
+        self.d_pool = torch.empty((n_slots + 2) * self.slot_bytes, dtype=torch.uint8, device=device)
+        self.host_pool = host_pool
+        self.cache = L.cache_slot_table_create(L_layers, E, n_slots, self.q, H, I, self.d_pool, host_pool)
+        self.table = L.cache_slot_table_device(self.cache)
+        self.copy_stream = torch.cuda.Stream()
+        self.buf = LayerBuffers(1, H, I, E, k, qtype, device=device)
+        self.ids_host = torch.empty((1, k), dtype=torch.int32, pin_memory=True)
+        self.mask_host = torch.zeros((2, E), dtype=torch.int32, pin_memory=True)
+        self.mask_dev = torch.zeros((2, E), dtype=torch.int32, device=device)
+        self.ev_ids = torch.cuda.Event()
+        self.misses_per_layer = []
+
+    def layer(self, l: int, x: torch.Tensor, logits: torch.Tensor, stream=None) -> torch.Tensor:
+        b = self.buf
+        s = stream or torch.cuda.current_stream()
+        L.moe_route_permute(self.ctx, x, None, None, logits, 1, self.H, self.E, self.k, b.logits, b.ids, b.w,
+                            b.offsets, b.sorted_pairs, b.pair_pos, b.active, None, 0, stream=s)
+        self.ids_host.copy_(b.ids, non_blocking=True)
+        self.ev_ids.record(s)
+        self.ev_ids.synchronize()
+        ids = self.ids_host.numpy()[0]
+        slots, misses = L.cache_slot_table_lookup(self.cache, l, ids)
+        self.misses_per_layer.append(len(misses))
+        hit = np.isin(np.arange(self.E), ids) & ~np.isin(np.arange(self.E), misses)
+        self.mask_host[0].copy_(torch.from_numpy(hit.astype(np.int32)))
+        self.mask_host[1].copy_(torch.from_numpy(np.isin(np.arange(self.E), misses).astype(np.int32)))
+        self.mask_dev.copy_(self.mask_host, non_blocking=True)
+        table = self.table + 4 * l * self.E
+        base = self.d_pool.data_ptr()
+        common = dict(ws=b.ws, ws_bytes=b.ws.numel(), x_dtype=L.DTYPE_F32)
+        if hit.any():
+            args = L.make_ffn_args(base, self.slot_bytes, self.n_slots + 2, self.q, self.H, self.I, 1, self.k,
+                                   self.E, table, x, b.offsets, b.sorted_pairs, b.active, b.y, L.MODE_DECODE,
+                                   expert_mask=self.mask_dev[0], **common)
+            L.moe_expert_ffn(self.ctx, args, stream=s)
+        if len(misses):
+            for e in misses:
+                L.prefetch_expert(self.cache, l, int(e), self.copy_stream, s)
+            args = L.make_ffn_args(base, self.slot_bytes, self.n_slots + 2, self.q, self.H, self.I, 1, self.k,
+                                   self.E, table, x, b.offsets, b.sorted_pairs, b.active, b.y, L.MODE_DECODE,
+                                   expert_mask=self.mask_dev[1], **common)
+            L.moe_expert_ffn(self.ctx, args, stream=s)
+        L.moe_combine(self.ctx, b.y, b.w, 1, self.k, self.H, b.out, stream=s)
+        L.cache_mark_layer_done(self.cache, l, s)
+        return b.out
+
+    def stats(self):
+        return L.cache_slot_table_stats(self.cache)
+
+    def close(self):
+        torch.cuda.synchronize()
+        self.cache.close()

@@ -1,0 +1,152 @@
+"""Expert cache on the GPU: the library's global LRU agrees exactly with the
+oracle's simulation, prefetched experts give the oracle's layer outputs,
+and the documented errors (unpinned pool, capacity, unmarked layer) fire."""
+import numpy as np
+import pytest
+import torch
+
+import expert_offload_amd as moe
+from expert_offload_amd import _lib as L
+from expert_offload_amd import layer
+from gen import inputs as gi
+import oracle
+
+from gpu_util import DEV, dev, max_rel_err, note
+
+pytestmark = pytest.mark.gpu
+
+SMALL = gi.Workload(6, "cache_small_q4_0", H=512, E=16, k=4, I=256, qtype="q4_0", batches=(1,),
+                    layers=3, router="trace", cache_fraction=0.6, steps=40, trace_keep_p=0.7,
+                    trace_zipf_s=1.0)
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = moe.Ctx(0)
+    yield c
+    c.close()
+
+
+def host_pool(wl):
+    sb = moe.moe_slot_bytes(L.QTYPE[wl.qtype], wl.H, wl.I)
+    pool = torch.empty(wl.layers * wl.E * sb, dtype=torch.uint8, pin_memory=True)
+    view = pool.numpy()
+    blocks = {}
+
+    def put(l, e, b):
+        blocks[(l, e)] = b
+        view[(l * wl.E + e) * sb:(l * wl.E + e + 1) * sb] = layer.pack_expert(wl.qtype, wl.H, wl.I, *b)
+
+    gi.generate_blocks_parallel(wl, [(l, e) for l in range(wl.layers) for e in range(wl.E)], put)
+    return pool, blocks
+
+
+def lookup_order(wl, trace):
+    """Per (step, layer) the ids in the order the router emits them (oracle top-k)."""
+    order = np.empty_like(trace)
+    for s in range(trace.shape[0]):
+        lg = gi.cache_trace_logits(wl, trace, s)
+        order[s] = oracle.topk_select(lg, wl.k)
+    return order
+
+
+@pytest.mark.parametrize("n_slots", [6, 10, 30])
+def test_lru_matches_oracle(ctx, n_slots):
+    wl = SMALL
+    pool, _ = host_pool(wl)
+    trace = lookup_order(wl, gi.cache_trace(wl))
+    sb = moe.moe_slot_bytes(L.QTYPE[wl.qtype], wl.H, wl.I)
+    d_pool = torch.zeros((n_slots + 2) * sb, dtype=torch.uint8, device=DEV)
+    cache = moe.cache_slot_table_create(wl.layers, wl.E, n_slots, L.QTYPE[wl.qtype], wl.H, wl.I, d_pool, pool)
+    copy_s = torch.cuda.Stream()
+    s = torch.cuda.current_stream()
+    hits = np.zeros(trace.shape, dtype=bool)
+    for st in range(trace.shape[0]):
+        for l in range(wl.layers):
+            slots, misses = moe.cache_slot_table_lookup(cache, l, trace[st, l])
+            assert len(set(slots.tolist())) == wl.k and (slots >= 0).all() and (slots < n_slots + 2).all()
+            hits[st, l] = ~np.isin(trace[st, l], misses)
+            for e in misses:
+                moe.prefetch_expert(cache, l, int(e), copy_s, s)
+            moe.cache_mark_layer_done(cache, l, s)
+    torch.cuda.synchronize()
+    want, _ = oracle.lru_simulate(trace, n_slots)
+    np.testing.assert_array_equal(hits, want)
+    h, m = moe.cache_slot_table_stats(cache)
+    assert h == int(want.sum()) and m == int((~want).sum())
+    # device table: resident keys map to distinct slots whose bytes are the expert's
+    table = torch.empty(wl.layers * wl.E, dtype=torch.int32, device=DEV)
+    table.copy_(torch.from_dlpack(_table_view(cache, wl)))
+    t = table.cpu().numpy()
+    res = t[t >= 0]
+    assert len(res) == len(set(res.tolist())) <= n_slots
+    dp = d_pool.cpu().numpy()
+    hp = pool.numpy()
+    for key in np.flatnonzero(t >= 0)[:8]:
+        np.testing.assert_array_equal(dp[t[key] * sb:(t[key] + 1) * sb], hp[key * sb:(key + 1) * sb])
+    cache.close()
+
+
+def _table_view(cache, wl):
+    ptr = moe.cache_slot_table_device(cache)
+    n = wl.layers * wl.E
+
+    class _Arr:
+        __cuda_array_interface__ = {"shape": (n,), "typestr": "<i4", "data": (ptr, False), "version": 3}
+    return torch.as_tensor(_Arr(), device=DEV)
+
+
+def test_cached_layers_match_oracle(ctx):
+    wl = SMALL
+    pool, blocks = host_pool(wl)
+    trace = gi.cache_trace(wl)
+    cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, 8, pool)
+    worst = 0.0
+    for st in range(12):
+        x = gi.activations(wl, 1, st)
+        lg = gi.cache_trace_logits(wl, trace, st)
+        xd = dev(x)
+        for l in range(wl.layers):
+            out = cl.layer(l, xd, dev(lg[l:l + 1])).cpu().numpy()
+            moe.moe_ctx_check(ctx)
+            ref = oracle.moe_layer(x, wl.qtype, lambda e: blocks[(l, e)], wl.k, logits=lg[l:l + 1])
+            worst = max(worst, max_rel_err(out, ref["out"]))
+    note(f"   cached layers worst max rel err {worst:.2e}, misses {sum(cl.misses_per_layer)}")
+    assert worst <= 1e-3
+    assert sum(cl.misses_per_layer) > 0
+    cl.close()
+
+
+def test_unpinned_pool_refused(ctx):
+    wl = SMALL
+    sb = moe.moe_slot_bytes(L.QTYPE[wl.qtype], wl.H, wl.I)
+    d_pool = torch.zeros(6 * sb, dtype=torch.uint8, device=DEV)
+    plain = np.zeros(wl.layers * wl.E * sb, dtype=np.uint8)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.cache_slot_table_create(wl.layers, wl.E, 4, L.QTYPE[wl.qtype], wl.H, wl.I, d_pool, plain.ctypes.data)
+    assert ei.value.name == "MOE_ERR_NOT_PINNED"
+
+
+def test_capacity_and_unmarked_layer_errors(ctx):
+    wl = SMALL
+    sb = moe.moe_slot_bytes(L.QTYPE[wl.qtype], wl.H, wl.I)
+    pool = torch.zeros(wl.layers * wl.E * sb, dtype=torch.uint8, pin_memory=True)
+    d_pool = torch.zeros(5 * sb, dtype=torch.uint8, device=DEV)
+    cache = moe.cache_slot_table_create(wl.layers, wl.E, 3, L.QTYPE[wl.qtype], wl.H, wl.I, d_pool, pool)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.cache_slot_table_lookup(cache, 0, [1, 2, 3, 4])
+    assert ei.value.name == "MOE_ERR_CAPACITY"
+    assert moe.cache_slot_table_stats(cache) == (0, 0)  # unchanged
+    moe.cache_slot_table_lookup(cache, 0, [1, 2])
+    with pytest.raises(moe.MoeError) as ei:
+        moe.cache_slot_table_lookup(cache, 1, [1, 2])
+    assert ei.value.name == "MOE_ERR_INVALID_ARG"
+    moe.cache_mark_layer_done(cache, 0, None)
+    slots, misses = moe.cache_slot_table_lookup(cache, 1, [1, 2])
+    assert misses.tolist() == [1, 2]
+    with pytest.raises(moe.MoeError) as ei:
+        moe.prefetch_expert(cache, 1, 5, None, None)  # never looked up
+    assert ei.value.name == "MOE_ERR_NOT_RESIDENT"
+    moe.cache_mark_layer_done(cache, 1, None)
+    torch.cuda.synchronize()
+    cache.close()
