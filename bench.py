@@ -15,6 +15,10 @@ Also reported on the same line:
   batches       the same stack at the other batch sizes
   prefill       4096-token grouped-GEMM layer (hidden 2048, 128 experts,
                 top-8, intermediate 768, Q4_0, bf16 activations)
+  cache         expert-cache decode: 8 layers (hidden 4096, 256 experts,
+                top-8, intermediate 2048, Q4_0) served from a pinned host
+                pool through a VRAM cache of 40% of the experts, 2048
+                single-token steps of a trace with temporal locality
 Progress goes to stderr; the JSON line is the only stdout output.
 """
 from __future__ import annotations
@@ -44,9 +48,14 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--batch", type=int, default=1, help="tokens per step of the decode stack")
     p.add_argument("--layers", type=int, default=48)
-    p.add_argument("--no-extras", action="store_true", help="skip the other batch sizes and prefill")
+    p.add_argument("--no-extras", action="store_true", help="skip the other batch sizes, prefill and the expert cache")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-cache", action="store_true", help="skip the expert-cache decode run")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="first run a device copy and an elementwise negate of MIB MiB each, the known-size "
+                        "kernels that scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
+    p.add_argument("--cache-steps", type=int, default=None, help="steps of the expert-cache trace (default 2048)")
     p.add_argument("--unfused", action="store_true",
                    help="run each layer as the four separate entry points instead of the two fused calls")
     return p.parse_args()
@@ -221,6 +230,93 @@ def prefill_extra(ctx, steps=10, warmup=3):
     }
 
 
+# ---------------------------------------------------------------- expert cache
+def cache_extra(ctx, steps=None, distinct=64, warm_from=256):
+    """Expert-cache decode: 8 layers (hidden 4096, 256 experts, top-8,
+    intermediate 2048, Q4_0), the whole pool in pinned host memory, a VRAM
+    cache of 40% of each layer's experts (816 slots), single-token steps
+    following a trace with temporal locality, from an empty cache.
+
+    The pinned pool holds `distinct` generated experts repeated over the
+    2048 (layer, expert) keys: the bytes moved and read are those of the
+    workload, and the copy and FFN times do not depend on the values
+    (parity of this path is covered by the tests)."""
+    import numpy as np
+    import torch
+    import expert_offload_amd as moe
+    from expert_offload_amd import _lib as L
+    from expert_offload_amd import layer
+    from gen import inputs as gi
+
+    wl = gi.workload("cache_q4_0_h4096_e256")
+    steps = steps or wl.steps
+    q = L.QTYPE[wl.qtype]
+    sb = moe.moe_slot_bytes(q, wl.H, wl.I)
+    keys = wl.layers * wl.E
+    n_slots = int(wl.cache_fraction * wl.E) * wl.layers
+    log(f"cache: pinning a {keys * sb / 1e9:.1f} GB host pool ({keys} experts of {sb} B)")
+    pool = torch.empty(keys * sb, dtype=torch.uint8, pin_memory=True)
+    base = {}
+    gi.generate_blocks_parallel(wl, [(b // wl.E, b % wl.E) for b in range(distinct)],
+                                lambda l, e, b: base.__setitem__(l * wl.E + e, layer.pack_expert(
+                                    wl.qtype, wl.H, wl.I, *b)))
+    view = pool.numpy()
+    for key in range(keys):
+        view[key * sb:(key + 1) * sb] = base[key % distinct]
+    del base
+    log("cache: pool filled; building the trace")
+    trace = gi.cache_trace(wl, steps)
+    logits = torch.from_numpy(np.stack([gi.cache_trace_logits(wl, trace, s) for s in range(steps)])).cuda()
+    xs = torch.from_numpy(np.stack([gi.activations(wl, 1, s)[0] for s in range(steps)])).cuda()
+    cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, n_slots, pool)
+    torch.cuda.synchronize()
+    stamps = [time.perf_counter()]
+    for s in range(steps):
+        x = xs[s:s + 1]
+        for l in range(wl.layers):
+            cl.layer(l, x, logits[s, l:l + 1])
+        stamps.append(time.perf_counter())
+        if (s + 1) % 512 == 0:
+            log(f"cache: step {s + 1}/{steps}")
+    torch.cuda.synchronize()
+    stamps[-1] = time.perf_counter()
+    moe.moe_ctx_check(ctx)
+    wall = stamps[-1] - stamps[0]
+    hits, misses = cl.stats()
+    mpl = np.array(cl.misses_per_layer).reshape(steps, wl.layers)
+    warm = slice(min(warm_from, steps - 1), steps)
+    warm_wall = stamps[-1] - stamps[warm.start]
+    warm_miss = int(mpl[warm].sum())
+    warm_pairs = (steps - warm.start) * wl.layers * wl.k
+    # PCIe ceiling: back-to-back expert copies from the pinned pool
+    cs = torch.cuda.Stream()
+    d = cl.d_pool
+    n_cp = 32
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        e0.record()
+        for i in range(n_cp):
+            j = (i * 37) % keys
+            d[(i % n_slots) * sb:(i % n_slots + 1) * sb].copy_(pool[j * sb:(j + 1) * sb], non_blocking=True)
+        e1.record()
+    torch.cuda.synchronize()
+    ceiling = n_cp * sb / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    cl.close()
+    res = {
+        "workload": wl.name, "layers": wl.layers, "steps": steps, "cache_slots": n_slots,
+        "cache_fraction": wl.cache_fraction, "expert_bytes": sb, "host_pool_bytes": keys * sb,
+        "tokens_per_s": steps / wall, "ms_per_token": wall * 1e3 / steps,
+        "hit_rate": hits / (hits + misses),
+        "warm": {"from_step": warm.start, "tokens_per_s": (steps - warm.start) / warm_wall,
+                 "hit_rate": 1.0 - warm_miss / warm_pairs},
+        "h2d_gbs": misses * sb / wall / 1e9,
+        "h2d_copy_ceiling_gbs": ceiling,
+        "pool_values": f"{distinct} generated experts repeated over the {keys} keys",
+    }
+    del pool
+    return res
+
+
 # ---------------------------------------------------------------- CPU oracle
 def cpu_baseline(wl, T, budget_s):
     import numpy as np
@@ -262,7 +358,18 @@ def main():
     import expert_offload_amd as moe
     from gen import inputs as gi
 
+    from expert_offload_amd.rocprof_summary import traffic_bytes
     moe.lib()
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n * 4} B copied and negated 3 times")
+        del src, dst
     wl = gi.workload("decode_q8_0_h2048_e128")
     if args.layers != wl.layers:
         log(f"NOTE: {args.layers} layers instead of {wl.layers} (profiling run)")
@@ -286,8 +393,10 @@ def main():
     achieved = kbytes[dom] / (avg_ms * 1e-3) / 1e9
     for name, (cnt, ms) in sorted(prof.items()):
         log(f"   kernel {name:14s} launches {cnt:5d} avg {ms / cnt * 1e3:8.2f} us")
+    rp_kernel = {"ffn_gateup": "ffn_gateup_decode", "ffn_down": "ffn_down_decode"}[dom]
+    traffic = traffic_bytes(rp_kernel, os.path.join(ROOT, "profiles", f"{rp_kernel}_h2048_e128_t{T}_traffic.txt"))
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "avg_us": avg_ms * 1e3,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "avg_us": avg_ms * 1e3,
                 "bytes_per_launch": kbytes[dom]}
     stack_bytes = sum(decode_layer_bytes(wl, T, a) for a in n_active)
     result = {
@@ -323,6 +432,15 @@ def main():
                 f"{result['prefill']['ffn_tflops']:.1f} TFLOP/s")
         except Exception as e:  # reported, never silently dropped
             result["prefill"] = {"error": repr(e)}
+        if not args.no_cache:
+            try:
+                result["cache"] = cache_extra(ctx, steps=args.cache_steps)
+                c = result["cache"]
+                log(f"cache: {c['tokens_per_s']:.1f} tok/s, hit rate {c['hit_rate']:.3f}, warm "
+                    f"{c['warm']['tokens_per_s']:.1f} tok/s at {c['warm']['hit_rate']:.3f}, "
+                    f"H2D {c['h2d_gbs']:.1f} GB/s of {c['h2d_copy_ceiling_gbs']:.1f}")
+            except Exception as e:
+                result["cache"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(wl, T, args.cpu_seconds)

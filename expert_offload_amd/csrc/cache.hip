@@ -274,7 +274,7 @@ int prefetch_expert(moe_cache* c, int layer, int expert, void* copy_stream, void
   if (pd.victim_key >= 0 && c->table[pd.victim_key] < 0) {
     u.idx[u.n] = pd.victim_key; u.val[u.n] = -1; ++u.n;
   }
-  table_update_kernel<<<1, 64, 0, ks>>>(c->d_table, u);
+  launch(table_update_kernel, 1, 64, 0, ks, c->d_table, u);
   int rc = check_launch("table_update_kernel");
   if (rc) return rc;
   if (slot_out) *slot_out = pd.slot;

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 int launch_combine(moe_ctx* ctx, const float* y, const float* w, int T, int k, int H, float* out, hipStream_t s) {
   dim3 grid((H + 255) / 256, T);
   KernelTimer timer(ctx, "combine", s);
-  combine_kernel<<<grid, 256, 0, s>>>(y, w, k, H, out);
+  launch(combine_kernel, grid, 256, 0, s, y, w, k, H, out);
   return check_launch("combine_kernel");
 }
 
@@ -85,11 +85,11 @@ extern "C" int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int r
   hipStream_t s = (hipStream_t)stream;
   KernelTimer timer(ctx, "dequant", s);
   if (qtype == MOE_QTYPE_Q8_0) {
-    if (out_dtype == MOE_DTYPE_F32) dequant_kernel<MOE_QTYPE_Q8_0, false><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
-    else dequant_kernel<MOE_QTYPE_Q8_0, true><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
+    if (out_dtype == MOE_DTYPE_F32) launch(dequant_kernel<MOE_QTYPE_Q8_0, false>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);
+    else launch(dequant_kernel<MOE_QTYPE_Q8_0, true>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);
   } else {
-    if (out_dtype == MOE_DTYPE_F32) dequant_kernel<MOE_QTYPE_Q4_0, false><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
-    else dequant_kernel<MOE_QTYPE_Q4_0, true><<<grid, 256, 0, s>>>((const uint8_t*)packed, rows, cols, out);
+    if (out_dtype == MOE_DTYPE_F32) launch(dequant_kernel<MOE_QTYPE_Q4_0, false>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);
+    else launch(dequant_kernel<MOE_QTYPE_Q4_0, true>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);
   }
   return check_launch("dequant_kernel");
 }

@@ -435,7 +435,7 @@ template <int QT, int LPR, int BPL>
 static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStream_t s) {
   constexpr int RPL0 = rows_per_lane<QT, BPL>();
   constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
-  ffn_gateup_decode<QT, LPR, BPL, RPL><<<grid, 256, 0, s>>>(p, x);
+  launch(ffn_gateup_decode<QT, LPR, BPL, RPL>, grid, 256, 0, s, p, x);
 }
 // Down tiles aim at 8 rows (H/8 workgroups): RPL = 8 / (64 / LPR) within
 // the register budget.
@@ -447,7 +447,7 @@ constexpr int down_rows_per_lane() {
 }
 template <int QT, int LPR, int BPL>
 static void launch_down(const FfnParams& p, int grid, hipStream_t s) {
-  ffn_down_decode<QT, LPR, BPL, down_rows_per_lane<QT, LPR, BPL>()><<<grid, kDownWaves * kWave, 0, s>>>(p);
+  launch(ffn_down_decode<QT, LPR, BPL, down_rows_per_lane<QT, LPR, BPL>()>, grid, kDownWaves * kWave, 0, s, p);
 }
 template <int QT, int LPR, int BPL>
 static constexpr int down_rows_per_tile() {

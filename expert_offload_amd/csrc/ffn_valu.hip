@@ -166,14 +166,14 @@ int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype
     KernelTimer timer(ctx, "ffn_gateup", s);
     if (p.qtype == MOE_QTYPE_Q8_0) {
       if (x_dtype == MOE_DTYPE_F32)
-        ffn_gateup_valu<MOE_QTYPE_Q8_0, float><<<g1, 256, 0, s>>>(p, (const float*)x);
+        launch(ffn_gateup_valu<MOE_QTYPE_Q8_0, float>, g1, 256, 0, s, p, (const float*)x);
       else
-        ffn_gateup_valu<MOE_QTYPE_Q8_0, uint16_t><<<g1, 256, 0, s>>>(p, (const uint16_t*)x);
+        launch(ffn_gateup_valu<MOE_QTYPE_Q8_0, uint16_t>, g1, 256, 0, s, p, (const uint16_t*)x);
     } else {
       if (x_dtype == MOE_DTYPE_F32)
-        ffn_gateup_valu<MOE_QTYPE_Q4_0, float><<<g1, 256, 0, s>>>(p, (const float*)x);
+        launch(ffn_gateup_valu<MOE_QTYPE_Q4_0, float>, g1, 256, 0, s, p, (const float*)x);
       else
-        ffn_gateup_valu<MOE_QTYPE_Q4_0, uint16_t><<<g1, 256, 0, s>>>(p, (const uint16_t*)x);
+        launch(ffn_gateup_valu<MOE_QTYPE_Q4_0, uint16_t>, g1, 256, 0, s, p, (const uint16_t*)x);
     }
   }
   int rc = check_launch("ffn_gateup_valu");
@@ -181,9 +181,9 @@ int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype
   {
     KernelTimer timer(ctx, "ffn_down", s);
     if (p.qtype == MOE_QTYPE_Q8_0)
-      ffn_down_valu<MOE_QTYPE_Q8_0><<<g2, 256, 0, s>>>(p);
+      launch(ffn_down_valu<MOE_QTYPE_Q8_0>, g2, 256, 0, s, p);
     else
-      ffn_down_valu<MOE_QTYPE_Q4_0><<<g2, 256, 0, s>>>(p);
+      launch(ffn_down_valu<MOE_QTYPE_Q4_0>, g2, 256, 0, s, p);
   }
   return check_launch("ffn_down_valu");
 }

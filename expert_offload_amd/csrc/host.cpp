@@ -54,20 +54,38 @@ static hipEvent_t take_event(moe_ctx* ctx) {
   return e;
 }
 
-KernelTimer::KernelTimer(moe_ctx* ctx, const char* kernel, hipStream_t s) : ctx_(ctx), s_(s) {
+static thread_local KernelTimer* g_timer = nullptr;
+
+KernelTimer::KernelTimer(moe_ctx* ctx, const char* kernel, hipStream_t s) : ctx_(ctx) {
   if (!ctx || !ctx->timing) return;
   hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return;
   rec_.kernel = kernel;
   rec_.start = take_event(ctx);
   rec_.stop = take_event(ctx);
-  if (!rec_.start || !rec_.stop) return;
-  on_ = hipEventRecord(rec_.start, s) == hipSuccess;
+  if (!rec_.start || !rec_.stop) {
+    if (rec_.start) ctx->spare_events.push_back(rec_.start);
+    if (rec_.stop) ctx->spare_events.push_back(rec_.stop);
+    return;
+  }
+  on_ = true;
+  prev_ = g_timer;
+  g_timer = this;
 }
 
 KernelTimer::~KernelTimer() {
   if (!on_) return;
-  if (hipEventRecord(rec_.stop, s_) == hipSuccess) ctx_->recs.push_back(rec_);
+  g_timer = prev_;
+  if (launched_) {
+    ctx_->recs.push_back(rec_);
+  } else {
+    ctx_->spare_events.push_back(rec_.start);
+    ctx_->spare_events.push_back(rec_.stop);
+  }
+}
+
+KernelTimer* KernelTimer::armed() {
+  return g_timer && !g_timer->launched_ ? g_timer : nullptr;
 }
 
 }  // namespace moe

@@ -1,6 +1,7 @@
 // Internal declarations shared by libmoe's translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -26,8 +27,10 @@ struct moe_ctx {
 
 namespace moe {
 
-// Brackets one kernel launch with HIP events on its stream while the
-// context's timing is on (never inside a stream capture).
+// Times the one kernel launched through launch() while it is alive, if the
+// context's timing is on and the stream is not being captured.  The start
+// and stop events ride on the launch itself (hipExtLaunchKernel), so their
+// elapsed time is the kernel's own execution, not the gap between markers.
 class KernelTimer {
  public:
   KernelTimer(moe_ctx* ctx, const char* kernel, hipStream_t s);
@@ -35,12 +38,29 @@ class KernelTimer {
   KernelTimer(const KernelTimer&) = delete;
   KernelTimer& operator=(const KernelTimer&) = delete;
 
+  // The innermost timer alive on this thread that still waits for its launch.
+  static KernelTimer* armed();
+  hipEvent_t start_event() const { return rec_.start; }
+  hipEvent_t stop_event() const { return rec_.stop; }
+  void launched() { launched_ = true; }
+
  private:
   moe_ctx* ctx_;
-  hipStream_t s_;
+  KernelTimer* prev_ = nullptr;
   moe_timing_rec rec_{};
-  bool on_ = false;
+  bool on_ = false, launched_ = false;
 };
+
+// Launch `kern` on `s`, timed by the armed KernelTimer if there is one.
+template <typename... P, typename... A>
+inline void launch(void (*kern)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s, A... args) {
+  if (KernelTimer* t = KernelTimer::armed()) {
+    hipExtLaunchKernelGGL(kern, grid, block, lds, s, t->start_event(), t->stop_event(), 0u, static_cast<P>(args)...);
+    t->launched();
+  } else {
+    kern<<<grid, block, lds, s>>>(static_cast<P>(args)...);
+  }
+}
 
 // ---------------------------------------------------------------- errors
 int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -19,7 +19,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
 int launch_permute(moe_ctx* ctx, const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,
                    int32_t* pair_pos, int32_t* active, hipStream_t s) {
   KernelTimer timer(ctx, "permute", s);
-  permute_kernel<<<1, kPermThreads, 0, s>>>(ids, P, E, offsets, sorted_pairs, pair_pos, active, ctx->d_err);
+  launch(permute_kernel, 1, kPermThreads, 0, s, ids, P, E, offsets, sorted_pairs, pair_pos, active, ctx->d_err);
   return check_launch("permute_kernel");
 }
 

@@ -277,7 +277,7 @@ int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws
   __bf16* hbuf = (__bf16*)((char*)ws + 256 + ((max_tiles * sizeof(int2) + 255) / 256) * 256);
   {
     KernelTimer timer(ctx, "prefill_tiles", s);
-    prefill_tiles_kernel<<<1, 256, 0, s>>>(p.offsets, p.E, tiles, count);
+    launch(prefill_tiles_kernel, 1, 256, 0, s, p.offsets, p.E, tiles, count);
   }
   int rc = check_launch("prefill_tiles_kernel");
   if (rc) return rc;
@@ -285,18 +285,18 @@ int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws
     KernelTimer timer(ctx, "ffn_gateup", s);
     const unsigned grid = (unsigned)max_tiles * (p.I / 64);
     if (p.qtype == MOE_QTYPE_Q4_0)
-      prefill_gateup_kernel<MOE_QTYPE_Q4_0><<<grid, 256, 0, s>>>(p, (const __bf16*)x, tiles, count, hbuf);
+      launch(prefill_gateup_kernel<MOE_QTYPE_Q4_0>, grid, 256, 0, s, p, (const __bf16*)x, tiles, count, hbuf);
     else
-      prefill_gateup_kernel<MOE_QTYPE_Q8_0><<<grid, 256, 0, s>>>(p, (const __bf16*)x, tiles, count, hbuf);
+      launch(prefill_gateup_kernel<MOE_QTYPE_Q8_0>, grid, 256, 0, s, p, (const __bf16*)x, tiles, count, hbuf);
   }
   if ((rc = check_launch("prefill_gateup_kernel"))) return rc;
   {
     KernelTimer timer(ctx, "ffn_down", s);
     const unsigned grid = (unsigned)max_tiles * (p.H / kPBN);
     if (p.qtype == MOE_QTYPE_Q4_0)
-      prefill_down_kernel<MOE_QTYPE_Q4_0><<<grid, 256, 0, s>>>(p, hbuf, tiles, count);
+      launch(prefill_down_kernel<MOE_QTYPE_Q4_0>, grid, 256, 0, s, p, hbuf, tiles, count);
     else
-      prefill_down_kernel<MOE_QTYPE_Q8_0><<<grid, 256, 0, s>>>(p, hbuf, tiles, count);
+      launch(prefill_down_kernel<MOE_QTYPE_Q8_0>, grid, 256, 0, s, p, hbuf, tiles, count);
   }
   return check_launch("prefill_down_kernel");
 }

@@ -169,9 +169,9 @@ static int launch_route(moe_ctx* ctx, const void* x, int x_dtype, const float* r
     {
       KernelTimer timer(ctx, "router_logits", s);
       if (x_dtype == MOE_DTYPE_F32)
-        router_logits_kernel<float><<<grid, 256, 0, s>>>((const float*)x, router_w, bias, T, H, E, logits_out);
+        launch(router_logits_kernel<float>, grid, 256, 0, s, (const float*)x, router_w, bias, T, H, E, logits_out);
       else
-        router_logits_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)x, router_w, bias, T, H, E,
+        launch(router_logits_kernel<uint16_t>, grid, 256, 0, s, (const uint16_t*)x, router_w, bias, T, H, E,
                                                             logits_out);
     }
     if ((rc = check_launch("router_logits_kernel"))) return rc;
@@ -179,7 +179,7 @@ static int launch_route(moe_ctx* ctx, const void* x, int x_dtype, const float* r
     tk_bias = nullptr;
   }
   KernelTimer timer(ctx, "topk", s);
-  topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(src, tk_bias, T, E, k, logits_in ? logits_out : nullptr, topk_ids,
+  launch(topk_kernel, (T + 3) / 4, 256, 0, s, src, tk_bias, T, E, k, logits_in ? logits_out : nullptr, topk_ids,
                                           topk_w);
   return check_launch("topk_kernel");
 }
@@ -235,9 +235,9 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
       KernelTimer timer(ctx, "router_logits", s);
       dim3 grid(E);
       if (x_dtype == MOE_DTYPE_F32)
-        router_logits_kernel<float><<<grid, 256, 0, s>>>((const float*)x, router_w, bias, T, H, E, logits_out);
+        launch(router_logits_kernel<float>, grid, 256, 0, s, (const float*)x, router_w, bias, T, H, E, logits_out);
       else
-        router_logits_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)x, router_w, bias, T, H, E,
+        launch(router_logits_kernel<uint16_t>, grid, 256, 0, s, (const uint16_t*)x, router_w, bias, T, H, E,
                                                             logits_out);
     }
     if ((rc = check_launch("router_logits_kernel"))) return rc;
@@ -245,7 +245,7 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
     tk_bias = nullptr;
   }
   KernelTimer timer(ctx, "topk_permute", s);
-  topk_permute_kernel<<<1, kTopkPermuteThreads, 0, s>>>(src, tk_bias, T, E, k, logits_in ? logits_out : nullptr, topk_ids,
+  launch(topk_permute_kernel, 1, kTopkPermuteThreads, 0, s, src, tk_bias, T, E, k, logits_in ? logits_out : nullptr, topk_ids,
                                         topk_w, expert_offsets, sorted_pairs, pair_pos, active, ctx->d_err);
   return check_launch("topk_permute_kernel");
 }

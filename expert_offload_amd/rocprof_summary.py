@@ -1,0 +1,191 @@
+"""Summaries of rocprofv3 CSV output for the kernels of libmoe.
+
+Two kinds of input, both written by ``rocprofv3 -f csv``:
+
+* ``--kernel-trace --stats``: ``*_kernel_stats.csv`` (per kernel name:
+  calls and durations).  The summary lists every kernel with its call count
+  and average / min / max duration in microseconds.
+* ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (one run each):
+  ``*_counter_collection.csv`` (one row per dispatch and counter, values in
+  KiB).  Each counter's per-dispatch average for a kernel is divided by the
+  ratio the same counter shows on a plain copy kernel of known size, giving
+  HBM bytes per launch.
+
+The traffic summary records a hash of the sources the kernel is built from;
+:func:`traffic_bytes` returns the recorded traffic only while that hash
+still matches, so a figure never outlives the kernel it was measured on.
+
+Usage::
+
+    python -m expert_offload_amd.rocprof_summary stats DIR --out FILE --command CMD
+    python -m expert_offload_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR --kernel NAME
+        --calib-bytes N --out FILE --command CMD
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+from typing import Dict, List, Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+# Sources each profiled kernel family is compiled from.
+KERNEL_SOURCES = {
+    "ffn_gateup_decode": ["csrc/decode.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
+    "ffn_down_decode": ["csrc/decode.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
+    "prefill_gateup_kernel": ["csrc/prefill.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
+    "prefill_down_kernel": ["csrc/prefill.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
+}
+# Calibration kernels, in order of preference: ROCm's device-to-device copy
+# blit, then an elementwise negate (reads and writes the same byte count).
+CALIB_PATTERNS = ("copyBuffer", "neg_kernel")
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def _short(name: str) -> str:
+    """Kernel name without return type and parameter list."""
+    n = re.sub(r"^void\s+", "", name.strip())
+    depth, out = 0, []
+    for c in n:
+        if c == "(" and depth == 0:
+            break
+        depth += c == "<"
+        depth -= c == ">"
+        out.append(c)
+    return "".join(out)
+
+
+def kernel_stats(d: str) -> List[Tuple[str, int, float, float, float]]:
+    """(name, calls, avg_us, min_us, max_us) from a --stats run, by total time."""
+    rows = []
+    with open(_find(d, "kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append((_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"])))
+    rows.sort(key=lambda r: -r[5])
+    return [r[:5] for r in rows]
+
+
+def counter_values(d: str, counter: str) -> Dict[str, List[float]]:
+    """kernel -> the counter's value for each of its dispatches."""
+    acc: Dict[str, List[float]] = {}
+    with open(_find(d, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def _calib(vals: Dict[str, List[float]], pattern: str) -> Tuple[str, int, float]:
+    """The calibration kernel's mean over its largest dispatches (within 10%
+    of the maximum): the known-size run dwarfs other uses of the same kernel."""
+    for k, v in vals.items():
+        if pattern in k:
+            top = [x for x in v if x >= 0.9 * max(v)]
+            return k, len(top), sum(top) / len(top)
+    raise KeyError(f"no {pattern} kernel in the counter output")
+
+
+def _pick(vals: Dict[str, List[float]], kernel: str) -> Tuple[str, int, float]:
+    for k, v in vals.items():
+        if kernel in k:
+            return k, len(v), sum(v) / len(v)
+    raise KeyError(f"kernel {kernel} not in the counter output")
+
+
+def write_stats(d: str, out: str, command: str) -> None:
+    rows = kernel_stats(d)
+    with open(out, "w") as f:
+        f.write("rocprofv3 kernel trace summary\n")
+        f.write(f"command: {command}\n\n")
+        f.write(f"{'kernel':70s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}\n")
+        for name, calls, avg, mn, mx in rows:
+            f.write(f"{name[:70]:70s} {calls:7d} {avg:9.2f} {mn:9.2f} {mx:9.2f}\n")
+
+
+def write_traffic(fetch_dir: str, write_dir: str, kernel: str, calib_bytes: int, out: str, command: str) -> None:
+    fetch = counter_values(fetch_dir, "FETCH_SIZE")
+    write = counter_values(write_dir, "WRITE_SIZE")
+    lines = []
+    factors = {}
+    for pat in CALIB_PATTERNS:
+        cf_name, nf, cf = _calib(fetch, pat)
+        cw_name, nw, cw = _calib(write, pat)
+        factors[pat] = (cf * 1024.0 / calib_bytes, cw * 1024.0 / calib_bytes)
+        lines.append(f"calibration {cf_name}: {calib_bytes} B read and written; FETCH_SIZE {cf:.1f} KiB "
+                     f"(factor {factors[pat][0]:.4f}, {nf} dispatches), WRITE_SIZE {cw:.1f} KiB "
+                     f"(factor {factors[pat][1]:.4f}, {nw} dispatches)")
+    f_fac, w_fac = factors[CALIB_PATTERNS[0]]
+    kf, nf, vf = _pick(fetch, kernel)
+    kw, nw, vw = _pick(write, kernel)
+    rd = vf * 1024.0 / f_fac
+    wr = vw * 1024.0 / w_fac
+    with open(out, "w") as f:
+        f.write(f"rocprofv3 HBM traffic of {kernel}\n")
+        f.write(f"command: {command}\n\n")
+        for ln in lines:
+            f.write(ln + "\n")
+        f.write(f"scaled by the {CALIB_PATTERNS[0]} factors\n")
+        f.write(f"{kf}: {nf} dispatches, FETCH_SIZE {vf:.1f} KiB/dispatch -> {rd:.0f} B read\n")
+        f.write(f"{kw}: {nw} dispatches, WRITE_SIZE {vw:.1f} KiB/dispatch -> {wr:.0f} B written\n")
+        f.write(f"traffic_bytes_per_launch: {rd + wr:.0f}\n")
+        f.write(f"source_hash: {source_hash(kernel)}\n")
+
+
+def traffic_bytes(kernel: str, path: str) -> Optional[float]:
+    """Recorded HBM bytes per launch, or None if absent or the sources changed."""
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash(kernel) or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def main() -> None:
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = p.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--out", required=True)
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--calib-bytes", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", required=True)
+    a = p.parse_args()
+    if a.what == "stats":
+        write_stats(a.dir, a.out, a.command)
+    else:
+        write_traffic(a.fetch_dir, a.write_dir, a.kernel, a.calib_bytes, a.out, a.command)
+
+
+if __name__ == "__main__":
+    main()

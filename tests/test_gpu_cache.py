@@ -150,3 +150,38 @@ def test_capacity_and_unmarked_layer_errors(ctx):
     moe.cache_mark_layer_done(cache, 1, None)
     torch.cuda.synchronize()
     cache.close()
+
+
+def test_cached_layer_full_size_sampled(ctx):
+    """One layer at the expert-cache workload's full shape (hidden 4096, 256
+    experts, top-8, intermediate 2048, Q4_0) through a 12-slot cache, so
+    later steps evict; only the experts the trace touches get content."""
+    import dataclasses
+    wl = dataclasses.replace(gi.workload("cache_q4_0_h4096_e256"), layers=1, steps=6)
+    sb = moe.moe_slot_bytes(L.QTYPE[wl.qtype], wl.H, wl.I)
+    trace = gi.cache_trace(wl)
+    touched = sorted(set(trace.reshape(-1).tolist()))
+    pool = torch.zeros(wl.E * sb, dtype=torch.uint8, pin_memory=True)
+    view = pool.numpy()
+    blocks = {}
+
+    def put(l, e, b):
+        blocks[e] = b
+        view[e * sb:(e + 1) * sb] = layer.pack_expert(wl.qtype, wl.H, wl.I, *b)
+
+    gi.generate_blocks_parallel(wl, [(0, e) for e in touched], put)
+    cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, 1, 12, pool)
+    outs = []
+    for st in range(wl.steps):
+        x = gi.activations(wl, 1, st)
+        lg = gi.cache_trace_logits(wl, trace, st)
+        outs.append((x, lg, cl.layer(0, dev(x), dev(lg)).cpu().numpy()))
+    moe.moe_ctx_check(ctx)
+    assert sum(cl.misses_per_layer[1:]) > 0  # later steps missed, so slots were reused
+    for st in (0, 3, wl.steps - 1):
+        x, lg, out = outs[st]
+        ref = oracle.moe_layer(x, wl.qtype, lambda e: blocks[e], wl.k, logits=lg)
+        err = max_rel_err(out, ref["out"])
+        note(f"   full-size cached step {st}: max rel err {err:.2e}")
+        assert err <= 1e-3
+    cl.close()
