@@ -88,9 +88,10 @@ int moe_ctx_destroy(moe_ctx* ctx);
 int moe_ctx_check(moe_ctx* ctx, void* stream);
 
 /* Per-kernel timing for profiling.  moe_ctx_set_timing(ctx, 1) makes every
- * later launch of this context record a HIP event pair around the kernel on
- * its stream (launches inside a stream capture are not timed); enabling or
- * disabling discards earlier records.  moe_ctx_kernel_time waits for the
+ * later launch of this context carry a start and a stop HIP event bound to
+ * the launch itself (hipExtLaunchKernel), so their elapsed time is the
+ * kernel's execution on its stream (launches inside a stream capture are
+ * not timed); enabling or disabling discards earlier records.  moe_ctx_kernel_time waits for the
  * recorded launches of `kernel` (names: "router_logits", "topk", "permute",
  * "ffn_gateup", "ffn_down", "combine", "dequant", "topk_permute") and
  * returns their number
