@@ -6,16 +6,23 @@
 // matrix-matrix kernels with prefill).  Per expert: h = silu(X Wg^T) *
 // (X Wu^T) with X the expert's gathered token rows, then y = h Wd^T.
 //
-// Tiles.  A workgroup (4 wavefronts, 2 x 2) computes a 128 x 128 output
-// tile of one expert with v_mfma_f32_32x32x16_bf16; each wavefront owns
-// 64 x 64 (2 x 2 MFMA tiles).  Per K step of 64: the A tile (gathered
-// activation rows, bf16) and the B tile (weight rows, Q4_0/Q8_0 blocks
-// dequantised to bf16 = round-to-nearest-even of d * q) are written to LDS
-// (rows padded by 16 B so the 16-byte fragment reads do not collide in the
-// banks), while the next step's global loads are already in flight.
-//
+// Tiles.  A workgroup (4 wavefronts) computes a 256 x 128 output tile of one
+// expert with v_mfma_f32_32x32x16_bf16.  Each wavefront owns 64 rows and all
+// 128 columns (2 x 4 MFMA tiles, 128 accumulators per lane), so:
+//  * activation rows are private to a wavefront and go from global memory
+//    (L2) straight into MFMA operand registers, the next K step's loads
+//    issued while the current step's MFMAs run;
+//  * the weight tile is shared by the four wavefronts through LDS: each
+//    thread dequantises one 32-weight block per K step (bf16 = round to
+//    nearest even of d * q, exact in fp32 before rounding) into one of two
+//    LDS buffers while the MFMAs read the other, one barrier per K step, and
+//    the blocks' global loads are issued two K steps ahead.
 // Gate/up tiles hold 64 gate rows and the 64 up rows of the same
 // intermediate indices, so SwiGLU is applied in the accumulator registers.
+//
+// Workgroups are dispatched to the 8 XCDs round-robin; the index mapping
+// puts all column tiles of one row tile on one XCD so its activation rows
+// are read into that XCD's L2 once.
 #include "device_common.h"
 #include "ffn.h"
 #include "route_common.h"
@@ -23,280 +30,286 @@
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPBM = 128, kPBN = 128, kPBK = 64;
-constexpr int kPLD = kPBK + 8;  // LDS row stride in bf16 elements
+constexpr int kWaveRows = 64;  // rows (pairs) per wavefront
+constexpr int kTN = 128;       // output columns per tile
+constexpr int kTK = 64;        // K step
+constexpr int kLdB = kTK + 8;  // LDS row stride of the weight tile (bf16)
+constexpr int kXcds = 8;
 
 // ------------------------------------------------------------ tile list
-// One workgroup: for every expert with pairs, the 128-row tiles
-// (expert, first row) in expert order; tiles[n] for n >= count is unused.
-__global__ __launch_bounds__(256) void prefill_tiles_kernel(const int32_t* __restrict__ offsets, int E,
+// One workgroup: for every expert with pairs (and not masked out), its
+// tiles of `tile_rows` rows (expert, first row) in expert order.
+__global__ __launch_bounds__(256) void prefill_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ mask, int E, int tile_rows,
                                                             int2* __restrict__ tiles, int* __restrict__ count) {
   __shared__ int s_n[kMaxE];
   __shared__ int s_base[kMaxE];
   __shared__ int s_wave[4];
   for (int e = threadIdx.x; e < E; e += 256) {
-    const int m = offsets[e + 1] - offsets[e];
-    s_n[e] = (m + kPBM - 1) / kPBM;
+    const int m = (mask && !mask[e]) ? 0 : offsets[e + 1] - offsets[e];
+    s_n[e] = (m + tile_rows - 1) / tile_rows;
   }
   __syncthreads();
   const int total = block_exclusive_scan<256>(s_n, s_base, E, s_wave);
   for (int e = threadIdx.x; e < E; e += 256)
-    for (int j = 0; j < s_n[e]; ++j) tiles[s_base[e] + j] = make_int2(e, j * kPBM);
+    for (int j = 0; j < s_n[e]; ++j) tiles[s_base[e] + j] = make_int2(e, j * tile_rows);
   if (threadIdx.x == 0) *count = total;
 }
 
-// --------------------------------------------------------- B tile staging
-// Thread t stages half a K step (one 32-weight block) of weight row t / 2.
+// ----------------------------------------------------- weight staging
+// 16 consecutive weights (half `h` of a 32-weight block) of a weight row:
+// raw codes and scale in registers, then dequantised to bf16 into LDS.
+// Q4_0 keeps elements 0..15 in the low nibbles and 16..31 in the high
+// nibbles of the block's 16 bytes; Q8_0 half h is bytes 16h..16h+15.
 template <int QT>
-struct BStage {
-  uint32_t w[QT == MOE_QTYPE_Q8_0 ? 8 : 4];
+struct WStage {
+  uint32_t w[4];
   float d;
-  __device__ __forceinline__ void load(const uint8_t* row, int b) {
-    const uint8_t* q = block_quants<QT>(row, b);
-    const uint4 v0 = *reinterpret_cast<const uint4*>(q);
-    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
-    if constexpr (QT == MOE_QTYPE_Q8_0) {
-      const uint4 v1 = *reinterpret_cast<const uint4*>(q + 16);
-      w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
-    }
+  __device__ __forceinline__ void load(const uint8_t* row, int b, int h) {
+    const uint8_t* q = block_quants<QT>(row, b) + (QT == MOE_QTYPE_Q8_0 ? 16 * h : 0);
+    const uint4 v = *reinterpret_cast<const uint4*>(q);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     d = block_scale<QT>(row, b);
   }
-  // 32 weights d*q (Q8_0) or d*(q-8) (Q4_0), exact in fp32, rounded to bf16.
-  __device__ __forceinline__ void store(__bf16* dst) const {
-    bf16x8 o[4];
+  // d*q (Q8_0) or d*(q-8) (Q4_0) as fma(d, u, -OFF*d) with u the unsigned
+  // code: the product of an 11-bit scale and a code of at most 8 bits is
+  // exact in fp32, so the only rounding is the final one to bf16.
+  __device__ __forceinline__ void store(__bf16* dst, int h) const {
+    bf16x8 o[2];
     if constexpr (QT == MOE_QTYPE_Q8_0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[i / 2][(i & 1) * 4 + j] = (__bf16)(d * (float)(int8_t)(w[i] >> (8 * j)));
-    } else {
-      const float d8 = -8.0f * d;
+      const float off = -128.0f * d;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const uint32_t u = w[i] ^ 0x80808080u;  // q + 128 in every byte
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int byte = (w[i] >> (8 * j)) & 0xFF;
-          o[i / 2][(i & 1) * 4 + j] = (__bf16)fmaf(d, (float)(byte & 0xF), d8);
-          o[2 + i / 2][(i & 1) * 4 + j] = (__bf16)fmaf(d, (float)(byte >> 4), d8);
-        }
+        for (int j = 0; j < 4; ++j) o[i / 2][(i & 1) * 4 + j] = (__bf16)fmaf(d, (float)((u >> (8 * j)) & 0xFFu), off);
+      }
+    } else {
+      const float off = -8.0f * d;
+      const int sh = 4 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t nib = (w[i] >> sh) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[i / 2][(i & 1) * 4 + j] = (__bf16)fmaf(d, (float)((nib >> (8 * j)) & 0xFFu), off);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(dst + 8 * i) = o[i];
+    *reinterpret_cast<bf16x8*>(dst) = o[0];
+    *reinterpret_cast<bf16x8*>(dst + 8) = o[1];
   }
 };
 
-// One wavefront's 64 x 64 of the 128 x 128 tile: acc[mt][nt] for the 32 x 32
-// MFMA tiles; a_row0 / b_row0 select the wavefront's rows in the LDS tiles.
-__device__ __forceinline__ void mma_k64(const __bf16 (*sA)[kPLD], const __bf16 (*sB)[kPLD], int a_row0,
-                                        const int (&b_row0)[2], f32x16 (&acc)[2][2]) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int ks = 0; ks < kPBK / 16; ++ks) {
-    const int kc = 16 * ks + 8 * (lane >> 5);
-    bf16x8 a[2], b[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(&sA[a_row0 + 32 * mt + (lane & 31)][kc]);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) b[nt] = *reinterpret_cast<const bf16x8*>(&sB[b_row0[nt] + (lane & 31)][kc]);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
-  }
-}
-
-// ------------------------------------------------------ gate/up + SwiGLU
-template <int QT>
-__global__ __launch_bounds__(256) void prefill_gateup_kernel(FfnParams p, const __bf16* __restrict__ x,
-                                                             const int2* __restrict__ tiles,
-                                                             const int* __restrict__ n_tiles,
-                                                             __bf16* __restrict__ hout) {
-  __shared__ __bf16 sA[kPBM][kPLD];
-  __shared__ __bf16 sB[kPBN][kPLD];
-  const int ntn = p.I / 64;
-  const int mt_i = blockIdx.x / ntn, nt_i = blockIdx.x - mt_i * ntn;
+// ------------------------------------------------------ grouped GEMM
+// GATEUP: A = gathered token rows of x (bf16 [T][H]), B = 64 gate + 64 up
+// rows, epilogue h = silu(g) * u into hbuf (bf16, grouped order [T*k][I]).
+// Down: A = hbuf rows (grouped order), B = 128 rows of Wd, epilogue y
+// (fp32, pair order [T*k][H]).  NW wavefronts, 64 rows each.
+template <int QT, bool GATEUP, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, const __bf16* __restrict__ x,
+                                                                  const int2* __restrict__ tiles,
+                                                                  const int* __restrict__ n_tiles, int ntn,
+                                                                  __bf16* __restrict__ hbuf) {
+  constexpr int kThreads = 64 * NW, kRows = kWaveRows * NW;
+  constexpr int kUnits = 2 * 2 * kTN / kThreads;  // half blocks staged per thread and K step
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][kTN][kLdB];
+  __shared__ int s_pair[kRows];
+  const int j = blockIdx.x / kXcds;
+  const int mt_i = kXcds * (j / ntn) + (int)(blockIdx.x % kXcds);
+  const int nt_i = j % ntn;
   if (mt_i >= *n_tiles) return;
   const int2 tl = tiles[mt_i];
   const int e = tl.x, m0 = tl.y;
-  const int slot = p.slot_table[e];
   const int pbeg = p.offsets[e];
-  const int rows = min(kPBM, p.offsets[e + 1] - pbeg - m0);
-  const int i0 = nt_i * 64;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int rows = min(kRows, p.offsets[e + 1] - pbeg - m0);
+  const int slot = p.slot_table[e];
+  const int K = GATEUP ? p.H : p.I;
+  const int n0 = GATEUP ? nt_i * (kTN / 2) : nt_i * kTN;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6, half = lane >> 5;
+  for (int r = tid; r < kRows; r += kThreads) s_pair[r] = r < rows ? p.sorted_pairs[pbeg + m0 + r] : 0;
+  __syncthreads();
   if (slot < 0 || slot >= p.n_slots) {
     if (tid == 0) atomicCAS(p.err, 0, e + 1);
-    for (int idx = tid; idx < rows * 64; idx += 256)
-      hout[(size_t)(pbeg + m0 + idx / 64) * p.I + i0 + idx % 64] = (__bf16)NAN;
+    if constexpr (GATEUP) {
+      for (int idx = tid; idx < rows * (kTN / 2); idx += kThreads)
+        hbuf[(size_t)(pbeg + m0 + idx / (kTN / 2)) * p.I + n0 + idx % (kTN / 2)] = (__bf16)NAN;
+    } else {
+      for (int idx = tid; idx < rows * kTN; idx += kThreads)
+        p.y[(size_t)s_pair[idx / kTN] * p.H + n0 + idx % kTN] = NAN;
+    }
     return;
   }
-  // A: thread t moves 16-byte chunks c = t + 256 j: row c / 8, chunk c % 8
-  const __bf16* asrc[4];
+  // activation rows of this lane: MFMA row block mt holds rows 16 mt + lane % 16
+  // (rows past the tile's end read row 0; their results are dropped)
+  const int quad = lane >> 4;
+  const __bf16* arow[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (tid + 256 * j) >> 3;
-    asrc[j] = r < rows ? x + (size_t)(p.sorted_pairs[pbeg + m0 + r] / p.k) * p.H + 8 * (tid & 7) : nullptr;
+  for (int mt = 0; mt < 4; ++mt) {
+    const int m = kWaveRows * wave + 16 * mt + (lane & 15);
+    const int mm = m < rows ? m : 0;
+    arow[mt] = GATEUP ? x + (size_t)(s_pair[mm] / p.k) * p.H + 8 * quad
+                      : hbuf + (size_t)(pbeg + m0 + mm) * p.I + 8 * quad;
   }
-  // B: thread t stages weight row t / 2 (gate rows 0..63, up rows 64..127), block half t & 1
-  const int brow = tid >> 1, bhalf = tid & 1;
-  const uint8_t* base = p.pool + (size_t)slot * p.slot_bytes;
-  const uint8_t* wrow = base + (brow < 64 ? slot_gate_off(QT, p.H, p.I) : slot_up_off(QT, p.H, p.I)) +
-                        (size_t)(i0 + (brow & 63)) * row_bytes(QT, p.H);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int b_row0[2] = {32 * wn, 64 + 32 * wn};
-  f32x16 acc[2][2];
+  const bool active = kWaveRows * wave < rows;
+  // weight staging: unit v = tid * kUnits + u is row v / 4, block (v / 2) % 2, half v % 2
+  const int v0 = tid * kUnits;
+  const int brow = v0 >> 2, bblk = (v0 >> 1) & 1;
+  const uint8_t* slotp = p.pool + (size_t)slot * p.slot_bytes;
+  const uint8_t* wrow;
+  if constexpr (GATEUP)
+    wrow = slotp + (brow < 64 ? slot_gate_off(QT, p.H, p.I) : slot_up_off(QT, p.H, p.I)) +
+           (size_t)(n0 + (brow & 63)) * row_bytes(QT, p.H);
+  else
+    wrow = slotp + slot_down_off(QT, p.H, p.I) + (size_t)(n0 + brow) * row_bytes(QT, p.I);
+  const int scol = 32 * bblk + 16 * (v0 & 1);
+  __bf16* const sdst0 = &sB[0][brow][scol];
+  __bf16* const sdst1 = &sB[1][brow][scol];
+
+  // 4 x 8 blocks of 16 x 16 accumulators (rows 16 mt + 4 (lane / 16) + r, column 16 nt + lane % 16)
+  f32x4 acc[4][8];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-  uint4 areg[4];
-  BStage<QT> breg;
-  auto fetch = [&](int kk) {
+    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{};
+  // activation fragments (row block, 32-wide K half of the step): two
+  // register sets, the next step's loads issued at the top of the current
+  // step (before the weight prefetch, so waiting for them never waits for
+  // a younger load).  Every wavefront loads, even one with no rows in this
+  // tile (its rows read row 0): a load under a branch makes the compiler's
+  // wait counts assume the path without it.
+  bf16x8 a0[4][2], a1[4][2];
+  const int nk = K / kTK;  // even (checked on the host)
+  auto load_a = [&](bf16x8 (&a)[4][2], int kc) {
+    const size_t koff = (size_t)min(kc, nk - 1) * kTK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      areg[j] = asrc[j] ? *reinterpret_cast<const uint4*>(asrc[j] + kk * kPBK) : make_uint4(0, 0, 0, 0);
-    breg.load(wrow, kk * 2 + bhalf);
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) a[mt][ks] = *reinterpret_cast<const bf16x8*>(arow[mt] + koff + 32 * ks);
   };
-  const int nk = p.H / kPBK;
-  fetch(0);
-  for (int kk = 0; kk < nk; ++kk) {
-    __syncthreads();
+  auto load_w = [&](WStage<QT> (&st)[kUnits], int kc) {
+    const int b = 2 * min(kc, nk - 1) + bblk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;
-      *reinterpret_cast<uint4*>(&sA[c >> 3][8 * (c & 7)]) = areg[j];
+    for (int u = 0; u < kUnits; ++u) st[u].load(wrow, b, (v0 + u) & 1);
+  };
+  auto store_w = [&](const WStage<QT> (&st)[kUnits], __bf16* dst) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) st[u].store(dst + 16 * u, (v0 + u) & 1);
+  };
+  load_a(a0, 0);
+  WStage<QT> st0[kUnits], st1[kUnits];
+  load_w(st0, 0);
+  load_w(st1, 1);
+  store_w(st0, sdst0);
+  load_w(st0, 2);
+  __syncthreads();
+
+  // One K step on buffer `sb` with activations `a`: load the next step's
+  // activations into `an`, stage step kc+1 from `nxt` into the other LDS
+  // buffer and reload `nxt` with step kc+3, then the MFMAs of step kc.
+  // Prefetch indices are clamped to the last step instead of branched on:
+  // near the end the repeated loads and the staging into the idle buffer
+  // are never read.
+  auto step = [&](int kc, const __bf16 (*sb)[kLdB], __bf16* sdst, WStage<QT> (&nxt)[kUnits],
+                  const bf16x8 (&a)[4][2], bf16x8 (&an)[4][2]) {
+    load_a(an, kc + 1);
+    store_w(nxt, sdst);
+    load_w(nxt, kc + 3);
+    if (active) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int nh = 0; nh < 2; ++nh) {
+          bf16x8 b[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            b[q] = *reinterpret_cast<const bf16x8*>(&sb[16 * (4 * nh + q) + (lane & 15)][32 * ks + 8 * quad]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[mt][4 * nh + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b[q], acc[mt][4 * nh + q], 0, 0, 0);
+        }
+      }
     }
-    breg.store(&sB[brow][32 * bhalf]);
     __syncthreads();
-    if (kk + 1 < nk) fetch(kk + 1);
-    mma_k64(sA, sB, 64 * wm, b_row0, acc);
+  };
+  for (int kc = 0; kc < nk; kc += 2) {
+    step(kc, sB[0], sdst1, st1, a0, a1);
+    step(kc + 1, sB[1], sdst0, st0, a1, a0);
   }
-  // SwiGLU in registers: acc[mt][0] holds gate, acc[mt][1] up at the same (m, n)
+  if (!active) return;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 64 * wm + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (m < rows) {
-        const float g = acc[mt][0][r], u = acc[mt][1][r];
-        hout[(size_t)(pbeg + m0 + m) * p.I + i0 + 32 * wn + (lane & 31)] = (__bf16)(g / (1.0f + expf(-g)) * u);
+    for (int r = 0; r < 4; ++r) {
+      const int m = kWaveRows * wave + 16 * mt + 4 * quad + r;
+      if (m >= rows) continue;
+      if constexpr (GATEUP) {
+        __bf16* hrow = hbuf + (size_t)(pbeg + m0 + m) * p.I + n0 + (lane & 15);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float g = acc[mt][nt][r], u = acc[mt][nt + 4][r];
+          hrow[16 * nt] = (__bf16)(g / (1.0f + expf(-g)) * u);
+        }
+      } else {
+        float* yrow = p.y + (size_t)s_pair[m] * p.H + n0 + (lane & 15);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) yrow[16 * nt] = acc[mt][nt][r];
       }
     }
   }
 }
 
-// ------------------------------------------------------------------ down
-template <int QT>
-__global__ __launch_bounds__(256) void prefill_down_kernel(FfnParams p, const __bf16* __restrict__ hin,
-                                                           const int2* __restrict__ tiles,
-                                                           const int* __restrict__ n_tiles) {
-  __shared__ __bf16 sA[kPBM][kPLD];
-  __shared__ __bf16 sB[kPBN][kPLD];
-  const int ntn = p.H / kPBN;
-  const int mt_i = blockIdx.x / ntn, nt_i = blockIdx.x - mt_i * ntn;
-  if (mt_i >= *n_tiles) return;
-  const int2 tl = tiles[mt_i];
-  const int e = tl.x, m0 = tl.y;
-  const int slot = p.slot_table[e];
-  const int pbeg = p.offsets[e];
-  const int rows = min(kPBM, p.offsets[e + 1] - pbeg - m0);
-  const int n0 = nt_i * kPBN;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  if (slot < 0 || slot >= p.n_slots) {
-    for (int idx = tid; idx < rows * kPBN; idx += 256)
-      p.y[(size_t)p.sorted_pairs[pbeg + m0 + idx / kPBN] * p.H + n0 + idx % kPBN] = NAN;
-    return;
-  }
-  const __bf16* asrc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (tid + 256 * j) >> 3;
-    asrc[j] = r < rows ? hin + (size_t)(pbeg + m0 + r) * p.I + 8 * (tid & 7) : nullptr;
-  }
-  const int brow = tid >> 1, bhalf = tid & 1;
-  const uint8_t* wrow = p.pool + (size_t)slot * p.slot_bytes + slot_down_off(QT, p.H, p.I) +
-                        (size_t)(n0 + brow) * row_bytes(QT, p.I);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int b_row0[2] = {64 * wn, 64 * wn + 32};
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-  uint4 areg[4];
-  BStage<QT> breg;
-  auto fetch = [&](int kk) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      areg[j] = asrc[j] ? *reinterpret_cast<const uint4*>(asrc[j] + kk * kPBK) : make_uint4(0, 0, 0, 0);
-    breg.load(wrow, kk * 2 + bhalf);
-  };
-  const int nk = p.I / kPBK;
-  fetch(0);
-  for (int kk = 0; kk < nk; ++kk) {
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;
-      *reinterpret_cast<uint4*>(&sA[c >> 3][8 * (c & 7)]) = areg[j];
-    }
-    breg.store(&sB[brow][32 * bhalf]);
-    __syncthreads();
-    if (kk + 1 < nk) fetch(kk + 1);
-    mma_k64(sA, sB, 64 * wm, b_row0, acc);
-  }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 64 * wm + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (m < rows) {
-        float* yrow = p.y + (size_t)p.sorted_pairs[pbeg + m0 + m] * p.H + n0 + 64 * wn + (lane & 31);
-        yrow[0] = acc[mt][0][r];
-        yrow[32] = acc[mt][1][r];
-      }
-    }
-  }
+bool prefill_mfma_supported(int H, int I) {
+  // column tiles of 128 (down) and 64 (gate/up), and an even number of K steps
+  return H % (2 * kTK) == 0 && I % (2 * kTK) == 0 && H % kTN == 0;
 }
 
-bool prefill_mfma_supported(int H, int I) { return H % kPBN == 0 && I % 64 == 0 && H % kPBK == 0; }
+// Wavefronts per workgroup (64 rows each).  Eight (512 rows, one tile per
+// expert of a 4096-token batch) measured slower than four: with one
+// workgroup per CU every barrier idles the matrix cores.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = kWaveRows * kPrefillWaves;
+
+static int prefill_max_tiles(size_t P, int E) { return (int)(P / kPrefillRows) + E + 1; }
 
 size_t prefill_ws_bytes(int T, int k, int I, int E) {
   const size_t P = (size_t)T * k;
-  const size_t max_tiles = P / kPBM + (size_t)E + 1;
-  return 256 + ((max_tiles * sizeof(int2) + 255) / 256) * 256 + P * I * sizeof(__bf16);
+  return 256 + ((prefill_max_tiles(P, E) * sizeof(int2) + 255) / 256) * 256 + P * I * sizeof(__bf16);
 }
 
 int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws, hipStream_t s) {
   const size_t P = (size_t)p.T * p.k;
-  const int max_tiles = (int)(P / kPBM) + p.E + 1;
+  const int max_tiles = prefill_max_tiles(P, p.E);
   int* count = (int*)ws;
   int2* tiles = (int2*)((char*)ws + 256);
   __bf16* hbuf = (__bf16*)((char*)ws + 256 + ((max_tiles * sizeof(int2) + 255) / 256) * 256);
+  const unsigned row_groups = (unsigned)((max_tiles + kXcds - 1) / kXcds);
   {
     KernelTimer timer(ctx, "prefill_tiles", s);
-    launch(prefill_tiles_kernel, 1, 256, 0, s, p.offsets, p.E, tiles, count);
+    launch(prefill_tiles_kernel, 1, 256, 0, s, p.offsets, p.mask, p.E, kPrefillRows, tiles, count);
   }
   int rc = check_launch("prefill_tiles_kernel");
   if (rc) return rc;
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
-    const unsigned grid = (unsigned)max_tiles * (p.I / 64);
+    const int ntn = p.I / (kTN / 2);
+    const unsigned grid = kXcds * row_groups * (unsigned)ntn;
     if (p.qtype == MOE_QTYPE_Q4_0)
-      launch(prefill_gateup_kernel<MOE_QTYPE_Q4_0>, grid, 256, 0, s, p, (const __bf16*)x, tiles, count, hbuf);
+      launch(prefill_gemm_kernel<MOE_QTYPE_Q4_0, true, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, (const __bf16*)x, tiles, count, ntn, hbuf);
     else
-      launch(prefill_gateup_kernel<MOE_QTYPE_Q8_0>, grid, 256, 0, s, p, (const __bf16*)x, tiles, count, hbuf);
+      launch(prefill_gemm_kernel<MOE_QTYPE_Q8_0, true, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, (const __bf16*)x, tiles, count, ntn, hbuf);
   }
   if ((rc = check_launch("prefill_gateup_kernel"))) return rc;
   {
     KernelTimer timer(ctx, "ffn_down", s);
-    const unsigned grid = (unsigned)max_tiles * (p.H / kPBN);
+    const int ntn = p.H / kTN;
+    const unsigned grid = kXcds * row_groups * (unsigned)ntn;
     if (p.qtype == MOE_QTYPE_Q4_0)
-      launch(prefill_down_kernel<MOE_QTYPE_Q4_0>, grid, 256, 0, s, p, hbuf, tiles, count);
+      launch(prefill_gemm_kernel<MOE_QTYPE_Q4_0, false, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, (const __bf16*)x, tiles, count, ntn, hbuf);
     else
-      launch(prefill_down_kernel<MOE_QTYPE_Q8_0>, grid, 256, 0, s, p, hbuf, tiles, count);
+      launch(prefill_gemm_kernel<MOE_QTYPE_Q8_0, false, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, (const __bf16*)x, tiles, count, ntn, hbuf);
   }
   return check_launch("prefill_down_kernel");
 }

@@ -364,3 +364,33 @@ def test_prefill_full_size_sampled(ctx, prefill_layer):
     note(f"   sampled out max rel err {err:.2e}, y {e_y:.2e}")
     assert err <= PREFILL_TOL and e_y <= PREFILL_TOL
     assert np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_expert_mask_skips_experts(ctx, prefill_layer, mode):
+    """Experts masked out are not computed: their y rows keep what they held;
+    the others equal an unmasked run bit for bit."""
+    wl = prefill_layer.wl
+    T = 300 if mode == "prefill" else 4
+    note(f"expert mask {mode} T={T}")
+    logits, xbits, x32 = _prefill_inputs(wl, T)
+    from gpu_util import bf16_tensor
+    if mode == "prefill":
+        m, xdt, xd = L.MODE_PREFILL, L.DTYPE_BF16, bf16_tensor(xbits)
+    else:
+        m, xdt, xd = L.MODE_DECODE, L.DTYPE_F32, dev(x32)
+    rl = prefill_layer
+    buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV, mode=m, x_dtype=xdt)
+    args = (ctx, buf, rl.pool.base(), rl.pool.slot_bytes, rl.pool.n_slots, rl.slot_table, xd)
+    layer.forward(*args, logits_in=dev(logits), steps=("route", "permute", "ffn"))
+    full = buf.y.cpu().numpy().reshape(T * wl.k, wl.H)
+    mask = (np.arange(wl.E) % 3 != 1).astype(np.int32)
+    buf.y.fill_(7.0)
+    layer.forward(*args, expert_mask=dev(mask), steps=("ffn",))
+    torch.cuda.synchronize()
+    moe.moe_ctx_check(ctx)
+    y = buf.y.cpu().numpy().reshape(T * wl.k, wl.H)
+    keep = mask[buf.ids.cpu().numpy().reshape(-1)] == 1
+    assert (~keep).any() and keep.any()
+    assert (y[~keep] == 7.0).all()
+    np.testing.assert_array_equal(y[keep], full[keep])
