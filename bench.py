@@ -56,14 +56,15 @@ def parse_args():
                    help="first run a device copy and an elementwise negate of MIB MiB each, the known-size "
                         "kernels that scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
     p.add_argument("--cache-steps", type=int, default=None, help="steps of the expert-cache trace (default 2048)")
-    p.add_argument("--unfused", action="store_true",
-                   help="run each layer as the four separate entry points instead of the two fused calls")
+    p.add_argument("--calls", choices=("layer", "two", "four"), default="layer",
+                   help="per layer: moe_decode_layer (one call), moe_route_permute + moe_expert_ffn with the "
+                        "combine (two), or moe_route, moe_permute, moe_expert_ffn, moe_combine (four)")
     return p.parse_args()
 
 
 # ---------------------------------------------------------------- decode
 class DecodeStack:
-    def __init__(self, ctx, wl, n_layers: int, fused: bool = True):
+    def __init__(self, ctx, wl, n_layers: int, fused="layer"):
         import numpy as np
         import torch
         from expert_offload_amd import layer
@@ -374,7 +375,7 @@ def main():
     if args.layers != wl.layers:
         log(f"NOTE: {args.layers} layers instead of {wl.layers} (profiling run)")
     ctx = moe.Ctx(0)
-    stack = DecodeStack(ctx, wl, args.layers, fused=not args.unfused)
+    stack = DecodeStack(ctx, wl, args.layers, fused={"layer": "layer", "two": True, "four": False}[args.calls])
 
     T = args.batch
     x, bufs, wall, gpu_ms = time_graph(stack, T, args.steps, args.warmup)
@@ -406,8 +407,8 @@ def main():
         "config": {"workload": wl.name, "layers": args.layers, "tokens_per_step": T, "hidden": wl.H,
                    "experts": wl.E, "top_k": wl.k, "intermediate": wl.I, "weights": "Q8_0",
                    "activations": "fp32", "graph": "hip graph of the whole stack",
-                   "calls_per_layer": "moe_route_permute + moe_expert_ffn(fused combine)" if not args.unfused
-                   else "moe_route, moe_permute, moe_expert_ffn, moe_combine"},
+                   "calls_per_layer": {"layer": "moe_decode_layer", "two": "moe_route_permute + moe_expert_ffn",
+                                       "four": "moe_route, moe_permute, moe_expert_ffn, moe_combine"}[args.calls]},
         "roofline": roofline,
         "stack_hbm_gbs": stack_bytes / (ms_per_step * 1e-3) / 1e9,
     }

@@ -34,7 +34,7 @@ EXPORTS = (
     "cache_slot_table_lookup", "cache_slot_table_device", "cache_slot_table_stats",
     "cache_slot_table_destroy", "prefetch_expert", "cache_mark_layer_done",
     "moe_check_bank_types", "moe_ctx_set_timing", "moe_ctx_kernel_time",
-    "moe_route_permute_workspace_size", "moe_route_permute",
+    "moe_route_permute_workspace_size", "moe_route_permute", "moe_decode_layer",
 )
 
 
@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
         "moe_permute": (i, [vp, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]),
         "moe_expert_ffn_workspace_size": (i, [ctypes.POINTER(moe_ffn_args), szp]),
         "moe_expert_ffn": (i, [vp, ctypes.POINTER(moe_ffn_args), vp]),
+        "moe_decode_layer": (i, [vp, ctypes.POINTER(moe_ffn_args), vp, vp, vp, vp, vp, vp, vp]),
         "moe_combine": (i, [vp, vp, vp, i, i, i, vp, vp]),
         "moe_dequantize": (i, [vp, i, vp, i, i, i, vp, vp]),
         "cache_slot_table_create": (i, [i, i, i, i, i, i, vp, vp, ctypes.POINTER(vp)]),
@@ -289,6 +290,13 @@ def moe_expert_ffn_workspace_size(args: moe_ffn_args) -> int:
 
 def moe_expert_ffn(ctx: Ctx, args: moe_ffn_args, stream=None) -> None:
     _check(lib().moe_expert_ffn(ctx.handle, ctypes.byref(args), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_decode_layer(ctx: Ctx, args: moe_ffn_args, router_w, bias, logits_in, logits_out, topk_ids, pair_pos,
+                     stream=None) -> None:
+    _check(lib().moe_decode_layer(ctx.handle, ctypes.byref(args), _dev_ptr(router_w), _dev_ptr(bias),
+                                  _dev_ptr(logits_in), _dev_ptr(logits_out), _dev_ptr(topk_ids),
+                                  _dev_ptr(pair_pos), _stream(stream)), "moe_decode_layer")
 
 
 def moe_combine(ctx: Ctx, y_pairs, topk_w, T: int, k: int, H: int, out, stream=None) -> None:

@@ -18,6 +18,7 @@
 
 #include "device_common.h"
 #include "ffn.h"
+#include "route_common.h"
 
 namespace moe {
 
@@ -207,14 +208,121 @@ __device__ __forceinline__ void stage_ctl(const FfnParams& p, CtlLds& s, bool wa
   __syncthreads();
 }
 
+// Routing inside the gate/up kernel (T*k <= 64).  Every workgroup selects
+// the top k of each token from the router logits (wavefront w takes tokens
+// w, w + NT/64, ...), keeping ids, weights and each token's selection as
+// bitmasks in LDS.  A wavefront then derives its work item from the masks
+// alone (route_item), so no grouping pass stands between the selection and
+// the weight loads; workgroup 0 groups the pairs and writes the routing
+// results after its FFN work (route_write), so no barrier of the
+// workgroup waits for those stores.
+struct RouteLds {
+  uint64_t taken[kRouteInFfnMaxPairs][kMaxE / kWave];  // per token (T <= T*k <= 64)
+  int ids[kRouteInFfnMaxPairs];
+  int pos[kRouteInFfnMaxPairs];
+};
+
+template <int NT, int NS>
+__device__ __forceinline__ void route_select(const FfnParams& p, const RouteArgs& ra, CtlLds& s, RouteLds& r) {
+  const int E = p.E, T = p.T, k = p.k;
+  float* lo = blockIdx.x == 0 ? ra.logits_out : nullptr;
+  // the slot table goes to registers first and to LDS after the selection,
+  // so its loads and the logits' loads are in flight together
+  constexpr int kPer = kMaxE / NT;
+  int sl[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + NT * u;
+    sl[u] = i < E ? p.slot_table[i] : 0;
+  }
+  for (int t = threadIdx.x >> 6; t < T; t += NT / kWave)
+    wave_topk_ns<NS>(ra.logits + (size_t)t * E, ra.bias, E, k, lo ? lo + (size_t)t * E : nullptr, nullptr, nullptr,
+                     r.ids + t * k, s.w + t * k, r.taken[t]);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + NT * u;
+    if (i < E) s.slots[i] = sl[u];
+  }
+  __syncthreads();
+}
+
+// Number of experts chosen by any token (uniform over the wavefront).
+__device__ __forceinline__ int route_active(const RouteLds& r, int T, int E) {
+  int n = 0;
+  for (int i = 0; i < (E + kWave - 1) / kWave; ++i) {
+    uint64_t u = 0;
+    for (int t = 0; t < T; ++t) u |= r.taken[t][i];
+    n += __builtin_popcountll(u);
+  }
+  return n;
+}
+
+// The a-th chosen expert in id order, its first place in the grouped order
+// (set bits below it over all tokens) and its pairs as a bitmask over pair
+// indices: set bits ascending are the stable order.  Wavefront-uniform.
+struct ItemCtl {
+  int e, pbeg, n_e;
+  uint64_t pairs;
+};
+__device__ __forceinline__ ItemCtl route_item(const RouteLds& r, int T, int k, int E, int a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int e = -1, before = 0;
+  for (int i = 0; i < (E + kWave - 1) / kWave && e < 0; ++i) {
+    uint64_t u = 0;
+    for (int t = 0; t < T; ++t) u |= r.taken[t][i];
+    const int c = __builtin_popcountll(u);
+    if (a - before < c) {
+      const uint64_t hit = __ballot(((u >> lane) & 1) && __builtin_popcountll(u & lt) == a - before);
+      e = kWave * i + (int)__builtin_ctzll(hit);
+    }
+    before += c;
+  }
+  const int wi = e / kWave, bit = e % kWave;
+  const uint64_t below = (bit == 0) ? 0ull : (~0ull >> (kWave - bit));
+  int pbeg = 0;
+  for (int t = 0; t < T; ++t) {
+    for (int i = 0; i < wi; ++i) pbeg += __builtin_popcountll(r.taken[t][i]);
+    pbeg += __builtin_popcountll(r.taken[t][wi] & below);
+  }
+  const uint64_t pm = __ballot(lane < T * k && r.ids[lane] == e);
+  return {e, pbeg, (int)__builtin_popcountll(pm), pm};
+}
+
+template <int NT>
+__device__ __forceinline__ void route_write(const FfnParams& p, const RouteArgs& ra, CtlLds& s, RouteLds& r) {
+  if (threadIdx.x < kWave) wave_group_masks(r.taken, r.ids, p.T, p.k, p.E, s.pairs, r.pos, s.offsets, s.active);
+  __syncthreads();
+  const int P = p.T * p.k;
+  for (int i = threadIdx.x; i < P; i += NT) {
+    ra.ids[i] = r.ids[i];
+    ra.w[i] = s.w[i];
+    ra.sorted_pairs[i] = s.pairs[i];
+    ra.pair_pos[i] = r.pos[i];
+  }
+  for (int i = threadIdx.x; i <= p.E; i += NT) ra.offsets[i] = s.offsets[i];
+  for (int i = threadIdx.x; i <= s.active[0]; i += NT) ra.active[i] = s.active[i];
+}
+
 // ------------------------------------------------------ gate/up + SwiGLU
 // A work item is one wavefront: (active expert, RW/2 intermediate indices);
 // its rows interleave gate and up: row 2m = gate(i0 + m), 2m + 1 = up(i0 + m).
-template <int QT, int LPR, int BPL, int RPL>
-__global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const float* __restrict__ x) {
+// RNS = 0: control data from moe_permute's results; RNS > 0: routing in the
+// kernel, with ceil(E / 64) <= RNS logits per lane in the top-k.
+template <int QT, int LPR, int BPL, int RPL, int RNS>
+__global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const float* __restrict__ x, RouteArgs ra) {
+  constexpr bool ROUTE = RNS > 0;
   constexpr int RPP = kWave / LPR, RW = RPP * RPL, NI = RW / 2;
   __shared__ CtlLds ctl;
-  stage_ctl<256>(p, ctl, false);
+  __shared__ RouteLds rlds;
+  int n_active;
+  if constexpr (ROUTE) {
+    route_select<256, RNS>(p, ra, ctl, rlds);
+    n_active = route_active(rlds, p.T, p.E);
+  } else {
+    stage_ctl<256>(p, ctl, false);
+    n_active = ctl.active[0];
+  }
   const int* pairs = ctl.pairs;
   constexpr int STRIDE = RPL >= 2 ? LPR / RPL : LPR;  // lane distance gate row -> up row
   const int lane = threadIdx.x & (kWave - 1);
@@ -222,15 +330,37 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
   const int rr = g * RPL + lg / (LPR / RPL);  // row this lane holds after the fold
   const bool writer = (lg % (LPR / RPL)) == 0 && (rr & 1) == 0;
   const int n_chunks = p.I / NI;
-  const int items = ctl.active[0] * n_chunks;
+  const int items = n_active * n_chunks;
   const size_t gate_off = slot_gate_off(QT, p.H, p.I), up_off = slot_up_off(QT, p.H, p.I);
   const size_t rbytes = row_bytes(QT, p.H);
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
     const int a = item / n_chunks, c = item - a * n_chunks;
-    const int e = ctl.active[1 + a];
+    int e, pbeg, n_e;
+    uint64_t pm = 0;  // routing variant: the expert's pairs as bits
+    if constexpr (ROUTE) {
+      const ItemCtl ic = route_item(rlds, p.T, p.k, p.E, a);
+      e = ic.e;
+      pbeg = ic.pbeg;
+      n_e = ic.n_e;
+      pm = ic.pairs;
+    } else {
+      e = ctl.active[1 + a];
+      pbeg = ctl.offsets[e];
+      n_e = ctl.offsets[e + 1] - pbeg;
+    }
+    // pair s of the expert, s = 0, 1, ... in turn
+    int s_next = 0;
+    auto next_pair = [&]() -> int {
+      if constexpr (ROUTE) {
+        const int q = (int)__builtin_ctzll(pm);
+        pm &= pm - 1;
+        return q;
+      } else {
+        return pairs[pbeg + s_next++];
+      }
+    };
     if (p.mask && !p.mask[e]) continue;
     const int slot = ctl.slots[e];
-    const int pbeg = ctl.offsets[e], n_e = ctl.offsets[e + 1] - pbeg;
     const int i0 = c * NI;
     if (slot < 0 || slot >= p.n_slots) {
       if (lane == 0) atomicCAS(p.err, 0, e + 1);
@@ -244,13 +374,11 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
       const int rw = g * RPL + r;
       rows[r] = base + ((rw & 1) ? up_off : gate_off) + (size_t)(i0 + rw / 2) * rbytes;
     }
-    // first token's activations go out before the weights (they are L2
-    // hits), so the per-row waits do not wait for the whole tile
     // the first token's activations go out before the weights (L2 hits), and
     // the first token is peeled out of the loop so its row-by-row waits cover
     // only the weight loads issued so far
     float xv[BPL][32];
-    load_act<LPR, BPL>(x + (size_t)(pairs[pbeg] / p.k) * p.H, lg, xv);
+    load_act<LPR, BPL>(x + (size_t)(next_pair() / p.k) * p.H, lg, xv);
     RowTile<QT, LPR, BPL, RPL> tile;
     tile.load(rows, lg);
     auto finish = [&](int s, float (&acc)[RPL]) {
@@ -267,11 +395,14 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
       finish(0, acc);
     }
     for (int s = 1; s < n_e; ++s) {
-      load_act<LPR, BPL>(x + (size_t)(pairs[pbeg + s] / p.k) * p.H, lg, xv);
+      load_act<LPR, BPL>(x + (size_t)(next_pair() / p.k) * p.H, lg, xv);
       float acc[RPL];
       tile.dot(xv, acc);
       finish(s, acc);
     }
+  }
+  if constexpr (ROUTE) {
+    if (blockIdx.x == 0) route_write<256>(p, ra, ctl, rlds);
   }
 }
 
@@ -432,10 +563,20 @@ constexpr int rows_per_lane() {
 }
 
 template <int QT, int LPR, int BPL>
-static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStream_t s) {
+static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStream_t s, const RouteArgs* ra) {
   constexpr int RPL0 = rows_per_lane<QT, BPL>();
   constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
-  launch(ffn_gateup_decode<QT, LPR, BPL, RPL>, grid, 256, 0, s, p, x);
+  if (!ra) {
+    launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 0>, grid, 256, 0, s, p, x, RouteArgs{});
+    return;
+  }
+  if constexpr (LPR == 64) {  // the routing variant exists for these shapes (decode_route_supported)
+    if (p.E <= 64) launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 1>, grid, 256, 0, s, p, x, *ra);
+    else if (p.E <= 128) launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 2>, grid, 256, 0, s, p, x, *ra);
+    else if (p.E <= 256) launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 4>, grid, 256, 0, s, p, x, *ra);
+    else if (p.E <= 512) launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 8>, grid, 256, 0, s, p, x, *ra);
+    else launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 16>, grid, 256, 0, s, p, x, *ra);
+  }
 }
 // Down tiles aim at 8 rows (H/8 workgroups): RPL = 8 / (64 / LPR) within
 // the register budget.
@@ -481,9 +622,10 @@ static int rows_per_wave_rt(GemvShape sh) {
 }
 
 template <int QT>
-static void dispatch_gateup(GemvShape sh, const FfnParams& p, const float* x, int grid, hipStream_t s) {
+static void dispatch_gateup(GemvShape sh, const FfnParams& p, const float* x, int grid, hipStream_t s,
+                            const RouteArgs* ra) {
 #define MOE_GU(L, B) \
-  if (sh.lpr == L && sh.bpl == B) return launch_gateup<QT, L, B>(p, x, grid, s);
+  if (sh.lpr == L && sh.bpl == B) return launch_gateup<QT, L, B>(p, x, grid, s, ra);
   MOE_GU(64, 1) MOE_GU(64, 2) MOE_GU(64, 3) MOE_GU(32, 1) MOE_GU(32, 2) MOE_GU(32, 3)
   MOE_GU(16, 1) MOE_GU(16, 2) MOE_GU(16, 3) MOE_GU(8, 1) MOE_GU(8, 2) MOE_GU(8, 3)
 #undef MOE_GU
@@ -497,12 +639,18 @@ static void dispatch_down(GemvShape sh, const FfnParams& p, int grid, hipStream_
 #undef MOE_DN
 }
 
+bool decode_route_supported(int H, int I, int T, int k) {
+  GemvShape a;
+  return decode_gemv_supported(H, I, T, k) && (long long)T * k <= kRouteInFfnMaxPairs && gemv_shape(H, &a) &&
+         a.lpr == 64;
+}
+
 bool decode_gemv_supported(int H, int I, int T, int k) {
   GemvShape a, b;
   return (long long)T * k <= kCtlMaxPairs && gemv_shape(H, &a) && gemv_shape(I, &b);
 }
 
-int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s) {
+int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route) {
   GemvShape gu, dn;
   gemv_shape(p.H, &gu);
   gemv_shape(p.I, &dn);
@@ -521,8 +669,8 @@ int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStrea
   const int grid_dn = std::max(1, p.H / rt_dn);
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
-    if (p.qtype == MOE_QTYPE_Q8_0) dispatch_gateup<MOE_QTYPE_Q8_0>(gu, p, x, grid_gu, s);
-    else dispatch_gateup<MOE_QTYPE_Q4_0>(gu, p, x, grid_gu, s);
+    if (p.qtype == MOE_QTYPE_Q8_0) dispatch_gateup<MOE_QTYPE_Q8_0>(gu, p, x, grid_gu, s, route);
+    else dispatch_gateup<MOE_QTYPE_Q4_0>(gu, p, x, grid_gu, s, route);
   }
   int rc = check_launch("ffn_gateup_decode");
   if (rc) return rc;

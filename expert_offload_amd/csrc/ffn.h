@@ -23,12 +23,35 @@ struct FfnParams {
   float* out;           // [T][H] or NULL: fused combine target
 };
 
+// Routing done inside the decode gate/up kernel (small batches, T*k <= 64):
+// every workgroup selects the top k of each token from `logits` (+ bias)
+// and groups the pairs in LDS; workgroup 0 also writes the results.
+struct RouteArgs {
+  const float* logits;   // [T][E]
+  const float* bias;     // [E] or NULL
+  float* logits_out;     // [T][E] biased logits, or NULL
+  int32_t* ids;          // [T][k]
+  float* w;              // [T][k]
+  int32_t* offsets;      // [E + 1]
+  int32_t* sorted_pairs; // [T*k]
+  int32_t* pair_pos;     // [T*k]
+  int32_t* active;       // [1 + E]
+};
+constexpr int kRouteInFfnMaxPairs = 64;
+
 int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype, hipStream_t s);
 bool decode_gemv_supported(int H, int I, int T, int k);
-int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s);
+bool decode_route_supported(int H, int I, int T, int k);
+int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s,
+                      const RouteArgs* route = nullptr);
 bool prefill_mfma_supported(int H, int I);
 size_t prefill_ws_bytes(int T, int k, int I, int E);
 int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws, hipStream_t s);
+int validate_route_args(const char* fn, const void* x, int x_dtype, const float* router_w,
+                        const float* logits_in, int T, int H, int E, int k, float* logits_out,
+                        int32_t* topk_ids, float* topk_w);
+int launch_router_logits(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w, const float* bias, int T,
+                         int H, int E, float* logits_out, hipStream_t s);
 int launch_combine(moe_ctx* ctx, const float* y, const float* w, int T, int k, int H, float* out, hipStream_t s);
 
 }  // namespace moe

@@ -70,13 +70,7 @@ extern "C" int moe_expert_ffn_workspace_size(const moe_ffn_args* args, size_t* b
   return MOE_OK;
 }
 
-extern "C" int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* a, void* stream) {
-  clear_error();
-  if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: ctx is NULL");
-  int rc = validate_ffn(a, true);
-  if (rc) return rc;
-  if (a->T == 0) return MOE_OK;
-  if ((rc = ensure_device(ctx))) return rc;
+static FfnParams ffn_params(const moe_ctx* ctx, const moe_ffn_args* a) {
   FfnParams p;
   p.pool = (const uint8_t*)a->pool_base;
   p.slot_bytes = a->slot_bytes;
@@ -93,6 +87,17 @@ extern "C" int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* a, void* stream)
   p.err = ctx->d_err;
   p.topk_w = a->topk_w;
   p.out = a->out;
+  return p;
+}
+
+extern "C" int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* a, void* stream) {
+  clear_error();
+  if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: ctx is NULL");
+  int rc = validate_ffn(a, true);
+  if (rc) return rc;
+  if (a->T == 0) return MOE_OK;
+  if ((rc = ensure_device(ctx))) return rc;
+  FfnParams p = ffn_params(ctx, a);
   hipStream_t s = (hipStream_t)stream;
   if (a->mode == MOE_MODE_DECODE && decode_gemv_supported(a->H, a->I, a->T, a->k))
     return launch_ffn_decode(ctx, p, (const float*)a->x, s);
@@ -103,4 +108,53 @@ extern "C" int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* a, void* stream)
     rc = launch_ffn_valu(ctx, p, a->x, a->x_dtype, s);
   if (rc || !a->out) return rc;
   return launch_combine(ctx, a->y_pairs, a->topk_w, a->T, a->k, a->H, a->out, s);
+}
+
+extern "C" int moe_decode_layer(moe_ctx* ctx, const moe_ffn_args* a, const float* router_w, const float* bias,
+                                const float* logits_in, float* logits_out, int32_t* topk_ids, int32_t* pair_pos,
+                                void* stream) {
+  clear_error();
+  if (!ctx || !a) return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: ctx or args is NULL");
+  if (a->mode != MOE_MODE_DECODE)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: args.mode must be MOE_MODE_DECODE");
+  if (!a->topk_w || !a->out)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: args.topk_w and args.out are required");
+  if (a->expert_mask) return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: args.expert_mask must be NULL");
+  // the routing results go to the args' topk_w / expert_offsets /
+  // sorted_pairs / active buffers, which moe_expert_ffn only reads
+  float* topk_w = const_cast<float*>(a->topk_w);
+  int32_t* offsets = const_cast<int32_t*>(a->expert_offsets);
+  int32_t* sorted = const_cast<int32_t*>(a->sorted_pairs);
+  int32_t* active = const_cast<int32_t*>(a->active);
+  int rc = validate_route_args("moe_decode_layer", a->x, a->x_dtype, router_w, logits_in, a->T, a->H, a->E, a->k,
+                               logits_out, topk_ids, topk_w);
+  if (rc) return rc;
+  if ((rc = validate_ffn(a, true))) return rc;
+  if (a->T == 0) return MOE_OK;
+  if (!pair_pos) return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: pair_pos is NULL");
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (!decode_route_supported(a->H, a->I, a->T, a->k)) {
+    rc = moe_route_permute(ctx, a->x, a->x_dtype, router_w, bias, logits_in, a->T, a->H, a->E, a->k, logits_out,
+                           topk_ids, topk_w, offsets, sorted, pair_pos, active, nullptr, 0, stream);
+    if (rc) return rc;
+    return moe_expert_ffn(ctx, a, stream);
+  }
+  RouteArgs ra{};
+  if (!logits_in) {
+    if ((rc = launch_router_logits(ctx, a->x, a->x_dtype, router_w, bias, a->T, a->H, a->E, logits_out, s)))
+      return rc;
+    ra.logits = logits_out;  // biased already
+  } else {
+    ra.logits = logits_in;
+    ra.bias = bias;
+    ra.logits_out = logits_out;
+  }
+  ra.ids = topk_ids;
+  ra.w = topk_w;
+  ra.offsets = offsets;
+  ra.sorted_pairs = sorted;
+  ra.pair_pos = pair_pos;
+  ra.active = active;
+  return launch_ffn_decode(ctx, ffn_params(ctx, a), (const float*)a->x, s, &ra);
 }

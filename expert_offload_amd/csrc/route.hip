@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kTopkPermuteThreads) void topk_permute_kernel(
   }
 }
 
-static int validate_route(const char* fn, const void* x, int x_dtype, const float* router_w,
+int validate_route_args(const char* fn, const void* x, int x_dtype, const float* router_w,
                           const float* logits_in, int T, int H, int E, int k, float* logits_out,
                           int32_t* topk_ids, float* topk_w) {
   if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK)
@@ -156,6 +156,17 @@ static int validate_route(const char* fn, const void* x, int x_dtype, const floa
       return set_error(MOE_ERR_ALIGNMENT, "%s: x and router_w must be 16-byte aligned", fn);
   }
   return MOE_OK;
+}
+
+int launch_router_logits(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w, const float* bias, int T,
+                         int H, int E, float* logits_out, hipStream_t s) {
+  KernelTimer timer(ctx, "router_logits", s);
+  dim3 grid(E);
+  if (x_dtype == MOE_DTYPE_F32)
+    launch(router_logits_kernel<float>, grid, 256, 0, s, (const float*)x, router_w, bias, T, H, E, logits_out);
+  else
+    launch(router_logits_kernel<uint16_t>, grid, 256, 0, s, (const uint16_t*)x, router_w, bias, T, H, E, logits_out);
+  return check_launch("router_logits_kernel");
 }
 
 static int launch_route(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w, const float* bias,
@@ -193,7 +204,7 @@ extern "C" int moe_route(moe_ctx* ctx, const void* x, int x_dtype, const float* 
                          float* logits_out, int32_t* topk_ids, float* topk_w, void* stream) {
   clear_error();
   if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_route: ctx is NULL");
-  int rc = validate_route("moe_route", x, x_dtype, router_w, logits_in, T, H, E, k, logits_out, topk_ids, topk_w);
+  int rc = validate_route_args("moe_route", x, x_dtype, router_w, logits_in, T, H, E, k, logits_out, topk_ids, topk_w);
   if (rc || T == 0) return rc;
   if ((rc = ensure_device(ctx))) return rc;
   return launch_route(ctx, x, x_dtype, router_w, bias, logits_in, T, H, E, k, logits_out, topk_ids, topk_w,
@@ -216,7 +227,7 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
   clear_error();
   (void)ws; (void)ws_bytes;
   if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: ctx is NULL");
-  int rc = validate_route("moe_route_permute", x, x_dtype, router_w, logits_in, T, H, E, k, logits_out,
+  int rc = validate_route_args("moe_route_permute", x, x_dtype, router_w, logits_in, T, H, E, k, logits_out,
                           topk_ids, topk_w);
   if (rc) return rc;
   if (!expert_offsets || !active || (T > 0 && (!sorted_pairs || !pair_pos)))

@@ -15,13 +15,16 @@ namespace moe {
 // (ballots over the slots): equal values go to the lower id.  Then w_j =
 // exp(l_j - l_max) / sum_j' exp(l_j' - l_max), which equals the softmax
 // probabilities renormalised over the kept experts.  NaN logits count as
-// -inf.  Writes ids/w (and the logits used, when logits_out is set); ids
-// also go to ids_copy if set.
+// -inf.  Writes ids/w when set (and the logits used, when logits_out is
+// set); ids and w also go to ids_copy / w_copy if set, and with `taken`
+// the selection as bitmasks: bit l of taken[i] set if expert l + 64 i was
+// chosen (NS words).
 template <int NS>
 __device__ __forceinline__ void wave_topk_ns(const float* __restrict__ src, const float* __restrict__ bias,
                                              int E, int k, float* __restrict__ logits_out,
                                              int32_t* __restrict__ ids, float* __restrict__ w,
-                                             int32_t* ids_copy) {
+                                             int32_t* ids_copy, float* w_copy = nullptr,
+                                             uint64_t* taken = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
   float v[NS];
   bool ok[NS];
@@ -59,25 +62,86 @@ __device__ __forceinline__ void wave_topk_ns(const float* __restrict__ src, cons
       if (lane + kWave * i == bi) ok[i] = false;  // taken
     if (lane == j) my_val = m;
     if (lane == 0) {
-      ids[j] = bi;
+      if (ids) ids[j] = bi;
       if (ids_copy) ids_copy[j] = bi;
+    }
+  }
+  if (taken) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const uint64_t m = __ballot(lane + kWave * i < E && !ok[i]);
+      if (lane == 0) taken[i] = m;
     }
   }
   const float m0 = __shfl(my_val, 0, kWave);
   const float ex = lane < k ? expf(my_val - m0) : 0.0f;
   const float s = wave_sum_dpp(ex);
-  if (lane < k) w[lane] = ex / s;
+  if (lane < k) {
+    if (w) w[lane] = ex / s;
+    if (w_copy) w_copy[lane] = ex / s;
+  }
 }
 
 __device__ __forceinline__ void wave_topk(const float* __restrict__ src, const float* __restrict__ bias,
                                           int E, int k, float* __restrict__ logits_out,
                                           int32_t* __restrict__ ids, float* __restrict__ w,
-                                          int32_t* ids_copy) {
-  if (E <= 64) wave_topk_ns<1>(src, bias, E, k, logits_out, ids, w, ids_copy);
-  else if (E <= 128) wave_topk_ns<2>(src, bias, E, k, logits_out, ids, w, ids_copy);
-  else if (E <= 256) wave_topk_ns<4>(src, bias, E, k, logits_out, ids, w, ids_copy);
-  else if (E <= 512) wave_topk_ns<8>(src, bias, E, k, logits_out, ids, w, ids_copy);
-  else wave_topk_ns<16>(src, bias, E, k, logits_out, ids, w, ids_copy);
+                                          int32_t* ids_copy, float* w_copy = nullptr,
+                                          uint64_t* taken = nullptr) {
+  if (E <= 64) wave_topk_ns<1>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
+  else if (E <= 128) wave_topk_ns<2>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
+  else if (E <= 256) wave_topk_ns<4>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
+  else if (E <= 512) wave_topk_ns<8>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
+  else wave_topk_ns<16>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
+}
+
+// Stable grouping of the P = T*k <= 64 pairs of T tokens by one wavefront,
+// from each token's selection bitmasks (taken[t][i], NW = ceil(E / 64)
+// words, as wave_topk_ns writes them) and ids (ids[p] for pair p = t*k+j).
+// Counting set bits replaces sorting: the pairs before expert v in the
+// grouped order are the set bits below v over all tokens; a pair of token t
+// follows its expert's pairs from tokens t' < t.  Writes s_sorted [P],
+// s_pos [P] (place of each pair), s_offsets [E + 1] and s_active (count,
+// then the experts with pairs, ascending) in LDS.
+__device__ __forceinline__ void wave_group_masks(const uint64_t (*taken)[kMaxE / kWave], const int32_t* ids, int T,
+                                                 int k, int E, int* s_sorted, int* s_pos, int* s_offsets,
+                                                 int* s_active) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int NW = (E + kWave - 1) / kWave;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int base = 0, abase = 0;  // set bits of all tokens / of the union, in words below i
+  for (int i = 0; i < NW; ++i) {
+    int below = 0, word = 0;
+    uint64_t uni = 0;
+    for (int t = 0; t < T; ++t) {
+      const uint64_t m = taken[t][i];
+      below += __builtin_popcountll(m & lt);
+      word += __builtin_popcountll(m);
+      uni |= m;
+    }
+    const int v = lane + kWave * i;
+    if (v < E) s_offsets[v] = base + below;
+    if ((uni >> lane) & 1) s_active[1 + abase + __builtin_popcountll(uni & lt)] = v;
+    base += word;
+    abase += __builtin_popcountll(uni);
+  }
+  if (lane == 0) {
+    s_offsets[E] = base;
+    s_active[0] = abase;
+  }
+  const int P = T * k;
+  if (lane < P) {
+    const int e = ids[lane], t = lane / k;
+    const int wi = e / kWave, bit = e % kWave;
+    const uint64_t lo = (bit == 0) ? 0ull : (~0ull >> (kWave - bit));
+    int place = 0;
+    for (int tt = 0; tt < T; ++tt) {
+      for (int i = 0; i < wi; ++i) place += __builtin_popcountll(taken[tt][i]);
+      place += __builtin_popcountll(taken[tt][wi] & lo);
+      place += tt < t ? (int)((taken[tt][wi] >> bit) & 1) : 0;
+    }
+    s_sorted[place] = lane;
+    s_pos[lane] = place;
+  }
 }
 
 // Exclusive scan of n <= kMaxE ints in LDS `a` into LDS `out` by a block of

@@ -74,10 +74,18 @@ def forward(ctx: L.Ctx, buf: LayerBuffers, pool_base: int, slot_bytes: int, n_sl
             steps=("route", "permute", "ffn", "combine"), fused: bool = False) -> torch.Tensor:
     """One layer forward; returns ``buf.out`` (valid in stream order).
 
-    ``fused``: moe_route_permute, then moe_expert_ffn with the combine folded
-    in (two calls); otherwise the four entry points one after another.
+    ``fused``: True = moe_route_permute, then moe_expert_ffn with the
+    combine folded in (two calls); "layer" = moe_decode_layer (one call);
+    otherwise the four entry points one after another.
     """
     T, H, I, E, k = buf.T, buf.H, buf.I, buf.E, buf.k
+    if fused == "layer":
+        args = L.make_ffn_args(pool_base, slot_bytes, n_slots, buf.q, H, I, T, k, E, slot_table, x,
+                               buf.offsets, buf.sorted_pairs, buf.active, buf.y, buf.mode,
+                               ws=buf.ws, ws_bytes=buf.ws.numel(), x_dtype=buf.x_dtype,
+                               topk_w=buf.w, out=buf.out)
+        L.moe_decode_layer(ctx, args, router_w, bias, logits_in, buf.logits, buf.ids, buf.pair_pos, stream=stream)
+        return buf.out
     if fused and expert_mask is None:
         L.moe_route_permute(ctx, x, router_w, bias, logits_in, T, H, E, k, buf.logits, buf.ids, buf.w,
                             buf.offsets, buf.sorted_pairs, buf.pair_pos, buf.active, buf.route_ws,

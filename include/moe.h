@@ -211,6 +211,24 @@ typedef struct moe_ffn_args {
 int moe_expert_ffn_workspace_size(const moe_ffn_args* args, size_t* bytes);
 int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* args, void* stream);
 
+/* ---------------------------------------------------- decode layer, fused
+ * One decode layer: the results of moe_route_permute (router logits, top-k,
+ * grouping) followed by moe_expert_ffn with the combine (args.topk_w and
+ * args.out set), in fewer launches.  For T*k <= 64 the top-k and the
+ * grouping run inside the gate/up kernel, every workgroup selecting from the
+ * logits it needs anyway (three launches with computed logits, two with
+ * logits_in); larger batches run the two calls.  Arguments are those of the
+ * two calls: args.x (fp32, args.mode = MOE_MODE_DECODE, no expert_mask) is
+ * also the router input; router_w/bias/logits_in/logits_out/topk_ids as in
+ * moe_route; args.topk_w, args.expert_offsets, args.sorted_pairs,
+ * args.active and pair_pos receive the routing results (this call writes
+ * through those args pointers, which moe_expert_ffn only reads); args.out
+ * receives the layer output.  Errors as in the two calls. */
+int moe_decode_layer(moe_ctx* ctx, const moe_ffn_args* args,
+                     const float* router_w, const float* bias,
+                     const float* logits_in, float* logits_out,
+                     int32_t* topk_ids, int32_t* pair_pos, void* stream);
+
 /* --------------------------------------------------------------- combine
  * out[t][:] = sum over j ascending of topk_w[t][j] * y_pairs[t*k + j][:]
  * (device fp32; out [T][H]). */

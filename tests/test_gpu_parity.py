@@ -394,3 +394,50 @@ def test_expert_mask_skips_experts(ctx, prefill_layer, mode):
     assert (~keep).any() and keep.any()
     assert (y[~keep] == 7.0).all()
     np.testing.assert_array_equal(y[keep], full[keep])
+
+
+def _layer_outputs(ctx, rl, T, x, wr, b, lg, fused):
+    wl = rl.wl
+    buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV)
+    for name in ("logits", "w", "y", "out"):
+        getattr(buf, name).fill_(float("nan"))
+    for name in ("ids", "offsets", "sorted_pairs", "pair_pos", "active"):
+        getattr(buf, name).fill_(-7)
+    layer.forward(ctx, buf, rl.pool.base(), rl.pool.slot_bytes, rl.pool.n_slots, rl.slot_table, dev(x),
+                  router_w=None if wr is None else dev(wr), bias=None if b is None else dev(b),
+                  logits_in=None if lg is None else dev(lg), fused=fused)
+    torch.cuda.synchronize()
+    moe.moe_ctx_check(ctx)
+    return buf, {n: getattr(buf, n).cpu().numpy() for n in
+                 ("logits", "ids", "w", "offsets", "sorted_pairs", "pair_pos", "active", "y", "out")}
+
+
+@pytest.mark.parametrize("case", ["decode-1", "decode-4", "decode-16", "decode-given-2", "wide-1", "wide-64",
+                                  "tiny-4"])
+def test_decode_layer_equals_two_calls(ctx, decode_layer, wide_layer, case):
+    """moe_decode_layer (routing inside the gate/up kernel for T*k <= 64, else
+    the two calls) gives bit-identical routing results and outputs to
+    moe_route_permute + moe_expert_ffn, and matches the oracle."""
+    name, T = case.rsplit("-", 1)
+    T = int(T)
+    note(f"decode layer {case}")
+    rl = {"decode": decode_layer, "decode-given": decode_layer, "wide": wide_layer}.get(name)
+    if name == "tiny":
+        rl = ResidentLayer(gi.workload("tiny_q8_0"))
+    wl = rl.wl
+    x = gi.activations(wl, T)
+    wr, b, lg = gi.router_weight(wl, 0), gi.router_bias(wl), None
+    if name == "decode-given":
+        rng = np.random.default_rng(3)
+        wr, lg, b = None, rng.standard_normal((T, wl.E)).astype(np.float32), \
+            (rng.standard_normal(wl.E) * 0.5).astype(np.float32)
+    _, two = _layer_outputs(ctx, rl, T, x, wr, b, lg, True)
+    for rep in range(2):
+        buf, one = _layer_outputs(ctx, rl, T, x, wr, b, lg, "layer")
+        for key in two:
+            np.testing.assert_array_equal(one[key], two[key], err_msg=f"{key} (call {rep})")
+    if lg is None:
+        ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, router_w=wr, bias=b)
+    else:  # the library adds the bias to given logits (in fp32) before selecting
+        ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, logits=(lg + b).astype(np.float32))
+    _check_layer(buf, one["out"], ref, DECODE_TOL, T)
