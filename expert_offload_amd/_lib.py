@@ -34,7 +34,7 @@ EXPORTS = (
     "cache_slot_table_lookup", "cache_slot_table_device", "cache_slot_table_stats",
     "cache_slot_table_destroy", "prefetch_expert", "cache_mark_layer_done",
     "moe_check_bank_types", "moe_ctx_set_timing", "moe_ctx_kernel_time",
-    "moe_route_permute_workspace_size", "moe_route_permute", "moe_decode_layer",
+    "moe_route_permute_workspace_size", "moe_route_permute", "moe_decode_layer", "cache_decode_layer",
 )
 
 
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         "cache_slot_table_destroy": (i, [vp]),
         "prefetch_expert": (i, [vp, i, i, vp, vp, i32p]),
         "cache_mark_layer_done": (i, [vp, i, vp]),
+        "cache_decode_layer": (i, [vp, vp, i, vp, vp, vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                   vp, vp]),
         "moe_check_bank_types": (i, [i, i, ip, ip]),
         "moe_ctx_set_timing": (i, [vp, i]),
         "moe_route_permute_workspace_size": (i, [i, i, i, szp]),
@@ -374,3 +376,14 @@ def prefetch_expert(cache: Cache, layer: int, expert: int, copy_stream, compute_
 def cache_mark_layer_done(cache: Cache, layer: int, compute_stream=None) -> None:
     _check(lib().cache_mark_layer_done(cache.handle, layer, _stream(compute_stream)),
            "cache_mark_layer_done")
+
+
+def cache_decode_layer(cache: Cache, ctx: Ctx, layer: int, x, router_w, bias, logits_in, T: int, k: int,
+                       logits_out, topk_ids, topk_w, expert_offsets, sorted_pairs, pair_pos, active, y_pairs,
+                       ws, ws_bytes: int, out, copy_stream=None, compute_stream=None) -> None:
+    _check(lib().cache_decode_layer(cache.handle, ctx.handle, layer, _dev_ptr(x), _dev_ptr(router_w),
+                                    _dev_ptr(bias), _dev_ptr(logits_in), T, k, _dev_ptr(logits_out),
+                                    _dev_ptr(topk_ids), _dev_ptr(topk_w), _dev_ptr(expert_offsets),
+                                    _dev_ptr(sorted_pairs), _dev_ptr(pair_pos), _dev_ptr(active),
+                                    _dev_ptr(y_pairs), _dev_ptr(ws), ws_bytes, _dev_ptr(out),
+                                    _stream(copy_stream), _stream(compute_stream)), "cache_decode_layer")

@@ -41,6 +41,7 @@ __global__ void table_update_kernel(int32_t* table, TableUpdate u) {
 }
 
 constexpr int kEventRing = 256;
+constexpr int kCtlStagePairs = 1024;  // T*k of one cache_decode_layer call
 
 }  // namespace moe
 
@@ -69,6 +70,12 @@ struct moe_cache {
   int next_event = 0, next_copy_event = 0;
   uint64_t clock = 0, epoch = 0;
   int64_t hits = 0, misses = 0;
+  // staging of cache_decode_layer, allocated with the cache: the routed ids
+  // (pinned host), the hit / miss expert masks (pinned host and device)
+  int32_t* h_ids = nullptr;   // [kCtlStagePairs]
+  int32_t* h_mask = nullptr;  // [2][E]
+  int32_t* d_mask = nullptr;  // [2][E]
+  hipEvent_t ids_ready = nullptr;
 };
 
 static int pop_free(moe_cache* c) {
@@ -136,6 +143,14 @@ int cache_slot_table_create(int L, int E, int n_slots, int qtype, int H, int I, 
       return hip_error(e, "hipEventCreate");
     }
   }
+  if ((e = hipHostMalloc((void**)&c->h_ids, sizeof(int32_t) * kCtlStagePairs, hipHostMallocDefault)) != hipSuccess ||
+      (e = hipHostMalloc((void**)&c->h_mask, sizeof(int32_t) * 2 * E, hipHostMallocDefault)) != hipSuccess ||
+      (e = hipMalloc(&c->d_mask, sizeof(int32_t) * 2 * E)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&c->ids_ready, hipEventDisableTiming)) != hipSuccess) {
+    cache_slot_table_destroy(c);
+    return hip_error(e, "cache staging allocation");
+  }
+  std::fill(c->h_mask, c->h_mask + 2 * E, 0);
   *out = c;
   return MOE_OK;
 }
@@ -149,6 +164,10 @@ int cache_slot_table_destroy(moe_cache* c) {
     if (c->copy_events[i]) (void)hipEventDestroy(c->copy_events[i]);
   }
   if (c->d_table) (void)hipFree(c->d_table);
+  if (c->h_ids) (void)hipHostFree(c->h_ids);
+  if (c->h_mask) (void)hipHostFree(c->h_mask);
+  if (c->d_mask) (void)hipFree(c->d_mask);
+  if (c->ids_ready) (void)hipEventDestroy(c->ids_ready);
   delete c;
   return MOE_OK;
 }
@@ -295,6 +314,81 @@ int cache_mark_layer_done(moe_cache* c, int layer, void* compute_stream) {
   c->layer_slots.clear();
   ++c->epoch;  // the layer's keys are no longer protected
   return MOE_OK;
+}
+
+int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, const float* router_w,
+                       const float* bias, const float* logits_in, int T, int k, float* logits_out,
+                       int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                       int32_t* pair_pos, int32_t* active, float* y_pairs, void* ws, size_t ws_bytes, float* out,
+                       void* copy_stream, void* compute_stream) {
+  clear_error();
+  if (!c || !ctx) return set_error(MOE_ERR_INVALID_ARG, "cache_decode_layer: cache or ctx is NULL");
+  if (layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID_ARG, "cache_decode_layer: layer=%d", layer);
+  if (T < 0 || k < 1 || (long long)T * k > kCtlStagePairs)
+    return set_error(MOE_ERR_INVALID_ARG, "cache_decode_layer: T*k must be in [0, %d] (T=%d k=%d)", kCtlStagePairs,
+                     T, k);
+  if (T == 0) return MOE_OK;
+  if (!out) return set_error(MOE_ERR_INVALID_ARG, "cache_decode_layer: out is NULL");
+  const int E = c->E, P = T * k;
+  int rc = moe_route_permute(ctx, x, MOE_DTYPE_F32, router_w, bias, logits_in, T, c->H, E, k, logits_out, topk_ids,
+                             topk_w, expert_offsets, sorted_pairs, pair_pos, active, nullptr, 0, compute_stream);
+  if (rc) return rc;
+  hipStream_t cs = (hipStream_t)compute_stream;
+  hipError_t e = hipMemcpyAsync(c->h_ids, topk_ids, sizeof(int32_t) * P, hipMemcpyDeviceToHost, cs);
+  if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync(ids)");
+  if ((e = hipEventRecord(c->ids_ready, cs)) != hipSuccess) return hip_error(e, "hipEventRecord(ids)");
+  if ((e = hipEventSynchronize(c->ids_ready)) != hipSuccess) return hip_error(e, "hipEventSynchronize(ids)");
+  std::vector<int32_t> slots(P), miss(P);
+  int n_miss = 0;
+  if ((rc = cache_slot_table_lookup(c, layer, c->h_ids, P, slots.data(), miss.data(), &n_miss))) return rc;
+  // hit / miss masks; the previous call's upload has run (it precedes this
+  // call's routing on the same stream, which the host waited for)
+  std::fill(c->h_mask, c->h_mask + 2 * E, 0);
+  for (int i = 0; i < P; ++i) c->h_mask[c->h_ids[i]] = 1;
+  for (int i = 0; i < n_miss; ++i) {
+    c->h_mask[miss[i]] = 0;
+    c->h_mask[E + miss[i]] = 1;
+  }
+  bool any_hit = false;
+  for (int i = 0; i < P; ++i) any_hit |= c->h_mask[c->h_ids[i]] != 0;
+  moe_ffn_args a{};
+  a.pool_base = c->d_pool;
+  a.slot_bytes = c->slot_bytes;
+  a.n_slots = c->n_slots + 2;
+  a.qtype = c->qtype;
+  a.H = c->H;
+  a.I = c->I;
+  a.T = T;
+  a.k = k;
+  a.E = E;
+  a.slot_table = c->d_table + (size_t)layer * E;
+  a.x = x;
+  a.x_dtype = MOE_DTYPE_F32;
+  a.expert_offsets = expert_offsets;
+  a.sorted_pairs = sorted_pairs;
+  a.active = active;
+  a.y_pairs = y_pairs;
+  a.mode = MOE_MODE_DECODE;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  a.topk_w = topk_w;
+  if (n_miss == 0) {  // every expert resident: one call with the combine folded in
+    a.out = out;
+    if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
+    return cache_mark_layer_done(c, layer, compute_stream);
+  }
+  if ((e = hipMemcpyAsync(c->d_mask, c->h_mask, sizeof(int32_t) * 2 * E, hipMemcpyHostToDevice, cs)) != hipSuccess)
+    return hip_error(e, "hipMemcpyAsync(masks)");
+  if (any_hit) {  // the resident experts run while the misses are copied
+    a.expert_mask = c->d_mask;
+    if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
+  }
+  for (int i = 0; i < n_miss; ++i)
+    if ((rc = prefetch_expert(c, layer, miss[i], copy_stream, compute_stream, nullptr))) return rc;
+  a.expert_mask = c->d_mask + E;
+  if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
+  if ((rc = moe_combine(ctx, y_pairs, topk_w, T, k, c->H, out, compute_stream))) return rc;
+  return cache_mark_layer_done(c, layer, compute_stream);
 }
 
 }  // extern "C"

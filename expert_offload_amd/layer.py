@@ -142,9 +142,19 @@ class CachedLayers:
         self.ev_ids = torch.cuda.Event()
         self.misses_per_layer = []
 
-    def layer(self, l: int, x: torch.Tensor, logits: torch.Tensor, stream=None) -> torch.Tensor:
+    def layer(self, l: int, x: torch.Tensor, logits: torch.Tensor, stream=None, native: bool = True) -> torch.Tensor:
+        """Layer `l` with given router logits; `native` runs the whole
+        sequence in one library call (cache_decode_layer), otherwise step by
+        step from Python (same calls, same results)."""
         b = self.buf
         s = stream or torch.cuda.current_stream()
+        if native:
+            before = self.stats()[1]
+            L.cache_decode_layer(self.cache, self.ctx, l, x, None, None, logits, 1, self.k, b.logits, b.ids, b.w,
+                                 b.offsets, b.sorted_pairs, b.pair_pos, b.active, b.y, b.ws, b.ws.numel(), b.out,
+                                 self.copy_stream, s)
+            self.misses_per_layer.append(self.stats()[1] - before)
+            return b.out
         L.moe_route_permute(self.ctx, x, None, None, logits, 1, self.H, self.E, self.k, b.logits, b.ids, b.w,
                             b.offsets, b.sorted_pairs, b.pair_pos, b.active, None, 0, stream=s)
         self.ids_host.copy_(b.ids, non_blocking=True)

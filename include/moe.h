@@ -293,6 +293,27 @@ int prefetch_expert(moe_cache* c, int layer, int expert, void* copy_stream,
                     void* compute_stream, int32_t* slot_out);
 int cache_mark_layer_done(moe_cache* c, int layer, void* compute_stream);
 
+/* cache_decode_layer: one decode layer of `layer` through the cache, the
+ * sequence above in one host call: moe_route_permute on compute_stream (x
+ * fp32 [T][H] device; router_w/bias/logits_in/logits_out/topk_ids/topk_w/
+ * expert_offsets/sorted_pairs/pair_pos/active as there), the routed ids
+ * read back to pinned staging owned by the cache (the host waits for them:
+ * a layer's misses are known only once it has routed), the LRU lookup,
+ * then moe_expert_ffn on the resident experts while prefetch_expert copies
+ * the misses on copy_stream, moe_expert_ffn on the misses once they land,
+ * moe_combine into out (device fp32 [T][H]) and cache_mark_layer_done.
+ * With no miss the FFN and the combine are one call.  y_pairs and ws as in
+ * moe_expert_ffn.  T*k <= 1024.  The staging is allocated with the cache,
+ * so the call allocates nothing.  Errors as in the calls it makes. */
+int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x,
+                       const float* router_w, const float* bias,
+                       const float* logits_in, int T, int k,
+                       float* logits_out, int32_t* topk_ids, float* topk_w,
+                       int32_t* expert_offsets, int32_t* sorted_pairs,
+                       int32_t* pair_pos, int32_t* active, float* y_pairs,
+                       void* ws, size_t ws_bytes, float* out,
+                       void* copy_stream, void* compute_stream);
+
 /* ------------------------------------------------------- bank type check
  * One block type for every expert bank: the slot pool is one allocation
  * indexed with a single row stride, so mixed types would read every block

@@ -185,3 +185,25 @@ def test_cached_layer_full_size_sampled(ctx):
         note(f"   full-size cached step {st}: max rel err {err:.2e}")
         assert err <= 1e-3
     cl.close()
+
+
+def test_native_layer_equals_stepwise(ctx):
+    """cache_decode_layer (one call per layer) gives the outputs and the hit /
+    miss sequence of the same calls made one by one from Python."""
+    wl = SMALL
+    pool, _ = host_pool(wl)
+    trace = gi.cache_trace(wl)
+    a = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, 8, pool)
+    b = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, 8, pool)
+    for st in range(12):
+        x = dev(gi.activations(wl, 1, st))
+        lg = gi.cache_trace_logits(wl, trace, st)
+        for l in range(wl.layers):
+            oa = a.layer(l, x, dev(lg[l:l + 1]), native=True).cpu().numpy()
+            ob = b.layer(l, x, dev(lg[l:l + 1]), native=False).cpu().numpy()
+            np.testing.assert_array_equal(oa, ob, err_msg=f"step {st} layer {l}")
+    moe.moe_ctx_check(ctx)
+    assert a.misses_per_layer == b.misses_per_layer
+    assert a.stats() == b.stats()
+    a.close()
+    b.close()
