@@ -1,0 +1,222 @@
+// Building blocks of the decode dequant-GEMV kernels: raw block loads,
+// the offset-trick block dot product, the transposed butterfly that folds
+// per-lane row sums, activation staging, and the shape rules (rows per lane
+// within a register budget).
+//
+// GEMV layout.  A wavefront owns RW = (64 / LPR) * RPL weight rows: lanes
+// form 64/LPR groups of LPR lanes, each group covers RPL rows, and every
+// lane owns the same BPL column blocks of all its rows.  The lane issues
+// all of its rows' 16-byte quant loads before any arithmetic (enough bytes
+// in flight to cover HBM latency), reuses each activation block for RPL
+// rows, and the RPL partial sums are folded across the LPR lanes with a
+// transposed butterfly (RPL - 1 + log2(LPR / RPL) shuffles instead of
+// RPL * log2(LPR)).
+//
+// Block arithmetic.  With u the stored byte (Q8_0: q + 128 after flipping
+// the sign bit; Q4_0: the nibble q), sum_k w_k x_k = d * (sum_k u_k x_k -
+// OFF * sum_k x_k), OFF = 128 or 8; sum_k x_k is formed once per block and
+// token and shared by the lane's RPL rows.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+// --------------------------------------------------------------- helpers
+template <int QT>
+struct QTraits;
+template <>
+struct QTraits<MOE_QTYPE_Q8_0> {
+  static constexpr int kWords = 8;  // 32 bytes of codes
+  static constexpr float kOff = 128.0f;
+};
+template <>
+struct QTraits<MOE_QTYPE_Q4_0> {
+  static constexpr int kWords = 4;  // 16 bytes of nibbles
+  static constexpr float kOff = 8.0f;
+};
+
+template <int QT>
+__device__ __forceinline__ void load_block_raw(const uint8_t* row, int b, uint32_t (&w)[QTraits<QT>::kWords],
+                                               float& d) {
+  const uint8_t* q = block_quants<QT>(row, b);
+  const uint4 v0 = *reinterpret_cast<const uint4*>(q);
+  w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+  if constexpr (QT == MOE_QTYPE_Q8_0) {
+    const uint4 v1 = *reinterpret_cast<const uint4*>(q + 16);
+    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+  }
+  d = block_scale<QT>(row, b);
+}
+
+// sum_k u_k * x_k over one block, u the unsigned stored code.
+template <int QT>
+__device__ __forceinline__ float block_udot(const uint32_t (&w)[QTraits<QT>::kWords], const float (&xv)[32]) {
+  float s = 0.0f;
+  if constexpr (QT == MOE_QTYPE_Q8_0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = w[i] ^ 0x80808080u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = fmaf((float)((u >> (8 * j)) & 0xFFu), xv[4 * i + j], s);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s = fmaf((float)((lo >> (8 * j)) & 0xFFu), xv[4 * i + j], s);
+        s = fmaf((float)((hi >> (8 * j)) & 0xFFu), xv[16 + 4 * i + j], s);
+      }
+    }
+  }
+  return s;
+}
+
+__device__ __forceinline__ void load_f32x32(const float* p, float (&xv)[32]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(p + 4 * i);
+    xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ float sum32(const float (&xv)[32]) {
+  float a = 0.0f, b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) {
+    a += xv[i];
+    b += xv[i + 1];
+  }
+  return a + b;
+}
+
+// Transposed butterfly over aligned groups of LPR lanes: on entry lane l
+// holds partial sums v[0..N) of N rows; on exit v[0] of every lane holds the
+// full sum of row (l % LPR) / (LPR / N) of its group.
+template <int OFF, int N, int M>
+__device__ __forceinline__ void fold_rows(float (&v)[M], int lane) {
+  if constexpr (OFF >= 1) {
+    if constexpr (N > 1) {
+      const bool hi = (lane & OFF) != 0;
+#pragma unroll
+      for (int r = 0; r < N / 2; ++r) {
+        const float keep = hi ? v[r + N / 2] : v[r];
+        const float send = hi ? v[r] : v[r + N / 2];
+        v[r] = keep + __shfl_xor(send, OFF, kWave);
+      }
+      fold_rows<OFF / 2, N / 2, M>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], OFF, kWave);
+      fold_rows<OFF / 2, 1, M>(v, lane);
+    }
+  }
+}
+
+// Rows of one lane's GEMV: RPL rows x BPL blocks of raw codes and scales.
+template <int QT, int LPR, int BPL, int RPL>
+struct RowTile {
+  uint32_t w[RPL][BPL][QTraits<QT>::kWords];
+  float d[RPL][BPL];
+
+  __device__ __forceinline__ void load(const uint8_t* const (&rows)[RPL], int lg) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) load_block_raw<QT>(rows[r], lg + LPR * i, w[r][i], d[r][i]);
+  }
+
+  // acc[r] = sum over the lane's blocks of d * (u . x - OFF * sum x), with
+  // the lane's activation blocks already in xv.  Rows are finished one at a
+  // time in load order, so the wait before row r covers only the loads up to
+  // row r and row r's math overlaps the later rows' transfers.  Each row's
+  // codes pass through an empty asm right before use so the compiler widens
+  // them here, inside the token loop, instead of keeping RPL*BPL*32 widened
+  // floats live; four partial sums per row break the FMA dependency chain.
+  __device__ __forceinline__ void dot(const float (&xv)[BPL][32], float (&acc)[RPL]) {
+    float sx[BPL];
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) sx[i] = sum32(xv[i]) * QTraits<QT>::kOff;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      acc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+#pragma unroll
+        for (int q = 0; q < QTraits<QT>::kWords; ++q) asm volatile("" : "+v"(w[r][i][q]));
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (QT == MOE_QTYPE_Q8_0) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t u = w[r][i][q] ^ 0x80808080u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part[j] = fmaf((float)((u >> (8 * j)) & 0xFFu), xv[i][4 * q + j], part[j]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = w[r][i][q] & 0x0F0F0F0Fu, hi = (w[r][i][q] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              part[j] = fmaf((float)((lo >> (8 * j)) & 0xFFu), xv[i][4 * q + j], part[j]);
+              part[j] = fmaf((float)((hi >> (8 * j)) & 0xFFu), xv[i][16 + 4 * q + j], part[j]);
+            }
+          }
+        }
+        acc[r] = fmaf(d[r][i], (part[0] + part[1]) + (part[2] + part[3]) - sx[i], acc[r]);
+      }
+    }
+  }
+};
+
+// The lane's BPL activation blocks of one token row.
+template <int LPR, int BPL>
+__device__ __forceinline__ void load_act(const float* act, int lg, float (&xv)[BPL][32]) {
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) load_f32x32(act + (size_t)(lg + LPR * i) * kQK, xv[i]);
+}
+
+
+constexpr int kDownWaves = 8;
+constexpr int kDownLdsFloats = 2048;    // y tile kept in LDS for the combine when T*k*RW fits
+constexpr int kDownStageFloats = 1024;  // per-wave staging of one h row when I fits
+constexpr int kStageVec = kDownStageFloats / (4 * kWave);  // float4 per lane
+
+// One h row (I <= kDownStageFloats floats) in registers, on its way to LDS.
+struct HRowRegs {
+  float4 v[kStageVec];
+  // Lanes past the row end re-read its last 4 floats (in bounds) and skip
+  // the store, so every element is written unconditionally here.
+  __device__ __forceinline__ void load(const float* src, int I, int lane) {
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const int c = min((lane + kWave * i) * 4, I - 4);
+      v[i] = *reinterpret_cast<const float4*>(src + c);
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int I, int lane) const {
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const int c = (lane + kWave * i) * 4;
+      if (c < I) *reinterpret_cast<float4*>(dst + c) = v[i];
+    }
+  }
+};
+
+// ----------------------------------------------------------- shape rules
+template <int QT, int BPL>
+constexpr int rows_per_lane() {
+  constexpr int budget = 64 / (BPL * QTraits<QT>::kWords);  // <= 64 registers of raw codes
+  return budget >= 8 ? 8 : budget >= 4 ? 4 : budget >= 2 ? 2 : 1;
+}
+// Down tiles aim at 8 rows (H/8 workgroups): RPL = 8 / (64 / LPR) within
+// the register budget.
+template <int QT, int LPR, int BPL>
+constexpr int down_rows_per_lane() {
+  constexpr int want = 8 / (kWave / LPR) > 0 ? 8 / (kWave / LPR) : 1;
+  constexpr int budget = rows_per_lane<QT, BPL>();
+  return want < budget ? want : budget;
+}
+
+}  // namespace moe

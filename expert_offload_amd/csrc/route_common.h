@@ -8,42 +8,21 @@
 
 namespace moe {
 
-// One wavefront selects the top k of token t's E logits (src row, plus
-// bias when given); NS = ceil(E / 64) logits per lane, slot i of lane l
-// holding id l + 64 i.  Each round takes the wave-wide maximum of the values
+// One wavefront selects the top k of E values held NS = ceil(E / 64) per
+// lane (slot i of lane l holds id l + 64 i; ok[i] false past E; NaN already
+// replaced by -inf).  Each round takes the wave-wide maximum of the values
 // still free (a 32-bit max reduction), then the lowest id holding that value
 // (ballots over the slots): equal values go to the lower id.  Then w_j =
 // exp(l_j - l_max) / sum_j' exp(l_j' - l_max), which equals the softmax
-// probabilities renormalised over the kept experts.  NaN logits count as
-// -inf.  Writes ids/w when set (and the logits used, when logits_out is
-// set); ids and w also go to ids_copy / w_copy if set, and with `taken`
-// the selection as bitmasks: bit l of taken[i] set if expert l + 64 i was
-// chosen (NS words).
+// probabilities renormalised over the kept experts.  Writes ids/w when set,
+// also to ids_copy / w_copy if set, and with `taken` the selection as
+// bitmasks: bit l of taken[i] set if expert l + 64 i was chosen (NS words).
+// Chosen slots are cleared in ok.
 template <int NS>
-__device__ __forceinline__ void wave_topk_ns(const float* __restrict__ src, const float* __restrict__ bias,
-                                             int E, int k, float* __restrict__ logits_out,
-                                             int32_t* __restrict__ ids, float* __restrict__ w,
-                                             int32_t* ids_copy, float* w_copy = nullptr,
-                                             uint64_t* taken = nullptr) {
+__device__ __forceinline__ void wave_topk_select(float (&v)[NS], bool (&ok)[NS], int E, int k,
+                                                 int32_t* __restrict__ ids, float* __restrict__ w,
+                                                 int32_t* ids_copy, float* w_copy, uint64_t* taken) {
   const int lane = threadIdx.x & (kWave - 1);
-  float v[NS];
-  bool ok[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int e = lane + kWave * i;
-    ok[i] = e < E;
-    v[i] = ok[i] ? src[e] : -INFINITY;
-  }
-  if (bias) {
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      if (ok[i]) v[i] += bias[lane + kWave * i];
-  }
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    if (ok[i] && logits_out) logits_out[lane + kWave * i] = v[i];
-    if (v[i] != v[i]) v[i] = -INFINITY;
-  }
   float my_val = -INFINITY;
   for (int j = 0; j < k; ++j) {
     float m = -INFINITY;
@@ -80,6 +59,37 @@ __device__ __forceinline__ void wave_topk_ns(const float* __restrict__ src, cons
     if (w) w[lane] = ex / s;
     if (w_copy) w_copy[lane] = ex / s;
   }
+}
+
+// The top k of token t's E logits (src row, plus bias when given), by
+// wave_topk_select.  NaN logits count as -inf.  Writes the logits used to
+// logits_out when it is set.
+template <int NS>
+__device__ __forceinline__ void wave_topk_ns(const float* __restrict__ src, const float* __restrict__ bias,
+                                             int E, int k, float* __restrict__ logits_out,
+                                             int32_t* __restrict__ ids, float* __restrict__ w,
+                                             int32_t* ids_copy, float* w_copy = nullptr,
+                                             uint64_t* taken = nullptr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float v[NS];
+  bool ok[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int e = lane + kWave * i;
+    ok[i] = e < E;
+    v[i] = ok[i] ? src[e] : -INFINITY;
+  }
+  if (bias) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (ok[i]) v[i] += bias[lane + kWave * i];
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (ok[i] && logits_out) logits_out[lane + kWave * i] = v[i];
+    if (v[i] != v[i]) v[i] = -INFINITY;
+  }
+  wave_topk_select<NS>(v, ok, E, k, ids, w, ids_copy, w_copy, taken);
 }
 
 __device__ __forceinline__ void wave_topk(const float* __restrict__ src, const float* __restrict__ bias,

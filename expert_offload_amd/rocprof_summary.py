@@ -35,11 +35,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 # Sources each profiled kernel family is compiled from.
+_DECODE = ["csrc/decode_gemv.h", "csrc/decode_ctl.h", "csrc/route_common.h", "csrc/ffn.h",
+           "csrc/device_common.h", "csrc/moe_internal.h"]
 KERNEL_SOURCES = {
-    "ffn_gateup_decode": ["csrc/decode.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
-    "ffn_down_decode": ["csrc/decode.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
-    "prefill_gateup_kernel": ["csrc/prefill.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
-    "prefill_down_kernel": ["csrc/prefill.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
+    "ffn_gateup_decode": ["csrc/decode.hip"] + _DECODE,
+    "ffn_down_decode": ["csrc/decode.hip"] + _DECODE,
+    "prefill_gemm_kernel": ["csrc/prefill.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
 }
 # Calibration kernels, in order of preference: ROCm's device-to-device copy
 # blit, then an elementwise negate (reads and writes the same byte count).

@@ -441,3 +441,74 @@ def test_decode_layer_equals_two_calls(ctx, decode_layer, wide_layer, case):
     else:  # the library adds the bias to given logits (in fp32) before selecting
         ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, logits=(lg + b).astype(np.float32))
     _check_layer(buf, one["out"], ref, DECODE_TOL, T)
+
+
+def test_decode_layer_many_launches_and_graph(ctx, decode_layer):
+    """moe_decode_layer called many times in a row on one stream, then the
+    same calls captured in a HIP graph and replayed (with eager calls between
+    the replays), gives results bit-identical to the two-call path on the
+    same inputs every time: no state of one call leaks into the next."""
+    rl, wl = decode_layer, decode_layer.wl
+    note("decode layer: 6 inputs x 4 eager rounds, then 3 graph replays")
+    x0 = gi.activations(wl, 1)
+    xs = [np.roll(x0, 97 * i, axis=1).copy() for i in range(6)]
+    bias = gi.router_bias(wl)
+    wr, b = dev(gi.router_weight(wl, 0)), None if bias is None else dev(bias)
+    keys = ("logits", "ids", "w", "offsets", "sorted_pairs", "pair_pos", "active", "y", "out")
+
+    def run(buf, x, fused, stream=None):
+        layer.forward(ctx, buf, rl.pool.base(), rl.pool.slot_bytes, rl.pool.n_slots, rl.slot_table, x,
+                      router_w=wr, bias=b, fused=fused, stream=stream)
+
+    def new_buf():
+        return layer.LayerBuffers(1, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV)
+
+    def poison(buf):
+        for name in ("logits", "w", "y", "out"):
+            getattr(buf, name).fill_(float("nan"))
+        for name in ("ids", "offsets", "sorted_pairs", "pair_pos", "active"):
+            getattr(buf, name).fill_(-7)
+
+    xd = [dev(x) for x in xs]
+    refs = []
+    for x in xd:
+        rb = new_buf()
+        poison(rb)
+        run(rb, x, True)
+        torch.cuda.synchronize()
+        refs.append({n: getattr(rb, n).cpu().numpy() for n in keys})
+    assert len({tuple(r["ids"].reshape(-1)) for r in refs}) > 1  # the inputs route differently
+    bufs = [new_buf() for _ in xd]
+
+    def check(tag):
+        torch.cuda.synchronize()
+        moe.moe_ctx_check(ctx)
+        for i, (bb, ref) in enumerate(zip(bufs, refs)):
+            for n in keys:
+                np.testing.assert_array_equal(getattr(bb, n).cpu().numpy(), ref[n], err_msg=f"{tag} input {i} {n}")
+
+    for rnd in range(4):
+        for bb in bufs:
+            poison(bb)
+        for bb, x in zip(bufs, xd):
+            run(bb, x, "layer")
+        check(f"eager round {rnd}")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for bb, x in zip(bufs, xd):
+            run(bb, x, "layer")
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for bb, x in zip(bufs, xd):
+            run(bb, x, "layer")
+    extra = new_buf()
+    for rep in range(3):
+        for bb in bufs:
+            poison(bb)
+        torch.cuda.synchronize()
+        g.replay()
+        check(f"graph replay {rep}")
+        run(extra, xd[rep], "layer")  # eager launches between replays
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(extra.out.cpu().numpy(), refs[rep]["out"])
