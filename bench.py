@@ -213,7 +213,8 @@ def prefill_extra(ctx, steps=10, warmup=3):
         run()
     torch.cuda.synchronize()
     kt = {}
-    for name in ("topk", "permute", "ffn_gateup", "ffn_down", "combine"):
+    for name in ("topk", "permute", "permute_count", "permute_scan", "permute_scatter", "ffn_gateup", "ffn_down",
+                 "combine"):
         n, t = moe.moe_ctx_kernel_time(ctx, name)
         if n:
             kt[name] = t / n

@@ -4,16 +4,36 @@
 
 namespace moe {
 
-// out[t][h] = sum over j ascending of w[t][j] * y[t*k + j][h].
+// out[t][h] = sum over j ascending of w[t][j] * y[t*k + j][h].  VEC (H % 4
+// == 0, y and out 16-byte aligned): each thread takes four consecutive h of
+// one token with 16-byte loads; otherwise one h per thread.
+template <bool VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ w, int k, int H,
                                                       float* __restrict__ out) {
-  const int h = blockIdx.x * 256 + threadIdx.x;
   const int t = blockIdx.y;
-  if (h >= H) return;
-  float acc = 0.0f;
-  for (int j = 0; j < k; ++j) acc = fmaf(w[(size_t)t * k + j], y[((size_t)t * k + j) * H + h], acc);
-  out[(size_t)t * H + h] = acc;
+  const float* yt = y + (size_t)t * k * H;
+  const float* wt = w + (size_t)t * k;
+  if constexpr (VEC) {
+    const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (h >= H) return;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int j = 0; j < k; ++j) {
+      const float wj = wt[j];
+      const float4 v = *reinterpret_cast<const float4*>(yt + (size_t)j * H + h);
+      acc.x = fmaf(wj, v.x, acc.x);
+      acc.y = fmaf(wj, v.y, acc.y);
+      acc.z = fmaf(wj, v.z, acc.z);
+      acc.w = fmaf(wj, v.w, acc.w);
+    }
+    *reinterpret_cast<float4*>(out + (size_t)t * H + h) = acc;
+  } else {
+    const int h = blockIdx.x * 256 + threadIdx.x;
+    if (h >= H) return;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) acc = fmaf(wt[j], yt[(size_t)j * H + h], acc);
+    out[(size_t)t * H + h] = acc;
+  }
 }
 
 // One thread per block of 32 weights: exact d*q (or d*(q-8)) in fp32.
@@ -40,9 +60,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 }
 
 int launch_combine(moe_ctx* ctx, const float* y, const float* w, int T, int k, int H, float* out, hipStream_t s) {
-  dim3 grid((H + 255) / 256, T);
+  const bool vec = (H & 3) == 0 && aligned(y, 16) && aligned(out, 16);
+  const int per = vec ? 4 * 256 : 256;  // h per workgroup
+  dim3 grid((H + per - 1) / per, T);
   KernelTimer timer(ctx, "combine", s);
-  launch(combine_kernel, grid, 256, 0, s, y, w, k, H, out);
+  if (vec) launch(combine_kernel<true>, grid, 256, 0, s, y, w, k, H, out);
+  else launch(combine_kernel<false>, grid, 256, 0, s, y, w, k, H, out);
   return check_launch("combine_kernel");
 }
 

@@ -13,7 +13,8 @@
 namespace moe {
 
 int launch_permute(moe_ctx* ctx, const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,
-                   int32_t* pair_pos, int32_t* active, hipStream_t s);
+                   int32_t* pair_pos, int32_t* active, void* ws, size_t ws_bytes, hipStream_t s);
+size_t permute_ws_bytes(long long P, int E);
 
 // logits[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e]) for expert e = one
 // wavefront: the router row stays in registers across tokens.
@@ -214,8 +215,11 @@ extern "C" int moe_route(moe_ctx* ctx, const void* x, int x_dtype, const float* 
 extern "C" int moe_route_permute_workspace_size(int T, int k, int E, size_t* bytes) {
   clear_error();
   if (!bytes) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute_workspace_size: bytes is NULL");
-  (void)T; (void)k; (void)E;
-  *bytes = 0;
+  if (T < 0 || k < 1 || E < 1 || E > kMaxE)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute_workspace_size: need T >= 0, k >= 1, 1 <= E <= %d",
+                     kMaxE);
+  // the separate permute of large batches takes its chunk counts from ws
+  *bytes = (long long)T * k > kFusedMaxPairs ? permute_ws_bytes((long long)T * k, E) : 0;
   return MOE_OK;
 }
 
@@ -225,7 +229,6 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
                                  int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
                                  int32_t* active, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  (void)ws; (void)ws_bytes;
   if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: ctx is NULL");
   int rc = validate_route_args("moe_route_permute", x, x_dtype, router_w, logits_in, T, H, E, k, logits_out,
                           topk_ids, topk_w);
@@ -237,7 +240,8 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
   if ((long long)T * k > kFusedMaxPairs) {  // large batches: separate kernels
     rc = launch_route(ctx, x, x_dtype, router_w, bias, logits_in, T, H, E, k, logits_out, topk_ids, topk_w, s);
     if (rc) return rc;
-    return launch_permute(ctx, topk_ids, T * k, E, expert_offsets, sorted_pairs, pair_pos, active, s);
+    if (ws && !aligned(ws, 4)) return set_error(MOE_ERR_ALIGNMENT, "moe_route_permute: ws must be 4-byte aligned");
+    return launch_permute(ctx, topk_ids, T * k, E, expert_offsets, sorted_pairs, pair_pos, active, ws, ws_bytes, s);
   }
   const float* src = logits_in;
   const float* tk_bias = bias;

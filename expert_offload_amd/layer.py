@@ -67,6 +67,8 @@ class LayerBuffers:
         self.ws = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.route_ws = torch.zeros(max(L.moe_route_permute_workspace_size(T, k, E), 256),
                                     dtype=torch.uint8, device=device)
+        self.perm_ws = torch.zeros(max(L.moe_permute_workspace_size(T, k, E), 256), dtype=torch.uint8,
+                                   device=device)
 
 
 def forward(ctx: L.Ctx, buf: LayerBuffers, pool_base: int, slot_bytes: int, n_slots: int, slot_table, x,
@@ -101,7 +103,7 @@ def forward(ctx: L.Ctx, buf: LayerBuffers, pool_base: int, slot_bytes: int, n_sl
                     stream=stream, x_dtype=buf.x_dtype)
     if "permute" in steps:
         L.moe_permute(ctx, buf.ids, T, k, E, buf.offsets, buf.sorted_pairs, buf.pair_pos,
-                      buf.active, stream=stream)
+                      buf.active, buf.perm_ws, buf.perm_ws.numel(), stream=stream)
     if "ffn" in steps:
         args = L.make_ffn_args(pool_base, slot_bytes, n_slots, buf.q, H, I, T, k, E, slot_table, x,
                                buf.offsets, buf.sorted_pairs, buf.active, buf.y, buf.mode,

@@ -93,7 +93,8 @@ int moe_ctx_check(moe_ctx* ctx, void* stream);
  * kernel's execution on its stream (launches inside a stream capture are
  * not timed); enabling or disabling discards earlier records.  moe_ctx_kernel_time waits for the
  * recorded launches of `kernel` (names: "router_logits", "topk", "permute",
- * "ffn_gateup", "ffn_down", "combine", "dequant", "topk_permute") and
+ * "ffn_gateup", "ffn_down", "combine", "dequant", "topk_permute",
+ * "permute_count", "permute_scan", "permute_scatter") and
  * returns their number
  * and summed duration in milliseconds. */
 int moe_ctx_set_timing(moe_ctx* ctx, int enable);
@@ -155,13 +156,16 @@ int moe_route(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w,
  *   pair_pos       [P]  : inverse: sorted_pairs[pair_pos[p]] == p
  *   active         [E+1]: active[0] = number of experts with pairs, then
  *                         those expert ids ascending
- * ws: device workspace of moe_permute_workspace_size() bytes (may be NULL
- * when that size is 0). */
+ * ws: device workspace (4-byte aligned) of moe_permute_workspace_size()
+ * bytes, 0 up to P = 4096 pairs and 2 x chunks x E x 4 above (chunks of
+ * 512 pairs), used for the per-chunk expert counts and bases of a grouping
+ * spread over many workgroups.  A NULL or smaller workspace selects the single-
+ * workgroup grouping instead: same results, slower for large P. */
 int moe_permute_workspace_size(int T, int k, int E, size_t* bytes);
 /* moe_route_permute: moe_route followed by moe_permute with the top-k and
  * the grouping in one launch, for decode-sized batches (T*k <= 4096;
- * larger batches run the separate kernels).  Same arguments and results;
- * the workspace size is 0 (ws may be NULL). */
+ * larger batches run the separate kernels, with ws as for moe_permute).
+ * Same arguments and results. */
 int moe_route_permute_workspace_size(int T, int k, int E, size_t* bytes);
 int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype,
                       const float* router_w, const float* bias,

@@ -123,10 +123,14 @@ def test_router_computed(ctx, name, T):
 
 
 # ------------------------------------------------------------------ permute
+@pytest.mark.parametrize("with_ws", [False, True])
 @pytest.mark.parametrize("T,k,E", [(0, 2, 8), (1, 1, 1), (4, 2, 8), (16, 8, 128), (64, 10, 512),
-                                   (100, 7, 1024), (4096, 8, 128), (513, 3, 5)])
-def test_permute_exact(ctx, T, k, E):
-    note(f"permute T={T} k={k} E={E}")
+                                   (100, 7, 1024), (4096, 8, 128), (513, 3, 5), (600, 7, 1024),
+                                   (4113, 8, 128), (2049, 2, 2)])
+def test_permute_exact(ctx, T, k, E, with_ws):
+    """Exact grouping against the oracle; with the workspace, batches above
+    4096 pairs take the chunked multi-workgroup path (last chunk ragged)."""
+    note(f"permute T={T} k={k} E={E} ws={with_ws}")
     rng = np.random.default_rng(T + 7 * k + E)
     if T == 0:
         ids = np.zeros((0, k), dtype=np.int32)
@@ -141,8 +145,12 @@ def test_permute_exact(ctx, T, k, E):
     sp = torch.full((P,), -9, dtype=torch.int32, device=DEV)
     pos = torch.full((P,), -9, dtype=torch.int32, device=DEV)
     act = torch.full((E + 1,), -9, dtype=torch.int32, device=DEV)
-    moe.moe_permute(ctx, dev(ids) if T else sp, T, k, E, off, sp, pos, act)
+    nws = moe.moe_permute_workspace_size(T, k, E)
+    assert (nws > 0) == (T * k > 4096)
+    ws = torch.full((max(nws, 4) // 4,), -3, dtype=torch.int32, device=DEV) if with_ws else None
+    moe.moe_permute(ctx, dev(ids) if T else sp, T, k, E, off, sp, pos, act, ws, nws if with_ws else 0)
     torch.cuda.synchronize()
+    moe.moe_ctx_check(ctx)
     r_off, r_sp, r_pos, r_act = oracle.permute(ids, E)
     np.testing.assert_array_equal(off.cpu().numpy(), r_off)
     if T:

@@ -121,6 +121,10 @@ def test_bank_type_rule():
 
 def test_workspace_queries():
     assert moe.moe_permute_workspace_size(16, 8, 128) == 0
+    assert moe.moe_permute_workspace_size(512, 8, 128) == 0  # 4096 pairs: one workgroup
+    # 4097..4608 pairs: 9 chunks of 512, counts and bases for 128 experts
+    assert moe.moe_permute_workspace_size(4097, 1, 128) == 2 * 9 * 128 * 4
+    assert moe.moe_permute_workspace_size(4096, 8, 128) == 2 * 64 * 128 * 4
     args = L.moe_ffn_args(qtype=8, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, n_slots=128,
                           slot_bytes=moe.moe_slot_bytes(8, 2048, 768))
     assert moe.moe_expert_ffn_workspace_size(args) >= 16 * 8 * 768 * 4
