@@ -229,7 +229,7 @@ def moe_layer(x: np.ndarray, qtype: str, get_blocks, k: int, *,
 #    "From Static Allocation to Dynamic Scheduling": VRAM is a cache over the
 #    host-resident pool and only missing experts move over PCIe)
 # --------------------------------------------------------------------------
-def lru_simulate(trace: np.ndarray, capacity: int):
+def lru_simulate(trace: np.ndarray, capacity: int, resizes: Optional[Dict[Tuple[int, int], int]] = None):
     """Replay lookups in order; returns (hit bool [steps, L, n], evicted keys).
 
     For every step, every layer and every id of that (step, layer) in
@@ -237,14 +237,26 @@ def lru_simulate(trace: np.ndarray, capacity: int):
     becomes most recently used.  A missing key is inserted; when the cache
     is full the least recently used key is evicted first, never one looked
     up earlier in the same (step, layer).  The cache starts empty.
+
+    resizes {(step, layer): capacity}: the cache size changes at run time
+    (the video-review article, "Dynamic Cache Adjustment Experiments"),
+    just before that (step, layer)'s lookups; the most recently used keys
+    stay, up to the new capacity, and the others are evicted.
     """
     steps, L, n = trace.shape
     last_use: Dict[Tuple[int, int], int] = {}
     clock = 0
     hit = np.zeros(trace.shape, dtype=bool)
     evicted: List[Tuple[int, int, Tuple[int, int]]] = []
+    resizes = resizes or {}
     for s in range(steps):
         for l in range(L):
+            if (s, l) in resizes:
+                capacity = resizes[(s, l)]
+                while len(last_use) > capacity:
+                    victim = min(last_use, key=lambda kk: last_use[kk])
+                    del last_use[victim]
+                    evicted.append((s, l, victim))
             current = set()
             for j in range(n):
                 key = (l, int(trace[s, l, j]))

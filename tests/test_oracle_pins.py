@@ -340,6 +340,43 @@ def test_lru_matches_ordered_dict_simulation():
         np.testing.assert_array_equal(hit, _ordered_dict_lru(trace, cap))
 
 
+def test_lru_resize_hand_trace():
+    # capacity 3, one layer, two lookups per step; shrink to 2 before step 2,
+    # grow to 3 before step 3 (worked out by hand)
+    trace = np.array([[[0, 1]], [[2, 3]], [[1, 3]], [[2, 1]]], dtype=np.int32)
+    hit, ev = oracle.lru_simulate(trace, 3, resizes={(2, 0): 2, (3, 0): 3})
+    # step 1: 3 evicts 0 (LRU).  Resize: {1, 2, 3} keeps the two most recent,
+    # 2 and 3.  Step 2: 1 evicts 2 (3 was used later), 3 hits.  Step 3: room
+    # for 2 again, 1 hits.
+    assert hit.reshape(-1).tolist() == [False, False, False, False, False, True, False, True]
+    assert ev == [(1, 0, (0, 0)), (2, 0, (0, 1)), (2, 0, (0, 2))]
+
+
+def test_lru_resize_invariants():
+    wl = gi.workload(5)
+    trace = gi.cache_trace(wl, steps=48)
+    base, _ = oracle.lru_simulate(trace, 100)
+    # resizing to the current capacity changes nothing
+    same, _ = oracle.lru_simulate(trace, 100, resizes={(10, 3): 100, (30, 0): 100})
+    np.testing.assert_array_equal(same, base)
+    # growing evicts nothing at the resize, and afterwards only misses of
+    # keys never seen, or seen but evicted before the resize, can occur
+    grown, ev = oracle.lru_simulate(trace, 40, resizes={(20, 0): 2048})
+    assert all(s < 20 for s, _l, _k in ev)
+    seen = set()
+    for st in range(trace.shape[0]):
+        for l in range(trace.shape[1]):
+            for j in range(trace.shape[2]):
+                key = (l, int(trace[st, l, j]))
+                if st >= 20 and key in seen and key not in {e[2] for e in ev}:
+                    assert grown[st, l, j]
+                seen.add(key)
+    # shrinking keeps the most recently used keys: after a shrink to the
+    # lookups of one step, the next step's repeats still hit
+    small, _ = oracle.lru_simulate(trace, 400, resizes={(24, 0): trace.shape[1] * trace.shape[2]})
+    np.testing.assert_array_equal(small[:24], oracle.lru_simulate(trace[:24], 400)[0])
+
+
 def test_lru_protects_current_layer_keys():
     trace = np.array([[[0, 1, 2]], [[3, 4, 5]]], dtype=np.int32)
     hit, ev = oracle.lru_simulate(trace, 3)
