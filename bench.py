@@ -18,7 +18,9 @@ Also reported on the same line:
   cache         expert-cache decode: 8 layers (hidden 4096, 256 experts,
                 top-8, intermediate 2048, Q4_0) served from a pinned host
                 pool through a VRAM cache of 40% of the experts, 2048
-                single-token steps of a trace with temporal locality
+                single-token steps of a trace with temporal locality; then
+                the same trace at cache fractions 0.1 .. 0.58, and a run
+                resized from 58% to 40% at run time halfway
 Progress goes to stderr; the JSON line is the only stdout output.
 """
 from __future__ import annotations
@@ -56,6 +58,8 @@ def parse_args():
                    help="first run a device copy and an elementwise negate of MIB MiB each, the known-size "
                         "kernels that scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
     p.add_argument("--cache-steps", type=int, default=None, help="steps of the expert-cache trace (default 2048)")
+    p.add_argument("--sweep-steps", type=int, default=1024,
+                   help="steps of each cache-fraction sweep point and of the run-time resize run")
     p.add_argument("--calls", choices=("layer", "two", "four"), default="layer",
                    help="per layer: moe_decode_layer (one call), moe_route_permute + moe_expert_ffn with the "
                         "combine (two), or moe_route, moe_permute, moe_expert_ffn, moe_combine (four)")
@@ -233,11 +237,19 @@ def prefill_extra(ctx, steps=10, warmup=3):
 
 
 # ---------------------------------------------------------------- expert cache
-def cache_extra(ctx, steps=None, distinct=64, warm_from=256):
+SWEEP_FRACTIONS = (0.1, 0.2, 0.3, 0.4, 0.5, 0.58)
+
+
+def cache_extra(ctx, steps=None, distinct=64, warm_from=256, sweep_steps=1024, resize_from=0.58):
     """Expert-cache decode: 8 layers (hidden 4096, 256 experts, top-8,
     intermediate 2048, Q4_0), the whole pool in pinned host memory, a VRAM
     cache of 40% of each layer's experts (816 slots), single-token steps
     following a trace with temporal locality, from an empty cache.
+
+    Then, on the same trace: `sweep_steps` steps at each cache fraction of
+    SWEEP_FRACTIONS, and one run that starts at `resize_from` and resizes the
+    cache to the main run's fraction at run time halfway (a new, smaller
+    pool; the kept experts move on device).
 
     The pinned pool holds `distinct` generated experts repeated over the
     2048 (layer, expert) keys: the bytes moved and read are those of the
@@ -267,29 +279,41 @@ def cache_extra(ctx, steps=None, distinct=64, warm_from=256):
         view[key * sb:(key + 1) * sb] = base[key % distinct]
     del base
     log("cache: pool filled; building the trace")
-    trace = gi.cache_trace(wl, steps)
-    logits = torch.from_numpy(np.stack([gi.cache_trace_logits(wl, trace, s) for s in range(steps)])).cuda()
-    xs = torch.from_numpy(np.stack([gi.activations(wl, 1, s)[0] for s in range(steps)])).cuda()
+    n_trace = max(steps, sweep_steps)
+    trace = gi.cache_trace(wl, n_trace)
+    logits = torch.from_numpy(np.stack([gi.cache_trace_logits(wl, trace, s) for s in range(n_trace)])).cuda()
+    xs = torch.from_numpy(np.stack([gi.activations(wl, 1, s)[0] for s in range(n_trace)])).cuda()
+
+    def run(cl, s0, s1, tag):
+        """Steps [s0, s1); wall-clock stamp after each step's host calls."""
+        torch.cuda.synchronize()
+        stamps = [time.perf_counter()]
+        for s in range(s0, s1):
+            x = xs[s:s + 1]
+            for l in range(wl.layers):
+                cl.layer(l, x, logits[s, l:l + 1])
+            stamps.append(time.perf_counter())
+            if (s + 1 - s0) % 512 == 0:
+                log(f"cache {tag}: step {s + 1 - s0}/{s1 - s0}")
+        torch.cuda.synchronize()
+        stamps[-1] = time.perf_counter()
+        moe.moe_ctx_check(ctx)
+        return stamps
+
+    def phase(cl, stamps, s0, s1, w0):
+        """tokens/s and hit rate over steps [w0, s1) of a run that began at s0."""
+        mpl = np.array(cl.misses_per_layer[(w0 - s0) * wl.layers:(s1 - s0) * wl.layers])
+        return {"steps": [w0, s1], "tokens_per_s": (s1 - w0) / (stamps[s1 - s0] - stamps[w0 - s0]),
+                "hit_rate": 1.0 - float(mpl.sum()) / ((s1 - w0) * wl.layers * wl.k)}
+
+    def slots_of(f):
+        return int(f * wl.E) * wl.layers
+
     cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, n_slots, pool)
-    torch.cuda.synchronize()
-    stamps = [time.perf_counter()]
-    for s in range(steps):
-        x = xs[s:s + 1]
-        for l in range(wl.layers):
-            cl.layer(l, x, logits[s, l:l + 1])
-        stamps.append(time.perf_counter())
-        if (s + 1) % 512 == 0:
-            log(f"cache: step {s + 1}/{steps}")
-    torch.cuda.synchronize()
-    stamps[-1] = time.perf_counter()
-    moe.moe_ctx_check(ctx)
+    stamps = run(cl, 0, steps, "main")
     wall = stamps[-1] - stamps[0]
     hits, misses = cl.stats()
-    mpl = np.array(cl.misses_per_layer).reshape(steps, wl.layers)
-    warm = slice(min(warm_from, steps - 1), steps)
-    warm_wall = stamps[-1] - stamps[warm.start]
-    warm_miss = int(mpl[warm].sum())
-    warm_pairs = (steps - warm.start) * wl.layers * wl.k
+    warm = phase(cl, stamps, 0, steps, min(warm_from, steps - 1))
     # PCIe ceiling: back-to-back expert copies from the pinned pool
     cs = torch.cuda.Stream()
     d = cl.d_pool
@@ -304,17 +328,57 @@ def cache_extra(ctx, steps=None, distinct=64, warm_from=256):
     torch.cuda.synchronize()
     ceiling = n_cp * sb / (e0.elapsed_time(e1) * 1e-3) / 1e9
     cl.close()
+    del cl, d
+    torch.cuda.empty_cache()
     res = {
         "workload": wl.name, "layers": wl.layers, "steps": steps, "cache_slots": n_slots,
         "cache_fraction": wl.cache_fraction, "expert_bytes": sb, "host_pool_bytes": keys * sb,
         "tokens_per_s": steps / wall, "ms_per_token": wall * 1e3 / steps,
         "hit_rate": hits / (hits + misses),
-        "warm": {"from_step": warm.start, "tokens_per_s": (steps - warm.start) / warm_wall,
-                 "hit_rate": 1.0 - warm_miss / warm_pairs},
+        "warm": {"from_step": warm["steps"][0], "tokens_per_s": warm["tokens_per_s"], "hit_rate": warm["hit_rate"]},
         "h2d_gbs": misses * sb / wall / 1e9,
         "h2d_copy_ceiling_gbs": ceiling,
         "pool_values": f"{distinct} generated experts repeated over the {keys} keys",
     }
+    # cache-fraction sweep, each from an empty cache over the first sweep_steps steps
+    sweep = []
+    w0 = min(warm_from, sweep_steps - 1)
+    for f in SWEEP_FRACTIONS:
+        cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, slots_of(f), pool)
+        st = run(cl, 0, sweep_steps, f"{f:.2f}")
+        ph = phase(cl, st, 0, sweep_steps, w0)
+        late = phase(cl, st, 0, sweep_steps, sweep_steps // 2)
+        sweep.append({"cache_fraction": f, "cache_slots": slots_of(f), "tokens_per_s": ph["tokens_per_s"],
+                      "hit_rate": ph["hit_rate"], "from_step": w0, "second_half": late})
+        log(f"cache sweep {f:.2f}: {ph['tokens_per_s']:.1f} tok/s at hit rate {ph['hit_rate']:.3f}")
+        cl.close()
+        del cl
+        torch.cuda.empty_cache()
+    res["sweep"] = {"steps": sweep_steps, "points": sweep}
+    # run-time resize from resize_from to the main fraction, halfway through
+    half = sweep_steps // 2
+    cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, slots_of(resize_from), pool)
+    st1 = run(cl, 0, half, "before resize")
+    before = phase(cl, st1, 0, half, min(w0, half - 1))
+    t0 = time.perf_counter()
+    cl.resize(slots_of(wl.cache_fraction))
+    torch.cuda.synchronize()
+    resize_ms = (time.perf_counter() - t0) * 1e3
+    cl.misses_per_layer = []
+    st2 = run(cl, half, sweep_steps, "after resize")
+    after = phase(cl, st2, half, sweep_steps, half)
+    cl.close()
+    del cl
+    torch.cuda.empty_cache()
+    res["resize"] = {"from_fraction": resize_from, "to_fraction": wl.cache_fraction,
+                     "from_slots": slots_of(resize_from), "to_slots": slots_of(wl.cache_fraction),
+                     "at_step": half, "resize_ms": resize_ms, "before": before, "after": after,
+                     "after_vs_before": after["tokens_per_s"] / before["tokens_per_s"]}
+    fixed = [p["second_half"] for p in sweep if p["cache_fraction"] == wl.cache_fraction]
+    if fixed:  # the same steps at a cache that was never resized
+        res["resize"]["after_vs_fixed"] = after["tokens_per_s"] / fixed[0]["tokens_per_s"]
+    log(f"cache resize {resize_from:.2f} -> {wl.cache_fraction:.2f}: {resize_ms:.1f} ms; "
+        f"{before['tokens_per_s']:.1f} -> {after['tokens_per_s']:.1f} tok/s")
     del pool
     return res
 
@@ -436,7 +500,7 @@ def main():
             result["prefill"] = {"error": repr(e)}
         if not args.no_cache:
             try:
-                result["cache"] = cache_extra(ctx, steps=args.cache_steps)
+                result["cache"] = cache_extra(ctx, steps=args.cache_steps, sweep_steps=args.sweep_steps)
                 c = result["cache"]
                 log(f"cache: {c['tokens_per_s']:.1f} tok/s, hit rate {c['hit_rate']:.3f}, warm "
                     f"{c['warm']['tokens_per_s']:.1f} tok/s at {c['warm']['hit_rate']:.3f}, "

@@ -32,7 +32,7 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
     "moe_expert_ffn", "moe_combine", "moe_dequantize", "cache_slot_table_create",
     "cache_slot_table_lookup", "cache_slot_table_device", "cache_slot_table_stats",
-    "cache_slot_table_destroy", "prefetch_expert", "cache_mark_layer_done",
+    "cache_slot_table_destroy", "prefetch_expert", "cache_mark_layer_done", "cache_slot_table_resize",
     "moe_check_bank_types", "moe_ctx_set_timing", "moe_ctx_kernel_time",
     "moe_route_permute_workspace_size", "moe_route_permute", "moe_decode_layer", "cache_decode_layer",
 )
@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
         "cache_slot_table_device": (vp, [vp]),
         "cache_slot_table_stats": (i, [vp, i64p, i64p]),
         "cache_slot_table_destroy": (i, [vp]),
+        "cache_slot_table_resize": (i, [vp, i, vp, vp]),
         "prefetch_expert": (i, [vp, i, i, vp, vp, i32p]),
         "cache_mark_layer_done": (i, [vp, i, vp]),
         "cache_decode_layer": (i, [vp, vp, i, vp, vp, vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
@@ -371,6 +372,12 @@ def prefetch_expert(cache: Cache, layer: int, expert: int, copy_stream, compute_
     _check(lib().prefetch_expert(cache.handle, layer, expert, _stream(copy_stream),
                                  _stream(compute_stream), ctypes.byref(s)), "prefetch_expert")
     return s.value
+
+
+def cache_slot_table_resize(cache: Cache, n_slots: int, d_pool=None, stream=None) -> None:
+    """New capacity n_slots; d_pool None resizes in place."""
+    _check(lib().cache_slot_table_resize(cache.handle, n_slots, None if d_pool is None else _dev_ptr(d_pool),
+                                         _stream(stream)), "cache_slot_table_resize")
 
 
 def cache_mark_layer_done(cache: Cache, layer: int, compute_stream=None) -> None:

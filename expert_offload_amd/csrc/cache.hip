@@ -40,6 +40,22 @@ __global__ void table_update_kernel(int32_t* table, TableUpdate u) {
   if (i < u.n) table[u.idx[i]] = u.val[i];
 }
 
+// Moves whole slots of the device pool: moves[m] = (from, to), slot indices
+// into src and dst.  blockIdx.y strides over the moves, blockIdx.x and the
+// threads over the 16-byte words of a slot.  No slot is both a source and a
+// destination, so src and dst may be one pool.
+__global__ void slot_move_kernel(const uint4* src, uint4* dst, const int2* moves, int n_moves,
+                                 long long words_per_slot) {
+  for (int m = blockIdx.y; m < n_moves; m += gridDim.y) {
+    const int2 mv = moves[m];
+    const uint4* from = src + (long long)mv.x * words_per_slot;
+    uint4* to = dst + (long long)mv.y * words_per_slot;
+    for (long long w = (long long)blockIdx.x * blockDim.x + threadIdx.x; w < words_per_slot;
+         w += (long long)gridDim.x * blockDim.x)
+      to[w] = from[w];
+  }
+}
+
 constexpr int kEventRing = 256;
 constexpr int kCtlStagePairs = 1024;  // T*k of one cache_decode_layer call
 
@@ -313,6 +329,90 @@ int cache_mark_layer_done(moe_cache* c, int layer, void* compute_stream) {
   for (int s : c->layer_slots) c->slot_event[s] = ev;
   c->layer_slots.clear();
   ++c->epoch;  // the layer's keys are no longer protected
+  return MOE_OK;
+}
+
+int cache_slot_table_resize(moe_cache* c, int n_slots, void* d_pool, void* stream) {
+  clear_error();
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_resize: cache is NULL");
+  if (n_slots < 1) return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_resize: n_slots=%d", n_slots);
+  if (!c->layer_slots.empty() || !c->pending.empty())
+    return set_error(MOE_ERR_INVALID_ARG,
+                     "cache_slot_table_resize: a lookup is in progress (copies not issued or layer not marked done)");
+  uint8_t* pool = d_pool ? (uint8_t*)d_pool : c->d_pool;
+  if (!aligned(pool, 16)) return set_error(MOE_ERR_ALIGNMENT, "cache_slot_table_resize: d_pool not 16-byte aligned");
+  const bool same = pool == c->d_pool;
+  const int count = n_slots + 2;
+  // the n_slots most recently used keys stay; the rest are evicted
+  std::vector<int> mru;
+  for (auto it = c->lru.rbegin(); it != c->lru.rend(); ++it) mru.push_back(it->second);
+  const int kept = std::min((int)mru.size(), n_slots);
+  std::vector<int32_t> table = c->table;
+  for (int i = kept; i < (int)mru.size(); ++i) table[mru[i]] = -1;
+  std::vector<int> slot_key(count, -1);
+  std::vector<int2> moves;
+  std::vector<int> order(mru.begin(), mru.begin() + kept);
+  std::sort(order.begin(), order.end(), [&](int a, int b) { return table[a] < table[b]; });
+  if (same) {  // keys already below the new slot count stay where they are
+    std::vector<int> movers;
+    for (int key : order) {
+      if (table[key] < count) slot_key[table[key]] = key;
+      else movers.push_back(key);
+    }
+    int next = 0;
+    for (int key : movers) {
+      while (slot_key[next] >= 0) ++next;
+      moves.push_back(make_int2(table[key], next));
+      table[key] = next;
+      slot_key[next] = key;
+    }
+  } else {  // every kept key is copied, packed from slot 0 in its old slot order
+    for (int i = 0; i < kept; ++i) {
+      moves.push_back(make_int2(table[order[i]], i));
+      table[order[i]] = i;
+      slot_key[i] = order[i];
+    }
+  }
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_error(e, "hipSetDevice");
+  // every earlier reader of the pool and every expert copy, on any stream
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_error(e, "hipDeviceSynchronize");
+  hipStream_t st = (hipStream_t)stream;
+  int2* d_moves = nullptr;
+  if (!moves.empty()) {
+    if ((e = hipMalloc(&d_moves, sizeof(int2) * moves.size())) != hipSuccess) return hip_error(e, "hipMalloc(moves)");
+    e = hipMemcpyAsync(d_moves, moves.data(), sizeof(int2) * moves.size(), hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) {
+      (void)hipFree(d_moves);
+      return hip_error(e, "hipMemcpyAsync(moves)");
+    }
+    const long long words = (long long)(c->slot_bytes / 16);
+    const int bx = (int)std::min<long long>((words + 1023) / 1024, 1024);
+    const int by = (int)std::min<size_t>(moves.size(), 4096);
+    launch(slot_move_kernel, dim3(bx, by), 256, 0, st, (const uint4*)c->d_pool, (uint4*)pool,
+           (const int2*)d_moves, (int)moves.size(), words);
+    int rc = check_launch("slot_move_kernel");
+    if (rc) {
+      (void)hipStreamSynchronize(st);
+      (void)hipFree(d_moves);
+      return rc;
+    }
+  }
+  e = hipMemcpyAsync(c->d_table, table.data(), sizeof(int32_t) * table.size(), hipMemcpyHostToDevice, st);
+  const hipError_t es = hipStreamSynchronize(st);
+  if (d_moves) (void)hipFree(d_moves);
+  if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync(slot table)");
+  if (es != hipSuccess) return hip_error(es, "hipStreamSynchronize");
+  for (int i = kept; i < (int)mru.size(); ++i) c->lru.erase({c->stamp[mru[i]], mru[i]});
+  c->table.swap(table);
+  c->slot_key.swap(slot_key);
+  c->slot_event.assign(count, -1);
+  c->free_fifo.clear();
+  c->free_head = 0;
+  for (int s = 0; s < count; ++s)
+    if (c->slot_key[s] < 0) c->free_fifo.push_back(s);
+  c->n_slots = n_slots;
+  c->d_pool = pool;
   return MOE_OK;
 }
 

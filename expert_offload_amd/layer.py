@@ -188,6 +188,21 @@ class CachedLayers:
         L.cache_mark_layer_done(self.cache, l, s)
         return b.out
 
+    def resize(self, n_slots: int, in_place: bool = False, stream=None) -> None:
+        """Change the cache capacity at run time.  By default the experts
+        kept move into a new pool of exactly (n_slots + 2) slots and the old
+        one is released; in_place keeps the current allocation (shrinking
+        only)."""
+        if in_place:
+            if n_slots > self.n_slots:
+                raise ValueError("an in-place resize can only shrink the cache")
+            L.cache_slot_table_resize(self.cache, n_slots, None, stream)
+        else:
+            pool = torch.empty((n_slots + 2) * self.slot_bytes, dtype=torch.uint8, device=self.d_pool.device)
+            L.cache_slot_table_resize(self.cache, n_slots, pool, stream)
+            self.d_pool = pool
+        self.n_slots = n_slots
+
     def stats(self):
         return L.cache_slot_table_stats(self.cache)
 

@@ -284,7 +284,24 @@ int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int rows,
  *
  * cache_mark_layer_done: records on compute_stream the point after which the
  * slots of the last lookup are no longer read (enqueue it after the layer's
- * FFN), and ends that lookup. */
+ * FFN), and ends that lookup.
+ *
+ * cache_slot_table_resize: changes the capacity to n_slots while the cache
+ * is in use, with no restart (the video-review article, "Dynamic Cache
+ * Adjustment Experiments": the expert cache is resized at run time).  The
+ * n_slots most recently used keys stay resident, in recency order; the
+ * others are evicted.  d_pool is the device pool to use from now on,
+ * (n_slots + 2) * slot_bytes, caller-owned, 16-byte aligned; NULL or the
+ * current pool resizes in place (the allocation must then hold
+ * (n_slots + 2) slots: shrinking always fits).  Kept experts move on
+ * device (slot_move_kernel on `stream`): into a new pool all of them, in
+ * place only those whose slot is past the new end.  The call waits for the
+ * device (every earlier reader of the pool and every expert copy) before the
+ * moves and for `stream` after them, so on return the old pool is no longer
+ * used and may be freed.  It allocates a small temporary device buffer for
+ * the move list.  Between a lookup and its cache_mark_layer_done (or with
+ * copies not yet issued by prefetch_expert) -> MOE_ERR_INVALID_ARG; the
+ * cache is unchanged on any error.  Hit and miss counts carry over. */
 int cache_slot_table_create(int L, int E, int n_slots, int qtype, int H, int I,
                             void* d_pool, const void* h_pool, moe_cache** out);
 int cache_slot_table_lookup(moe_cache* c, int layer, const int32_t* ids,
@@ -296,6 +313,8 @@ int cache_slot_table_destroy(moe_cache* c);
 int prefetch_expert(moe_cache* c, int layer, int expert, void* copy_stream,
                     void* compute_stream, int32_t* slot_out);
 int cache_mark_layer_done(moe_cache* c, int layer, void* compute_stream);
+int cache_slot_table_resize(moe_cache* c, int n_slots, void* d_pool,
+                            void* stream);
 
 /* cache_decode_layer: one decode layer of `layer` through the cache, the
  * sequence above in one host call: moe_route_permute on compute_stream (x

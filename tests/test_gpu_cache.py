@@ -207,3 +207,127 @@ def test_native_layer_equals_stepwise(ctx):
     assert a.stats() == b.stats()
     a.close()
     b.close()
+
+
+def _oracle_resident(trace, hits, evicted):
+    """Keys resident at the end of an oracle run: misses insert, evictions
+    remove; within one (step, layer) the evictions come first (a key looked
+    up in a call is not evicted by it)."""
+    res = set()
+    ev = {}
+    for s, l, key in evicted:
+        ev.setdefault((s, l), []).append(key)
+    for s in range(trace.shape[0]):
+        for l in range(trace.shape[1]):
+            for key in ev.get((s, l), []):
+                res.discard(key)
+            for j in range(trace.shape[2]):
+                if not hits[s, l, j]:
+                    res.add((l, int(trace[s, l, j])))
+    return res
+
+
+def test_resize_matches_oracle(ctx):
+    """Shrink in place, grow into a new pool, shrink into a new pool, in the
+    middle of a trace: hits, misses and the resident set follow the oracle's
+    LRU with the same capacity schedule, and every resident slot holds its
+    expert's bytes after the moves."""
+    wl = SMALL
+    pool, _ = host_pool(wl)
+    trace = lookup_order(wl, gi.cache_trace(wl))
+    q = L.QTYPE[wl.qtype]
+    sb = moe.moe_slot_bytes(q, wl.H, wl.I)
+    schedule = {(10, 0): (12, "in_place"), (20, 1): (20, "new"), (30, 2): (6, "new"), (35, 0): (6, "in_place")}
+    n_slots = 30
+    d_pool = torch.zeros((n_slots + 2) * sb, dtype=torch.uint8, device=DEV)
+    cache = moe.cache_slot_table_create(wl.layers, wl.E, n_slots, q, wl.H, wl.I, d_pool, pool)
+    copy_s = torch.cuda.Stream()
+    s = torch.cuda.current_stream()
+    hp = pool.numpy()
+    hits = np.zeros(trace.shape, dtype=bool)
+
+    def check_bytes(n):
+        t = _table_view(cache, wl).cpu().numpy()
+        res = t[t >= 0]
+        assert len(res) == len(set(res.tolist())) <= n and (res < n + 2).all()
+        dp = d_pool.cpu().numpy()
+        for key in np.flatnonzero(t >= 0):
+            np.testing.assert_array_equal(dp[t[key] * sb:(t[key] + 1) * sb], hp[key * sb:(key + 1) * sb])
+        return {(int(key) // wl.E, int(key) % wl.E) for key in np.flatnonzero(t >= 0)}
+
+    for st in range(trace.shape[0]):
+        for l in range(wl.layers):
+            if (st, l) in schedule:
+                n_slots, how = schedule[(st, l)]
+                if how == "new":
+                    new_pool = torch.full(((n_slots + 2) * sb,), 0xA5, dtype=torch.uint8, device=DEV)
+                    moe.cache_slot_table_resize(cache, n_slots, new_pool, s)
+                    d_pool = new_pool
+                else:
+                    moe.cache_slot_table_resize(cache, n_slots, None, s)
+                note(f"   resize at step {st} layer {l} -> {n_slots} slots ({how})")
+                check_bytes(n_slots)
+            slots, misses = moe.cache_slot_table_lookup(cache, l, trace[st, l])
+            assert (slots >= 0).all() and (slots < n_slots + 2).all()
+            hits[st, l] = ~np.isin(trace[st, l], misses)
+            for e in misses:
+                moe.prefetch_expert(cache, l, int(e), copy_s, s)
+            moe.cache_mark_layer_done(cache, l, s)
+    torch.cuda.synchronize()
+    resizes = {k: v[0] for k, v in schedule.items()}
+    want, evicted = oracle.lru_simulate(trace, 30, resizes=resizes)
+    np.testing.assert_array_equal(hits, want)
+    assert moe.cache_slot_table_stats(cache) == (int(want.sum()), int((~want).sum()))
+    assert check_bytes(n_slots) == _oracle_resident(trace, want, evicted)
+    cache.close()
+
+
+def test_resize_errors(ctx):
+    wl = SMALL
+    q = L.QTYPE[wl.qtype]
+    sb = moe.moe_slot_bytes(q, wl.H, wl.I)
+    pool = torch.zeros(wl.layers * wl.E * sb, dtype=torch.uint8, pin_memory=True)
+    d_pool = torch.zeros(8 * sb, dtype=torch.uint8, device=DEV)
+    cache = moe.cache_slot_table_create(wl.layers, wl.E, 6, q, wl.H, wl.I, d_pool, pool)
+    moe.cache_slot_table_lookup(cache, 0, [1, 2])
+    with pytest.raises(moe.MoeError) as ei:  # misses looked up, copies not issued
+        moe.cache_slot_table_resize(cache, 4)
+    assert ei.value.name == "MOE_ERR_INVALID_ARG"
+    for e in (1, 2):
+        moe.prefetch_expert(cache, 0, e, torch.cuda.Stream(), torch.cuda.current_stream())
+    with pytest.raises(moe.MoeError):  # layer not marked done
+        moe.cache_slot_table_resize(cache, 4)
+    moe.cache_mark_layer_done(cache, 0)
+    with pytest.raises(moe.MoeError):
+        moe.cache_slot_table_resize(cache, 0)
+    moe.cache_slot_table_resize(cache, 1)  # keeps expert 2, the most recent
+    slots, misses = moe.cache_slot_table_lookup(cache, 0, [2])
+    assert len(misses) == 0
+    moe.cache_mark_layer_done(cache, 0)
+    torch.cuda.synchronize()
+    cache.close()
+
+
+def test_cached_layers_resize_outputs(ctx):
+    """Layer outputs through the cache stay the oracle's across run-time
+    resizes (in place and into a new pool)."""
+    wl = SMALL
+    pool, blocks = host_pool(wl)
+    trace = gi.cache_trace(wl)
+    cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, 12, pool)
+    plan = {4: (5, True), 8: (14, False), 11: (4, False)}
+    worst = 0.0
+    for st in range(14):
+        if st in plan:
+            cl.resize(plan[st][0], in_place=plan[st][1])
+        x = gi.activations(wl, 1, st)
+        lg = gi.cache_trace_logits(wl, trace, st)
+        xd = dev(x)
+        for l in range(wl.layers):
+            out = cl.layer(l, xd, dev(lg[l:l + 1]), native=(st % 2 == 0)).cpu().numpy()
+            moe.moe_ctx_check(ctx)
+            ref = oracle.moe_layer(x, wl.qtype, lambda e: blocks[(l, e)], wl.k, logits=lg[l:l + 1])
+            worst = max(worst, max_rel_err(out, ref["out"]))
+    note(f"   cached layers with resizes: worst max rel err {worst:.2e}")
+    assert worst <= 1e-3
+    cl.close()
