@@ -287,10 +287,10 @@ int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int rows,
  * FFN), and ends that lookup.
  *
  * cache_slot_table_resize: changes the capacity to n_slots while the cache
- * is in use, with no restart (the video-review article, "Dynamic Cache
- * Adjustment Experiments": the expert cache is resized at run time).  The
- * n_slots most recently used keys stay resident, in recency order; the
- * others are evicted.  d_pool is the device pool to use from now on,
+ * is in use, with no restart ("FreeToken Inference Engine: 3x Speed Boost
+ * for MoE Models", "Dynamic Cache Adjustment Experiments": the expert cache
+ * is resized at run time).  The n_slots most recently used keys stay
+ * resident; the others are evicted.  d_pool is the device pool to use from now on,
  * (n_slots + 2) * slot_bytes, caller-owned, 16-byte aligned; NULL or the
  * current pool resizes in place (the allocation must then hold
  * (n_slots + 2) slots: shrinking always fits).  Kept experts move on

@@ -239,9 +239,10 @@ def lru_simulate(trace: np.ndarray, capacity: int, resizes: Optional[Dict[Tuple[
     up earlier in the same (step, layer).  The cache starts empty.
 
     resizes {(step, layer): capacity}: the cache size changes at run time
-    (the video-review article, "Dynamic Cache Adjustment Experiments"),
-    just before that (step, layer)'s lookups; the most recently used keys
-    stay, up to the new capacity, and the others are evicted.
+    ("FreeToken Inference Engine: 3x Speed Boost for MoE Models", section
+    "Dynamic Cache Adjustment Experiments"), just before that (step,
+    layer)'s lookups; the most recently used keys stay, up to the new
+    capacity, and the others are evicted.
     """
     steps, L, n = trace.shape
     last_use: Dict[Tuple[int, int], int] = {}
