@@ -15,6 +15,8 @@ Also reported on the same line:
   batches       the same stack at the other batch sizes
   prefill       4096-token grouped-GEMM layer (hidden 2048, 128 experts,
                 top-8, intermediate 768, Q4_0, bf16 activations)
+  prefill_stream the same layer over 8 layers whose experts stream from
+                pinned host memory through two device buffers
   cache         expert-cache decode: 8 layers (hidden 4096, 256 experts,
                 top-8, intermediate 2048, Q4_0) served from a pinned host
                 pool through a VRAM cache of 40% of the experts, 2048
@@ -233,6 +235,102 @@ def prefill_extra(ctx, steps=10, warmup=3):
         "kernel_ms": kt, "ffn_tflops": tflops, "ffn_frac_bf16_peak": tflops / BF16_PEAK_TFLOPS if tflops else None,
         "gateup_tflops": gu_tflops,
         "flops_per_layer": flops,
+    }
+
+
+# ---------------------------------------------------------------- prefill streaming
+def prefill_stream_extra(ctx, layers=8, reps=3):
+    """The 4096-token prefill layer (hidden 2048, 128 experts, top-8,
+    intermediate 768, Q4_0) over `layers` layers whose experts all live in
+    pinned host memory: each layer's 339.7 MB of experts crosses PCIe into
+    one of two device buffers while the previous layer computes.  Timed
+    beside it: the copies alone, the layers alone (experts resident), and
+    copy-then-compute with no overlap.
+
+    Every layer's host experts are the bytes of one generated layer; the
+    copy and FFN times do not depend on the values, while the routing
+    (given logits) differs per layer.  Parity of this path is covered by
+    the tests."""
+    import dataclasses
+    import numpy as np
+    import torch
+    import expert_offload_amd as moe
+    from expert_offload_amd import _lib as L
+    from expert_offload_amd import layer
+    from gen import inputs as gi
+
+    wl = dataclasses.replace(gi.workload("prefill_q4_0_h2048_e128"), layers=layers)
+    T = wl.batches[0]
+    q = L.QTYPE[wl.qtype]
+    sb = moe.moe_slot_bytes(q, wl.H, wl.I)
+    lb = wl.E * sb
+    pool = torch.empty(layers * lb, dtype=torch.uint8, pin_memory=True)
+    view = pool.numpy()
+    one = np.empty(lb, dtype=np.uint8)
+
+    def put(l, e, b):
+        one[e * sb:(e + 1) * sb] = layer.pack_expert(wl.qtype, wl.H, wl.I, *b)
+
+    gi.generate_blocks_parallel(wl, [(0, e) for e in range(wl.E)], put)
+    for l in range(layers):
+        view[l * lb:(l + 1) * lb] = one
+    xd = torch.from_numpy(gi.activations(wl, T).view(np.int16)).view(torch.bfloat16).cuda()
+    logits = [torch.from_numpy(gi.given_logits(wl, T, l)).cuda() for l in range(layers)]
+    sp = layer.StreamedPrefill(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, layers, T, pool)
+    s = torch.cuda.current_stream()
+
+    def timed(fn, stream=None):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def streamed():
+        for l in range(layers):
+            sp.layer(l, xd, logits[l])
+
+    def copies():
+        with torch.cuda.stream(sp.copy_stream):
+            for l in range(layers):
+                b = l % 2
+                sp.d_bufs[b * lb:(b + 1) * lb].copy_(pool[l * lb:(l + 1) * lb], non_blocking=True)
+
+    ident = torch.arange(wl.E, dtype=torch.int32, device="cuda")
+    rbuf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device="cuda", mode=L.MODE_PREFILL,
+                              x_dtype=L.DTYPE_BF16)
+
+    def computes(copy_first=False):
+        for l in range(layers):
+            if copy_first:  # on the compute stream: no overlap
+                sp.d_bufs[:lb].copy_(pool[l * lb:(l + 1) * lb], non_blocking=True)
+            layer.forward(ctx, rbuf, sp.d_bufs.data_ptr(), sb, wl.E, ident, xd, logits_in=logits[l], fused=True)
+
+    streamed()
+    computes()
+    t_stream = min(timed(streamed) for _ in range(reps))
+    t_copy = min(timed(copies, sp.copy_stream) for _ in range(reps))
+    t_compute = min(timed(computes) for _ in range(reps))
+    t_serial = min(timed(lambda: computes(True)) for _ in range(reps))
+    moe.moe_ctx_check(ctx)
+    loads, demand = sp.stats()
+    sp.close()
+    del sp, pool, rbuf
+    torch.cuda.empty_cache()
+    hidden = t_copy + t_compute - t_stream
+    return {
+        "workload": f"{wl.name} x {layers} layers streamed", "tokens": T, "layers": layers,
+        "layer_expert_bytes": lb, "host_pool_bytes": layers * lb,
+        "tokens_per_s": T * layers / (t_stream * 1e-3), "ms_per_layer": t_stream / layers,
+        "h2d_gbs": layers * lb / (t_stream * 1e-3) / 1e9,
+        "copy_only_ms_per_layer": t_copy / layers, "copy_only_gbs": layers * lb / (t_copy * 1e-3) / 1e9,
+        "compute_only_ms_per_layer": t_compute / layers, "serial_ms_per_layer": t_serial / layers,
+        "speedup_vs_serial": t_serial / t_stream,
+        "overlap_efficiency": hidden / min(t_copy, t_compute),
+        "copies": loads, "demand_loads": demand,
+        "pool_values": "one generated layer's experts repeated over the layers",
     }
 
 
@@ -498,6 +596,15 @@ def main():
                 f"{result['prefill']['ffn_tflops']:.1f} TFLOP/s")
         except Exception as e:  # reported, never silently dropped
             result["prefill"] = {"error": repr(e)}
+        try:
+            result["prefill_stream"] = prefill_stream_extra(ctx)
+            ps = result["prefill_stream"]
+            log(f"prefill streamed: {ps['ms_per_layer']:.2f} ms/layer ({ps['tokens_per_s']:.0f} tok/s), H2D "
+                f"{ps['h2d_gbs']:.1f} GB/s; copy alone {ps['copy_only_ms_per_layer']:.2f}, compute alone "
+                f"{ps['compute_only_ms_per_layer']:.2f}, serial {ps['serial_ms_per_layer']:.2f} ms/layer; overlap "
+                f"efficiency {ps['overlap_efficiency']:.2f}")
+        except Exception as e:
+            result["prefill_stream"] = {"error": repr(e)}
         if not args.no_cache:
             try:
                 result["cache"] = cache_extra(ctx, steps=args.cache_steps, sweep_steps=args.sweep_steps)

@@ -35,6 +35,7 @@ EXPORTS = (
     "cache_slot_table_destroy", "prefetch_expert", "cache_mark_layer_done", "cache_slot_table_resize",
     "moe_check_bank_types", "moe_ctx_set_timing", "moe_ctx_kernel_time",
     "moe_route_permute_workspace_size", "moe_route_permute", "moe_decode_layer", "cache_decode_layer",
+    "prefill_stream_create", "prefill_stream_layer", "prefill_stream_stats", "prefill_stream_destroy",
 )
 
 
@@ -100,6 +101,11 @@ def lib() -> ctypes.CDLL:
         "cache_slot_table_resize": (i, [vp, i, vp, vp]),
         "prefetch_expert": (i, [vp, i, i, vp, vp, i32p]),
         "cache_mark_layer_done": (i, [vp, i, vp]),
+        "prefill_stream_create": (i, [i, i, i, i, i, vp, vp, ctypes.POINTER(vp)]),
+        "prefill_stream_layer": (i, [vp, vp, i, ctypes.POINTER(moe_ffn_args), vp, vp, vp, vp, vp, vp, vp, sz,
+                                     vp, vp]),
+        "prefill_stream_stats": (i, [vp, i64p, i64p]),
+        "prefill_stream_destroy": (i, [vp]),
         "cache_decode_layer": (i, [vp, vp, i, vp, vp, vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                    vp, vp]),
         "moe_check_bank_types": (i, [i, i, ip, ip]),
@@ -394,3 +400,46 @@ def cache_decode_layer(cache: Cache, ctx: Ctx, layer: int, x, router_w, bias, lo
                                     _dev_ptr(sorted_pairs), _dev_ptr(pair_pos), _dev_ptr(active),
                                     _dev_ptr(y_pairs), _dev_ptr(ws), ws_bytes, _dev_ptr(out),
                                     _stream(copy_stream), _stream(compute_stream)), "cache_decode_layer")
+
+
+# --------------------------------------------------------- prefill streaming
+class PrefillStream:
+    def __init__(self, L, E, qtype, H, I, d_bufs, h_pool):
+        h = ctypes.c_void_p()
+        _check(lib().prefill_stream_create(L, E, qtype, H, I, _dev_ptr(d_bufs), _ptr(h_pool), ctypes.byref(h)),
+               "prefill_stream_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            lib().prefill_stream_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def prefill_stream_create(L, E, qtype, H, I, d_bufs, h_pool) -> PrefillStream:
+    return PrefillStream(L, E, qtype, H, I, d_bufs, h_pool)
+
+
+def prefill_stream_layer(ps: PrefillStream, ctx: Ctx, layer: int, args: moe_ffn_args, router_w, bias, logits_in,
+                         logits_out, topk_ids, pair_pos, route_ws, route_ws_bytes: int, copy_stream=None,
+                         compute_stream=None) -> None:
+    _check(lib().prefill_stream_layer(ps.handle, ctx.handle, layer, ctypes.byref(args), _dev_ptr(router_w),
+                                      _dev_ptr(bias), _dev_ptr(logits_in), _dev_ptr(logits_out),
+                                      _dev_ptr(topk_ids), _dev_ptr(pair_pos), _dev_ptr(route_ws), route_ws_bytes,
+                                      _stream(copy_stream), _stream(compute_stream)), "prefill_stream_layer")
+
+
+def prefill_stream_stats(ps: PrefillStream) -> Tuple[int, int]:
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().prefill_stream_stats(ps.handle, ctypes.byref(a), ctypes.byref(b)), "prefill_stream_stats")
+    return a.value, b.value
+
+
+def prefill_stream_destroy(ps: PrefillStream) -> None:
+    ps.close()

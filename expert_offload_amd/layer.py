@@ -209,3 +209,42 @@ class CachedLayers:
     def close(self):
         torch.cuda.synchronize()
         self.cache.close()
+
+
+class StreamedPrefill:
+    """Prefill through L layers whose experts live in a pinned host pool and
+    stream through two device buffers of one layer each (prefill_stream_*):
+    the next layer's experts are copied while the current layer computes."""
+
+    def __init__(self, ctx: L.Ctx, qtype: str, H: int, I: int, E: int, k: int, L_layers: int, T_max: int,
+                 host_pool: torch.Tensor, device="cuda"):
+        self.ctx, self.qtype, self.H, self.I, self.E, self.k, self.L = ctx, qtype, H, I, E, k, L_layers
+        self.q = L.QTYPE[qtype]
+        self.slot_bytes = L.moe_slot_bytes(self.q, H, I)
+        self.d_bufs = torch.empty(2 * E * self.slot_bytes, dtype=torch.uint8, device=device)
+        self.host_pool = host_pool
+        self.ps = L.prefill_stream_create(L_layers, E, self.q, H, I, self.d_bufs, host_pool)
+        self.copy_stream = torch.cuda.Stream()
+        self.buf = LayerBuffers(T_max, H, I, E, k, qtype, device=device, mode=L.MODE_PREFILL,
+                                x_dtype=L.DTYPE_BF16)
+
+    def layer(self, l: int, x: torch.Tensor, logits: torch.Tensor, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+        """Layer `l` over x (bf16 [T, H]) with given router logits (fp32
+        [T, E]); writes `out` (fp32 [T, H], default the buffers' own)."""
+        b = self.buf
+        T = x.shape[0]
+        out = b.out if out is None else out
+        args = L.make_ffn_args(None, self.slot_bytes, self.E, self.q, self.H, self.I, T, self.k, self.E, None, x,
+                               b.offsets, b.sorted_pairs, b.active, b.y, L.MODE_PREFILL, ws=b.ws,
+                               ws_bytes=b.ws.numel(), x_dtype=L.DTYPE_BF16, topk_w=b.w, out=out)
+        L.prefill_stream_layer(self.ps, self.ctx, l, args, None, None, logits, None, b.ids, b.pair_pos,
+                               b.route_ws, b.route_ws.numel(), self.copy_stream, stream)
+        return out
+
+    def stats(self):
+        return L.prefill_stream_stats(self.ps)
+
+    def close(self):
+        torch.cuda.synchronize()
+        self.ps.close()

@@ -237,9 +237,10 @@ def activations(wl: Workload, T: int, step: int = 0) -> np.ndarray:
     return x
 
 
-def given_logits(wl: Workload, T: int) -> np.ndarray:
-    """Router logits supplied directly: i.i.d. N(0, 1) fp32 [T, E]."""
-    g = rng_for(wl.index, "logits", T)
+def given_logits(wl: Workload, T: int, layer: int = 0) -> np.ndarray:
+    """Router logits supplied directly: i.i.d. N(0, 1) fp32 [T, E], one
+    independent draw per layer."""
+    g = rng_for(wl.index, "logits", T, layer)
     return g.standard_normal((T, wl.E), dtype=np.float32)
 
 

@@ -337,6 +337,51 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x,
                        void* ws, size_t ws_bytes, float* out,
                        void* copy_stream, void* compute_stream);
 
+/* ------------------------------------------------- prefill layer streaming
+ * Dual buffering for long prompts ("FreeToken Inference Engine: 3x Speed
+ * Boost for MoE Models", "Dual-Buffering to Solve the Prefill Bottleneck"):
+ * a prompt touches nearly every expert of every layer, so every layer's
+ * experts cross PCIe, and the next layer's copy overlaps the current
+ * layer's compute.
+ *   d_bufs   device, 2 * E * slot_bytes, caller-owned, 16-byte aligned: two
+ *            buffers of one layer's E experts (expert e in slot e).
+ *   h_pool   pinned host memory, experts [L][E] in the device slot layout
+ *            (the expert cache's host pool layout), caller-owned; not
+ *            pinned -> MOE_ERR_NOT_PINNED.
+ * The stream object owns an identity slot table and four events.
+ *
+ * prefill_stream_layer: one layer's forward with its experts streamed.  If
+ * no buffer holds `layer` it is copied now (a demand load, counted) into
+ * the buffer the previous call did not use.  moe_route_permute then runs on
+ * compute_stream (router_w/bias/logits_in/logits_out/topk_ids/pair_pos and
+ * route_ws as there; its other outputs go to args.topk_w,
+ * args.expert_offsets, args.sorted_pairs, args.active), compute_stream
+ * waits for the layer's copy, and moe_expert_ffn with the combine runs out
+ * of the buffer (args as in moe_expert_ffn with args.topk_w and args.out
+ * set and no expert_mask; args.pool_base, slot_bytes, n_slots and
+ * slot_table are ignored, and args.H, I, E and qtype must equal the
+ * stream's).  Then layer + 1, if it exists and is not held, is copied into
+ * the other buffer with hipMemcpyAsync on copy_stream, after the last layer
+ * that read that buffer has finished on its compute stream.  Calls in
+ * layer order keep PCIe busy back to back; any order is correct.  Errors
+ * as in the calls it makes.
+ *
+ * prefill_stream_stats: layer copies issued in total and how many of them
+ * were demand loads (not prefetched by the previous call). */
+typedef struct moe_prefill_stream moe_prefill_stream;
+int prefill_stream_create(int L, int E, int qtype, int H, int I, void* d_bufs,
+                          const void* h_pool, moe_prefill_stream** out);
+int prefill_stream_layer(moe_prefill_stream* s, moe_ctx* ctx, int layer,
+                         const moe_ffn_args* args, const float* router_w,
+                         const float* bias, const float* logits_in,
+                         float* logits_out, int32_t* topk_ids,
+                         int32_t* pair_pos, void* route_ws,
+                         size_t route_ws_bytes, void* copy_stream,
+                         void* compute_stream);
+int prefill_stream_stats(moe_prefill_stream* s, int64_t* loads,
+                         int64_t* demand_loads);
+int prefill_stream_destroy(moe_prefill_stream* s);
+
 /* ------------------------------------------------------- bank type check
  * One block type for every expert bank: the slot pool is one allocation
  * indexed with a single row stride, so mixed types would read every block
