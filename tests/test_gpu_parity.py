@@ -451,6 +451,41 @@ def test_decode_layer_equals_two_calls(ctx, decode_layer, wide_layer, case):
     _check_layer(buf, one["out"], ref, DECODE_TOL, T)
 
 
+def _tie_logits(E):
+    """Four tokens of router logits built to stress the selection order:
+    small integers (many exact ties, a NaN, a -inf); a row whose top values
+    are +0 and -0; a row of one value; ten equal maxima straddling the k-th
+    place."""
+    rng = np.random.default_rng(4)
+    lg = rng.integers(-3, 4, size=(4, E)).astype(np.float32)
+    lg[0, 5], lg[0, 20] = np.nan, -np.inf
+    lg[1] = -1.0
+    lg[1, 3:43:4] = np.array([0.0, -0.0] * 5, dtype=np.float32)
+    lg[2] = 0.5
+    lg[3] = rng.standard_normal(E).astype(np.float32)
+    lg[3, 7:107:10] = 4.0
+    return lg
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_layer_selection_ties(ctx, decode_layer, T):
+    """In-kernel routing on logits with exact ties, signed zeros, NaN and
+    -inf: ids equal the oracle's (logit desc, id asc) order exactly, and
+    every routing result is bit-identical to the two-call path."""
+    rl, wl = decode_layer, decode_layer.wl
+    x = gi.activations(wl, T)
+    lg = _tie_logits(wl.E)[:T].copy()
+    _, two = _layer_outputs(ctx, rl, T, x, None, None, lg, True)
+    buf, one = _layer_outputs(ctx, rl, T, x, None, None, lg, "layer")
+    for key in two:
+        np.testing.assert_array_equal(one[key], two[key], err_msg=key)
+    lg_ref = np.where(np.isnan(lg), -np.inf, lg).astype(np.float32)  # the library counts NaN as -inf
+    np.testing.assert_array_equal(one["ids"], oracle.topk_select(lg_ref, wl.k))
+    ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, logits=lg_ref)
+    np.testing.assert_allclose(one["w"], ref["w"], rtol=1e-5, atol=1e-7)
+    assert max_rel_err(one["out"], ref["out"]) <= DECODE_TOL
+
+
 def test_decode_layer_many_launches_and_graph(ctx, decode_layer):
     """moe_decode_layer called many times in a row on one stream, then the
     same calls captured in a HIP graph and replayed (with eager calls between
