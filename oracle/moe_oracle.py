@@ -229,7 +229,8 @@ def moe_layer(x: np.ndarray, qtype: str, get_blocks, k: int, *,
 #    "From Static Allocation to Dynamic Scheduling": VRAM is a cache over the
 #    host-resident pool and only missing experts move over PCIe)
 # --------------------------------------------------------------------------
-def lru_simulate(trace: np.ndarray, capacity: int, resizes: Optional[Dict[Tuple[int, int], int]] = None):
+def lru_simulate(trace: np.ndarray, capacity: int, resizes: Optional[Dict[Tuple[int, int], int]] = None,
+                 host: Optional[Dict[Tuple[int, int], set]] = None):
     """Replay lookups in order; returns (hit bool [steps, L, n], evicted keys).
 
     For every step, every layer and every id of that (step, layer) in
@@ -243,8 +244,16 @@ def lru_simulate(trace: np.ndarray, capacity: int, resizes: Optional[Dict[Tuple[
     "Dynamic Cache Adjustment Experiments"), just before that (step,
     layer)'s lookups; the most recently used keys stay, up to the new
     capacity, and the others are evicted.
+
+    host {(step, layer): ids}: missing experts of that (step, layer) that
+    are computed on the CPU instead of being moved to the GPU ("FreeToken
+    Inference Engine: 3x Speed Boost for MoE Models", section "Q* Strategy:
+    Intelligently Choosing Where to Compute").  Their lookups are misses
+    that leave the cache as it was: nothing is inserted, refreshed or
+    evicted for them.
     """
     steps, L, n = trace.shape
+    host = host or {}
     last_use: Dict[Tuple[int, int], int] = {}
     clock = 0
     hit = np.zeros(trace.shape, dtype=bool)
@@ -259,8 +268,13 @@ def lru_simulate(trace: np.ndarray, capacity: int, resizes: Optional[Dict[Tuple[
                     del last_use[victim]
                     evicted.append((s, l, victim))
             current = set()
+            on_host = host.get((s, l), ())
             for j in range(n):
                 key = (l, int(trace[s, l, j]))
+                if key[1] in on_host:
+                    if key in last_use:
+                        raise ValueError(f"expert {key} is resident, so it cannot be computed on the host")
+                    continue
                 clock += 1
                 if key in last_use:
                     hit[s, l, j] = True

@@ -377,6 +377,36 @@ def test_lru_resize_invariants():
     np.testing.assert_array_equal(small[:24], oracle.lru_simulate(trace[:24], 400)[0])
 
 
+def test_lru_host_misses_hand_trace():
+    # capacity 2, one layer: s0 [0, 1] copied; s1 [2, 0] with 2 on the host:
+    # 2 misses and changes nothing, 0 hits; s2 [2, 1]: 2 now copied evicts
+    # the LRU key 1 (0 was used at s1), then 1 misses and evicts 0.
+    trace = np.array([[[0, 1]], [[2, 0]], [[2, 1]]], dtype=np.int32)
+    hit, ev = oracle.lru_simulate(trace, 2, host={(1, 0): {2}})
+    assert hit.reshape(-1).tolist() == [False, False, False, True, False, False]
+    assert ev == [(2, 0, (0, 1)), (2, 0, (0, 0))]
+    # without the host decision, 2 is inserted at s1 (evicting 0, so 0
+    # misses too) and hits at s2
+    hit2, _ = oracle.lru_simulate(trace, 2)
+    assert hit2.reshape(-1).tolist() == [False, False, False, False, True, False]
+
+
+def test_lru_host_invariants():
+    wl = gi.workload(5)
+    trace = gi.cache_trace(wl, steps=32)
+    base, ev0 = oracle.lru_simulate(trace, 100)
+    same, ev1 = oracle.lru_simulate(trace, 100, host={})
+    np.testing.assert_array_equal(same, base)
+    assert ev0 == ev1
+    # every miss on the host: the cache never fills, so nothing ever hits
+    everything = {(s, l): set(range(wl.E)) for s in range(trace.shape[0]) for l in range(trace.shape[1])}
+    none_hit, ev = oracle.lru_simulate(trace, 100, host=everything)
+    assert not none_hit.any() and ev == []
+    # a resident expert cannot be sent to the host
+    with pytest.raises(ValueError):
+        oracle.lru_simulate(np.array([[[0]], [[0]]], dtype=np.int32), 2, host={(1, 0): {0}})
+
+
 def test_lru_protects_current_layer_keys():
     trace = np.array([[[0, 1, 2]], [[3, 4, 5]]], dtype=np.int32)
     hit, ev = oracle.lru_simulate(trace, 3)
