@@ -21,8 +21,10 @@ Also reported on the same line:
                 top-8, intermediate 2048, Q4_0) served from a pinned host
                 pool through a VRAM cache of 40% of the experts, 2048
                 single-token steps of a trace with temporal locality; then
-                the same trace at cache fractions 0.1 .. 0.58, and a run
-                resized from 58% to 40% at run time halfway
+                the same trace with misses computed on the host cores
+                (all, and split by measured rates: q*), at cache
+                fractions 0.1 .. 0.58 (copy and q*), and a run resized
+                from 58% to 40% at run time halfway
 Progress goes to stderr; the JSON line is the only stdout output.
 """
 from __future__ import annotations
@@ -438,6 +440,25 @@ def cache_extra(ctx, steps=None, distinct=64, warm_from=256, sweep_steps=1024, r
         "h2d_copy_ceiling_gbs": ceiling,
         "pool_values": f"{distinct} generated experts repeated over the {keys} keys",
     }
+    # misses on the host cores (MOE_MISS_HOST) and split by measured rates
+    # (MOE_MISS_QSTAR), same trace and cache size
+    for name, pol in (("host", L.MISS_HOST), ("qstar", L.MISS_QSTAR), ("host_copy", L.MISS_HOST_COPY)):
+        cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, n_slots, pool)
+        cl.set_miss_policy(pol)
+        st = run(cl, 0, steps, name)
+        ph = phase(cl, st, 0, steps, min(warm_from, steps - 1))
+        copied, on_host, r_copy, r_host = cl.miss_stats()
+        res[name] = {"tokens_per_s": steps / (st[-1] - st[0]), "warm": ph,
+                     "hit_rate": 1.0 - float(sum(cl.misses_per_layer)) / (steps * wl.layers * wl.k),
+                     "experts_copied": copied, "experts_on_host": on_host,
+                     "copy_gbs_estimate": r_copy, "host_gbs_estimate": r_host,
+                     "host_threads": "all hardware threads but four"}
+        log(f"cache {name}: {res[name]['tokens_per_s']:.1f} tok/s (warm {ph['tokens_per_s']:.1f} at hit rate "
+            f"{ph['hit_rate']:.3f}); copied {copied}, on host {on_host}; rates copy {r_copy:.1f} host "
+            f"{r_host:.1f} GB/s")
+        cl.close()
+        del cl
+        torch.cuda.empty_cache()
     # cache-fraction sweep, each from an empty cache over the first sweep_steps steps
     sweep = []
     w0 = min(warm_from, sweep_steps - 1)
@@ -446,12 +467,25 @@ def cache_extra(ctx, steps=None, distinct=64, warm_from=256, sweep_steps=1024, r
         st = run(cl, 0, sweep_steps, f"{f:.2f}")
         ph = phase(cl, st, 0, sweep_steps, w0)
         late = phase(cl, st, 0, sweep_steps, sweep_steps // 2)
-        sweep.append({"cache_fraction": f, "cache_slots": slots_of(f), "tokens_per_s": ph["tokens_per_s"],
-                      "hit_rate": ph["hit_rate"], "from_step": w0, "second_half": late})
-        log(f"cache sweep {f:.2f}: {ph['tokens_per_s']:.1f} tok/s at hit rate {ph['hit_rate']:.3f}")
+        point = {"cache_fraction": f, "cache_slots": slots_of(f), "tokens_per_s": ph["tokens_per_s"],
+                 "hit_rate": ph["hit_rate"], "from_step": w0, "second_half": late}
         cl.close()
         del cl
         torch.cuda.empty_cache()
+        msg = ""
+        for name, pol in (("qstar", L.MISS_QSTAR), ("host_copy", L.MISS_HOST_COPY)):
+            cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, slots_of(f), pool)
+            cl.set_miss_policy(pol)
+            st = run(cl, 0, sweep_steps, f"{f:.2f} {name}")
+            qph = phase(cl, st, 0, sweep_steps, w0)
+            point[name] = {"tokens_per_s": qph["tokens_per_s"], "hit_rate": qph["hit_rate"],
+                           "experts_on_host": cl.miss_stats()[1]}
+            msg += f"; {name} {qph['tokens_per_s']:.1f} tok/s at {qph['hit_rate']:.3f}"
+            cl.close()
+            del cl
+            torch.cuda.empty_cache()
+        sweep.append(point)
+        log(f"cache sweep {f:.2f}: {ph['tokens_per_s']:.1f} tok/s at hit rate {ph['hit_rate']:.3f}{msg}")
     res["sweep"] = {"steps": sweep_steps, "points": sweep}
     # run-time resize from resize_from to the main fraction, halfway through
     half = sweep_steps // 2

@@ -36,6 +36,8 @@ EXPORTS = (
     "moe_check_bank_types", "moe_ctx_set_timing", "moe_ctx_kernel_time",
     "moe_route_permute_workspace_size", "moe_route_permute", "moe_decode_layer", "cache_decode_layer",
     "prefill_stream_create", "prefill_stream_layer", "prefill_stream_stats", "prefill_stream_destroy",
+    "moe_host_expert_ffn", "moe_host_has_avx512", "cache_set_miss_policy", "cache_miss_stats",
+    "cache_last_misses",
 )
 
 
@@ -101,6 +103,11 @@ def lib() -> ctypes.CDLL:
         "cache_slot_table_resize": (i, [vp, i, vp, vp]),
         "prefetch_expert": (i, [vp, i, i, vp, vp, i32p]),
         "cache_mark_layer_done": (i, [vp, i, vp]),
+        "cache_set_miss_policy": (i, [vp, i, i]),
+        "cache_miss_stats": (i, [vp, i64p, i64p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
+        "cache_last_misses": (i, [vp, i32p, ip, i32p, ip, ip]),
+        "moe_host_expert_ffn": (i, [i, i, i, vp, vp, i, vp, i, i]),
+        "moe_host_has_avx512": (i, []),
         "prefill_stream_create": (i, [i, i, i, i, i, vp, vp, ctypes.POINTER(vp)]),
         "prefill_stream_layer": (i, [vp, vp, i, ctypes.POINTER(moe_ffn_args), vp, vp, vp, vp, vp, vp, vp, sz,
                                      vp, vp]),
@@ -386,6 +393,35 @@ def cache_slot_table_resize(cache: Cache, n_slots: int, d_pool=None, stream=None
                                          _stream(stream)), "cache_slot_table_resize")
 
 
+MISS_COPY, MISS_HOST, MISS_QSTAR, MISS_HOST_COPY = 0, 1, 2, 3
+
+
+def cache_set_miss_policy(cache: Cache, policy: int, host_threads: int = 0) -> None:
+    _check(lib().cache_set_miss_policy(cache.handle, policy, host_threads), "cache_set_miss_policy")
+
+
+def cache_miss_stats(cache: Cache):
+    """(experts copied, experts computed on the host, copy GB/s, host GB/s)."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    p, h = ctypes.c_double(), ctypes.c_double()
+    _check(lib().cache_miss_stats(cache.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(p), ctypes.byref(h)),
+           "cache_miss_stats")
+    return a.value, b.value, p.value, h.value
+
+
+def cache_last_misses(cache: Cache):
+    """(copied expert ids, host expert ids, how many of the host ids were
+    misses left out of the cache) of the last cache_decode_layer."""
+    import numpy as np
+    cp = np.empty(max(cache.E, 1), dtype=np.int32)
+    hs = np.empty(max(cache.E, 1), dtype=np.int32)
+    nc, nh, no = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    P = ctypes.POINTER(ctypes.c_int32)
+    _check(lib().cache_last_misses(cache.handle, cp.ctypes.data_as(P), ctypes.byref(nc), hs.ctypes.data_as(P),
+                                   ctypes.byref(nh), ctypes.byref(no)), "cache_last_misses")
+    return cp[:nc.value].copy(), hs[:nh.value].copy(), no.value
+
+
 def cache_mark_layer_done(cache: Cache, layer: int, compute_stream=None) -> None:
     _check(lib().cache_mark_layer_done(cache.handle, layer, _stream(compute_stream)),
            "cache_mark_layer_done")
@@ -443,3 +479,25 @@ def prefill_stream_stats(ps: PrefillStream) -> Tuple[int, int]:
 
 def prefill_stream_destroy(ps: PrefillStream) -> None:
     ps.close()
+
+
+# ------------------------------------------------------------ host executor
+def _host_ptr(a) -> int:
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError("expected a host buffer")
+        return _ptr(a)
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("libmoe takes contiguous arrays")
+    return a.ctypes.data
+
+
+def moe_host_expert_ffn(qtype: int, H: int, I: int, slot, x, y, threads: int = 0, vector: bool = True) -> None:
+    """Host buffers (numpy or CPU tensors): slot bytes, x fp32 [n, H] -> y fp32 [n, H]."""
+    n = int(x.shape[0])
+    _check(lib().moe_host_expert_ffn(qtype, H, I, _host_ptr(slot), _host_ptr(x), n, _host_ptr(y), threads,
+                                     1 if vector else 0), "moe_host_expert_ffn")
+
+
+def moe_host_has_avx512() -> bool:
+    return bool(lib().moe_host_has_avx512())

@@ -20,6 +20,9 @@
 // once, with its destination slot.  prefetch_expert then moves the bytes
 // and installs the slot in the device table in stream order.
 #include <algorithm>
+#include <chrono>
+#include <deque>
+#include <cmath>
 #include <set>
 #include <unordered_map>
 #include <vector>
@@ -56,6 +59,16 @@ __global__ void slot_move_kernel(const uint4* src, uint4* dst, const int2* moves
   }
 }
 
+// Rows of y_pairs computed on the host: pair p's row is copied from the
+// staging rows when its expert is marked in host_mask.
+__global__ void host_rows_kernel(const float4* __restrict__ src, const int32_t* __restrict__ host_mask,
+                                 const int32_t* __restrict__ ids, float4* __restrict__ y, int H4) {
+  const int p = blockIdx.y;
+  if (!host_mask[ids[p]]) return;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < H4; i += gridDim.x * blockDim.x)
+    y[(size_t)p * H4 + i] = src[(size_t)p * H4 + i];
+}
+
 constexpr int kEventRing = 256;
 constexpr int kCtlStagePairs = 1024;  // T*k of one cache_decode_layer call
 
@@ -80,6 +93,7 @@ struct moe_cache {
   struct Pending { int slot; int victim_key; };
   std::unordered_map<int, Pending> pending;  // key -> destination (copy not issued)
   std::vector<int> slot_event;           // slot -> index into events or -1
+  std::vector<int> slot_ready;           // slot -> index into copy_events of its last copy, or -1
   std::vector<int> layer_slots;          // slots touched by the current lookup
   hipEvent_t events[kEventRing] = {};       // layer-done events (compute stream)
   hipEvent_t copy_events[kEventRing] = {};  // copy-done events (copy streams)
@@ -89,10 +103,29 @@ struct moe_cache {
   // staging of cache_decode_layer, allocated with the cache: the routed ids
   // (pinned host), the hit / miss expert masks (pinned host and device)
   int32_t* h_ids = nullptr;   // [kCtlStagePairs]
-  int32_t* h_mask = nullptr;  // [2][E]
-  int32_t* d_mask = nullptr;  // [2][E]
+  int32_t* h_mask = nullptr;  // [3][E]: hits, copied misses, host misses
+  int32_t* d_mask = nullptr;  // [3][E]
   hipEvent_t ids_ready = nullptr;
+  // misses computed on the host (cache_set_miss_policy), staging made when
+  // such a policy is first set
+  int policy = MOE_MISS_COPY;
+  int host_threads = 1;
+  float* h_x = nullptr;   // pinned [kCtlStagePairs][H]: the layer's tokens
+  float* h_y = nullptr;   // pinned [kCtlStagePairs][H]: host-computed pair rows
+  float* d_yh = nullptr;  // device [kCtlStagePairs][H]
+  std::vector<float> h_scratch;  // [kCtlStagePairs][I]
+  hipEvent_t copy_t0 = nullptr, copy_t1 = nullptr;  // around one layer's copies
+  int timed_copies = 0;                             // copies between them, not yet read
+  double rate_pcie = 0.0, rate_host = 0.0;          // bytes per second
+  int64_t n_copied = 0, n_host = 0;
+  std::vector<int32_t> last_copy, last_host;
+  int last_host_only = 0;  // the first of last_host that were not inserted
+  std::deque<int> inflight;  // copy_events of background copies, oldest first
 };
+
+// Background copies allowed in flight under MOE_MISS_HOST_COPY; a miss
+// beyond them is computed on the host and not inserted.
+constexpr int kCopyBacklog = 8;
 
 static int pop_free(moe_cache* c) {
   if (c->free_head >= c->free_fifo.size()) return -1;
@@ -142,6 +175,7 @@ int cache_slot_table_create(int L, int E, int n_slots, int qtype, int H, int I, 
   c->protect.assign(keys, 0);
   c->slot_key.assign(n_slots + 2, -1);
   c->slot_event.assign(n_slots + 2, -1);
+  c->slot_ready.assign(n_slots + 2, -1);
   for (int s = 0; s < n_slots + 2; ++s) c->free_fifo.push_back(s);
   if ((e = hipMalloc(&c->d_table, sizeof(int32_t) * keys)) != hipSuccess) {
     delete c;
@@ -160,13 +194,13 @@ int cache_slot_table_create(int L, int E, int n_slots, int qtype, int H, int I, 
     }
   }
   if ((e = hipHostMalloc((void**)&c->h_ids, sizeof(int32_t) * kCtlStagePairs, hipHostMallocDefault)) != hipSuccess ||
-      (e = hipHostMalloc((void**)&c->h_mask, sizeof(int32_t) * 2 * E, hipHostMallocDefault)) != hipSuccess ||
-      (e = hipMalloc(&c->d_mask, sizeof(int32_t) * 2 * E)) != hipSuccess ||
+      (e = hipHostMalloc((void**)&c->h_mask, sizeof(int32_t) * 3 * E, hipHostMallocDefault)) != hipSuccess ||
+      (e = hipMalloc(&c->d_mask, sizeof(int32_t) * 3 * E)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&c->ids_ready, hipEventDisableTiming)) != hipSuccess) {
     cache_slot_table_destroy(c);
     return hip_error(e, "cache staging allocation");
   }
-  std::fill(c->h_mask, c->h_mask + 2 * E, 0);
+  std::fill(c->h_mask, c->h_mask + 3 * E, 0);
   *out = c;
   return MOE_OK;
 }
@@ -184,6 +218,11 @@ int cache_slot_table_destroy(moe_cache* c) {
   if (c->h_mask) (void)hipHostFree(c->h_mask);
   if (c->d_mask) (void)hipFree(c->d_mask);
   if (c->ids_ready) (void)hipEventDestroy(c->ids_ready);
+  if (c->h_x) (void)hipHostFree(c->h_x);
+  if (c->h_y) (void)hipHostFree(c->h_y);
+  if (c->d_yh) (void)hipFree(c->d_yh);
+  if (c->copy_t0) (void)hipEventDestroy(c->copy_t0);
+  if (c->copy_t1) (void)hipEventDestroy(c->copy_t1);
   delete c;
   return MOE_OK;
 }
@@ -198,9 +237,11 @@ int cache_slot_table_stats(moe_cache* c, int64_t* hits, int64_t* misses) {
   return MOE_OK;
 }
 
-int cache_slot_table_lookup(moe_cache* c, int layer, const int32_t* ids, int n, int32_t* slots_out,
-                            int32_t* miss_ids, int* n_miss) {
-  clear_error();
+// The LRU lookup of cache_slot_table_lookup.  Ids marked in `host` (or all
+// none when it is NULL) are misses computed on the host: counted as misses
+// and otherwise left out (no refresh, no insertion), slot -1.
+static int lookup_impl(moe_cache* c, int layer, const int32_t* ids, int n, const int32_t* host, int32_t* slots_out,
+                       int32_t* miss_ids, int* n_miss) {
   if (!c) return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_lookup: cache is NULL");
   if (layer < 0 || layer >= c->L || n < 0 || (n > 0 && (!ids || !slots_out)) || !n_miss)
     return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_lookup: layer=%d n=%d", layer, n);
@@ -209,7 +250,9 @@ int cache_slot_table_lookup(moe_cache* c, int layer, const int32_t* ids, int n, 
       return set_error(MOE_ERR_INVALID_ARG, "cache_slot_table_lookup: expert id %d of layer %d not in [0, %d)",
                        ids[i], layer, c->E);
   {
-    std::vector<int32_t> distinct(ids, ids + n);
+    std::vector<int32_t> distinct;
+    for (int i = 0; i < n; ++i)
+      if (!host || !host[ids[i]]) distinct.push_back(ids[i]);
     std::sort(distinct.begin(), distinct.end());
     const long nd = std::unique(distinct.begin(), distinct.end()) - distinct.begin();
     if (nd > c->n_slots)
@@ -224,6 +267,11 @@ int cache_slot_table_lookup(moe_cache* c, int layer, const int32_t* ids, int n, 
   int nm = 0;
   for (int i = 0; i < n; ++i) {
     const int key = layer * c->E + ids[i];
+    if (host && host[ids[i]]) {
+      ++c->misses;
+      slots_out[i] = -1;
+      continue;
+    }
     ++c->clock;
     if (c->table[key] >= 0) {
       ++c->hits;
@@ -272,6 +320,15 @@ int cache_slot_table_lookup(moe_cache* c, int layer, const int32_t* ids, int n, 
   return MOE_OK;
 }
 
+int cache_slot_table_lookup(moe_cache* c, int layer, const int32_t* ids, int n, int32_t* slots_out,
+                            int32_t* miss_ids, int* n_miss) {
+  clear_error();
+  return lookup_impl(c, layer, ids, n, nullptr, slots_out, miss_ids, n_miss);
+}
+
+static int issue_copy(moe_cache* c, int key, moe_cache::Pending pd, hipStream_t cs, hipStream_t ks,
+                      bool compute_waits);
+
 int prefetch_expert(moe_cache* c, int layer, int expert, void* copy_stream, void* compute_stream,
                     int32_t* slot_out) {
   clear_error();
@@ -289,9 +346,25 @@ int prefetch_expert(moe_cache* c, int layer, int expert, void* copy_stream, void
   }
   const moe_cache::Pending pd = it->second;
   c->pending.erase(it);
+  int rc = issue_copy(c, key, pd, (hipStream_t)copy_stream, (hipStream_t)compute_stream, true);
+  if (rc) return rc;
+  if (slot_out) *slot_out = pd.slot;
+  return MOE_OK;
+}
+
+// The copy of key into its destination slot on copy stream cs, after the
+// slot's previous reader; the slot table update on compute stream ks.  With
+// compute_waits, ks waits for the copy (the expert is used in stream order);
+// without, the caller must not let a kernel read the slot before the copy's
+// event (slot_ready) has completed.
+static int issue_copy(moe_cache* c, int key, moe_cache::Pending pd, hipStream_t cs, hipStream_t ks,
+                      bool compute_waits) {
   hipError_t e = hipSetDevice(c->device);
   if (e != hipSuccess) return hip_error(e, "hipSetDevice");
-  hipStream_t cs = (hipStream_t)copy_stream, ks = (hipStream_t)compute_stream;
+  // an earlier copy into the slot (possibly on another stream) comes first
+  if (c->slot_ready[pd.slot] >= 0 &&
+      (e = hipStreamWaitEvent(cs, c->copy_events[c->slot_ready[pd.slot]], 0)) != hipSuccess)
+    return hip_error(e, "hipStreamWaitEvent(earlier copy)");
   // the slot's previous reader must be done before the copy overwrites it
   if (c->slot_event[pd.slot] >= 0) {
     if ((e = hipStreamWaitEvent(cs, c->events[c->slot_event[pd.slot]], 0)) != hipSuccess)
@@ -300,20 +373,20 @@ int prefetch_expert(moe_cache* c, int layer, int expert, void* copy_stream, void
   if ((e = hipMemcpyAsync(c->d_pool + (size_t)pd.slot * c->slot_bytes, c->h_pool + (size_t)key * c->slot_bytes,
                           c->slot_bytes, hipMemcpyHostToDevice, cs)) != hipSuccess)
     return hip_error(e, "hipMemcpyAsync(expert)");
-  hipEvent_t done = c->copy_events[c->next_copy_event];
+  const int ce = c->next_copy_event;
+  hipEvent_t done = c->copy_events[ce];
   c->next_copy_event = (c->next_copy_event + 1) % kEventRing;
   if ((e = hipEventRecord(done, cs)) != hipSuccess) return hip_error(e, "hipEventRecord(copy)");
-  if ((e = hipStreamWaitEvent(ks, done, 0)) != hipSuccess) return hip_error(e, "hipStreamWaitEvent(compute)");
+  c->slot_ready[pd.slot] = ce;
+  if (compute_waits && (e = hipStreamWaitEvent(ks, done, 0)) != hipSuccess)
+    return hip_error(e, "hipStreamWaitEvent(compute)");
   TableUpdate u{};
   u.idx[u.n] = key; u.val[u.n] = pd.slot; ++u.n;
   if (pd.victim_key >= 0 && c->table[pd.victim_key] < 0) {
     u.idx[u.n] = pd.victim_key; u.val[u.n] = -1; ++u.n;
   }
   launch(table_update_kernel, 1, 64, 0, ks, c->d_table, u);
-  int rc = check_launch("table_update_kernel");
-  if (rc) return rc;
-  if (slot_out) *slot_out = pd.slot;
-  return MOE_OK;
+  return check_launch("table_update_kernel");
 }
 
 int cache_mark_layer_done(moe_cache* c, int layer, void* compute_stream) {
@@ -407,6 +480,7 @@ int cache_slot_table_resize(moe_cache* c, int n_slots, void* d_pool, void* strea
   c->table.swap(table);
   c->slot_key.swap(slot_key);
   c->slot_event.assign(count, -1);
+  c->slot_ready.assign(count, -1);
   c->free_fifo.clear();
   c->free_head = 0;
   for (int s = 0; s < count; ++s)
@@ -414,6 +488,122 @@ int cache_slot_table_resize(moe_cache* c, int n_slots, void* d_pool, void* strea
   c->n_slots = n_slots;
   c->d_pool = pool;
   return MOE_OK;
+}
+
+static double now_s() {
+  return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+static void update_rate(double& rate, double sample) {
+  if (!(sample > 0.0) || !std::isfinite(sample)) return;
+  rate = rate > 0.0 ? 0.75 * rate + 0.25 * sample : sample;
+}
+
+// Bytes per second of expert copies and of the host executor, measured
+// once when a policy that needs them is set (the running estimates then
+// follow every layer).
+static int calibrate_rates(moe_cache* c) {
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_error(e, "hipSetDevice");
+  const size_t stage = sizeof(float) * (size_t)kCtlStagePairs * c->H;
+  const size_t chunk = std::min(c->slot_bytes, stage);
+  double best = 1e30;
+  for (int r = 0; r < 3; ++r) {
+    const double t0 = now_s();
+    const uint8_t* src = c->h_pool + (size_t)(r % (c->L * c->E)) * c->slot_bytes;  // chunk <= slot_bytes
+    if ((e = hipMemcpy(c->d_yh, src, chunk, hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_error(e, "hipMemcpy(calibration)");
+    best = std::min(best, now_s() - t0);
+  }
+  c->rate_pcie = (double)chunk / best;
+  std::fill(c->h_x, c->h_x + c->H, 0.0f);
+  best = 1e30;
+  for (int r = 0; r < 3; ++r) {
+    const uint8_t* slot = c->h_pool + (size_t)(r % (c->L * c->E)) * c->slot_bytes;
+    const int one = 1, tok0 = 0;
+    const int* tp = &tok0;
+    const double t0 = now_s();
+    int rc = host_experts_ffn(c->qtype, c->H, c->I, 1, &slot, &one, &tp, &tp, c->h_x, c->h_y, c->h_scratch.data(),
+                              c->host_threads, true);
+    if (rc) return rc;
+    best = std::min(best, now_s() - t0);
+  }
+  c->rate_host = (double)c->slot_bytes / best;
+  return MOE_OK;
+}
+
+int cache_set_miss_policy(moe_cache* c, int policy, int host_threads) {
+  clear_error();
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "cache_set_miss_policy: cache is NULL");
+  if (policy != MOE_MISS_COPY && policy != MOE_MISS_HOST && policy != MOE_MISS_QSTAR && policy != MOE_MISS_HOST_COPY)
+    return set_error(MOE_ERR_INVALID_ARG, "cache_set_miss_policy: policy %d unknown", policy);
+  if (host_threads < 0) return set_error(MOE_ERR_INVALID_ARG, "cache_set_miss_policy: host_threads=%d", host_threads);
+  c->host_threads = host_threads == 0 ? default_host_threads() : host_threads;
+  if (policy != MOE_MISS_COPY && !c->h_x) {
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_error(e, "hipSetDevice");
+    const size_t rows = (size_t)kCtlStagePairs * c->H;
+    if ((e = hipHostMalloc((void**)&c->h_x, sizeof(float) * rows, hipHostMallocDefault)) != hipSuccess ||
+        (e = hipHostMalloc((void**)&c->h_y, sizeof(float) * rows, hipHostMallocDefault)) != hipSuccess ||
+        (e = hipMalloc(&c->d_yh, sizeof(float) * rows)) != hipSuccess ||
+        (e = hipEventCreate(&c->copy_t0)) != hipSuccess || (e = hipEventCreate(&c->copy_t1)) != hipSuccess) {
+      if (c->h_x) (void)hipHostFree(c->h_x);
+      if (c->h_y) (void)hipHostFree(c->h_y);
+      if (c->d_yh) (void)hipFree(c->d_yh);
+      if (c->copy_t0) (void)hipEventDestroy(c->copy_t0);
+      if (c->copy_t1) (void)hipEventDestroy(c->copy_t1);
+      c->h_x = c->h_y = c->d_yh = nullptr;
+      c->copy_t0 = c->copy_t1 = nullptr;
+      return hip_error(e, "cache_set_miss_policy: staging");
+    }
+    c->h_scratch.assign((size_t)kCtlStagePairs * c->I, 0.0f);
+  }
+  if (policy == MOE_MISS_QSTAR && (c->rate_pcie <= 0.0 || c->rate_host <= 0.0)) {
+    int rc = calibrate_rates(c);
+    if (rc) return rc;
+  }
+  c->policy = policy;
+  return MOE_OK;
+}
+
+int cache_miss_stats(moe_cache* c, int64_t* copied, int64_t* host, double* pcie_gbs, double* host_gbs) {
+  clear_error();
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "cache_miss_stats: cache is NULL");
+  if (copied) *copied = c->n_copied;
+  if (host) *host = c->n_host;
+  if (pcie_gbs) *pcie_gbs = c->rate_pcie / 1e9;
+  if (host_gbs) *host_gbs = c->rate_host / 1e9;
+  return MOE_OK;
+}
+
+int cache_last_misses(moe_cache* c, int32_t* copy_ids, int* n_copy, int32_t* host_ids, int* n_host,
+                      int* n_host_only) {
+  clear_error();
+  if (!c || !n_copy || !n_host) return set_error(MOE_ERR_INVALID_ARG, "cache_last_misses: NULL argument");
+  *n_copy = (int)c->last_copy.size();
+  *n_host = (int)c->last_host.size();
+  if (n_host_only) *n_host_only = c->last_host_only;
+  if (copy_ids) std::copy(c->last_copy.begin(), c->last_copy.end(), copy_ids);
+  if (host_ids) std::copy(c->last_host.begin(), c->last_host.end(), host_ids);
+  return MOE_OK;
+}
+
+// How many of n missing experts go to the host: the split that finishes
+// both sides soonest at the measured rates (copies and host work run at the
+// same time), the fewest host experts on a tie.
+static int qstar_split(const moe_cache* c, int n) {
+  const double B = (double)c->slot_bytes;
+  const double kHostFixed = 20e-6;  // waking the workers, moving the rows back
+  int best = 0;
+  double best_t = n * B / c->rate_pcie;
+  for (int m = 1; m <= n; ++m) {
+    const double t = std::max((n - m) * B / c->rate_pcie, m * B / c->rate_host + kHostFixed);
+    if (t < best_t) {
+      best_t = t;
+      best = m;
+    }
+  }
+  return best;
 }
 
 int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, const float* router_w,
@@ -430,27 +620,87 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
   if (T == 0) return MOE_OK;
   if (!out) return set_error(MOE_ERR_INVALID_ARG, "cache_decode_layer: out is NULL");
   const int E = c->E, P = T * k;
+  const bool host_ok = c->policy != MOE_MISS_COPY;
   int rc = moe_route_permute(ctx, x, MOE_DTYPE_F32, router_w, bias, logits_in, T, c->H, E, k, logits_out, topk_ids,
                              topk_w, expert_offsets, sorted_pairs, pair_pos, active, nullptr, 0, compute_stream);
   if (rc) return rc;
-  hipStream_t cs = (hipStream_t)compute_stream;
+  hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
   hipError_t e = hipMemcpyAsync(c->h_ids, topk_ids, sizeof(int32_t) * P, hipMemcpyDeviceToHost, cs);
   if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync(ids)");
+  if (host_ok && (e = hipMemcpyAsync(c->h_x, x, sizeof(float) * (size_t)T * c->H, hipMemcpyDeviceToHost, cs)) !=
+                     hipSuccess)
+    return hip_error(e, "hipMemcpyAsync(x)");
   if ((e = hipEventRecord(c->ids_ready, cs)) != hipSuccess) return hip_error(e, "hipEventRecord(ids)");
   if ((e = hipEventSynchronize(c->ids_ready)) != hipSuccess) return hip_error(e, "hipEventSynchronize(ids)");
+  // the previous layer's copies have long finished: fold their rate in
+  if (c->timed_copies > 0 && hipEventQuery(c->copy_t1) == hipSuccess) {
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, c->copy_t0, c->copy_t1) == hipSuccess && ms > 0.0f)
+      update_rate(c->rate_pcie, c->timed_copies * (double)c->slot_bytes / (ms * 1e-3));
+    c->timed_copies = 0;
+  }
+  // which experts are missing, in the order the router named them
+  std::vector<int32_t> host_flag(E, 0), missing;
+  for (int i = 0; i < P; ++i) {
+    const int id = c->h_ids[i];
+    if (id < 0 || id >= E) return set_error(MOE_ERR_INVALID_ARG, "cache_decode_layer: routed id %d", id);
+    if (c->table[layer * E + id] < 0 && std::find(missing.begin(), missing.end(), id) == missing.end())
+      missing.push_back(id);
+  }
+  int n_host = 0;
+  if (c->policy == MOE_MISS_HOST) {
+    n_host = (int)missing.size();
+  } else if (c->policy == MOE_MISS_QSTAR) {
+    n_host = qstar_split(c, (int)missing.size());
+  } else if (c->policy == MOE_MISS_HOST_COPY) {
+    while (!c->inflight.empty() && hipEventQuery(c->copy_events[c->inflight.front()]) == hipSuccess)
+      c->inflight.pop_front();
+    const int room = std::max(0, kCopyBacklog - (int)c->inflight.size());
+    n_host = std::max(0, (int)missing.size() - room);  // host only: not inserted
+  }
+  c->last_host.assign(missing.end() - n_host, missing.end());
+  c->last_host_only = n_host;
+  for (int id : c->last_host) host_flag[id] = 1;
   std::vector<int32_t> slots(P), miss(P);
   int n_miss = 0;
-  if ((rc = cache_slot_table_lookup(c, layer, c->h_ids, P, slots.data(), miss.data(), &n_miss))) return rc;
-  // hit / miss masks; the previous call's upload has run (it precedes this
-  // call's routing on the same stream, which the host waited for)
-  std::fill(c->h_mask, c->h_mask + 2 * E, 0);
-  for (int i = 0; i < P; ++i) c->h_mask[c->h_ids[i]] = 1;
+  if ((rc = lookup_impl(c, layer, c->h_ids, P, host_ok ? host_flag.data() : nullptr, slots.data(), miss.data(),
+                        &n_miss)))
+    return rc;
+  c->last_copy.assign(miss.begin(), miss.begin() + n_miss);
+  const bool both = c->policy == MOE_MISS_HOST_COPY;
+  if (both) {
+    // the misses are computed here (those past the backlog only here, the
+    // others also copied for later); so is a hit whose copy has not landed
+    // yet (its slot may not be read before that)
+    c->last_host.insert(c->last_host.end(), c->last_copy.begin(), c->last_copy.end());
+    for (int i = 0; i < P; ++i) {
+      const int id = c->h_ids[i];
+      if (std::find(c->last_host.begin(), c->last_host.end(), id) != c->last_host.end()) continue;
+      const int slot = c->table[layer * E + id];
+      if (slot < 0) continue;
+      const int r = c->slot_ready[slot];
+      if (r < 0) continue;
+      if (hipEventQuery(c->copy_events[r]) == hipSuccess) c->slot_ready[slot] = -1;
+      else c->last_host.push_back(id);
+    }
+    n_host = (int)c->last_host.size();
+  }
+  c->n_copied += n_miss;
+  c->n_host += n_host;
+  // masks: resident experts, copied misses, host misses
+  int32_t* hm = c->h_mask;
+  std::fill(hm, hm + 3 * E, 0);
+  for (int i = 0; i < P; ++i) hm[c->h_ids[i]] = 1;
   for (int i = 0; i < n_miss; ++i) {
-    c->h_mask[miss[i]] = 0;
-    c->h_mask[E + miss[i]] = 1;
+    hm[miss[i]] = 0;
+    hm[E + miss[i]] = both ? 0 : 1;
+  }
+  for (int id : c->last_host) {
+    hm[id] = 0;
+    hm[2 * E + id] = 1;
   }
   bool any_hit = false;
-  for (int i = 0; i < P; ++i) any_hit |= c->h_mask[c->h_ids[i]] != 0;
+  for (int i = 0; i < P; ++i) any_hit |= hm[c->h_ids[i]] != 0;
   moe_ffn_args a{};
   a.pool_base = c->d_pool;
   a.slot_bytes = c->slot_bytes;
@@ -472,21 +722,78 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
   a.ws = ws;
   a.ws_bytes = ws_bytes;
   a.topk_w = topk_w;
-  if (n_miss == 0) {  // every expert resident: one call with the combine folded in
+  if (n_miss == 0 && n_host == 0) {  // every expert resident: one call with the combine folded in
     a.out = out;
     if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
     return cache_mark_layer_done(c, layer, compute_stream);
   }
-  if ((e = hipMemcpyAsync(c->d_mask, c->h_mask, sizeof(int32_t) * 2 * E, hipMemcpyHostToDevice, cs)) != hipSuccess)
+  if ((e = hipMemcpyAsync(c->d_mask, hm, sizeof(int32_t) * 3 * E, hipMemcpyHostToDevice, cs)) != hipSuccess)
     return hip_error(e, "hipMemcpyAsync(masks)");
   if (any_hit) {  // the resident experts run while the misses are copied
     a.expert_mask = c->d_mask;
     if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
   }
-  for (int i = 0; i < n_miss; ++i)
-    if ((rc = prefetch_expert(c, layer, miss[i], copy_stream, compute_stream, nullptr))) return rc;
-  a.expert_mask = c->d_mask + E;
-  if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
+  if (n_miss > 0 && both) {  // in the background: nothing on the compute stream waits for these
+    for (int i = 0; i < n_miss; ++i) {
+      const int key = layer * E + miss[i];
+      auto it = c->pending.find(key);
+      if (it == c->pending.end()) continue;
+      const moe_cache::Pending pd = it->second;
+      c->pending.erase(it);
+      if ((rc = issue_copy(c, key, pd, ps, cs, false))) return rc;
+      c->inflight.push_back(c->slot_ready[pd.slot]);
+    }
+  } else if (n_miss > 0) {
+    const bool timed = host_ok && c->timed_copies == 0;
+    if (timed) {  // the copies' own time: wait for the slots' readers first
+      for (int i = 0; i < n_miss; ++i) {
+        const auto it = c->pending.find(layer * E + miss[i]);
+        if (it == c->pending.end()) continue;
+        const int slot = it->second.slot;
+        if (c->slot_event[slot] >= 0 && (e = hipStreamWaitEvent(ps, c->events[c->slot_event[slot]], 0)) != hipSuccess)
+          return hip_error(e, "hipStreamWaitEvent(copy)");
+      }
+      if ((e = hipEventRecord(c->copy_t0, ps)) != hipSuccess) return hip_error(e, "hipEventRecord(copy start)");
+    }
+    for (int i = 0; i < n_miss; ++i)
+      if ((rc = prefetch_expert(c, layer, miss[i], copy_stream, compute_stream, nullptr))) return rc;
+    if (timed) {
+      if ((e = hipEventRecord(c->copy_t1, ps)) != hipSuccess) return hip_error(e, "hipEventRecord(copy end)");
+      c->timed_copies = n_miss;
+    }
+    a.expert_mask = c->d_mask + E;
+    if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
+  }
+  if (n_host > 0) {  // on the host cores while the GPU works through the above
+    std::vector<const uint8_t*> hs(n_host);
+    std::vector<std::vector<int>> tok(n_host), yrow(n_host);
+    for (int j = 0; j < n_host; ++j) hs[j] = c->h_pool + (size_t)(layer * E + c->last_host[j]) * c->slot_bytes;
+    for (int p = 0; p < P; ++p)
+      for (int j = 0; j < n_host; ++j)
+        if (c->h_ids[p] == c->last_host[j]) {
+          tok[j].push_back(p / k);
+          yrow[j].push_back(p);
+        }
+    std::vector<int> cnt(n_host);
+    std::vector<const int*> tp(n_host), yp(n_host);
+    for (int j = 0; j < n_host; ++j) {
+      cnt[j] = (int)tok[j].size();
+      tp[j] = tok[j].data();
+      yp[j] = yrow[j].data();
+    }
+    const double t0 = now_s();
+    if ((rc = host_experts_ffn(c->qtype, c->H, c->I, n_host, hs.data(), cnt.data(), tp.data(), yp.data(), c->h_x,
+                               c->h_y, c->h_scratch.data(), c->host_threads, true)))
+      return rc;
+    update_rate(c->rate_host, n_host * (double)c->slot_bytes / (now_s() - t0));
+    if ((e = hipMemcpyAsync(c->d_yh, c->h_y, sizeof(float) * (size_t)P * c->H, hipMemcpyHostToDevice, cs)) !=
+        hipSuccess)
+      return hip_error(e, "hipMemcpyAsync(host rows)");
+    const int H4 = c->H / 4;
+    launch(host_rows_kernel, dim3((H4 + 255) / 256, P), 256, 0, cs, (const float4*)c->d_yh,
+           (const int32_t*)(c->d_mask + 2 * E), (const int32_t*)topk_ids, (float4*)y_pairs, H4);
+    if ((rc = check_launch("host_rows_kernel"))) return rc;
+  }
   if ((rc = moe_combine(ctx, y_pairs, topk_w, T, k, c->H, out, compute_stream))) return rc;
   return cache_mark_layer_done(c, layer, compute_stream);
 }

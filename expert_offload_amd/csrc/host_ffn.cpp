@@ -1,0 +1,300 @@
+// Host executor of the expert FFN: the CPU side of CPU-GPU co-execution.
+//
+// On a cache miss the expert can either cross PCIe into VRAM or be computed
+// where it already is, on the host cores that can read it from system RAM
+// ("FreeToken Inference Engine: 3x Speed Boost for MoE Models", section
+// "Q* Strategy: Intelligently Choosing Where to Compute"; the fork README
+// names the CPU dot product as the part that needs AVX2/AVX-512).  This
+// file computes h = silu(Wg x) * (Wu x), y = Wd h for a few tokens straight
+// from the pinned host pool, in the same slot layout the GPU reads: rows of
+// 256-weight groups, each group the quant bytes of 8 ggml blocks followed
+// by their 8 fp16 scales.  x and y are fp32; every dot product accumulates
+// in fp32.
+//
+// The rows of one call are split over a small pool of worker threads; the
+// inner loops use AVX-512 when the CPU has it (checked at run time) and
+// plain C++ otherwise.
+#include <immintrin.h>
+
+#include <atomic>
+#include <cmath>
+#include <condition_variable>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+float half_to_float(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t ex = (h >> 10) & 0x1Fu, man = h & 0x3FFu;
+  uint32_t bits;
+  if (ex == 0) {
+    if (man == 0) {
+      bits = sign;
+    } else {  // subnormal: normalise
+      int e = -1;
+      uint32_t m = man;
+      do {
+        m <<= 1;
+        ++e;
+      } while (!(m & 0x400u));
+      bits = sign | ((uint32_t)(127 - 15 - e) << 23) | ((m & 0x3FFu) << 13);
+    }
+  } else if (ex == 31) {
+    bits = sign | 0x7F800000u | (man << 13);
+  } else {
+    bits = sign | ((ex - 15 + 127) << 23) | (man << 13);
+  }
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return f;
+}
+
+// ---------------------------------------------------------------- row dots
+// sum_k w_k x_k over one row of `cols` weights (cols % 256 == 0).
+template <int QT>
+float row_dot_scalar(const uint8_t* row, const float* x, int cols) {
+  constexpr int qb = QT == MOE_QTYPE_Q8_0 ? 32 : 16;
+  float acc = 0.0f;
+  for (int g = 0; g < cols / kGroupWeights; ++g) {
+    const uint8_t* grp = row + (size_t)g * group_bytes(QT);
+    const uint8_t* sc = grp + kGroupBlocks * qb;
+    for (int b = 0; b < kGroupBlocks; ++b) {
+      uint16_t hs;
+      std::memcpy(&hs, sc + 2 * b, 2);
+      const float d = half_to_float(hs);
+      const uint8_t* q = grp + b * qb;
+      const float* xb = x + g * kGroupWeights + b * kQK;
+      float s = 0.0f;
+      if constexpr (QT == MOE_QTYPE_Q8_0) {
+        for (int j = 0; j < 32; ++j) s += (float)(int8_t)q[j] * xb[j];
+      } else {
+        for (int j = 0; j < 16; ++j) {
+          s += (float)((int)(q[j] & 0x0F) - 8) * xb[j];
+          s += (float)((int)(q[j] >> 4) - 8) * xb[j + 16];
+        }
+      }
+      acc += d * s;
+    }
+  }
+  return acc;
+}
+
+template <int QT>
+__attribute__((target("avx512f,avx512bw,avx512vl,f16c"))) float row_dot_avx512(const uint8_t* row, const float* x,
+                                                                               int cols) {
+  constexpr int qb = QT == MOE_QTYPE_Q8_0 ? 32 : 16;
+  __m512 acc = _mm512_setzero_ps();
+  for (int g = 0; g < cols / kGroupWeights; ++g) {
+    const uint8_t* grp = row + (size_t)g * group_bytes(QT);
+    const __m256 d8 = _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i*>(grp + kGroupBlocks * qb)));
+    alignas(32) float d[8];
+    _mm256_store_ps(d, d8);
+    const float* xg = x + g * kGroupWeights;
+#pragma GCC unroll 8
+    for (int b = 0; b < kGroupBlocks; ++b) {
+      const uint8_t* q = grp + b * qb;
+      const float* xb = xg + b * kQK;
+      __m512 lo, hi;
+      if constexpr (QT == MOE_QTYPE_Q8_0) {
+        lo = _mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(q))));
+        hi = _mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(q + 16))));
+      } else {
+        const __m512i u = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(q)));
+        const __m512i eight = _mm512_set1_epi32(8);
+        lo = _mm512_cvtepi32_ps(_mm512_sub_epi32(_mm512_and_si512(u, _mm512_set1_epi32(0x0F)), eight));
+        hi = _mm512_cvtepi32_ps(_mm512_sub_epi32(_mm512_srli_epi32(u, 4), eight));
+      }
+      __m512 s = _mm512_mul_ps(lo, _mm512_loadu_ps(xb));
+      s = _mm512_fmadd_ps(hi, _mm512_loadu_ps(xb + 16), s);
+      acc = _mm512_fmadd_ps(_mm512_set1_ps(d[b]), s, acc);
+    }
+  }
+  return _mm512_reduce_add_ps(acc);
+}
+
+using RowDot = float (*)(const uint8_t*, const float*, int);
+
+bool has_avx512() {
+  static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                         __builtin_cpu_supports("avx512vl") && __builtin_cpu_supports("f16c");
+  return ok;
+}
+
+RowDot row_dot_for(int qtype, bool vector) {
+  if (qtype == MOE_QTYPE_Q8_0) return vector ? row_dot_avx512<MOE_QTYPE_Q8_0> : row_dot_scalar<MOE_QTYPE_Q8_0>;
+  return vector ? row_dot_avx512<MOE_QTYPE_Q4_0> : row_dot_scalar<MOE_QTYPE_Q4_0>;
+}
+
+// ---------------------------------------------------------------- threads
+// Fork-join pool: run(n, fn) calls fn(0..n-1) spread over the workers and
+// the calling thread and returns when all calls are done.  Idle workers
+// spin briefly (a layer's two phases follow each other within
+// microseconds), then sleep.
+class HostPool {
+ public:
+  explicit HostPool(int workers) {
+    for (int i = 0; i < workers; ++i) threads_.emplace_back([this] { loop(); });
+  }
+  ~HostPool() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+      gen_.fetch_add(1);
+    }
+    cv_.notify_all();
+    for (auto& t : threads_) t.join();
+  }
+  int size() const { return (int)threads_.size() + 1; }
+
+  void run(int n, const std::function<void(int)>& fn) {
+    if (n <= 0) return;
+    if (threads_.empty() || n == 1) {
+      for (int i = 0; i < n; ++i) fn(i);
+      return;
+    }
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      fn_ = &fn;
+      n_ = n;
+      next_.store(0);
+      busy_.store((int)threads_.size());
+      gen_.fetch_add(1);
+    }
+    cv_.notify_all();
+    work();
+    while (busy_.load(std::memory_order_acquire) > 0) _mm_pause();
+    fn_ = nullptr;
+  }
+
+ private:
+  void work() {
+    for (int i = next_.fetch_add(1); i < n_; i = next_.fetch_add(1)) (*fn_)(i);
+  }
+  void loop() {
+    uint64_t seen = 0;  // the generation at construction: a run() may come before this thread starts
+    for (;;) {
+      int spins = 0;
+      while (gen_.load(std::memory_order_acquire) == seen && spins < (1 << 14)) {
+        _mm_pause();
+        ++spins;
+      }
+      if (gen_.load(std::memory_order_acquire) == seen) {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_.wait(lk, [&] { return gen_.load() != seen; });
+      }
+      seen = gen_.load();
+      if (stop_) return;
+      work();
+      busy_.fetch_sub(1, std::memory_order_release);
+    }
+  }
+  std::vector<std::thread> threads_;
+  std::mutex mu_;
+  std::condition_variable cv_;
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<int> next_{0}, busy_{0};
+  const std::function<void(int)>* fn_ = nullptr;
+  int n_ = 0;
+  bool stop_ = false;
+};
+
+// One pool per process; calls are serialised (g_exec_mu is held for a whole
+// host_experts_ffn), so the pool is never resized while it runs.
+std::mutex g_exec_mu;
+HostPool* g_pool = nullptr;
+int g_pool_threads = 0;
+
+HostPool* pool_for(int threads) {
+  if (!g_pool || g_pool_threads != threads) {
+    delete g_pool;
+    g_pool = new HostPool(threads - 1);
+    g_pool_threads = threads;
+  }
+  return g_pool;
+}
+
+constexpr int kRowChunk = 64;  // rows per task
+
+}  // namespace
+
+// All hardware threads but four, left to the GPU runtime and the calling
+// thread's own launches (with every core busy the layer loop slowed down
+// by up to a third on a 16-core host).
+int default_host_threads() {
+  const int n = (int)std::min(std::thread::hardware_concurrency(), 64u);
+  return n <= 1 ? 1 : n <= 8 ? std::max(1, n / 2) : n - 4;
+}
+
+// n_exp experts, expert i at slots[i] (host), over tokens tok[i][0..cnt[i])
+// of x [*, H]; writes y rows yrow[i][j] (row index into y [*, H]) .  h is
+// scratch of sum(cnt) * I floats.
+int host_experts_ffn(int qtype, int H, int I, int n_exp, const uint8_t* const* slots, const int* cnt,
+                     const int* const* tok, const int* const* yrow, const float* x, float* y, float* h,
+                     int threads, bool vector) {
+  std::lock_guard<std::mutex> lk(g_exec_mu);
+  HostPool* pool = pool_for(std::max(1, threads));
+  const RowDot dot = row_dot_for(qtype, vector && has_avx512());
+  std::vector<int> hbase(n_exp + 1, 0);
+  for (int i = 0; i < n_exp; ++i) hbase[i + 1] = hbase[i] + cnt[i];
+  const int ci = (I + kRowChunk - 1) / kRowChunk, ch = (H + kRowChunk - 1) / kRowChunk;
+  const size_t gate = slot_gate_off(qtype, H, I), up = slot_up_off(qtype, H, I), down = slot_down_off(qtype, H, I);
+  const size_t rb_h = row_bytes(qtype, H), rb_i = row_bytes(qtype, I);
+  pool->run(n_exp * ci, [&](int task) {
+    const int e = task / ci, r0 = (task % ci) * kRowChunk, r1 = std::min(I, r0 + kRowChunk);
+    for (int r = r0; r < r1; ++r) {
+      const uint8_t* gr = slots[e] + gate + (size_t)r * rb_h;
+      const uint8_t* ur = slots[e] + up + (size_t)r * rb_h;
+      for (int j = 0; j < cnt[e]; ++j) {
+        const float* xt = x + (size_t)tok[e][j] * H;
+        const float g = dot(gr, xt, H), u = dot(ur, xt, H);
+        h[(size_t)(hbase[e] + j) * I + r] = g / (1.0f + std::exp(-g)) * u;
+      }
+    }
+  });
+  pool->run(n_exp * ch, [&](int task) {
+    const int e = task / ch, r0 = (task % ch) * kRowChunk, r1 = std::min(H, r0 + kRowChunk);
+    for (int r = r0; r < r1; ++r) {
+      const uint8_t* dr = slots[e] + down + (size_t)r * rb_i;
+      for (int j = 0; j < cnt[e]; ++j)
+        y[(size_t)yrow[e][j] * H + r] = dot(dr, h + (size_t)(hbase[e] + j) * I, I);
+    }
+  });
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_host_expert_ffn(int qtype, int H, int I, const void* slot, const float* x, int n, float* y, int threads,
+                        int vector) {
+  clear_error();
+  if (!qtype_supported(qtype))
+    return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "moe_host_expert_ffn: block type %d is not supported", qtype);
+  if (H <= 0 || I <= 0 || H % kGroupWeights || I % kGroupWeights)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_host_expert_ffn: H=%d I=%d must be multiples of %d", H, I,
+                     kGroupWeights);
+  if (n < 0 || threads < 0) return set_error(MOE_ERR_INVALID_ARG, "moe_host_expert_ffn: n=%d threads=%d", n, threads);
+  if (n == 0) return MOE_OK;
+  if (!slot || !x || !y) return set_error(MOE_ERR_INVALID_ARG, "moe_host_expert_ffn: NULL slot, x or y");
+  std::vector<int> tok(n);
+  for (int i = 0; i < n; ++i) tok[i] = i;
+  std::vector<float> h((size_t)n * I);
+  const uint8_t* s = (const uint8_t*)slot;
+  const int* tp = tok.data();
+  return host_experts_ffn(qtype, H, I, 1, &s, &n, &tp, &tp, x, y, h.data(),
+                          threads == 0 ? default_host_threads() : threads, vector != 0);
+}
+
+int moe_host_has_avx512(void) { return has_avx512() ? 1 : 0; }
+
+}  // extern "C"

@@ -113,4 +113,14 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 
+// ------------------------------------------------------------ host executor
+// The expert FFN on the host cores (host_ffn.cpp): n_exp experts, expert i
+// in the slot at slots[i] (host memory), over the tokens tok[i][0..cnt[i])
+// of x [*][H]; the output of its j-th token goes to row yrow[i][j] of
+// y [*][H].  h: scratch of sum(cnt) * I floats.  Calls are serialised.
+int host_experts_ffn(int qtype, int H, int I, int n_exp, const uint8_t* const* slots, const int* cnt,
+                     const int* const* tok, const int* const* yrow, const float* x, float* y, float* h,
+                     int threads, bool vector);
+int default_host_threads();
+
 }  // namespace moe

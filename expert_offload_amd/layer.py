@@ -203,6 +203,18 @@ class CachedLayers:
             self.d_pool = pool
         self.n_slots = n_slots
 
+    def set_miss_policy(self, policy: int, host_threads: int = 0) -> None:
+        """L.MISS_COPY, L.MISS_HOST or L.MISS_QSTAR for the native layer path."""
+        L.cache_set_miss_policy(self.cache, policy, host_threads)
+
+    def last_misses(self):
+        """(copied ids, host ids, number of host ids left out of the cache)
+        of the last native layer call."""
+        return L.cache_last_misses(self.cache)
+
+    def miss_stats(self):
+        return L.cache_miss_stats(self.cache)
+
     def stats(self):
         return L.cache_slot_table_stats(self.cache)
 

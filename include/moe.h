@@ -72,6 +72,13 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  * types": separate decode and prefill kernels per block type). */
 enum { MOE_MODE_DECODE = 0, MOE_MODE_PREFILL = 1 };
 
+/* What cache_decode_layer does with an expert that is not in VRAM:
+ * MOE_MISS_COPY copies it in (it becomes resident); MOE_MISS_HOST computes
+ * its FFN on the host cores from the pinned pool (it stays out of the
+ * cache); MOE_MISS_QSTAR splits each layer's misses between the two;
+ * MOE_MISS_HOST_COPY computes it on the host and copies it in behind. */
+enum { MOE_MISS_COPY = 0, MOE_MISS_HOST = 1, MOE_MISS_QSTAR = 2, MOE_MISS_HOST_COPY = 3 };
+
 typedef struct moe_ctx moe_ctx;
 typedef struct moe_cache moe_cache;
 
@@ -381,6 +388,72 @@ int prefill_stream_layer(moe_prefill_stream* s, moe_ctx* ctx, int layer,
 int prefill_stream_stats(moe_prefill_stream* s, int64_t* loads,
                          int64_t* demand_loads);
 int prefill_stream_destroy(moe_prefill_stream* s);
+
+/* ------------------------------------------------------ host executor
+ * moe_host_expert_ffn: the expert FFN of n tokens computed on the host
+ * cores, reading one expert where it already is, in pinned host memory
+ * ("FreeToken Inference Engine: 3x Speed Boost for MoE Models", "Q*
+ * Strategy: Intelligently Choosing Where to Compute": a missing expert is
+ * either moved to the GPU or computed on the CPU).  slot: host, one expert
+ * in the device slot layout (moe_pack_expert); x: host fp32 [n][H]; y: host
+ * fp32 [n][H], written.  h = silu(Wg x) * (Wu x) and y = Wd h accumulate
+ * in fp32.  threads: worker threads including the caller (0 = all
+ * hardware threads but four, at least one); vector: 1 uses AVX-512 when
+ * the CPU has it, 0 plain C++.  Errors: MOE_ERR_UNSUPPORTED_QTYPE,
+ * MOE_ERR_INVALID_ARG.
+ * moe_host_has_avx512: 1 when the AVX-512 path is available. */
+int moe_host_expert_ffn(int qtype, int H, int I, const void* slot,
+                        const float* x, int n, float* y, int threads,
+                        int vector);
+int moe_host_has_avx512(void);
+
+/* ------------------------------------------- misses on the host (Q*)
+ * On a miss FreeToken either moves the expert to the GPU or computes it on
+ * the CPU, choosing per batch of missing experts from the measured PCIe
+ * bandwidth and RAM speed ("FreeToken Inference Engine: 3x Speed Boost for
+ * MoE Models", "Q* Strategy: Intelligently Choosing Where to Compute").
+ *
+ * cache_set_miss_policy: the policy of later cache_decode_layer calls
+ * (MOE_MISS_*; default MOE_MISS_COPY) and the host threads of the host
+ * executor, caller included (0 = all hardware threads but four, at
+ * least one).  The first policy
+ * other than MOE_MISS_COPY allocates the staging it needs (pinned and
+ * device, kCtlStagePairs = 1024 rows of H floats each, and host scratch);
+ * MOE_MISS_QSTAR first measures both rates (a few expert-sized copies and
+ * host FFNs).  Calling it between layers is allowed.
+ *
+ * In cache_decode_layer, for each layer: the missing experts are found in
+ * the order the router named them; MOE_MISS_HOST sends all to the host,
+ * MOE_MISS_QSTAR sends the last m, where m minimises
+ * max((n - m) B / r_copy, m B / r_host + 20 us) (n missing experts of B
+ * bytes; r_copy and r_host running estimates of the copy and host
+ * executor rates, updated every layer), the fewest on a tie.  A host
+ * expert is not inserted into the cache (its lookup is a miss and changes
+ * nothing); the layer's tokens are read back, the host computes its rows
+ * while the GPU runs the resident and copied experts, and the rows are
+ * copied back into y_pairs before the combine.
+ *
+ * MOE_MISS_HOST_COPY (not on the pages; it keeps the cache learning while
+ * the host takes the misses): this layer computes every missing expert on
+ * the host; the first ones (router order), up to 8 background copies in
+ * flight, are also inserted and copied as with MOE_MISS_COPY, but on
+ * copy_stream only, with nothing on compute_stream waiting for them; the
+ * rest are left out of the cache as with MOE_MISS_HOST.  A later hit on an
+ * expert whose copy has not completed (its event, checked on the host at
+ * lookup) is computed on the host as well.  Use one copy_stream per cache.
+ *
+ * cache_miss_stats: experts copied and computed on the host so far, and
+ * the current rate estimates (GB/s; 0 before any measurement).
+ * cache_last_misses: the experts the last cache_decode_layer copied and
+ * computed on the host (arrays of at least E entries, may be NULL); the
+ * first *n_host_only (may be NULL) host experts were misses left out of
+ * the cache, the others (MOE_MISS_HOST_COPY) were also copied or are
+ * resident with their copy still in flight. */
+int cache_set_miss_policy(moe_cache* c, int policy, int host_threads);
+int cache_miss_stats(moe_cache* c, int64_t* copied, int64_t* host,
+                     double* pcie_gbs, double* host_gbs);
+int cache_last_misses(moe_cache* c, int32_t* copy_ids, int* n_copy,
+                      int32_t* host_ids, int* n_host, int* n_host_only);
 
 /* ------------------------------------------------------- bank type check
  * One block type for every expert bank: the slot pool is one allocation

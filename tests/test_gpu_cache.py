@@ -331,3 +331,113 @@ def test_cached_layers_resize_outputs(ctx):
     note(f"   cached layers with resizes: worst max rel err {worst:.2e}")
     assert worst <= 1e-3
     cl.close()
+
+
+def _run_policies(ctx, wl, pool, blocks, n_slots, plan, steps):
+    """Native cached layers under a per-step miss policy; returns the
+    per-(step, layer) host and copied ids, misses and the worst output
+    error against the oracle."""
+    raw = gi.cache_trace(wl)
+    trace = lookup_order(wl, raw)
+    cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, n_slots, pool)
+    host, copied, computed, worst = {}, {}, {}, 0.0
+    for st in range(steps):
+        if st in plan:
+            cl.set_miss_policy(plan[st], host_threads=4)
+        x = gi.activations(wl, 1, st)
+        lg = gi.cache_trace_logits(wl, raw, st)
+        xd = dev(x)
+        for l in range(wl.layers):
+            out = cl.layer(l, xd, dev(lg[l:l + 1])).cpu().numpy()
+            moe.moe_ctx_check(ctx)
+            cp, hs, n_only = cl.last_misses()
+            host[(st, l)], copied[(st, l)] = set(hs[:n_only].tolist()), cp.tolist()
+            computed[(st, l)] = set(hs.tolist())
+            ref = oracle.moe_layer(x, wl.qtype, lambda e: blocks[(l, e)], wl.k, logits=lg[l:l + 1])
+            worst = max(worst, max_rel_err(out, ref["out"]))
+    misses = np.array(cl.misses_per_layer).reshape(steps, wl.layers)
+    stats = cl.miss_stats()
+    cl.close()
+    return trace[:steps], host, copied, computed, misses, worst, stats
+
+
+def test_miss_policies_match_oracle(ctx):
+    """Copy, host and Q* policies in turn: layer outputs stay within the
+    decode tolerance of the oracle, and the cache follows the oracle's LRU
+    given the experts the library computed on the host (misses per layer,
+    and the copied experts in router order)."""
+    wl = SMALL
+    pool, blocks = host_pool(wl)
+    plan = {0: L.MISS_COPY, 8: L.MISS_HOST, 16: L.MISS_QSTAR, 24: L.MISS_COPY}
+    trace, host, copied, computed, misses, worst, stats = _run_policies(ctx, wl, pool, blocks, 8, plan, 30)
+    note(f"   policies: worst max rel err {worst:.2e}; copied {stats[0]}, host {stats[1]}, "
+         f"rates {stats[2]:.1f} / {stats[3]:.1f} GB/s")
+    assert worst <= 1e-3
+    assert stats[1] > 0 and stats[0] > 0
+    assert all(not host[(s, l)] for s in range(8) for l in range(wl.layers))
+    want, _ = oracle.lru_simulate(trace, 8, host=host)
+    np.testing.assert_array_equal(misses, (~want).sum(axis=2))
+    for (s, l), cp in copied.items():
+        order = []
+        for j in range(wl.k):
+            e = int(trace[s, l, j])
+            if not want[s, l, j] and e not in host[(s, l)] and e not in order:
+                order.append(e)
+        assert cp == order, (s, l)
+    for s in range(8, 16):  # the host policy copies nothing
+        assert all(not copied[(s, l)] for l in range(wl.layers))
+
+
+def test_host_policy_full_size_sampled(ctx):
+    """The expert-cache workload's shape (hidden 4096, intermediate 2048,
+    Q4_0) with every miss on the host for a few steps: outputs within the
+    decode tolerance of the oracle."""
+    wl = gi.workload("cache_q4_0_h4096_e256")
+    wl = gi.Workload(wl.index, wl.name, H=wl.H, E=wl.E, k=wl.k, I=wl.I, qtype=wl.qtype, batches=(1,), layers=1,
+                     router="trace", cache_fraction=wl.cache_fraction, steps=4, trace_keep_p=wl.trace_keep_p,
+                     trace_zipf_s=wl.trace_zipf_s)
+    trace = gi.cache_trace(wl, 4)
+    need = sorted({(0, int(e)) for e in trace.reshape(-1)})
+    sb = moe.moe_slot_bytes(L.QTYPE[wl.qtype], wl.H, wl.I)
+    pool = torch.zeros(wl.E * sb, dtype=torch.uint8, pin_memory=True)
+    view = pool.numpy()
+    blocks = {}
+
+    def put(l, e, b):
+        blocks[(l, e)] = b
+        view[e * sb:(e + 1) * sb] = layer.pack_expert(wl.qtype, wl.H, wl.I, *b)
+
+    gi.generate_blocks_parallel(wl, need, put)
+    cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, 1, 16, pool)
+    cl.set_miss_policy(L.MISS_HOST)
+    worst = 0.0
+    for st in range(4):
+        x = gi.activations(wl, 1, st)
+        lg = gi.cache_trace_logits(wl, trace, st)
+        out = cl.layer(0, dev(x), dev(lg[0:1])).cpu().numpy()
+        moe.moe_ctx_check(ctx)
+        ref = oracle.moe_layer(x, wl.qtype, lambda e: blocks[(0, e)], wl.k, logits=lg[0:1])
+        worst = max(worst, max_rel_err(out, ref["out"]))
+    assert cl.miss_stats()[1] == cl.stats()[1] > 0
+    note(f"   host policy at full size: worst max rel err {worst:.2e}")
+    assert worst <= 1e-3
+    cl.close()
+
+
+def test_host_copy_policy_keeps_the_lru(ctx):
+    """Misses computed on the host while their copies run behind: the cache
+    follows the plain LRU (every miss inserted), every copied expert was
+    also computed on the host, and outputs stay within the decode tolerance
+    of the oracle."""
+    wl = SMALL
+    pool, blocks = host_pool(wl)
+    trace, host, copied, computed, misses, worst, stats = _run_policies(ctx, wl, pool, blocks, 8,
+                                                                        {0: L.MISS_HOST_COPY}, 30)
+    note(f"   host+copy: worst max rel err {worst:.2e}; copied {stats[0]}, host {stats[1]}, "
+         f"left out {sum(len(h) for h in host.values())}")
+    assert worst <= 1e-3
+    want, _ = oracle.lru_simulate(trace, 8, host=host)
+    np.testing.assert_array_equal(misses, (~want).sum(axis=2))
+    for key, cp in copied.items():
+        assert set(cp) <= computed[key] and not (set(cp) & host[key])
+    assert stats[1] >= stats[0] > 0
