@@ -17,6 +17,17 @@ consecutive weights along the input dimension of a weight row:
   holds element ``j`` in its low nibble and element ``j + 16`` in its high
   nibble.  Quantiser: ``m`` = signed element of largest magnitude (first on
   ties), ``d = m / -8``, ``q = min(15, floor(w / d + 8.5))``.
+* Q4_1: fp16 ``d``, fp16 ``m`` then 16 B of nibbles (as Q4_0) -> 20 B;
+  ``w = d q + m``.  Quantiser: ``m = min``, ``d = (max - min) / 15``,
+  ``q = min(15, floor((w - m) / d + 0.5))``.
+* Q5_0: fp16 ``d``, 4 B of fifth bits (bit ``j`` of the little-endian word
+  for element ``j``), 16 B of nibbles -> 22 B; ``w = d (q - 16)``.
+  Quantiser as Q4_0 with 16 for 8 and 31 for 15.
+* Q5_1: fp16 ``d``, fp16 ``m``, 4 B of fifth bits, 16 B of nibbles -> 24 B;
+  ``w = d q + m``.  Quantiser as Q4_1 with 31 for 15.
+
+The quantisers only make input bytes; both the GPU library and the oracle
+decode the same bytes.
 
 Matrix orientation: every weight matrix is ``[out_rows][in_cols / 32]``
 blocks; per expert the tensors are gate ``[I][H]``, up ``[I][H]`` and
@@ -34,7 +45,8 @@ import numpy as np
 
 __all__ = [
     "QK", "BLOCK_BYTES", "KIND", "Workload", "WORKLOADS", "workload",
-    "rng_for", "quantize_q8_0", "quantize_q4_0", "expert_weights_f32",
+    "rng_for", "quantize_q8_0", "quantize_q4_0", "quantize_q4_1", "quantize_q5_0",
+    "quantize_q5_1", "expert_weights_f32",
     "expert_blocks", "router_weight", "router_bias", "activations",
     "given_logits", "slot_permutation", "zipf_cdf", "cache_trace",
     "cache_trace_logits", "f32_to_bf16_bits", "bf16_bits_to_f32",
@@ -42,7 +54,7 @@ __all__ = [
 ]
 
 QK = 32
-BLOCK_BYTES = {"q8_0": 34, "q4_0": 18}
+BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24}
 
 # substream "kind" field
 KIND = {
@@ -174,7 +186,82 @@ def quantize_q4_0(w: np.ndarray) -> np.ndarray:
     return out
 
 
-_QUANT = {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0}
+def _fp16_bytes(v: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(v.astype(np.float16)).view(np.uint8).reshape(*v.shape, 2)
+
+
+def _pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """codes [..., 32] (0..15 after masking) -> 16 bytes: j low, j + 16 high."""
+    q = q.astype(np.uint8) & 0x0F
+    return q[..., :16] | (q[..., 16:] << 4)
+
+
+def _pack_fifth_bits(q: np.ndarray) -> np.ndarray:
+    """codes [..., 32] in 0..31 -> 4 bytes: bit j of the little-endian word is bit 4 of code j."""
+    bits = (q.astype(np.uint32) >> 4) & 1
+    word = (bits << np.arange(32, dtype=np.uint32)).sum(axis=-1, dtype=np.uint64).astype("<u4")
+    return np.ascontiguousarray(word).view(np.uint8).reshape(*q.shape[:-1], 4)
+
+
+def _affine_codes(b: np.ndarray, top: int):
+    """min / max quantiser: m = min, d = (max - min) / top, q = min(top, floor((w - m) / d + 0.5))."""
+    mn = b.min(axis=2)
+    d = ((b.max(axis=2) - mn) / np.float32(top)).astype(np.float32)
+    nz = d != 0
+    inv = np.zeros_like(d)
+    inv[nz] = np.float32(1.0) / d[nz]
+    t = ((b - mn[..., None]) * inv[..., None] + np.float32(0.5)).astype(np.float32)
+    q = np.minimum(np.trunc(t), top).astype(np.uint8)
+    return d, mn, q
+
+
+def quantize_q4_1(w: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K] -> uint8 [rows, K/32, 20] ggml Q4_1 blocks."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    d, mn, q = _affine_codes(w.reshape(rows, K // QK, QK), 15)
+    out = np.empty((rows, K // QK, 20), dtype=np.uint8)
+    out[..., 0:2] = _fp16_bytes(d)
+    out[..., 2:4] = _fp16_bytes(mn)
+    out[..., 4:] = _pack_nibbles(q)
+    return out
+
+
+def quantize_q5_0(w: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K] -> uint8 [rows, K/32, 22] ggml Q5_0 blocks."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    b = w.reshape(rows, K // QK, QK)
+    idx = np.abs(b).argmax(axis=2)
+    m = np.take_along_axis(b, idx[..., None], axis=2)[..., 0]
+    d = (m / np.float32(-16.0)).astype(np.float32)
+    nz = d != 0
+    inv = np.zeros_like(d)
+    inv[nz] = np.float32(1.0) / d[nz]
+    t = (b * inv[..., None] + np.float32(16.5)).astype(np.float32)
+    q = np.minimum(np.trunc(t), 31).astype(np.uint8)
+    out = np.empty((rows, K // QK, 22), dtype=np.uint8)
+    out[..., 0:2] = _fp16_bytes(d)
+    out[..., 2:6] = _pack_fifth_bits(q)
+    out[..., 6:] = _pack_nibbles(q)
+    return out
+
+
+def quantize_q5_1(w: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K] -> uint8 [rows, K/32, 24] ggml Q5_1 blocks."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    d, mn, q = _affine_codes(w.reshape(rows, K // QK, QK), 31)
+    out = np.empty((rows, K // QK, 24), dtype=np.uint8)
+    out[..., 0:2] = _fp16_bytes(d)
+    out[..., 2:4] = _fp16_bytes(mn)
+    out[..., 4:8] = _pack_fifth_bits(q)
+    out[..., 8:] = _pack_nibbles(q)
+    return out
+
+
+_QUANT = {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0, "q4_1": quantize_q4_1, "q5_0": quantize_q5_0,
+          "q5_1": quantize_q5_1}
 
 
 # --------------------------------------------------------------------------

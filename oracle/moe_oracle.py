@@ -11,8 +11,9 @@ pool in host memory and uses VRAM as an expert cache
 ("FreeToken github moe: Setup Guide & MoE Runtime Comparison", introduction;
 "FreeToken Inference Engine: 3x Speed Boost for MoE Models", section "From
 Static Allocation to Dynamic Scheduling").  The expert banks are ggml
-Q4_0 / Q8_0 blocks held in one slot pool of one type (FreeToken fork README,
-sections "Quant types" and "Known limits").  Each token activates only a
+blocks of the standard types (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0) held in one
+slot pool of one type (FreeToken fork README, sections "Quant types" and
+"Known limits").  Each token activates only a
 subset of the experts (setup guide, introduction).  The steps below are the
 plainest reading of that layer: softmax over expert logits, keep the k
 largest (ties to the lower expert id), renormalise the kept probabilities,
@@ -34,11 +35,12 @@ from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-QK = 32  # weights per block, both formats
+QK = 32  # weights per block, every format here
 
 
 # --------------------------------------------------------------------------
-# 1. block dequantisation (ggml Q8_0 / Q4_0; FreeToken fork README, "Quant types")
+# 1. block dequantisation (ggml Q8_0 / Q4_0 / Q4_1 / Q5_0 / Q5_1; FreeToken fork
+#    README, "Quant types": the standard ggml types)
 # --------------------------------------------------------------------------
 def _block_scale(blocks: np.ndarray) -> np.ndarray:
     """fp16 little-endian scale in bytes 0..1 of every block, as float64."""
@@ -66,12 +68,58 @@ def dequant_q4_0(blocks: np.ndarray) -> np.ndarray:
     return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK)
 
 
+def _half(blocks: np.ndarray, at: int) -> np.ndarray:
+    """fp16 little-endian in bytes at..at+1 of every block, as float64."""
+    return np.ascontiguousarray(blocks[..., at:at + 2]).view(np.float16)[..., 0].astype(np.float64)
+
+
+def _nibbles(qs: np.ndarray) -> np.ndarray:
+    """16 bytes -> 32 codes: element j in the low nibble of byte j, element
+    j + 16 in its high nibble."""
+    return np.concatenate([qs & 0x0F, qs >> 4], axis=-1).astype(np.int64)
+
+
+def _high_bits(qh: np.ndarray) -> np.ndarray:
+    """4 bytes read as a little-endian uint32 -> 32 bits, bit j for element j."""
+    word = np.ascontiguousarray(qh).view("<u4")[..., 0].astype(np.int64)
+    return (word[..., None] >> np.arange(32)) & 1
+
+
+def dequant_q4_1(blocks: np.ndarray) -> np.ndarray:
+    """uint8 [..., nblk, 20] -> float64; d (fp16), m (fp16), 16 nibble bytes:
+    w = d * q + m with q in 0..15."""
+    d, m = _half(blocks, 0), _half(blocks, 2)
+    q = _nibbles(blocks[..., 4:20]).astype(np.float64)
+    w = d[..., None] * q + m[..., None]
+    return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK)
+
+
+def dequant_q5_0(blocks: np.ndarray) -> np.ndarray:
+    """uint8 [..., nblk, 22] -> float64; d (fp16), 4 bytes of fifth bits,
+    16 nibble bytes: q = nibble + 16 * bit in 0..31, w = d * (q - 16)."""
+    d = _half(blocks, 0)
+    q = _nibbles(blocks[..., 6:22]) + 16 * _high_bits(blocks[..., 2:6])
+    w = d[..., None] * (q.astype(np.float64) - 16.0)
+    return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK)
+
+
+def dequant_q5_1(blocks: np.ndarray) -> np.ndarray:
+    """uint8 [..., nblk, 24] -> float64; d, m (fp16), 4 bytes of fifth bits,
+    16 nibble bytes: q = nibble + 16 * bit in 0..31, w = d * q + m."""
+    d, m = _half(blocks, 0), _half(blocks, 2)
+    q = _nibbles(blocks[..., 8:24]) + 16 * _high_bits(blocks[..., 4:8])
+    w = d[..., None] * q.astype(np.float64) + m[..., None]
+    return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK)
+
+
+_DEQUANT = {"q8_0": dequant_q8_0, "q4_0": dequant_q4_0, "q4_1": dequant_q4_1, "q5_0": dequant_q5_0,
+            "q5_1": dequant_q5_1}
+
+
 def dequant(qtype: str, blocks: np.ndarray) -> np.ndarray:
-    if qtype == "q8_0":
-        return dequant_q8_0(blocks)
-    if qtype == "q4_0":
-        return dequant_q4_0(blocks)
-    raise ValueError(f"unsupported block type {qtype!r}")
+    if qtype not in _DEQUANT:
+        raise ValueError(f"unsupported block type {qtype!r}")
+    return _DEQUANT[qtype](blocks)
 
 
 # --------------------------------------------------------------------------

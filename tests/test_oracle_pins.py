@@ -42,6 +42,43 @@ def build_block(qtype: str, d_bits: int, codes) -> np.ndarray:
     return np.array([d_bits & 0xFF, d_bits >> 8] + body, dtype=np.uint8)
 
 
+GOLDEN_AFFINE = os.path.join(os.path.dirname(__file__), "golden", "hand_blocks_affine.txt")
+
+
+def build_block_affine(qtype: str, d_bits: int, m_bits: int, codes) -> np.ndarray:
+    """Pack one Q4_1 / Q5_0 / Q5_1 block by hand from the format description."""
+    codes = list(codes)
+    assert len(codes) == 32
+    out = [d_bits & 0xFF, d_bits >> 8]
+    if qtype in ("q4_1", "q5_1"):
+        out += [m_bits & 0xFF, m_bits >> 8]
+    if qtype in ("q5_0", "q5_1"):
+        word = 0
+        for j, c in enumerate(codes):
+            if c & 0x10:
+                word |= 1 << j
+        out += list(word.to_bytes(4, "little"))
+    out += [(codes[j] & 0xF) | ((codes[j + 16] & 0xF) << 4) for j in range(16)]
+    return np.array(out, dtype=np.uint8)
+
+
+def affine_weight(qtype: str, d, m, c):
+    """Exact weight from the format description (Fractions)."""
+    return d * (c - 16) if qtype == "q5_0" else d * c + m
+
+
+def load_golden_affine():
+    rows = []
+    for line in open(GOLDEN_AFFINE):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        qt, dh, dv, mh, mv, codes = [f.strip() for f in line.split(";")]
+        rows.append((qt, int(dh, 16), float(dv), None if mh == "-" else int(mh, 16), float(mv),
+                     [int(c) for c in codes.split()]))
+    return rows
+
+
 def load_golden():
     rows = []
     for line in open(GOLDEN):
@@ -81,6 +118,54 @@ def test_dequant_brute_force_all_codes(qt):
             for i, c in enumerate(chunk):
                 exact = Fraction(dv) * (c - off)
                 assert Fraction(float(got[i])) == exact
+
+
+@pytest.mark.parametrize("row", load_golden_affine(), ids=lambda r: f"{r[0]}-{r[1]:04X}")
+def test_dequant_hand_blocks_affine(row):
+    qt, d_bits, d_val, m_bits, m_val, codes = row
+    assert fp16_bits_to_float(d_bits) == d_val
+    if m_bits is not None:
+        assert fp16_bits_to_float(m_bits) == m_val
+    blk = build_block_affine(qt, d_bits, m_bits or 0, codes)[None, None, :]
+    assert blk.shape[-1] == gi.BLOCK_BYTES[qt]
+    got = oracle.dequant(qt, blk)[0]
+    for i, c in enumerate(codes):
+        assert Fraction(float(got[i])) == affine_weight(qt, Fraction(d_val), Fraction(m_val), c), (i, c)
+
+
+@pytest.mark.parametrize("qt", ["q4_1", "q5_0", "q5_1"])
+def test_dequant_brute_force_all_codes_affine(qt):
+    """Every code at every position, a set of scales and offsets."""
+    top = 15 if qt == "q4_1" else 31
+    d_bits_set = [0x3C00, 0x0001, 0x03FF, 0x7BFF, 0xB555, 0x2E66]
+    m_bits_set = [0x0000, 0xC280, 0x7BFF, 0x8001] if qt != "q5_0" else [0]
+    for d_bits in d_bits_set:
+        for m_bits in m_bits_set:
+            dv, mv = Fraction(fp16_bits_to_float(d_bits)), Fraction(fp16_bits_to_float(m_bits))
+            for shift in range(0, 32, 5):
+                codes = [(j + shift) % (top + 1) for j in range(32)]
+                got = oracle.dequant(qt, build_block_affine(qt, d_bits, m_bits, codes)[None, None, :])[0]
+                for i, c in enumerate(codes):
+                    assert Fraction(float(got[i])) == affine_weight(qt, dv, mv, c)
+
+
+@pytest.mark.parametrize("qt", ["q4_1", "q5_0", "q5_1"])
+def test_quantiser_error_bound_affine(qt):
+    """The harness quantisers stay within half a step (plus fp16 rounding of
+    the scale) of the fp32 input, decoded by the oracle; Q5_0's code range
+    is one step short on the side opposite the largest element, which is
+    clipped by up to a full step."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    blocks = {"q4_1": gi.quantize_q4_1, "q5_0": gi.quantize_q5_0, "q5_1": gi.quantize_q5_1}[qt](w)
+    got = oracle.dequant(qt, blocks)
+    b = w.reshape(8, 8, 32).astype(np.float64)
+    if qt == "q5_0":
+        bound = np.abs(b).max(axis=2) / 16.0
+    else:
+        bound = 0.5 * (b.max(axis=2) - b.min(axis=2)) / (15 if qt == "q4_1" else 31)
+    err = np.abs(got - w).reshape(8, 8, 32).max(axis=2)
+    assert (err <= bound * 1.01 + 2 * np.abs(b).max(axis=2) * 2.0 ** -10).all()
 
 
 def test_dequant_layout_rows_and_blocks():
