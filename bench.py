@@ -17,6 +17,8 @@ Also reported on the same line:
                 top-8, intermediate 768, Q4_0, bf16 activations)
   prefill_stream the same layer over 8 layers whose experts stream from
                 pinned host memory through two device buffers
+  block_types   every block type (Q8_0, Q5_1, Q5_0, Q4_1, Q4_0) on the
+                decode shape (8 layers, T=1) and on the prefill layer
   cache         expert-cache decode: 8 layers (hidden 4096, 256 experts,
                 top-8, intermediate 2048, Q4_0) served from a pinned host
                 pool through a VRAM cache of 40% of the experts, 2048
@@ -72,7 +74,7 @@ def parse_args():
 
 # ---------------------------------------------------------------- decode
 class DecodeStack:
-    def __init__(self, ctx, wl, n_layers: int, fused="layer"):
+    def __init__(self, ctx, wl, n_layers: int, fused="layer", distinct=None):
         import numpy as np
         import torch
         from expert_offload_amd import layer
@@ -83,10 +85,17 @@ class DecodeStack:
         self.perm = [gi.slot_permutation(wl, l) for l in range(n_layers)]
         t0 = time.time()
 
-        def put(l, e, b):
-            self.pool.put(l * wl.E + int(self.perm[l][e]), layer.pack_expert(wl.qtype, wl.H, wl.I, *b))
+        if distinct:  # `distinct` generated experts repeated over every slot (timing only)
+            made = {}
+            gi.generate_blocks_parallel(wl, [(0, e) for e in range(distinct)], lambda l, e, b: made.__setitem__(
+                e, layer.pack_expert(wl.qtype, wl.H, wl.I, *b)))
+            for slot in range(n_layers * wl.E):
+                self.pool.put(slot, made[slot % distinct])
+        else:
+            def put(l, e, b):
+                self.pool.put(l * wl.E + int(self.perm[l][e]), layer.pack_expert(wl.qtype, wl.H, wl.I, *b))
 
-        gi.generate_blocks_parallel(wl, [(l, e) for l in range(n_layers) for e in range(wl.E)], put)
+            gi.generate_blocks_parallel(wl, [(l, e) for l in range(n_layers) for e in range(wl.E)], put)
         torch.cuda.synchronize()
         log(f"generated and packed {n_layers}x{wl.E} experts "
             f"({self.pool.data.numel() / 1e9:.1f} GB) in {time.time() - t0:.1f}s")
@@ -179,7 +188,39 @@ def decode_layer_bytes(wl, T, n_active):
 
 
 # ---------------------------------------------------------------- prefill
-def prefill_extra(ctx, steps=10, warmup=3):
+def types_extra(ctx, layers=8, steps=40, warmup=5):
+    """Every block type on the decode shape (hidden 2048, 128 experts, top-8,
+    intermediate 768, T=1; 8 layers from 32 generated experts repeated,
+    since values do not change the timing) and on the 4096-token prefill
+    layer: time per decode layer and its algorithmic bytes over that time,
+    and the prefill FFN TFLOP/s."""
+    import dataclasses
+    import torch
+    from gen import inputs as gi
+    out = {}
+    for qt in ("q8_0", "q5_1", "q5_0", "q4_1", "q4_0"):
+        wl = dataclasses.replace(gi.workload("decode_q8_0_h2048_e128"), qtype=qt, name=f"decode_{qt}_h2048_e128")
+        stack = DecodeStack(ctx, wl, layers, distinct=32)
+        x, bufs, _, gpu_ms = time_graph(stack, 1, steps, warmup)
+        ms = gpu_ms / steps
+        na = stack.n_active(bufs)
+        layer_bytes = sum(decode_layer_bytes(wl, 1, a) for a in na) / len(na)
+        res = {"decode_layer_us": ms / layers * 1e3, "decode_tokens_per_s_per_layer": layers / (ms * 1e-3),
+               "decode_layer_hbm_gbs": layer_bytes / (ms / layers * 1e-3) / 1e9,
+               "bytes_per_expert": gi.bytes_per_expert(wl)}
+        del stack, bufs, x
+        torch.cuda.empty_cache()
+        pf = prefill_extra(ctx, steps=5, warmup=2, qtype=qt)
+        res["prefill_tokens_per_s"] = pf["tokens_per_s"]
+        res["prefill_ffn_tflops"] = pf["ffn_tflops"]
+        out[qt] = res
+        log(f"type {qt}: decode {ms / layers * 1e3:.1f} us/layer ({res['decode_layer_hbm_gbs']:.0f} GB/s over the "
+            f"layer); prefill {pf['tokens_per_s']:.0f} tok/s, FFN {pf['ffn_tflops']:.0f} TFLOP/s")
+        torch.cuda.empty_cache()
+    return out
+
+
+def prefill_extra(ctx, steps=10, warmup=3, qtype=None):
     import numpy as np
     import torch
     import expert_offload_amd as moe
@@ -188,6 +229,9 @@ def prefill_extra(ctx, steps=10, warmup=3):
     from gen import inputs as gi
 
     wl = gi.workload("prefill_q4_0_h2048_e128")
+    if qtype:
+        import dataclasses
+        wl = dataclasses.replace(wl, qtype=qtype, name=f"prefill_{qtype}_h2048_e128")
     T = wl.batches[0]
     pool = layer.SlotPool(wl.qtype, wl.H, wl.I, wl.E, device="cuda")
     perm = gi.slot_permutation(wl, 0)
@@ -639,6 +683,10 @@ def main():
                 f"efficiency {ps['overlap_efficiency']:.2f}")
         except Exception as e:
             result["prefill_stream"] = {"error": repr(e)}
+        try:
+            result["block_types"] = types_extra(ctx)
+        except Exception as e:
+            result["block_types"] = {"error": repr(e)}
         if not args.no_cache:
             try:
                 result["cache"] = cache_extra(ctx, steps=args.cache_steps, sweep_steps=args.sweep_steps)

@@ -21,7 +21,7 @@ ERRORS = {
     -4: "MOE_ERR_ALIGNMENT", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_NOT_RESIDENT",
     -7: "MOE_ERR_NOT_PINNED", -8: "MOE_ERR_CAPACITY", -9: "MOE_ERR_HIP",
 }
-QTYPE = {"q4_0": 2, "q8_0": 8}
+QTYPE = {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE_DECODE, MODE_PREFILL = 0, 1
 

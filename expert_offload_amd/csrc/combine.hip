@@ -48,14 +48,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   float q[32];
   block_codes<QT>(row, b, q);
   const float d = block_scale<QT>(row, b);
+  const float m = block_min<QT>(row, b);
+  // d * q is exact in fp32 (11-bit scale, at most 8-bit code); with an
+  // offset, d * u + m rounds once, as the format's definition does
+  float wv[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) wv[i] = qtype_has_min(QT) ? fmaf(d, q[i], m) : d * q[i];
   if constexpr (BF16) {
     uint16_t* o = (uint16_t*)out + (size_t)r * cols + b * kQK;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] = f32_to_bf16_rne(d * q[i]);
+    for (int i = 0; i < 32; ++i) o[i] = f32_to_bf16_rne(wv[i]);
   } else {
     float* o = (float*)out + (size_t)r * cols + b * kQK;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] = d * q[i];
+    for (int i = 0; i < 32; ++i) o[i] = wv[i];
   }
 }
 
@@ -107,12 +113,19 @@ extern "C" int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int r
   const unsigned grid = (unsigned)((n + 255) / 256);
   hipStream_t s = (hipStream_t)stream;
   KernelTimer timer(ctx, "dequant", s);
-  if (qtype == MOE_QTYPE_Q8_0) {
-    if (out_dtype == MOE_DTYPE_F32) launch(dequant_kernel<MOE_QTYPE_Q8_0, false>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);
-    else launch(dequant_kernel<MOE_QTYPE_Q8_0, true>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);
-  } else {
-    if (out_dtype == MOE_DTYPE_F32) launch(dequant_kernel<MOE_QTYPE_Q4_0, false>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);
-    else launch(dequant_kernel<MOE_QTYPE_Q4_0, true>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);
+#define MOE_DQ(Q)                                                                                           \
+  case Q:                                                                                                   \
+    if (out_dtype == MOE_DTYPE_F32) launch(dequant_kernel<Q, false>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out); \
+    else launch(dequant_kernel<Q, true>, grid, 256, 0, s, (const uint8_t*)packed, rows, cols, out);         \
+    break;
+  switch (qtype) {
+    MOE_DQ(MOE_QTYPE_Q8_0)
+    MOE_DQ(MOE_QTYPE_Q4_0)
+    MOE_DQ(MOE_QTYPE_Q4_1)
+    MOE_DQ(MOE_QTYPE_Q5_0)
+    MOE_DQ(MOE_QTYPE_Q5_1)
+    default: break;
   }
+#undef MOE_DQ
   return check_launch("dequant_kernel");
 }

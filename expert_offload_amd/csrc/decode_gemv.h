@@ -24,16 +24,12 @@ namespace moe {
 
 // --------------------------------------------------------------- helpers
 template <int QT>
-struct QTraits;
-template <>
-struct QTraits<MOE_QTYPE_Q8_0> {
-  static constexpr int kWords = 8;  // 32 bytes of codes
-  static constexpr float kOff = 128.0f;
-};
-template <>
-struct QTraits<MOE_QTYPE_Q4_0> {
-  static constexpr int kWords = 4;  // 16 bytes of nibbles
-  static constexpr float kOff = 8.0f;
+struct QTraits {
+  static constexpr int kWords = QT == MOE_QTYPE_Q8_0 ? 8 : 4;  // 32 or 16 bytes of codes
+  static constexpr bool kQh = qtype_has_qh(QT);               // a word of fifth bits
+  static constexpr bool kMin = qtype_has_min(QT);             // w = d*u + m
+  static constexpr float kOff = qtype_code_off(QT);           // else w = d*(u - kOff)
+  static constexpr int kRegs = kWords + (kQh ? 1 : 0);
 };
 
 template <int QT>
@@ -47,31 +43,6 @@ __device__ __forceinline__ void load_block_raw(const uint8_t* row, int b, uint32
     w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
   }
   d = block_scale<QT>(row, b);
-}
-
-// sum_k u_k * x_k over one block, u the unsigned stored code.
-template <int QT>
-__device__ __forceinline__ float block_udot(const uint32_t (&w)[QTraits<QT>::kWords], const float (&xv)[32]) {
-  float s = 0.0f;
-  if constexpr (QT == MOE_QTYPE_Q8_0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t u = w[i] ^ 0x80808080u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s = fmaf((float)((u >> (8 * j)) & 0xFFu), xv[4 * i + j], s);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s = fmaf((float)((lo >> (8 * j)) & 0xFFu), xv[4 * i + j], s);
-        s = fmaf((float)((hi >> (8 * j)) & 0xFFu), xv[16 + 4 * i + j], s);
-      }
-    }
-  }
-  return s;
 }
 
 __device__ __forceinline__ void load_f32x32(const float* p, float (&xv)[32]) {
@@ -114,37 +85,46 @@ __device__ __forceinline__ void fold_rows(float (&v)[M], int lane) {
   }
 }
 
-// Rows of one lane's GEMV: RPL rows x BPL blocks of raw codes and scales.
+// Rows of one lane's GEMV: RPL rows x BPL blocks of raw codes, fifth bits,
+// scales and offsets (the last two only for the types that have them).
 template <int QT, int LPR, int BPL, int RPL>
 struct RowTile {
-  uint32_t w[RPL][BPL][QTraits<QT>::kWords];
+  using Q = QTraits<QT>;
+  uint32_t w[RPL][BPL][Q::kWords];
+  uint32_t qh[RPL][BPL];
   float d[RPL][BPL];
+  float m[RPL][BPL];
 
   __device__ __forceinline__ void load(const uint8_t* const (&rows)[RPL], int lg) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) load_block_raw<QT>(rows[r], lg + LPR * i, w[r][i], d[r][i]);
+      for (int i = 0; i < BPL; ++i) {
+        load_block_raw<QT>(rows[r], lg + LPR * i, w[r][i], d[r][i]);
+        if constexpr (Q::kQh) qh[r][i] = block_qh<QT>(rows[r], lg + LPR * i);
+        if constexpr (Q::kMin) m[r][i] = block_min<QT>(rows[r], lg + LPR * i);
+      }
   }
 
-  // acc[r] = sum over the lane's blocks of d * (u . x - OFF * sum x), with
-  // the lane's activation blocks already in xv.  Rows are finished one at a
-  // time in load order, so the wait before row r covers only the loads up to
-  // row r and row r's math overlaps the later rows' transfers.  Each row's
-  // codes pass through an empty asm right before use so the compiler widens
-  // them here, inside the token loop, instead of keeping RPL*BPL*32 widened
+  // acc[r] = sum over the lane's blocks of d * (u . x - OFF * sum x), or
+  // d * (u . x) + m * sum x for the types with an offset m, with the lane's
+  // activation blocks already in xv.  Rows are finished one at a time in
+  // load order, so the wait before row r covers only the loads up to row r
+  // and row r's math overlaps the later rows' transfers.  Each row's codes
+  // pass through an empty asm right before use so the compiler widens them
+  // here, inside the token loop, instead of keeping RPL*BPL*32 widened
   // floats live; four partial sums per row break the FMA dependency chain.
   __device__ __forceinline__ void dot(const float (&xv)[BPL][32], float (&acc)[RPL]) {
     float sx[BPL];
 #pragma unroll
-    for (int i = 0; i < BPL; ++i) sx[i] = sum32(xv[i]) * QTraits<QT>::kOff;
+    for (int i = 0; i < BPL; ++i) sx[i] = Q::kMin ? sum32(xv[i]) : sum32(xv[i]) * Q::kOff;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       acc[r] = 0.0f;
 #pragma unroll
       for (int i = 0; i < BPL; ++i) {
 #pragma unroll
-        for (int q = 0; q < QTraits<QT>::kWords; ++q) asm volatile("" : "+v"(w[r][i][q]));
+        for (int q = 0; q < Q::kWords; ++q) asm volatile("" : "+v"(w[r][i][q]));
         float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (QT == MOE_QTYPE_Q8_0) {
 #pragma unroll
@@ -156,7 +136,11 @@ struct RowTile {
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = w[r][i][q] & 0x0F0F0F0Fu, hi = (w[r][i][q] >> 4) & 0x0F0F0F0Fu;
+            uint32_t lo = w[r][i][q] & 0x0F0F0F0Fu, hi = (w[r][i][q] >> 4) & 0x0F0F0F0Fu;
+            if constexpr (Q::kQh) {
+              lo |= spread_fifth_bits(qh[r][i] >> (4 * q));
+              hi |= spread_fifth_bits(qh[r][i] >> (16 + 4 * q));
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               part[j] = fmaf((float)((lo >> (8 * j)) & 0xFFu), xv[i][4 * q + j], part[j]);
@@ -164,7 +148,9 @@ struct RowTile {
             }
           }
         }
-        acc[r] = fmaf(d[r][i], (part[0] + part[1]) + (part[2] + part[3]) - sx[i], acc[r]);
+        const float su = (part[0] + part[1]) + (part[2] + part[3]);
+        if constexpr (Q::kMin) acc[r] = fmaf(d[r][i], su, fmaf(m[r][i], sx[i], acc[r]));
+        else acc[r] = fmaf(d[r][i], su - sx[i], acc[r]);
       }
     }
   }
@@ -207,7 +193,7 @@ struct HRowRegs {
 // ----------------------------------------------------------- shape rules
 template <int QT, int BPL>
 constexpr int rows_per_lane() {
-  constexpr int budget = 64 / (BPL * QTraits<QT>::kWords);  // <= 64 registers of raw codes
+  constexpr int budget = 64 / (BPL * QTraits<QT>::kRegs);  // <= 64 registers of raw codes
   return budget >= 8 ? 8 : budget >= 4 ? 4 : budget >= 2 ? 2 : 1;
 }
 // Down tiles aim at 8 rows (H/8 workgroups): RPL = 8 / (64 / LPR) within

@@ -71,7 +71,7 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Start of block `b` of one packed row, and its scale.
+// Start of block `b` of one packed row, its scale d, offset m, fifth bits.
 template <int QT>
 __device__ __forceinline__ const uint8_t* block_quants(const uint8_t* row, int b) {
   return row + (size_t)(b >> 3) * group_bytes(QT) + (b & 7) * quant_bytes_per_block(QT);
@@ -79,12 +79,36 @@ __device__ __forceinline__ const uint8_t* block_quants(const uint8_t* row, int b
 template <int QT>
 __device__ __forceinline__ float block_scale(const uint8_t* row, int b) {
   const uint8_t* g = row + (size_t)(b >> 3) * group_bytes(QT);
-  const __half d = *reinterpret_cast<const __half*>(g + kGroupBlocks * quant_bytes_per_block(QT) + 2 * (b & 7));
-  return __half2float(d);
+  return __half2float(*reinterpret_cast<const __half*>(g + group_d_off(QT) + 2 * (b & 7)));
+}
+template <int QT>
+__device__ __forceinline__ float block_min(const uint8_t* row, int b) {
+  if constexpr (qtype_has_min(QT)) {
+    const uint8_t* g = row + (size_t)(b >> 3) * group_bytes(QT);
+    return __half2float(*reinterpret_cast<const __half*>(g + group_m_off(QT) + 2 * (b & 7)));
+  } else {
+    return 0.0f;
+  }
+}
+template <int QT>
+__device__ __forceinline__ uint32_t block_qh(const uint8_t* row, int b) {
+  if constexpr (qtype_has_qh(QT)) {
+    const uint8_t* g = row + (size_t)(b >> 3) * group_bytes(QT);
+    return *reinterpret_cast<const uint32_t*>(g + group_qh_off(QT) + 4 * (b & 7));
+  } else {
+    return 0u;
+  }
 }
 
-// The 32 integer codes of block `b` as floats in logical element order:
-// Q8_0 -> q (int8), Q4_0 -> q - 8.
+// Bits 0..3 of t (the fifth code bits of four consecutive elements) moved
+// to bit 4 of each byte, to be or-ed into four nibble bytes.
+__device__ __forceinline__ uint32_t spread_fifth_bits(uint32_t t) {
+  return (((t & 0xFu) * 0x00204081u) & 0x01010101u) << 4;
+}
+
+// The 32 codes of block `b` as floats in logical element order: the signed
+// code q (w = d * q) for Q8_0 (int8), Q4_0 (u - 8), Q5_0 (u - 16); the
+// unsigned code u (w = d * u + m) for Q4_1 and Q5_1.
 template <int QT>
 __device__ __forceinline__ void block_codes(const uint8_t* row, int b, float (&q)[32]) {
   const uint8_t* p = block_quants<QT>(row, b);
@@ -99,14 +123,20 @@ __device__ __forceinline__ void block_codes(const uint8_t* row, int b, float (&q
     }
   } else {
     const int4 v = *reinterpret_cast<const int4*>(p);
-    const int w[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+    const uint32_t qh = block_qh<QT>(row, b);
+    constexpr int off = (int)qtype_code_off(QT);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+      if constexpr (qtype_has_qh(QT)) {
+        lo |= spread_fifth_bits(qh >> (4 * i));
+        hi |= spread_fifth_bits(qh >> (16 + 4 * i));
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int byte = (w[i] >> (8 * j)) & 0xFF;
-        q[4 * i + j] = (float)((byte & 0xF) - 8);
-        q[16 + 4 * i + j] = (float)((byte >> 4) - 8);
+        q[4 * i + j] = (float)((int)((lo >> (8 * j)) & 0xFFu) - off);
+        q[16 + 4 * i + j] = (float)((int)((hi >> (8 * j)) & 0xFFu) - off);
       }
     }
   }

@@ -42,6 +42,11 @@ constexpr int kRouteInFfnMaxPairs = 64;
 int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype, hipStream_t s);
 bool decode_gemv_supported(int H, int I, int T, int k);
 bool decode_route_supported(int H, int I, int T, int k);
+int launch_ffn_decode_q8_0(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
+int launch_ffn_decode_q4_0(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
+int launch_ffn_decode_q4_1(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
+int launch_ffn_decode_q5_0(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
+int launch_ffn_decode_q5_1(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
 int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s,
                       const RouteArgs* route = nullptr);
 bool prefill_mfma_supported(int H, int I);

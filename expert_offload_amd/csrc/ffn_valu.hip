@@ -75,15 +75,20 @@ __global__ __launch_bounds__(256) void ffn_gateup_valu(FfnParams p, const XT* __
       for (int b = l16; b < nblk; b += 16) {
         float q[32];
         block_codes<QT>(row, b, q);
-        const float d = block_scale<QT>(row, b);
+        const float d = block_scale<QT>(row, b), m = block_min<QT>(row, b);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (j < nt) {
             float xv[32];
             load_x32(xr[j], b * kQK, xv);
-            float dot = 0.0f;
+            float dot = 0.0f, sx = 0.0f;
 #pragma unroll
             for (int i = 0; i < 32; ++i) dot = fmaf(q[i], xv[i], dot);
+            if constexpr (qtype_has_min(QT)) {
+#pragma unroll
+              for (int i = 0; i < 32; ++i) sx += xv[i];
+              acc[j] = fmaf(m, sx, acc[j]);
+            }
             acc[j] = fmaf(d, dot, acc[j]);
           }
         }
@@ -135,15 +140,20 @@ __global__ __launch_bounds__(256) void ffn_down_valu(FfnParams p) {
       for (int b = l16; b < nblk; b += 16) {
         float q[32];
         block_codes<QT>(row, b, q);
-        const float d = block_scale<QT>(row, b);
+        const float d = block_scale<QT>(row, b), m = block_min<QT>(row, b);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (j < nt) {
             float hv[32];
             load_x32(p.hbuf + (size_t)(pbeg + tg + j) * p.I, b * kQK, hv);
-            float dot = 0.0f;
+            float dot = 0.0f, sx = 0.0f;
 #pragma unroll
             for (int i = 0; i < 32; ++i) dot = fmaf(q[i], hv[i], dot);
+            if constexpr (qtype_has_min(QT)) {
+#pragma unroll
+              for (int i = 0; i < 32; ++i) sx += hv[i];
+              acc[j] = fmaf(m, sx, acc[j]);
+            }
             acc[j] = fmaf(d, dot, acc[j]);
           }
         }
@@ -157,35 +167,35 @@ __global__ __launch_bounds__(256) void ffn_down_valu(FfnParams p) {
   }
 }
 
-int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype, hipStream_t s) {
+template <int QT>
+static int launch_ffn_valu_t(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype, hipStream_t s) {
   const int grid_cap = 8 * ctx->num_cus;
   const int max_active = std::min(p.E, p.T * p.k);
   const int g1 = std::max(1, std::min(grid_cap, max_active * (p.I / 8)));
   const int g2 = std::max(1, std::min(grid_cap, max_active * (p.H / 16)));
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
-    if (p.qtype == MOE_QTYPE_Q8_0) {
-      if (x_dtype == MOE_DTYPE_F32)
-        launch(ffn_gateup_valu<MOE_QTYPE_Q8_0, float>, g1, 256, 0, s, p, (const float*)x);
-      else
-        launch(ffn_gateup_valu<MOE_QTYPE_Q8_0, uint16_t>, g1, 256, 0, s, p, (const uint16_t*)x);
-    } else {
-      if (x_dtype == MOE_DTYPE_F32)
-        launch(ffn_gateup_valu<MOE_QTYPE_Q4_0, float>, g1, 256, 0, s, p, (const float*)x);
-      else
-        launch(ffn_gateup_valu<MOE_QTYPE_Q4_0, uint16_t>, g1, 256, 0, s, p, (const uint16_t*)x);
-    }
+    if (x_dtype == MOE_DTYPE_F32) launch(ffn_gateup_valu<QT, float>, g1, 256, 0, s, p, (const float*)x);
+    else launch(ffn_gateup_valu<QT, uint16_t>, g1, 256, 0, s, p, (const uint16_t*)x);
   }
   int rc = check_launch("ffn_gateup_valu");
   if (rc) return rc;
   {
     KernelTimer timer(ctx, "ffn_down", s);
-    if (p.qtype == MOE_QTYPE_Q8_0)
-      launch(ffn_down_valu<MOE_QTYPE_Q8_0>, g2, 256, 0, s, p);
-    else
-      launch(ffn_down_valu<MOE_QTYPE_Q4_0>, g2, 256, 0, s, p);
+    launch(ffn_down_valu<QT>, g2, 256, 0, s, p);
   }
   return check_launch("ffn_down_valu");
+}
+
+int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype, hipStream_t s) {
+  switch (p.qtype) {
+    case MOE_QTYPE_Q8_0: return launch_ffn_valu_t<MOE_QTYPE_Q8_0>(ctx, p, x, x_dtype, s);
+    case MOE_QTYPE_Q4_0: return launch_ffn_valu_t<MOE_QTYPE_Q4_0>(ctx, p, x, x_dtype, s);
+    case MOE_QTYPE_Q4_1: return launch_ffn_valu_t<MOE_QTYPE_Q4_1>(ctx, p, x, x_dtype, s);
+    case MOE_QTYPE_Q5_0: return launch_ffn_valu_t<MOE_QTYPE_Q5_0>(ctx, p, x, x_dtype, s);
+    case MOE_QTYPE_Q5_1: return launch_ffn_valu_t<MOE_QTYPE_Q5_1>(ctx, p, x, x_dtype, s);
+    default: return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "expert FFN: block type %d", p.qtype);
+  }
 }
 
 }  // namespace moe

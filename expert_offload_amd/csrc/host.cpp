@@ -197,10 +197,11 @@ int moe_ctx_check(moe_ctx* ctx, void* stream) {
 int moe_qtype_info(int qtype, int* block_elems, int* block_bytes) {
   clear_error();
   if (!qtype_supported(qtype))
-    return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "block type %d is not supported (Q4_0=%d, Q8_0=%d)",
-                     qtype, MOE_QTYPE_Q4_0, MOE_QTYPE_Q8_0);
+    return set_error(MOE_ERR_UNSUPPORTED_QTYPE,
+                     "block type %d is not supported (Q4_0=%d, Q4_1=%d, Q5_0=%d, Q5_1=%d, Q8_0=%d)", qtype,
+                     MOE_QTYPE_Q4_0, MOE_QTYPE_Q4_1, MOE_QTYPE_Q5_0, MOE_QTYPE_Q5_1, MOE_QTYPE_Q8_0);
   if (block_elems) *block_elems = kQK;
-  if (block_bytes) *block_bytes = 2 + quant_bytes_per_block(qtype);
+  if (block_bytes) *block_bytes = ggml_block_bytes(qtype);
   return MOE_OK;
 }
 
@@ -223,10 +224,12 @@ int moe_slot_bytes(int qtype, int H, int I, size_t* out_bytes) {
 }
 
 // ggml blocks [rows][cols/32] -> device layout (groups of 8 blocks: quant
-// bytes then scales).
+// bytes, fifth-bit words, scales d, offsets m).
 static void pack_matrix(int qtype, int rows, int cols, const uint8_t* src, uint8_t* dst) {
   const int qb = quant_bytes_per_block(qtype);
-  const int bb = 2 + qb;
+  const int bb = ggml_block_bytes(qtype);
+  const bool has_m = qtype_has_min(qtype), has_qh = qtype_has_qh(qtype);
+  const int qh_in = 2 + (has_m ? 2 : 0), qs_in = qh_in + (has_qh ? 4 : 0);  // field offsets in a ggml block
   const int groups = cols / kGroupWeights;
   const size_t gbytes = group_bytes(qtype);
   for (int r = 0; r < rows; ++r) {
@@ -234,8 +237,11 @@ static void pack_matrix(int qtype, int rows, int cols, const uint8_t* src, uint8
       const uint8_t* s = src + ((size_t)r * (cols / kQK) + (size_t)g * kGroupBlocks) * bb;
       uint8_t* d = dst + (size_t)r * row_bytes(qtype, cols) + (size_t)g * gbytes;
       for (int b = 0; b < kGroupBlocks; ++b) {
-        std::memcpy(d + (size_t)b * qb, s + (size_t)b * bb + 2, qb);
-        std::memcpy(d + (size_t)kGroupBlocks * qb + 2 * b, s + (size_t)b * bb, 2);
+        const uint8_t* blk = s + (size_t)b * bb;
+        std::memcpy(d + (size_t)b * qb, blk + qs_in, qb);
+        if (has_qh) std::memcpy(d + group_qh_off(qtype) + 4 * b, blk + qh_in, 4);
+        std::memcpy(d + group_d_off(qtype) + 2 * b, blk, 2);
+        if (has_m) std::memcpy(d + group_m_off(qtype) + 2 * b, blk + 2, 2);
       }
     }
   }

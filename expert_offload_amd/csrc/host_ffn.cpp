@@ -8,7 +8,7 @@
 // file computes h = silu(Wg x) * (Wu x), y = Wd h for a few tokens straight
 // from the pinned host pool, in the same slot layout the GPU reads: rows of
 // 256-weight groups, each group the quant bytes of 8 ggml blocks followed
-// by their 8 fp16 scales.  x and y are fp32; every dot product accumulates
+// by their fifth bits, scales and offsets (for the types that have them).  x and y are fp32; every dot product accumulates
 // in fp32.
 //
 // The rows of one call are split over a small pool of worker threads; the
@@ -56,31 +56,53 @@ float half_to_float(uint16_t h) {
   return f;
 }
 
+__attribute__((target("avx2"))) inline float _mm256_reduce_add_ps_(__m256 v) {
+  const __m128 s = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));
+  const __m128 t = _mm_add_ps(s, _mm_movehl_ps(s, s));
+  return _mm_cvtss_f32(_mm_add_ss(t, _mm_shuffle_ps(t, t, 1)));
+}
+
 // ---------------------------------------------------------------- row dots
-// sum_k w_k x_k over one row of `cols` weights (cols % 256 == 0).
+// sum_k w_k x_k over one row of `cols` weights (cols % 256 == 0); xs holds
+// the sum of x over each 32-element block (used by the types with an offset
+// m: w = d*u + m).
+inline uint16_t load_u16(const uint8_t* p) {
+  uint16_t v;
+  std::memcpy(&v, p, 2);
+  return v;
+}
+inline uint32_t load_u32(const uint8_t* p) {
+  uint32_t v;
+  std::memcpy(&v, p, 4);
+  return v;
+}
+
 template <int QT>
-float row_dot_scalar(const uint8_t* row, const float* x, int cols) {
-  constexpr int qb = QT == MOE_QTYPE_Q8_0 ? 32 : 16;
+float row_dot_scalar(const uint8_t* row, const float* x, const float* xs, int cols) {
+  constexpr int qb = quant_bytes_per_block(QT);
+  constexpr int off = (int)qtype_code_off(QT);
   float acc = 0.0f;
   for (int g = 0; g < cols / kGroupWeights; ++g) {
     const uint8_t* grp = row + (size_t)g * group_bytes(QT);
-    const uint8_t* sc = grp + kGroupBlocks * qb;
     for (int b = 0; b < kGroupBlocks; ++b) {
-      uint16_t hs;
-      std::memcpy(&hs, sc + 2 * b, 2);
-      const float d = half_to_float(hs);
+      const float d = half_to_float(load_u16(grp + group_d_off(QT) + 2 * b));
       const uint8_t* q = grp + b * qb;
       const float* xb = x + g * kGroupWeights + b * kQK;
       float s = 0.0f;
       if constexpr (QT == MOE_QTYPE_Q8_0) {
         for (int j = 0; j < 32; ++j) s += (float)(int8_t)q[j] * xb[j];
       } else {
+        const uint32_t qh = qtype_has_qh(QT) ? load_u32(grp + group_qh_off(QT) + 4 * b) : 0u;
         for (int j = 0; j < 16; ++j) {
-          s += (float)((int)(q[j] & 0x0F) - 8) * xb[j];
-          s += (float)((int)(q[j] >> 4) - 8) * xb[j + 16];
+          const int u0 = (q[j] & 0x0F) | (int)(((qh >> j) & 1u) << 4);
+          const int u1 = (q[j] >> 4) | (int)(((qh >> (j + 16)) & 1u) << 4);
+          s += (float)(u0 - off) * xb[j];
+          s += (float)(u1 - off) * xb[j + 16];
         }
       }
       acc += d * s;
+      if constexpr (qtype_has_min(QT))
+        acc += half_to_float(load_u16(grp + group_m_off(QT) + 2 * b)) * xs[g * kGroupBlocks + b];
     }
   }
   return acc;
@@ -88,16 +110,22 @@ float row_dot_scalar(const uint8_t* row, const float* x, int cols) {
 
 template <int QT>
 __attribute__((target("avx512f,avx512bw,avx512vl,f16c"))) float row_dot_avx512(const uint8_t* row, const float* x,
-                                                                               int cols) {
-  constexpr int qb = QT == MOE_QTYPE_Q8_0 ? 32 : 16;
+                                                                               const float* xs, int cols) {
+  constexpr int qb = quant_bytes_per_block(QT);
   __m512 acc = _mm512_setzero_ps();
+  float macc = 0.0f;
+  const __m512i iota = _mm512_setr_epi32(0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
   for (int g = 0; g < cols / kGroupWeights; ++g) {
     const uint8_t* grp = row + (size_t)g * group_bytes(QT);
-    const __m256 d8 = _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i*>(grp + kGroupBlocks * qb)));
+    const __m256 d8 = _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i*>(grp + group_d_off(QT))));
     alignas(32) float d[8];
     _mm256_store_ps(d, d8);
+    if constexpr (qtype_has_min(QT)) {
+      const __m256 m8 = _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i*>(grp + group_m_off(QT))));
+      macc += _mm256_reduce_add_ps_(_mm256_mul_ps(m8, _mm256_loadu_ps(xs + g * kGroupBlocks)));
+    }
     const float* xg = x + g * kGroupWeights;
-#pragma GCC unroll 8
+#pragma unroll
     for (int b = 0; b < kGroupBlocks; ++b) {
       const uint8_t* q = grp + b * qb;
       const float* xb = xg + b * kQK;
@@ -107,19 +135,31 @@ __attribute__((target("avx512f,avx512bw,avx512vl,f16c"))) float row_dot_avx512(c
         hi = _mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(q + 16))));
       } else {
         const __m512i u = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(q)));
-        const __m512i eight = _mm512_set1_epi32(8);
-        lo = _mm512_cvtepi32_ps(_mm512_sub_epi32(_mm512_and_si512(u, _mm512_set1_epi32(0x0F)), eight));
-        hi = _mm512_cvtepi32_ps(_mm512_sub_epi32(_mm512_srli_epi32(u, 4), eight));
+        __m512i ul = _mm512_and_si512(u, _mm512_set1_epi32(0x0F)), uh = _mm512_srli_epi32(u, 4);
+        if constexpr (qtype_has_qh(QT)) {
+          const uint32_t qh = load_u32(grp + group_qh_off(QT) + 4 * b);
+          const __m512i one = _mm512_set1_epi32(1);
+          ul = _mm512_or_si512(ul, _mm512_slli_epi32(_mm512_and_si512(_mm512_srlv_epi32(_mm512_set1_epi32((int)qh), iota), one), 4));
+          uh = _mm512_or_si512(uh, _mm512_slli_epi32(
+                                       _mm512_and_si512(_mm512_srlv_epi32(_mm512_set1_epi32((int)(qh >> 16)), iota), one), 4));
+        }
+        if constexpr (!qtype_has_min(QT)) {
+          const __m512i off = _mm512_set1_epi32((int)qtype_code_off(QT));
+          ul = _mm512_sub_epi32(ul, off);
+          uh = _mm512_sub_epi32(uh, off);
+        }
+        lo = _mm512_cvtepi32_ps(ul);
+        hi = _mm512_cvtepi32_ps(uh);
       }
       __m512 s = _mm512_mul_ps(lo, _mm512_loadu_ps(xb));
       s = _mm512_fmadd_ps(hi, _mm512_loadu_ps(xb + 16), s);
       acc = _mm512_fmadd_ps(_mm512_set1_ps(d[b]), s, acc);
     }
   }
-  return _mm512_reduce_add_ps(acc);
+  return _mm512_reduce_add_ps(acc) + macc;
 }
 
-using RowDot = float (*)(const uint8_t*, const float*, int);
+using RowDot = float (*)(const uint8_t*, const float*, const float*, int);
 
 bool has_avx512() {
   static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
@@ -128,8 +168,22 @@ bool has_avx512() {
 }
 
 RowDot row_dot_for(int qtype, bool vector) {
-  if (qtype == MOE_QTYPE_Q8_0) return vector ? row_dot_avx512<MOE_QTYPE_Q8_0> : row_dot_scalar<MOE_QTYPE_Q8_0>;
-  return vector ? row_dot_avx512<MOE_QTYPE_Q4_0> : row_dot_scalar<MOE_QTYPE_Q4_0>;
+  switch (qtype) {
+    case MOE_QTYPE_Q8_0: return vector ? row_dot_avx512<MOE_QTYPE_Q8_0> : row_dot_scalar<MOE_QTYPE_Q8_0>;
+    case MOE_QTYPE_Q4_1: return vector ? row_dot_avx512<MOE_QTYPE_Q4_1> : row_dot_scalar<MOE_QTYPE_Q4_1>;
+    case MOE_QTYPE_Q5_0: return vector ? row_dot_avx512<MOE_QTYPE_Q5_0> : row_dot_scalar<MOE_QTYPE_Q5_0>;
+    case MOE_QTYPE_Q5_1: return vector ? row_dot_avx512<MOE_QTYPE_Q5_1> : row_dot_scalar<MOE_QTYPE_Q5_1>;
+    default: return vector ? row_dot_avx512<MOE_QTYPE_Q4_0> : row_dot_scalar<MOE_QTYPE_Q4_0>;
+  }
+}
+
+// Sums of v over each 32-element block.
+void block_sums(const float* v, int n, float* out) {
+  for (int b = 0; b < n / kQK; ++b) {
+    float s = 0.0f;
+    for (int j = 0; j < kQK; ++j) s += v[b * kQK + j];
+    out[b] = s;
+  }
 }
 
 // ---------------------------------------------------------------- threads
@@ -246,6 +300,12 @@ int host_experts_ffn(int qtype, int H, int I, int n_exp, const uint8_t* const* s
   const int ci = (I + kRowChunk - 1) / kRowChunk, ch = (H + kRowChunk - 1) / kRowChunk;
   const size_t gate = slot_gate_off(qtype, H, I), up = slot_up_off(qtype, H, I), down = slot_down_off(qtype, H, I);
   const size_t rb_h = row_bytes(qtype, H), rb_i = row_bytes(qtype, I);
+  // block sums of every token's x and, after the first phase, of every h row
+  const int n_rows = hbase[n_exp];
+  std::vector<float> xs((size_t)n_rows * (H / kQK)), hs((size_t)n_rows * (I / kQK));
+  for (int e = 0; e < n_exp; ++e)
+    for (int j = 0; j < cnt[e]; ++j)
+      block_sums(x + (size_t)tok[e][j] * H, H, xs.data() + (size_t)(hbase[e] + j) * (H / kQK));
   pool->run(n_exp * ci, [&](int task) {
     const int e = task / ci, r0 = (task % ci) * kRowChunk, r1 = std::min(I, r0 + kRowChunk);
     for (int r = r0; r < r1; ++r) {
@@ -253,17 +313,21 @@ int host_experts_ffn(int qtype, int H, int I, int n_exp, const uint8_t* const* s
       const uint8_t* ur = slots[e] + up + (size_t)r * rb_h;
       for (int j = 0; j < cnt[e]; ++j) {
         const float* xt = x + (size_t)tok[e][j] * H;
-        const float g = dot(gr, xt, H), u = dot(ur, xt, H);
+        const float* st = xs.data() + (size_t)(hbase[e] + j) * (H / kQK);
+        const float g = dot(gr, xt, st, H), u = dot(ur, xt, st, H);
         h[(size_t)(hbase[e] + j) * I + r] = g / (1.0f + std::exp(-g)) * u;
       }
     }
   });
+  if (qtype_has_min(qtype))
+    for (int i = 0; i < n_rows; ++i) block_sums(h + (size_t)i * I, I, hs.data() + (size_t)i * (I / kQK));
   pool->run(n_exp * ch, [&](int task) {
     const int e = task / ch, r0 = (task % ch) * kRowChunk, r1 = std::min(H, r0 + kRowChunk);
     for (int r = r0; r < r1; ++r) {
       const uint8_t* dr = slots[e] + down + (size_t)r * rb_i;
       for (int j = 0; j < cnt[e]; ++j)
-        y[(size_t)yrow[e][j] * H + r] = dot(dr, h + (size_t)(hbase[e] + j) * I, I);
+        y[(size_t)yrow[e][j] * H + r] =
+            dot(dr, h + (size_t)(hbase[e] + j) * I, hs.data() + (size_t)(hbase[e] + j) * (I / kQK), I);
     }
   });
   return MOE_OK;

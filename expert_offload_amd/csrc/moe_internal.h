@@ -80,8 +80,28 @@ constexpr int kGroupWeights = kQK * kGroupBlocks;  // 256
 __host__ __device__ constexpr int quant_bytes_per_block(int qtype) {
   return qtype == MOE_QTYPE_Q8_0 ? 32 : 16;
 }
-__host__ __device__ constexpr int group_bytes(int qtype) {
-  return kGroupBlocks * quant_bytes_per_block(qtype) + 2 * kGroupBlocks;
+__host__ __device__ constexpr bool qtype_has_min(int qtype) {  // w = d*q + m
+  return qtype == MOE_QTYPE_Q4_1 || qtype == MOE_QTYPE_Q5_1;
+}
+__host__ __device__ constexpr bool qtype_has_qh(int qtype) {  // fifth code bits
+  return qtype == MOE_QTYPE_Q5_0 || qtype == MOE_QTYPE_Q5_1;
+}
+// ggml block bytes: fp16 d, [fp16 m], [4 B fifth bits], quant bytes.
+__host__ __device__ constexpr int ggml_block_bytes(int qtype) {
+  return 2 + (qtype_has_min(qtype) ? 2 : 0) + (qtype_has_qh(qtype) ? 4 : 0) + quant_bytes_per_block(qtype);
+}
+__host__ __device__ constexpr int group_bytes(int qtype) { return kGroupBlocks * ggml_block_bytes(qtype); }
+// Offsets inside a group: quant bytes at 0, then fifth-bit words, scales d,
+// offsets m.
+__host__ __device__ constexpr int group_qh_off(int qtype) { return kGroupBlocks * quant_bytes_per_block(qtype); }
+__host__ __device__ constexpr int group_d_off(int qtype) {
+  return group_qh_off(qtype) + (qtype_has_qh(qtype) ? 4 * kGroupBlocks : 0);
+}
+__host__ __device__ constexpr int group_m_off(int qtype) { return group_d_off(qtype) + 2 * kGroupBlocks; }
+// The stored code u (Q8_0: q + 128; 4-bit: the nibble; 5-bit: nibble + 16 *
+// fifth bit) maps to w = d*u - OFF*d, or d*u + m for the types with m.
+__host__ __device__ constexpr float qtype_code_off(int qtype) {
+  return qtype == MOE_QTYPE_Q8_0 ? 128.0f : qtype == MOE_QTYPE_Q4_0 ? 8.0f : qtype == MOE_QTYPE_Q5_0 ? 16.0f : 0.0f;
 }
 __host__ __device__ constexpr size_t row_bytes(int qtype, int cols) {
   return (size_t)(cols / kGroupWeights) * group_bytes(qtype);
@@ -102,10 +122,18 @@ __host__ __device__ constexpr size_t slot_bytes_of(int qtype, int H, int I) {
 }
 
 inline bool qtype_supported(int qtype) {
-  return qtype == MOE_QTYPE_Q8_0 || qtype == MOE_QTYPE_Q4_0;
+  return qtype == MOE_QTYPE_Q8_0 || qtype == MOE_QTYPE_Q4_0 || qtype == MOE_QTYPE_Q4_1 || qtype == MOE_QTYPE_Q5_0 ||
+         qtype == MOE_QTYPE_Q5_1;
 }
 inline const char* qtype_name(int qtype) {
-  return qtype == MOE_QTYPE_Q8_0 ? "Q8_0" : qtype == MOE_QTYPE_Q4_0 ? "Q4_0" : "?";
+  switch (qtype) {
+    case MOE_QTYPE_Q8_0: return "Q8_0";
+    case MOE_QTYPE_Q4_0: return "Q4_0";
+    case MOE_QTYPE_Q4_1: return "Q4_1";
+    case MOE_QTYPE_Q5_0: return "Q5_0";
+    case MOE_QTYPE_Q5_1: return "Q5_1";
+    default: return "?";
+  }
 }
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }

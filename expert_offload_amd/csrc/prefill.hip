@@ -66,16 +66,20 @@ __global__ __launch_bounds__(256) void prefill_tiles_kernel(const int32_t* __res
 template <int QT>
 struct WStage {
   uint32_t w[4];
-  float d;
+  uint32_t qh;
+  float d, m;
   __device__ __forceinline__ void load(const uint8_t* row, int b, int h) {
     const uint8_t* q = block_quants<QT>(row, b) + (QT == MOE_QTYPE_Q8_0 ? 16 * h : 0);
     const uint4 v = *reinterpret_cast<const uint4*>(q);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     d = block_scale<QT>(row, b);
+    if constexpr (qtype_has_min(QT)) m = block_min<QT>(row, b);
+    if constexpr (qtype_has_qh(QT)) qh = block_qh<QT>(row, b);
   }
-  // d*q (Q8_0) or d*(q-8) (Q4_0) as fma(d, u, -OFF*d) with u the unsigned
-  // code: the product of an 11-bit scale and a code of at most 8 bits is
-  // exact in fp32, so the only rounding is the final one to bf16.
+  // d*q (Q8_0), d*(q-8) (Q4_0), d*(q-16) (Q5_0) as fma(d, u, -OFF*d) with u
+  // the unsigned code, or fma(d, u, m) (Q4_1, Q5_1): the product of an
+  // 11-bit scale and a code of at most 8 bits is exact in fp32, so the only
+  // roundings are the fma's (none without m) and the final one to bf16.
   __device__ __forceinline__ void store(__bf16* dst, int h) const {
     bf16x8 o[2];
     if constexpr (QT == MOE_QTYPE_Q8_0) {
@@ -87,11 +91,12 @@ struct WStage {
         for (int j = 0; j < 4; ++j) o[i / 2][(i & 1) * 4 + j] = (__bf16)fmaf(d, (float)((u >> (8 * j)) & 0xFFu), off);
       }
     } else {
-      const float off = -8.0f * d;
+      const float off = qtype_has_min(QT) ? m : -qtype_code_off(QT) * d;
       const int sh = 4 * h;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t nib = (w[i] >> sh) & 0x0F0F0F0Fu;
+        uint32_t nib = (w[i] >> sh) & 0x0F0F0F0Fu;
+        if constexpr (qtype_has_qh(QT)) nib |= spread_fifth_bits(qh >> (16 * h + 4 * i));
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[i / 2][(i & 1) * 4 + j] = (__bf16)fmaf(d, (float)((nib >> (8 * j)) & 0xFFu), off);
       }
@@ -279,6 +284,25 @@ size_t prefill_ws_bytes(int T, int k, int I, int E) {
   return 256 + ((prefill_max_tiles(P, E) * sizeof(int2) + 255) / 256) * 256 + P * I * sizeof(__bf16);
 }
 
+template <bool GATEUP>
+static void launch_prefill_gemm(const FfnParams& p, unsigned grid, hipStream_t s, const __bf16* x, const int2* tiles,
+                                const int* count, int ntn, __bf16* hbuf) {
+#define MOE_PF(Q)                                                                                          \
+  case Q:                                                                                                  \
+    launch(prefill_gemm_kernel<Q, GATEUP, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, x, tiles, count, ntn, \
+           hbuf);                                                                                          \
+    break;
+  switch (p.qtype) {
+    MOE_PF(MOE_QTYPE_Q8_0)
+    MOE_PF(MOE_QTYPE_Q4_0)
+    MOE_PF(MOE_QTYPE_Q4_1)
+    MOE_PF(MOE_QTYPE_Q5_0)
+    MOE_PF(MOE_QTYPE_Q5_1)
+    default: break;
+  }
+#undef MOE_PF
+}
+
 int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws, hipStream_t s) {
   const size_t P = (size_t)p.T * p.k;
   const int max_tiles = prefill_max_tiles(P, p.E);
@@ -296,20 +320,14 @@ int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws
     KernelTimer timer(ctx, "ffn_gateup", s);
     const int ntn = p.I / (kTN / 2);
     const unsigned grid = kXcds * row_groups * (unsigned)ntn;
-    if (p.qtype == MOE_QTYPE_Q4_0)
-      launch(prefill_gemm_kernel<MOE_QTYPE_Q4_0, true, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, (const __bf16*)x, tiles, count, ntn, hbuf);
-    else
-      launch(prefill_gemm_kernel<MOE_QTYPE_Q8_0, true, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, (const __bf16*)x, tiles, count, ntn, hbuf);
+    launch_prefill_gemm<true>(p, grid, s, (const __bf16*)x, tiles, count, ntn, hbuf);
   }
   if ((rc = check_launch("prefill_gateup_kernel"))) return rc;
   {
     KernelTimer timer(ctx, "ffn_down", s);
     const int ntn = p.H / kTN;
     const unsigned grid = kXcds * row_groups * (unsigned)ntn;
-    if (p.qtype == MOE_QTYPE_Q4_0)
-      launch(prefill_gemm_kernel<MOE_QTYPE_Q4_0, false, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, (const __bf16*)x, tiles, count, ntn, hbuf);
-    else
-      launch(prefill_gemm_kernel<MOE_QTYPE_Q8_0, false, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, (const __bf16*)x, tiles, count, ntn, hbuf);
+    launch_prefill_gemm<false>(p, grid, s, (const __bf16*)x, tiles, count, ntn, hbuf);
   }
   return check_launch("prefill_down_kernel");
 }

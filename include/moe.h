@@ -6,7 +6,8 @@
  * treats VRAM as a cache of experts ("FreeToken github moe: Setup Guide &
  * MoE Runtime Comparison", introduction; "FreeToken Inference Engine: 3x
  * Speed Boost for MoE Models", section "From Static Allocation to Dynamic
- * Scheduling").  Expert banks are ggml Q4_0 / Q8_0 blocks in one GPU slot
+ * Scheduling").  Expert banks are ggml blocks of the standard types
+ * (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0) in one GPU slot
  * pool of a single type (FreeToken fork README, "Quant types" and "Known
  * limits"); decode and prefill use different kernel families there (matrix
  * x vector for decode, matrix x matrix for prefill, same section).  One
@@ -61,7 +62,13 @@ enum {
 };
 
 /* Block types, numbered as in ggml's type enum. */
-enum { MOE_QTYPE_Q4_0 = 2, MOE_QTYPE_Q8_0 = 8 };
+enum {
+  MOE_QTYPE_Q4_0 = 2,
+  MOE_QTYPE_Q4_1 = 3,
+  MOE_QTYPE_Q5_0 = 6,
+  MOE_QTYPE_Q5_1 = 7,
+  MOE_QTYPE_Q8_0 = 8
+};
 
 /* Activation dtypes. */
 enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
@@ -109,9 +116,17 @@ int moe_ctx_kernel_time(moe_ctx* ctx, const char* kernel, int* count,
                         double* total_ms);
 
 /* ------------------------------------------------------------ block types
- * Q8_0: 32 weights, fp16 scale d + 32 int8 q (34 B), w = d*q.
- * Q4_0: 32 weights, fp16 scale d + 16 nibble bytes (18 B), w = d*(q-8);
- *       byte j holds element j (low nibble) and element j+16 (high nibble).
+ * The standard ggml types (fork README, "Quant types"), 32 weights per
+ * block, fields little endian in this order:
+ * Q8_0: fp16 d, 32 int8 q (34 B), w = d*q.
+ * Q4_0: fp16 d, 16 nibble bytes (18 B), w = d*(q-8), q in 0..15.
+ * Q4_1: fp16 d, fp16 m, 16 nibble bytes (20 B), w = d*q + m, q in 0..15.
+ * Q5_0: fp16 d, 4 bytes of fifth bits, 16 nibble bytes (22 B),
+ *       w = d*(q-16), q in 0..31.
+ * Q5_1: fp16 d, fp16 m, 4 bytes of fifth bits, 16 nibble bytes (24 B),
+ *       w = d*q + m, q in 0..31.
+ * Nibble byte j holds element j (low nibble) and element j+16 (high
+ * nibble); bit j of the little-endian fifth-bit word is bit 4 of element j.
  * Unknown qtype -> MOE_ERR_UNSUPPORTED_QTYPE and the outputs untouched. */
 int moe_qtype_info(int qtype, int* block_elems, int* block_bytes);
 
@@ -119,8 +134,10 @@ int moe_qtype_info(int qtype, int* block_elems, int* block_bytes);
  * Device layout of one expert slot (same byte count as the ggml blocks):
  * gate [I rows][H], up [I rows][H], down [H rows][I], each matrix row-major
  * by rows, each row a sequence of groups of 8 blocks; a group is the 8
- * blocks' quant bytes (ggml order, 8*32 B for Q8_0, 8*16 B for Q4_0)
- * followed by their 8 fp16 scales (16 B), so every group is 16-B aligned.
+ * blocks' quant bytes (ggml order, 8*32 B for Q8_0, 8*16 B otherwise),
+ * then for Q5_0 / Q5_1 their 8 fifth-bit words (32 B), then their 8 fp16
+ * scales d (16 B), then for Q4_1 / Q5_1 their 8 fp16 offsets m (16 B), so
+ * every group is 16-B aligned.
  * The pinned host pool holds experts in this same layout, so staging an
  * expert into VRAM is one verbatim copy ("FreeToken Inference Engine",
  * FTW paragraph: load straight into the engine's layout, no repacking).

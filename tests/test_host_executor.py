@@ -22,6 +22,9 @@ CASES = [
     gi.Workload(21, "host_q8_0", H=256, E=2, k=1, I=512, qtype="q8_0", batches=(3,)),
     gi.Workload(22, "host_q4_0", H=512, E=2, k=1, I=256, qtype="q4_0", batches=(3,)),
     gi.Workload(23, "host_q4_0_wide", H=2048, E=2, k=1, I=768, qtype="q4_0", batches=(2,)),
+    gi.Workload(24, "host_q4_1", H=512, E=2, k=1, I=256, qtype="q4_1", batches=(3,)),
+    gi.Workload(25, "host_q5_0", H=256, E=2, k=1, I=512, qtype="q5_0", batches=(2,)),
+    gi.Workload(26, "host_q5_1", H=512, E=2, k=1, I=768, qtype="q5_1", batches=(3,)),
 ]
 
 

@@ -34,7 +34,11 @@ def test_exports_every_declared_symbol():
 def test_qtype_table():
     assert moe.moe_qtype_info(L.QTYPE["q8_0"]) == (32, 34)
     assert moe.moe_qtype_info(L.QTYPE["q4_0"]) == (32, 18)
-    for bad in (0, 1, 3, 6, 7, 12, -1, 99):
+    assert moe.moe_qtype_info(L.QTYPE["q4_1"]) == (32, 20)
+    assert moe.moe_qtype_info(L.QTYPE["q5_0"]) == (32, 22)
+    assert moe.moe_qtype_info(L.QTYPE["q5_1"]) == (32, 24)
+    assert L.QTYPE == {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8}  # ggml's type numbers
+    for bad in (0, 1, 4, 5, 9, 10, 12, 14, -1, 99):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_qtype_info(bad)
         assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"
@@ -48,9 +52,10 @@ def test_unsupported_qtype_leaves_outputs_untouched():
 
 
 @pytest.mark.parametrize("qt,H,I", [("q8_0", 256, 512), ("q8_0", 2048, 768), ("q4_0", 2048, 768),
-                                    ("q4_0", 2048, 512), ("q4_0", 4096, 2048)])
+                                    ("q4_0", 2048, 512), ("q4_0", 4096, 2048), ("q4_1", 2048, 768),
+                                    ("q5_0", 2048, 768), ("q5_1", 4096, 2048)])
 def test_slot_bytes_equal_ggml_bytes(qt, H, I):
-    per_block = {"q8_0": 34, "q4_0": 18}[qt]
+    per_block = {"q8_0": 34, "q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24}[qt]
     assert moe.moe_slot_bytes(L.QTYPE[qt], H, I) == 3 * H * I // 32 * per_block
 
 
@@ -64,25 +69,40 @@ def test_slot_bytes_errors():
 
 
 def _unpack_doc_layout(qt, rows, cols, packed):
-    """Read the documented device layout back into ggml blocks."""
+    """Read the documented device layout back into ggml blocks: per group of
+    8 blocks the quant bytes, then the fifth-bit words (Q5_*), the scales d,
+    the offsets m (Q4_1, Q5_1); a ggml block is d, [m], [fifth bits], quants."""
     qb = 32 if qt == "q8_0" else 16
-    gbytes = 8 * qb + 16
-    out = np.empty((rows, cols // 32, qb + 2), dtype=np.uint8)
+    has_m, has_qh = qt in ("q4_1", "q5_1"), qt in ("q5_0", "q5_1")
+    bb = gi.BLOCK_BYTES[qt]
+    gbytes = 8 * bb
+    qh_off, d_off = 8 * qb, 8 * qb + (32 if has_qh else 0)
+    m_off = d_off + 16
+    out = np.empty((rows, cols // 32, bb), dtype=np.uint8)
     rb = cols // 256 * gbytes
     for r in range(rows):
         for g in range(cols // 256):
             grp = packed[r * rb + g * gbytes: r * rb + (g + 1) * gbytes]
             for b in range(8):
-                out[r, 8 * g + b, 2:] = grp[b * qb:(b + 1) * qb]
-                out[r, 8 * g + b, :2] = grp[8 * qb + 2 * b: 8 * qb + 2 * b + 2]
+                blk = out[r, 8 * g + b]
+                blk[0:2] = grp[d_off + 2 * b: d_off + 2 * b + 2]
+                at = 2
+                if has_m:
+                    blk[2:4] = grp[m_off + 2 * b: m_off + 2 * b + 2]
+                    at = 4
+                if has_qh:
+                    blk[at:at + 4] = grp[qh_off + 4 * b: qh_off + 4 * b + 4]
+                    at += 4
+                blk[at:] = grp[b * qb:(b + 1) * qb]
     return out
 
 
-@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0", "q4_1", "q5_0", "q5_1"])
 def test_pack_expert_layout(qt):
     H, I = 512, 256
     rng = np.random.default_rng(1)
-    quant = gi.quantize_q8_0 if qt == "q8_0" else gi.quantize_q4_0
+    quant = {"q8_0": gi.quantize_q8_0, "q4_0": gi.quantize_q4_0, "q4_1": gi.quantize_q4_1,
+             "q5_0": gi.quantize_q5_0, "q5_1": gi.quantize_q5_1}[qt]
     g = quant(rng.standard_normal((I, H)).astype(np.float32))
     u = quant(rng.standard_normal((I, H)).astype(np.float32))
     d = quant(rng.standard_normal((H, I)).astype(np.float32))
@@ -128,7 +148,7 @@ def test_workspace_queries():
     args = L.moe_ffn_args(qtype=8, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, n_slots=128,
                           slot_bytes=moe.moe_slot_bytes(8, 2048, 768))
     assert moe.moe_expert_ffn_workspace_size(args) >= 16 * 8 * 768 * 4
-    bad = L.moe_ffn_args(qtype=3, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, slot_bytes=1)
+    bad = L.moe_ffn_args(qtype=12, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, slot_bytes=1)
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_expert_ffn_workspace_size(bad)
     assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"
