@@ -38,8 +38,8 @@ ROOT = os.path.dirname(PKG)
 _DECODE = ["csrc/decode_gemv.h", "csrc/decode_ctl.h", "csrc/route_common.h", "csrc/ffn.h",
            "csrc/device_common.h", "csrc/moe_internal.h"]
 KERNEL_SOURCES = {
-    "ffn_gateup_decode": ["csrc/decode.hip"] + _DECODE,
-    "ffn_down_decode": ["csrc/decode.hip"] + _DECODE,
+    "ffn_gateup_decode": ["csrc/decode_impl.h", "csrc/decode_q8_0.hip"] + _DECODE,
+    "ffn_down_decode": ["csrc/decode_impl.h", "csrc/decode_q8_0.hip"] + _DECODE,
     "prefill_gemm_kernel": ["csrc/prefill.hip", "csrc/ffn.h", "csrc/device_common.h", "csrc/moe_internal.h"],
 }
 # Calibration kernels, in order of preference: ROCm's device-to-device copy
