@@ -52,100 +52,16 @@ struct RouteLds {
   uint64_t taken[kRouteInFfnMaxPairs][kMaxE / kWave];  // per token (T <= T*k <= 64)
   int ids[kRouteInFfnMaxPairs];
   int pos[kRouteInFfnMaxPairs];
-  float val[kRouteInFfnMaxPairs];  // the selected logits, (token, rank) order
 };
 
-// Threshold selection.  tau, the smallest of G >= k group maxima (groups of
-// 64 / G lanes), is at most the k-th largest logit: the G maxima are G
-// different logits, all >= tau.  So every member of the top k is >= tau,
-// and a logit below tau outranks no logit >= tau.  The candidates (logits
-// >= tau, usually about twice k) are compacted into LDS and ranked among
-// themselves: the rank of a candidate is the number of candidates whose
-// (logit, id) comes first (larger logit, or equal logit and smaller id), and
-// a rank below k is its place in the output.  This replaces k rounds of
-// wave-wide arg-max with a few DPP steps and one pass of broadcast reads.
-template <int NS>
+// Per-wavefront scratch of the top-k (threshold selection).
 struct RankLds {
-  uint64_t key[4][kWave * NS];  // per wavefront: candidate keys
+  TopkScratch s[4];
 };
-
-// 64-bit key whose unsigned order puts (larger logit, then smaller id)
-// first.  -0 is made +0 so that the two tie, as they do as floats.
-__device__ __forceinline__ uint64_t rank_key(float v, int e) {
-  if (v == 0.0f) v = 0.0f;
-  uint32_t b = __float_as_uint(v);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-__device__ __forceinline__ float rank_key_value(uint64_t key) {
-  const uint32_t b = (uint32_t)(key >> 32);
-  return __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
-}
-__device__ __forceinline__ int rank_key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// One wavefront, one token: v[i] = logit of id lane + 64 i (NaN already
-// -inf), ok[i] false past E.  Writes ids[0..k) and val[0..k) (the chosen
-// ids and logits by rank) and the selection bitmasks taken[0..NS), in LDS;
-// cand is the wavefront's scratch of 64 * NS keys.
-template <int NS>
-__device__ __forceinline__ void wave_select_thresh(const float (&v)[NS], const bool (&ok)[NS], int k, int* ids,
-                                                   float* val, uint64_t* taken, uint64_t* cand) {
-  const int lane = threadIdx.x & (kWave - 1);
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-    if (ok[i]) m = fmaxf(m, v[i]);
-  // group maxima over 8, 4, 2 or 1 lanes: 8, 16, 32 or 64 groups >= k
-  if (k <= 32) m = fmaxf(m, dpp_f32<kDppXor1>(m));
-  if (k <= 16) m = fmaxf(m, dpp_f32<kDppXor2>(m));
-  if (k <= 8) m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
-  float tau = fminf(m, dpp_f32<kDppXor1>(m));
-  tau = fminf(tau, dpp_f32<kDppXor2>(tau));
-  tau = fminf(tau, dpp_f32<kDppHalfMirror>(tau));
-  tau = fminf(tau, dpp_f32<kDppMirror>(tau));
-  {
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 48));
-    tau = fminf(fminf(r0, r1), fminf(r2, r3));
-  }
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const bool c = ok[i] && v[i] >= tau;
-    const uint64_t bm = __ballot(c);
-    if (c) cand[n + __builtin_popcountll(bm & below)] = rank_key(v[i], lane + kWave * i);
-    n += __builtin_popcountll(bm);
-  }
-  if (lane < NS) taken[lane] = 0;
-  wave_lds_sync();
-  for (int c0 = 0; c0 < n; c0 += kWave) {
-    const int ci = c0 + lane;
-    const uint64_t mine = ci < n ? cand[ci] : ~0ull;
-    int cnt = 0;
-#pragma unroll 4
-    for (int j = 0; j < n; ++j) cnt += cand[j] > mine ? 1 : 0;
-    if (ci < n && cnt < k) {
-      const int e = rank_key_id(mine);
-      ids[cnt] = e;
-      val[cnt] = rank_key_value(mine);
-      atomicOr(reinterpret_cast<unsigned long long*>(&taken[e / kWave]), 1ull << (e % kWave));
-    }
-  }
-  wave_lds_sync();
-}
 
 template <int NT, int NS>
 __device__ __forceinline__ void route_select(const FfnParams& p, const RouteArgs& ra, CtlLds& s, RouteLds& r,
-                                             RankLds<NS>& q) {
+                                             RankLds& q) {
   const int E = p.E, T = p.T, k = p.k;
   float* lo = blockIdx.x == 0 ? ra.logits_out : nullptr;
   // the slot table goes to registers first and to LDS after the selection,
@@ -157,36 +73,10 @@ __device__ __forceinline__ void route_select(const FfnParams& p, const RouteArgs
     const int i = threadIdx.x + NT * u;
     sl[u] = i < E ? p.slot_table[i] : 0;
   }
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  for (int t = wave; t < T; t += NT / kWave) {
-    const float* src = ra.logits + (size_t)t * E;
-    float v[NS];
-    bool ok[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int e = lane + kWave * i;
-      ok[i] = e < E;
-      v[i] = ok[i] ? src[e] : -INFINITY;
-    }
-    if (ra.bias) {
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-        if (ok[i]) v[i] += ra.bias[lane + kWave * i];
-    }
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (ok[i] && lo) lo[(size_t)t * E + lane + kWave * i] = v[i];
-      if (v[i] != v[i]) v[i] = -INFINITY;
-    }
-    wave_select_thresh<NS>(v, ok, k, r.ids + t * k, r.val + t * k, r.taken[t], q.key[wave]);
-    // renormalised softmax over the chosen logits, lane j holding rank j:
-    // the arithmetic of wave_topk_select
-    const float my_val = lane < k ? r.val[t * k + lane] : -INFINITY;
-    const float m0 = r.val[t * k];
-    const float ex = lane < k ? expf(my_val - m0) : 0.0f;
-    const float sum = wave_sum_dpp(ex);
-    if (lane < k) s.w[t * k + lane] = ex / sum;
-  }
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += NT / kWave)
+    wave_topk_ns<NS>(ra.logits + (size_t)t * E, ra.bias, E, k, lo ? lo + (size_t)t * E : nullptr, nullptr, nullptr,
+                     r.ids + t * k, s.w + t * k, r.taken[t], &q.s[wave]);
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int i = threadIdx.x + NT * u;

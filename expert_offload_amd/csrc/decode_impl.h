@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
   constexpr int RPP = kWave / LPR, RW = RPP * RPL, NI = RW / 2;
   __shared__ CtlLds ctl;
   __shared__ RouteLds rlds;
-  __shared__ RankLds<RNS == 0 ? 1 : RNS> rank_lds;
+  __shared__ RankLds rank_lds;
   int n_active;
   if constexpr (ROUTE) {
     route_select<256, RNS>(p, ra, ctl, rlds, rank_lds);

@@ -100,10 +100,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ src
                                                    const float* __restrict__ bias, int T, int E,
                                                    int k, float* __restrict__ logits_out,
                                                    int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ TopkScratch sc[4];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   wave_topk(src + (size_t)t * E, bias, E, k, logits_out ? logits_out + (size_t)t * E : nullptr,
-            ids + (size_t)t * k, w + (size_t)t * k, nullptr);
+            ids + (size_t)t * k, w + (size_t)t * k, nullptr, nullptr, nullptr, &sc[threadIdx.x >> 6]);
 }
 
 // Top-k of every token plus the stable grouping, in one workgroup (decode
@@ -123,11 +124,12 @@ __global__ __launch_bounds__(kTopkPermuteThreads) void topk_permute_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
     int32_t* __restrict__ active, int* __restrict__ err) {
   __shared__ TopkPermuteLds s;
+  __shared__ TopkScratch sc[kTopkPermuteThreads / kWave];
   const int wave = threadIdx.x >> 6;
   constexpr int waves = kTopkPermuteThreads / kWave;
   for (int t = wave; t < T; t += waves)
     wave_topk(src + (size_t)t * E, bias, E, k, logits_out ? logits_out + (size_t)t * E : nullptr,
-              ids + (size_t)t * k, w + (size_t)t * k, s.ids + t * k);
+              ids + (size_t)t * k, w + (size_t)t * k, s.ids + t * k, nullptr, nullptr, &sc[wave]);
   __syncthreads();
   if (T * k <= 1024) {
     if (wave == 0) wave_permute(s.ids, T * k, E, offsets, sorted_pairs, pair_pos, active, err, s.perm.cnt, s.perm.cur);

@@ -1,5 +1,6 @@
-// Device routines shared by the routing kernels: the wavefront top-k and
-// the single-workgroup stable grouping of pairs by expert.
+// Device routines shared by the routing kernels: the wavefront top-k (a
+// threshold selection, with k rounds of arg-max as the fallback) and the
+// single-workgroup stable grouping of pairs by expert.
 #pragma once
 
 #include <climits>
@@ -61,15 +62,116 @@ __device__ __forceinline__ void wave_topk_select(float (&v)[NS], bool (&ok)[NS],
   }
 }
 
-// The top k of token t's E logits (src row, plus bias when given), by
-// wave_topk_select.  NaN logits count as -inf.  Writes the logits used to
-// logits_out when it is set.
+// ------------------------------------------------- threshold selection
+// tau, the smallest of G >= k group maxima (groups of 64 / G lanes), is at
+// most the k-th largest logit: the G maxima are G different logits, all
+// >= tau.  So every member of the top k is >= tau, and a logit below tau
+// outranks no logit >= tau.  The candidates (logits >= tau, usually about
+// twice k) are compacted into LDS and ranked among themselves: the rank of
+// a candidate is the number of candidates whose (logit, id) comes first
+// (larger logit, or equal logit and smaller id), and a rank below k is its
+// place in the output.  A few DPP steps and one pass of broadcast reads
+// replace the k rounds of wave_topk_select, which remains the path when
+// more than kTopkCand logits tie at or above tau.
+constexpr int kTopkCand = 128;
+struct TopkScratch {
+  uint64_t cand[kTopkCand];
+  float val[kMaxK];
+};
+
+// 64-bit key whose unsigned order puts (larger logit, then smaller id)
+// first.  -0 is made +0 so that the two tie, as they do as floats.
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  if (v == 0.0f) v = 0.0f;
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ float rank_key_value(uint64_t key) {
+  const uint32_t b = (uint32_t)(key >> 32);
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
+}
+__device__ __forceinline__ int rank_key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wavefront: v[i] = logit of id lane + 64 i (NaN already -inf), ok[i]
+// false past E.  Returns false (having written nothing) when more than
+// kTopkCand logits are >= tau.  Otherwise writes ids[0..k) and ids_copy
+// (each may be NULL), sc.val[0..k) (the chosen logits by rank) and, with
+// `taken` (LDS), the selection bitmasks taken[0..NS).
+template <int NS>
+__device__ __forceinline__ bool wave_select_thresh(const float (&v)[NS], const bool (&ok)[NS], int k, int32_t* ids,
+                                                   int32_t* ids_copy, uint64_t* taken, TopkScratch& sc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (ok[i]) m = fmaxf(m, v[i]);
+  // group maxima over 8, 4, 2 or 1 lanes: 8, 16, 32 or 64 groups >= k
+  if (k <= 32) m = fmaxf(m, dpp_f32<kDppXor1>(m));
+  if (k <= 16) m = fmaxf(m, dpp_f32<kDppXor2>(m));
+  if (k <= 8) m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
+  float tau = fminf(m, dpp_f32<kDppXor1>(m));
+  tau = fminf(tau, dpp_f32<kDppXor2>(tau));
+  tau = fminf(tau, dpp_f32<kDppHalfMirror>(tau));
+  tau = fminf(tau, dpp_f32<kDppMirror>(tau));
+  {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 48));
+    tau = fminf(fminf(r0, r1), fminf(r2, r3));
+  }
+  uint64_t bm[NS];
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    bm[i] = __ballot(ok[i] && v[i] >= tau);
+    n += __builtin_popcountll(bm[i]);
+  }
+  if (n > kTopkCand) return false;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if ((bm[i] >> lane) & 1) sc.cand[base + __builtin_popcountll(bm[i] & below)] = rank_key(v[i], lane + kWave * i);
+    base += __builtin_popcountll(bm[i]);
+  }
+  if (taken && lane < NS) taken[lane] = 0;
+  wave_lds_sync();
+  for (int c0 = 0; c0 < n; c0 += kWave) {
+    const int ci = c0 + lane;
+    const uint64_t mine = ci < n ? sc.cand[ci] : ~0ull;
+    int cnt = 0;
+#pragma unroll 4
+    for (int j = 0; j < n; ++j) cnt += sc.cand[j] > mine ? 1 : 0;
+    if (ci < n && cnt < k) {
+      const int e = rank_key_id(mine);
+      if (ids) ids[cnt] = e;
+      if (ids_copy) ids_copy[cnt] = e;
+      sc.val[cnt] = rank_key_value(mine);
+      if (taken) atomicOr(reinterpret_cast<unsigned long long*>(&taken[e / kWave]), 1ull << (e % kWave));
+    }
+  }
+  wave_lds_sync();
+  return true;
+}
+
+// The top k of token t's E logits (src row, plus bias when given): the
+// threshold selection when `scratch` (LDS) is given and the candidates fit,
+// else wave_topk_select.  NaN logits count as -inf.  Writes the logits used
+// to logits_out when it is set.  Both paths give the same ids and weights.
 template <int NS>
 __device__ __forceinline__ void wave_topk_ns(const float* __restrict__ src, const float* __restrict__ bias,
                                              int E, int k, float* __restrict__ logits_out,
                                              int32_t* __restrict__ ids, float* __restrict__ w,
                                              int32_t* ids_copy, float* w_copy = nullptr,
-                                             uint64_t* taken = nullptr) {
+                                             uint64_t* taken = nullptr, TopkScratch* scratch = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
   float v[NS];
   bool ok[NS];
@@ -89,6 +191,19 @@ __device__ __forceinline__ void wave_topk_ns(const float* __restrict__ src, cons
     if (ok[i] && logits_out) logits_out[lane + kWave * i] = v[i];
     if (v[i] != v[i]) v[i] = -INFINITY;
   }
+  if (scratch && wave_select_thresh<NS>(v, ok, k, ids, ids_copy, taken, *scratch)) {
+    // renormalised softmax over the chosen logits, lane j holding rank j:
+    // the arithmetic of wave_topk_select
+    const float my_val = lane < k ? scratch->val[lane] : -INFINITY;
+    const float m0 = scratch->val[0];
+    const float ex = lane < k ? expf(my_val - m0) : 0.0f;
+    const float s = wave_sum_dpp(ex);
+    if (lane < k) {
+      if (w) w[lane] = ex / s;
+      if (w_copy) w_copy[lane] = ex / s;
+    }
+    return;
+  }
   wave_topk_select<NS>(v, ok, E, k, ids, w, ids_copy, w_copy, taken);
 }
 
@@ -96,12 +211,12 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ src, const f
                                           int E, int k, float* __restrict__ logits_out,
                                           int32_t* __restrict__ ids, float* __restrict__ w,
                                           int32_t* ids_copy, float* w_copy = nullptr,
-                                          uint64_t* taken = nullptr) {
-  if (E <= 64) wave_topk_ns<1>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
-  else if (E <= 128) wave_topk_ns<2>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
-  else if (E <= 256) wave_topk_ns<4>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
-  else if (E <= 512) wave_topk_ns<8>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
-  else wave_topk_ns<16>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken);
+                                          uint64_t* taken = nullptr, TopkScratch* sc = nullptr) {
+  if (E <= 64) wave_topk_ns<1>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken, sc);
+  else if (E <= 128) wave_topk_ns<2>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken, sc);
+  else if (E <= 256) wave_topk_ns<4>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken, sc);
+  else if (E <= 512) wave_topk_ns<8>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken, sc);
+  else wave_topk_ns<16>(src, bias, E, k, logits_out, ids, w, ids_copy, w_copy, taken, sc);
 }
 
 // Stable grouping of the P = T*k <= 64 pairs of T tokens by one wavefront,
