@@ -85,6 +85,23 @@ def test_topk_exact_given_logits(ctx, T, E, k):
     assert np.abs(w - ref_w).max() <= WEIGHT_TOL * np.abs(ref_w).max()
 
 
+@pytest.mark.parametrize("E,k", [(512, 10), (256, 8), (1024, 64), (130, 3)])
+def test_topk_many_equal_candidates(ctx, E, k):
+    """More logits tied at the top than the threshold selection's candidate
+    scratch holds (its fallback, k rounds of arg-max, takes over), next to
+    rows that fit: lowest ids first among equals, weights uniform."""
+    T = 4
+    rng = np.random.default_rng(E + k)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    l[0] = 1.0                    # every logit equal
+    l[1, : E - 1] = 2.5           # all but the last equal and largest
+    l[2, rng.permutation(E)[:200 % E]] = 9.0  # a block of equal maxima at random ids
+    ids, w, _ = _route_given(ctx, l, k)
+    np.testing.assert_array_equal(ids, oracle.topk_select(l, k))
+    assert ids[0].tolist() == list(range(k)) and ids[1].tolist() == list(range(k))
+    np.testing.assert_allclose(w[0], np.full(k, 1.0 / k), rtol=1e-6)
+
+
 def test_topk_bias_and_nan(ctx):
     E, k = 16, 4
     l = np.zeros((2, E), dtype=np.float32)
@@ -483,6 +500,26 @@ def test_decode_layer_selection_ties(ctx, decode_layer, T):
     np.testing.assert_array_equal(one["ids"], oracle.topk_select(lg_ref, wl.k))
     ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, logits=lg_ref)
     np.testing.assert_allclose(one["w"], ref["w"], rtol=1e-5, atol=1e-7)
+    assert max_rel_err(one["out"], ref["out"]) <= DECODE_TOL
+
+
+def test_decode_layer_selection_fallback(ctx, wide_layer):
+    """512 experts with every logit equal, and 300 equal maxima: more
+    candidates than the threshold selection holds, so the in-kernel routing
+    falls back to arg-max rounds; still the oracle's ids and bit-identical
+    to the two-call path."""
+    rl, wl = wide_layer, wide_layer.wl
+    T = 2
+    x = gi.activations(wl, T)
+    lg = np.zeros((T, wl.E), dtype=np.float32)
+    lg[1] = -1.0
+    lg[1, np.random.default_rng(9).permutation(wl.E)[:300]] = 0.5
+    _, two = _layer_outputs(ctx, rl, T, x, None, None, lg, True)
+    _, one = _layer_outputs(ctx, rl, T, x, None, None, lg, "layer")
+    for key in two:
+        np.testing.assert_array_equal(one[key], two[key], err_msg=key)
+    np.testing.assert_array_equal(one["ids"], oracle.topk_select(lg, wl.k))
+    ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, logits=lg)
     assert max_rel_err(one["out"], ref["out"]) <= DECODE_TOL
 
 
