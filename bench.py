@@ -272,10 +272,11 @@ def prefill_extra(ctx, steps=10, warmup=3, qtype=None):
             kt[name] = t / n
     moe.moe_ctx_set_timing(ctx, False)
     flops = 2.0 * T * wl.k * 3 * wl.H * wl.I
-    ffn_ms = kt.get("ffn_gateup", 0) + kt.get("ffn_down", 0)
+    gu_ms = kt.get("ffn_gateup", 0)
+    ffn_ms = gu_ms + kt.get("ffn_down", 0)
     tflops = flops / (ffn_ms * 1e-3) / 1e12 if ffn_ms else None
     gate_up_flops = 2.0 * T * wl.k * 2 * wl.H * wl.I
-    gu_tflops = gate_up_flops / (kt["ffn_gateup"] * 1e-3) / 1e12 if kt.get("ffn_gateup") else None
+    gu_tflops = gate_up_flops / (gu_ms * 1e-3) / 1e12 if gu_ms else None
     return {
         "workload": wl.name, "tokens": T, "layer_ms": ms, "tokens_per_s": T / (ms * 1e-3),
         "kernel_ms": kt, "ffn_tflops": tflops, "ffn_frac_bf16_peak": tflops / BF16_PEAK_TFLOPS if tflops else None,

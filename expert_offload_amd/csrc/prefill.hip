@@ -40,22 +40,34 @@ constexpr int kXcds = 8;
 
 // ------------------------------------------------------------ tile list
 // One workgroup: for every expert with pairs (and not masked out), its
-// tiles of `tile_rows` rows (expert, first row) in expert order.
+// tiles of `tile_rows` rows (expert, first row) in expert order, except
+// that a last tile of at most `small_rows` rows goes to a second list,
+// stored right after the first: count[0] tiles, then count[1] small ones.
 __global__ __launch_bounds__(256) void prefill_tiles_kernel(const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ mask, int E, int tile_rows,
-                                                            int2* __restrict__ tiles, int* __restrict__ count) {
-  __shared__ int s_n[kMaxE];
-  __shared__ int s_base[kMaxE];
+                                                            int small_rows, int2* __restrict__ tiles,
+                                                            int* __restrict__ count) {
+  __shared__ int s_n[kMaxE], s_base[kMaxE], s_ns[kMaxE], s_sbase[kMaxE];
   __shared__ int s_wave[4];
   for (int e = threadIdx.x; e < E; e += 256) {
     const int m = (mask && !mask[e]) ? 0 : offsets[e + 1] - offsets[e];
-    s_n[e] = (m + tile_rows - 1) / tile_rows;
+    const int rem = m % tile_rows;
+    const bool small = rem > 0 && rem <= small_rows;
+    s_n[e] = m / tile_rows + (rem > small_rows ? 1 : 0);
+    s_ns[e] = small ? 1 : 0;
   }
   __syncthreads();
   const int total = block_exclusive_scan<256>(s_n, s_base, E, s_wave);
-  for (int e = threadIdx.x; e < E; e += 256)
+  __syncthreads();
+  const int total_small = block_exclusive_scan<256>(s_ns, s_sbase, E, s_wave);
+  for (int e = threadIdx.x; e < E; e += 256) {
     for (int j = 0; j < s_n[e]; ++j) tiles[s_base[e] + j] = make_int2(e, j * tile_rows);
-  if (threadIdx.x == 0) *count = total;
+    if (s_ns[e]) tiles[total + s_sbase[e]] = make_int2(e, s_n[e] * tile_rows);
+  }
+  if (threadIdx.x == 0) {
+    count[0] = total;
+    count[1] = total_small;
+  }
 }
 
 // ----------------------------------------------------- weight staging
@@ -111,20 +123,17 @@ struct WStage {
 // rows, epilogue h = silu(g) * u into hbuf (bf16, grouped order [T*k][I]).
 // Down: A = hbuf rows (grouped order), B = 128 rows of Wd, epilogue y
 // (fp32, pair order [T*k][H]).  NW wavefronts, 64 rows each.
-template <int QT, bool GATEUP, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, const __bf16* __restrict__ x,
-                                                                  const int2* __restrict__ tiles,
-                                                                  const int* __restrict__ n_tiles, int ntn,
-                                                                  __bf16* __restrict__ hbuf) {
+// One tile (expert e, first row m0; column tile nt_i).  SPLIT: a small
+// tile (at most 64 rows, an expert's last rows), where one wavefront of
+// rows would leave the others without MFMA work: every wavefront takes the
+// same rows and two of the eight 16-column blocks (gate/up: gate block
+// `wave` and its up block `wave + 4`, so SwiGLU stays in the wavefront).
+template <int QT, bool GATEUP, int NW, bool SPLIT>
+__device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* __restrict__ x, int2 tl, int nt_i,
+                                             __bf16* __restrict__ hbuf, __bf16 (&sB)[2][kTN][kLdB],
+                                             int (&s_pair)[kWaveRows * NW]) {
   constexpr int kThreads = 64 * NW, kRows = kWaveRows * NW;
   constexpr int kUnits = 2 * 2 * kTN / kThreads;  // half blocks staged per thread and K step
-  __shared__ __attribute__((aligned(16))) __bf16 sB[2][kTN][kLdB];
-  __shared__ int s_pair[kRows];
-  const int j = blockIdx.x / kXcds;
-  const int mt_i = kXcds * (j / ntn) + (int)(blockIdx.x % kXcds);
-  const int nt_i = j % ntn;
-  if (mt_i >= *n_tiles) return;
-  const int2 tl = tiles[mt_i];
   const int e = tl.x, m0 = tl.y;
   const int pbeg = p.offsets[e];
   const int rows = min(kRows, p.offsets[e + 1] - pbeg - m0);
@@ -149,14 +158,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, c
   // (rows past the tile's end read row 0; their results are dropped)
   const int quad = lane >> 4;
   const __bf16* arow[4];
+  const int row0 = SPLIT ? 0 : kWaveRows * wave;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const int m = kWaveRows * wave + 16 * mt + (lane & 15);
+    const int m = row0 + 16 * mt + (lane & 15);
     const int mm = m < rows ? m : 0;
     arow[mt] = GATEUP ? x + (size_t)(s_pair[mm] / p.k) * p.H + 8 * quad
                       : hbuf + (size_t)(pbeg + m0 + mm) * p.I + 8 * quad;
   }
-  const bool active = kWaveRows * wave < rows;
+  const bool active = row0 < rows;
   // weight staging: unit v = tid * kUnits + u is row v / 4, block (v / 2) % 2, half v % 2
   const int v0 = tid * kUnits;
   const int brow = v0 >> 2, bblk = (v0 >> 1) & 1;
@@ -220,7 +230,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, c
     load_a(an, kc + 1);
     store_w(nxt, sdst);
     load_w(nxt, kc + 3);
-    if (active) {
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&sb[16 * wave + (lane & 15)][32 * ks + 8 * quad]);
+        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sb[16 * (wave + 4) + (lane & 15)][32 * ks + 8 * quad]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b0, acc[mt][0], 0, 0, 0);
+          acc[mt][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b1, acc[mt][4], 0, 0, 0);
+        }
+      }
+    } else if (active) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -244,6 +265,25 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, c
     step(kc + 1, sB[1], sdst0, st0, a1, a0);
   }
   if (!active) return;
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * mt + 4 * quad + r;
+        if (m >= rows) continue;
+        if constexpr (GATEUP) {
+          const float g = acc[mt][0][r], u = acc[mt][4][r];
+          hbuf[(size_t)(pbeg + m0 + m) * p.I + n0 + 16 * wave + (lane & 15)] = (__bf16)(g / (1.0f + expf(-g)) * u);
+        } else {
+          float* yrow = p.y + (size_t)s_pair[m] * p.H + n0 + (lane & 15);
+          yrow[16 * wave] = acc[mt][0][r];
+          yrow[16 * (wave + 4)] = acc[mt][4][r];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -264,6 +304,25 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, c
       }
     }
   }
+}
+
+// One launch over both lists: the tiles, then the small tiles (so the
+// small ones are dispatched last, into the big ones' tail).  Each branch is
+// a whole tile, so the two register allocations never overlap.
+template <int QT, bool GATEUP, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, const __bf16* __restrict__ x,
+                                                                  const int2* __restrict__ tiles,
+                                                                  const int* __restrict__ count, int ntn,
+                                                                  __bf16* __restrict__ hbuf) {
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][kTN][kLdB];
+  __shared__ int s_pair[kWaveRows * NW];
+  const int j = blockIdx.x / kXcds;
+  const int mt_i = kXcds * (j / ntn) + (int)(blockIdx.x % kXcds);
+  const int nt_i = j % ntn;
+  const int n_big = count[0];
+  if (mt_i >= n_big + count[1]) return;
+  if (mt_i < n_big) prefill_tile<QT, GATEUP, NW, false>(p, x, tiles[mt_i], nt_i, hbuf, sB, s_pair);
+  else prefill_tile<QT, GATEUP, NW, true>(p, x, tiles[mt_i], nt_i, hbuf, sB, s_pair);
 }
 
 bool prefill_mfma_supported(int H, int I) {
@@ -312,24 +371,23 @@ int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws
   const unsigned row_groups = (unsigned)((max_tiles + kXcds - 1) / kXcds);
   {
     KernelTimer timer(ctx, "prefill_tiles", s);
-    launch(prefill_tiles_kernel, 1, 256, 0, s, p.offsets, p.mask, p.E, kPrefillRows, tiles, count);
+    launch(prefill_tiles_kernel, 1, 256, 0, s, p.offsets, p.mask, p.E, kPrefillRows, kWaveRows, tiles, count);
   }
   int rc = check_launch("prefill_tiles_kernel");
   if (rc) return rc;
+  const __bf16* xb = (const __bf16*)x;
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
     const int ntn = p.I / (kTN / 2);
-    const unsigned grid = kXcds * row_groups * (unsigned)ntn;
-    launch_prefill_gemm<true>(p, grid, s, (const __bf16*)x, tiles, count, ntn, hbuf);
+    launch_prefill_gemm<true>(p, kXcds * row_groups * (unsigned)ntn, s, xb, tiles, count, ntn, hbuf);
   }
-  if ((rc = check_launch("prefill_gateup_kernel"))) return rc;
+  if ((rc = check_launch("prefill_gemm_kernel"))) return rc;
   {
     KernelTimer timer(ctx, "ffn_down", s);
     const int ntn = p.H / kTN;
-    const unsigned grid = kXcds * row_groups * (unsigned)ntn;
-    launch_prefill_gemm<false>(p, grid, s, (const __bf16*)x, tiles, count, ntn, hbuf);
+    launch_prefill_gemm<false>(p, kXcds * row_groups * (unsigned)ntn, s, xb, tiles, count, ntn, hbuf);
   }
-  return check_launch("prefill_down_kernel");
+  return check_launch("prefill_gemm_kernel");
 }
 
 }  // namespace moe
