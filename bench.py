@@ -60,6 +60,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cache", action="store_true", help="skip the expert-cache decode run")
+    p.add_argument("--legs", default="batches,prefill,prefill_stream,block_types,cache",
+                   help="comma-separated extra legs to run after the headline decode stack")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run a device copy and an elementwise negate of MIB MiB each, the known-size "
                         "kernels that scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -654,7 +656,10 @@ def main():
         "roofline": roofline,
         "stack_hbm_gbs": stack_bytes / (ms_per_step * 1e-3) / 1e9,
     }
-    if not args.no_extras:
+    legs = set(args.legs.split(",")) if not args.no_extras else set()
+    if args.no_cache:
+        legs.discard("cache")
+    if "batches" in legs:
         extra = {}
         for tb in wl.batches:
             if tb == T:
@@ -667,14 +672,16 @@ def main():
                               "stack_hbm_gbs": sum(decode_layer_bytes(wl, tb, a) for a in na2) / (ms2 * 1e-3) / 1e9}
             log(f"T={tb}: {ms2:.3f} ms/step, {tb / (ms2 * 1e-3):.1f} tok/s")
         result["batches"] = extra
-        del stack
-        torch.cuda.empty_cache()
+    del stack
+    torch.cuda.empty_cache()
+    if "prefill" in legs:
         try:
             result["prefill"] = prefill_extra(ctx)
             log(f"prefill: {result['prefill']['tokens_per_s']:.0f} tok/s, FFN "
                 f"{result['prefill']['ffn_tflops']:.1f} TFLOP/s")
         except Exception as e:  # reported, never silently dropped
             result["prefill"] = {"error": repr(e)}
+    if "prefill_stream" in legs:
         try:
             result["prefill_stream"] = prefill_stream_extra(ctx)
             ps = result["prefill_stream"]
@@ -684,19 +691,20 @@ def main():
                 f"efficiency {ps['overlap_efficiency']:.2f}")
         except Exception as e:
             result["prefill_stream"] = {"error": repr(e)}
+    if "block_types" in legs:
         try:
             result["block_types"] = types_extra(ctx)
         except Exception as e:
             result["block_types"] = {"error": repr(e)}
-        if not args.no_cache:
-            try:
-                result["cache"] = cache_extra(ctx, steps=args.cache_steps, sweep_steps=args.sweep_steps)
-                c = result["cache"]
-                log(f"cache: {c['tokens_per_s']:.1f} tok/s, hit rate {c['hit_rate']:.3f}, warm "
-                    f"{c['warm']['tokens_per_s']:.1f} tok/s at {c['warm']['hit_rate']:.3f}, "
-                    f"H2D {c['h2d_gbs']:.1f} GB/s of {c['h2d_copy_ceiling_gbs']:.1f}")
-            except Exception as e:
-                result["cache"] = {"error": repr(e)}
+    if "cache" in legs:
+        try:
+            result["cache"] = cache_extra(ctx, steps=args.cache_steps, sweep_steps=args.sweep_steps)
+            c = result["cache"]
+            log(f"cache: {c['tokens_per_s']:.1f} tok/s, hit rate {c['hit_rate']:.3f}, warm "
+                f"{c['warm']['tokens_per_s']:.1f} tok/s at {c['warm']['hit_rate']:.3f}, "
+                f"H2D {c['h2d_gbs']:.1f} GB/s of {c['h2d_copy_ceiling_gbs']:.1f}")
+        except Exception as e:
+            result["cache"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(wl, T, args.cpu_seconds)
