@@ -28,6 +28,7 @@
 #include <vector>
 
 #include "device_common.h"
+#include "ffn.h"
 
 namespace moe {
 
@@ -621,12 +622,13 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
   if (!out) return set_error(MOE_ERR_INVALID_ARG, "cache_decode_layer: out is NULL");
   const int E = c->E, P = T * k;
   const bool host_ok = c->policy != MOE_MISS_COPY;
-  int rc = moe_route_permute(ctx, x, MOE_DTYPE_F32, router_w, bias, logits_in, T, c->H, E, k, logits_out, topk_ids,
-                             topk_w, expert_offsets, sorted_pairs, pair_pos, active, nullptr, 0, compute_stream);
+  // the routing kernel writes the ids into the pinned staging as well
+  int rc = route_permute_impl(ctx, x, MOE_DTYPE_F32, router_w, bias, logits_in, T, c->H, E, k, logits_out, topk_ids,
+                              topk_w, expert_offsets, sorted_pairs, pair_pos, active, nullptr, 0, c->h_ids,
+                              compute_stream);
   if (rc) return rc;
   hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
-  hipError_t e = hipMemcpyAsync(c->h_ids, topk_ids, sizeof(int32_t) * P, hipMemcpyDeviceToHost, cs);
-  if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync(ids)");
+  hipError_t e;
   if (host_ok && (e = hipMemcpyAsync(c->h_x, x, sizeof(float) * (size_t)T * c->H, hipMemcpyDeviceToHost, cs)) !=
                      hipSuccess)
     return hip_error(e, "hipMemcpyAsync(x)");

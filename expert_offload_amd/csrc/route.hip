@@ -8,6 +8,7 @@
 #include <cfloat>
 #include <climits>
 
+#include "ffn.h"
 #include "route_common.h"
 
 namespace moe {
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kTopkPermuteThreads) void topk_permute_kernel(
     const float* __restrict__ src, const float* __restrict__ bias, int T, int E, int k,
     float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
-    int32_t* __restrict__ active, int* __restrict__ err) {
+    int32_t* __restrict__ active, int* __restrict__ err, int32_t* __restrict__ ids_host) {
   __shared__ TopkPermuteLds s;
   __shared__ TopkScratch sc[kTopkPermuteThreads / kWave];
   const int wave = threadIdx.x >> 6;
@@ -131,6 +132,10 @@ __global__ __launch_bounds__(kTopkPermuteThreads) void topk_permute_kernel(
     wave_topk(src + (size_t)t * E, bias, E, k, logits_out ? logits_out + (size_t)t * E : nullptr,
               ids + (size_t)t * k, w + (size_t)t * k, s.ids + t * k, nullptr, nullptr, &sc[wave]);
   __syncthreads();
+  // a copy of the ids straight into host memory for a caller that waits for
+  // them (the expert cache's lookup), instead of a separate read-back
+  if (ids_host)
+    for (int i = threadIdx.x; i < T * k; i += kTopkPermuteThreads) ids_host[i] = s.ids[i];
   if (T * k <= 1024) {
     if (wave == 0) wave_permute(s.ids, T * k, E, offsets, sorted_pairs, pair_pos, active, err, s.perm.cnt, s.perm.cur);
   } else {
@@ -231,6 +236,15 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
                                  int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
                                  int32_t* active, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
+  return route_permute_impl(ctx, x, x_dtype, router_w, bias, logits_in, T, H, E, k, logits_out, topk_ids, topk_w,
+                            expert_offsets, sorted_pairs, pair_pos, active, ws, ws_bytes, nullptr, stream);
+}
+
+namespace moe {
+int route_permute_impl(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w, const float* bias,
+                       const float* logits_in, int T, int H, int E, int k, float* logits_out, int32_t* topk_ids,
+                       float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                       int32_t* active, void* ws, size_t ws_bytes, int32_t* ids_host, void* stream) {
   if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: ctx is NULL");
   int rc = validate_route_args("moe_route_permute", x, x_dtype, router_w, logits_in, T, H, E, k, logits_out,
                           topk_ids, topk_w);
@@ -240,6 +254,8 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
   if ((rc = ensure_device(ctx))) return rc;
   hipStream_t s = (hipStream_t)stream;
   if ((long long)T * k > kFusedMaxPairs) {  // large batches: separate kernels
+    if (ids_host) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: a host copy of the ids needs T*k <= %d",
+                                   kFusedMaxPairs);
     rc = launch_route(ctx, x, x_dtype, router_w, bias, logits_in, T, H, E, k, logits_out, topk_ids, topk_w, s);
     if (rc) return rc;
     if (ws && !aligned(ws, 4)) return set_error(MOE_ERR_ALIGNMENT, "moe_route_permute: ws must be 4-byte aligned");
@@ -263,6 +279,7 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
   }
   KernelTimer timer(ctx, "topk_permute", s);
   launch(topk_permute_kernel, 1, kTopkPermuteThreads, 0, s, src, tk_bias, T, E, k, logits_in ? logits_out : nullptr, topk_ids,
-                                        topk_w, expert_offsets, sorted_pairs, pair_pos, active, ctx->d_err);
+                                        topk_w, expert_offsets, sorted_pairs, pair_pos, active, ctx->d_err, ids_host);
   return check_launch("topk_permute_kernel");
 }
+}  // namespace moe
