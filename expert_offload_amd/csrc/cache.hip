@@ -72,6 +72,7 @@ __global__ void host_rows_kernel(const float4* __restrict__ src, const int32_t* 
 
 constexpr int kEventRing = 256;
 constexpr int kCtlStagePairs = 1024;  // T*k of one cache_decode_layer call
+constexpr int kFlagPad = 64;          // the ids-ready flag sits on a line of its own after the ids
 
 }  // namespace moe
 
@@ -103,7 +104,8 @@ struct moe_cache {
   int64_t hits = 0, misses = 0;
   // staging of cache_decode_layer, allocated with the cache: the routed ids
   // (pinned host), the hit / miss expert masks (pinned host and device)
-  int32_t* h_ids = nullptr;   // [kCtlStagePairs]
+  int32_t* h_ids = nullptr;   // coherent [kCtlStagePairs + kFlagPad]: ids, then the ids-ready flag
+  int32_t ids_seq = 0;        // the last value the routing kernel was told to raise the flag to
   int32_t* h_mask = nullptr;  // [3][E]: hits, copied misses, host misses
   int32_t* d_mask = nullptr;  // [3][E]
   hipEvent_t ids_ready = nullptr;
@@ -194,7 +196,8 @@ int cache_slot_table_create(int L, int E, int n_slots, int qtype, int H, int I, 
       return hip_error(e, "hipEventCreate");
     }
   }
-  if ((e = hipHostMalloc((void**)&c->h_ids, sizeof(int32_t) * kCtlStagePairs, hipHostMallocDefault)) != hipSuccess ||
+  if ((e = hipHostMalloc((void**)&c->h_ids, sizeof(int32_t) * (kCtlStagePairs + kFlagPad), hipHostMallocCoherent)) !=
+          hipSuccess ||
       (e = hipHostMalloc((void**)&c->h_mask, sizeof(int32_t) * 3 * E, hipHostMallocDefault)) != hipSuccess ||
       (e = hipMalloc(&c->d_mask, sizeof(int32_t) * 3 * E)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&c->ids_ready, hipEventDisableTiming)) != hipSuccess) {
@@ -202,6 +205,7 @@ int cache_slot_table_create(int L, int E, int n_slots, int qtype, int H, int I, 
     return hip_error(e, "cache staging allocation");
   }
   std::fill(c->h_mask, c->h_mask + 3 * E, 0);
+  std::fill(c->h_ids, c->h_ids + kCtlStagePairs + kFlagPad, 0);
   *out = c;
   return MOE_OK;
 }
@@ -622,9 +626,12 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
   if (!out) return set_error(MOE_ERR_INVALID_ARG, "cache_decode_layer: out is NULL");
   const int E = c->E, P = T * k;
   const bool host_ok = c->policy != MOE_MISS_COPY;
-  // the routing kernel writes the ids into the pinned staging as well
+  // the routing kernel writes the ids into the coherent staging and then
+  // raises the flag to a value no earlier call used
+  int32_t* flag = c->h_ids + kCtlStagePairs;
+  const int32_t seq = c->ids_seq = c->ids_seq == INT32_MAX ? 1 : c->ids_seq + 1;
   int rc = route_permute_impl(ctx, x, MOE_DTYPE_F32, router_w, bias, logits_in, T, c->H, E, k, logits_out, topk_ids,
-                              topk_w, expert_offsets, sorted_pairs, pair_pos, active, nullptr, 0, c->h_ids,
+                              topk_w, expert_offsets, sorted_pairs, pair_pos, active, nullptr, 0, c->h_ids, flag, seq,
                               compute_stream);
   if (rc) return rc;
   hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
@@ -633,7 +640,19 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
                      hipSuccess)
     return hip_error(e, "hipMemcpyAsync(x)");
   if ((e = hipEventRecord(c->ids_ready, cs)) != hipSuccess) return hip_error(e, "hipEventRecord(ids)");
-  if ((e = hipEventSynchronize(c->ids_ready)) != hipSuccess) return hip_error(e, "hipEventSynchronize(ids)");
+  // wait for the flag, not for the kernel's end; the event bounds the wait:
+  // once it has completed the flag must be up
+  for (unsigned it = 1;; ++it) {
+    if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == seq) break;
+    if (it % 64 == 0) {
+      e = hipEventQuery(c->ids_ready);
+      if (e == hipSuccess) {
+        if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == seq) break;
+        return set_error(MOE_ERR_HIP, "cache_decode_layer: the routing kernel ended without publishing the ids");
+      }
+      if (e != hipErrorNotReady) return hip_error(e, "hipEventQuery(ids)");
+    }
+  }
   // the previous layer's copies have long finished: fold their rate in
   if (c->timed_copies > 0 && hipEventQuery(c->copy_t1) == hipSuccess) {
     float ms = 0.0f;
@@ -783,6 +802,8 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
       tp[j] = tok[j].data();
       yp[j] = yrow[j].data();
     }
+    // the tokens were staged behind the routing kernel
+    if ((e = hipEventSynchronize(c->ids_ready)) != hipSuccess) return hip_error(e, "hipEventSynchronize(x)");
     const double t0 = now_s();
     if ((rc = host_experts_ffn(c->qtype, c->H, c->I, n_host, hs.data(), cnt.data(), tp.data(), yp.data(), c->h_x,
                                c->h_y, c->h_scratch.data(), c->host_threads, true)))

@@ -53,11 +53,13 @@ bool prefill_mfma_supported(int H, int I);
 size_t prefill_ws_bytes(int T, int k, int I, int E);
 int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws, hipStream_t s);
 // moe_route_permute with an optional copy of the ids written straight into
-// (pinned) host memory by the routing kernel; needs T*k <= 4096.
+// coherent pinned host memory by the routing kernel, which then stores seq
+// into *ids_flag (both or neither); needs T*k <= 4096.
 int route_permute_impl(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w, const float* bias,
                        const float* logits_in, int T, int H, int E, int k, float* logits_out, int32_t* topk_ids,
                        float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
-                       int32_t* active, void* ws, size_t ws_bytes, int32_t* ids_host, void* stream);
+                       int32_t* active, void* ws, size_t ws_bytes, int32_t* ids_host, int32_t* ids_flag,
+                       int32_t seq, void* stream);
 int validate_route_args(const char* fn, const void* x, int x_dtype, const float* router_w,
                         const float* logits_in, int T, int H, int E, int k, float* logits_out,
                         int32_t* topk_ids, float* topk_w);

@@ -123,7 +123,8 @@ __global__ __launch_bounds__(kTopkPermuteThreads) void topk_permute_kernel(
     const float* __restrict__ src, const float* __restrict__ bias, int T, int E, int k,
     float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
-    int32_t* __restrict__ active, int* __restrict__ err, int32_t* __restrict__ ids_host) {
+    int32_t* __restrict__ active, int* __restrict__ err, int32_t* __restrict__ ids_host, int32_t* ids_flag,
+    int32_t seq) {
   __shared__ TopkPermuteLds s;
   __shared__ TopkScratch sc[kTopkPermuteThreads / kWave];
   const int wave = threadIdx.x >> 6;
@@ -134,8 +135,14 @@ __global__ __launch_bounds__(kTopkPermuteThreads) void topk_permute_kernel(
   __syncthreads();
   // a copy of the ids straight into host memory for a caller that waits for
   // them (the expert cache's lookup), instead of a separate read-back
-  if (ids_host)
+  if (ids_host) {  // uniform: a kernel argument
     for (int i = threadIdx.x; i < T * k; i += kTopkPermuteThreads) ids_host[i] = s.ids[i];
+    // every id reaches host memory before the flag does: a host that waits
+    // for seq can start its lookup while this kernel still permutes
+    __threadfence_system();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(ids_flag, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
   if (T * k <= 1024) {
     if (wave == 0) wave_permute(s.ids, T * k, E, offsets, sorted_pairs, pair_pos, active, err, s.perm.cnt, s.perm.cur);
   } else {
@@ -237,14 +244,15 @@ extern "C" int moe_route_permute(moe_ctx* ctx, const void* x, int x_dtype, const
                                  int32_t* active, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
   return route_permute_impl(ctx, x, x_dtype, router_w, bias, logits_in, T, H, E, k, logits_out, topk_ids, topk_w,
-                            expert_offsets, sorted_pairs, pair_pos, active, ws, ws_bytes, nullptr, stream);
+                            expert_offsets, sorted_pairs, pair_pos, active, ws, ws_bytes, nullptr, nullptr, 0, stream);
 }
 
 namespace moe {
 int route_permute_impl(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w, const float* bias,
                        const float* logits_in, int T, int H, int E, int k, float* logits_out, int32_t* topk_ids,
                        float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
-                       int32_t* active, void* ws, size_t ws_bytes, int32_t* ids_host, void* stream) {
+                       int32_t* active, void* ws, size_t ws_bytes, int32_t* ids_host, int32_t* ids_flag, int32_t seq,
+                       void* stream) {
   if (!ctx) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: ctx is NULL");
   int rc = validate_route_args("moe_route_permute", x, x_dtype, router_w, logits_in, T, H, E, k, logits_out,
                           topk_ids, topk_w);
@@ -252,9 +260,10 @@ int route_permute_impl(moe_ctx* ctx, const void* x, int x_dtype, const float* ro
   if (!expert_offsets || !active || (T > 0 && (!sorted_pairs || !pair_pos)))
     return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: NULL grouping output");
   if ((rc = ensure_device(ctx))) return rc;
+  if (!ids_host != !ids_flag) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: host ids need their flag");
   hipStream_t s = (hipStream_t)stream;
   if ((long long)T * k > kFusedMaxPairs) {  // large batches: separate kernels
-    if (ids_host) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: a host copy of the ids needs T*k <= %d",
+    if (ids_host || ids_flag) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: a host copy of the ids needs T*k <= %d",
                                    kFusedMaxPairs);
     rc = launch_route(ctx, x, x_dtype, router_w, bias, logits_in, T, H, E, k, logits_out, topk_ids, topk_w, s);
     if (rc) return rc;
@@ -279,7 +288,7 @@ int route_permute_impl(moe_ctx* ctx, const void* x, int x_dtype, const float* ro
   }
   KernelTimer timer(ctx, "topk_permute", s);
   launch(topk_permute_kernel, 1, kTopkPermuteThreads, 0, s, src, tk_bias, T, E, k, logits_in ? logits_out : nullptr, topk_ids,
-                                        topk_w, expert_offsets, sorted_pairs, pair_pos, active, ctx->d_err, ids_host);
+                                        topk_w, expert_offsets, sorted_pairs, pair_pos, active, ctx->d_err, ids_host, ids_flag, seq);
   return check_launch("topk_permute_kernel");
 }
 }  // namespace moe
