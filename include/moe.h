@@ -344,8 +344,10 @@ int cache_slot_table_resize(moe_cache* c, int n_slots, void* d_pool,
  * sequence above in one host call: moe_route_permute on compute_stream (x
  * fp32 [T][H] device; router_w/bias/logits_in/logits_out/topk_ids/topk_w/
  * expert_offsets/sorted_pairs/pair_pos/active as there), the routed ids
- * read back to pinned staging owned by the cache (the host waits for them:
- * a layer's misses are known only once it has routed), the LRU lookup,
+ * written by the routing kernel itself into coherent pinned staging owned
+ * by the cache, followed by a flag word (the host waits for the flag, not
+ * for the kernel's end, bounded by an event on the kernel: a layer's
+ * misses are known only once it has routed), the LRU lookup,
  * then moe_expert_ffn on the resident experts while prefetch_expert copies
  * the misses on copy_stream, moe_expert_ffn on the misses once they land,
  * moe_combine into out (device fp32 [T][H]) and cache_mark_layer_done.
