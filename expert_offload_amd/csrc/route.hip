@@ -17,43 +17,13 @@ int launch_permute(moe_ctx* ctx, const int32_t* ids, int P, int E, int32_t* offs
                    int32_t* pair_pos, int32_t* active, void* ws, size_t ws_bytes, hipStream_t s);
 size_t permute_ws_bytes(long long P, int E);
 
-// logits[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e]) for expert e = one
-// wavefront: the router row stays in registers across tokens.
-template <typename XT>
-__device__ __forceinline__ void router_row(const XT* __restrict__ x, const float* __restrict__ wr,
-                                           const float* __restrict__ bias, int T, int H, int E, int e,
-                                           float* __restrict__ logits) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const float* w = wr + (size_t)e * H;
-  const float b = bias ? bias[e] : 0.0f;
-  for (int t = 0; t < T; ++t) {
-    const XT* xt = x + (size_t)t * H;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int h = lane * 4; h < H; h += 4 * kWave) {
-      const float4 wv = *reinterpret_cast<const float4*>(w + h);
-      float xv[4];
-      if constexpr (sizeof(XT) == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(xt + h);
-        xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(xt + h);
-        xv[0] = bf16_to_f32(v.x & 0xFFFF); xv[1] = bf16_to_f32(v.x >> 16);
-        xv[2] = bf16_to_f32(v.y & 0xFFFF); xv[3] = bf16_to_f32(v.y >> 16);
-      }
-      acc = fmaf(xv[0], wv.x, acc);
-      acc = fmaf(xv[1], wv.y, acc);
-      acc = fmaf(xv[2], wv.z, acc);
-      acc = fmaf(xv[3], wv.w, acc);
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) logits[(size_t)t * E + e] = acc + b;
-  }
-}
-
 // One workgroup per expert: its four wavefronts each take a quarter of the
-// hidden dimension (loads issued together), partial sums meet in LDS.
-template <typename XT>
+// hidden dimension, partial sums meet in LDS.  TB tokens at a time: their
+// activation loads go out together and their dot products run side by side
+// (each token's own sum keeps one fixed order, so TB does not change the
+// result); with fewer than TB tokens left the last one is repeated and the
+// repeats are dropped.
+template <typename XT, int TB>
 __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x,
                                                             const float* __restrict__ wr,
                                                             const float* __restrict__ bias, int T,
@@ -66,28 +36,41 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   const float b = bias ? bias[e] : 0.0f;
   for (int t0 = 0; t0 < T; t0 += 64) {
     const int nt = min(64, T - t0);
-    for (int tt = 0; tt < nt; ++tt) {
-      const XT* xt = x + (size_t)(t0 + tt) * H + wave * q;
-      float acc = 0.0f;
-#pragma unroll 4
+    for (int tb = 0; tb < nt; tb += TB) {
+      const XT* xt[TB];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) xt[u] = x + (size_t)(t0 + min(tb + u, nt - 1)) * H + wave * q;
+      float acc[TB];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) acc[u] = 0.0f;
+#pragma unroll 2
       for (int h = lane * 4; h < q; h += 4 * kWave) {
         const float4 wv = *reinterpret_cast<const float4*>(w + h);
-        float xv[4];
-        if constexpr (sizeof(XT) == 4) {
-          const float4 v = *reinterpret_cast<const float4*>(xt + h);
-          xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
-        } else {
-          const uint2 v = *reinterpret_cast<const uint2*>(xt + h);
-          xv[0] = bf16_to_f32(v.x & 0xFFFF); xv[1] = bf16_to_f32(v.x >> 16);
-          xv[2] = bf16_to_f32(v.y & 0xFFFF); xv[3] = bf16_to_f32(v.y >> 16);
+        float xv[TB][4];
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          if constexpr (sizeof(XT) == 4) {
+            const float4 v = *reinterpret_cast<const float4*>(xt[u] + h);
+            xv[u][0] = v.x; xv[u][1] = v.y; xv[u][2] = v.z; xv[u][3] = v.w;
+          } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(xt[u] + h);
+            xv[u][0] = bf16_to_f32(v.x & 0xFFFF); xv[u][1] = bf16_to_f32(v.x >> 16);
+            xv[u][2] = bf16_to_f32(v.y & 0xFFFF); xv[u][3] = bf16_to_f32(v.y >> 16);
+          }
         }
-        acc = fmaf(xv[0], wv.x, acc);
-        acc = fmaf(xv[1], wv.y, acc);
-        acc = fmaf(xv[2], wv.z, acc);
-        acc = fmaf(xv[3], wv.w, acc);
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          acc[u] = fmaf(xv[u][0], wv.x, acc[u]);
+          acc[u] = fmaf(xv[u][1], wv.y, acc[u]);
+          acc[u] = fmaf(xv[u][2], wv.z, acc[u]);
+          acc[u] = fmaf(xv[u][3], wv.w, acc[u]);
+        }
       }
-      acc = wave_sum_dpp(acc);
-      if (lane == 0) part[wave][tt] = acc;
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const float v = wave_sum_dpp(acc[u]);
+        if (lane == 0 && tb + u < nt) part[wave][tb + u] = v;
+      }
     }
     __syncthreads();
     if (threadIdx.x < nt)
@@ -95,6 +78,25 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
           ((part[0][threadIdx.x] + part[1][threadIdx.x]) + (part[2][threadIdx.x] + part[3][threadIdx.x])) + b;
     __syncthreads();
   }
+}
+
+template <typename XT>
+static void launch_router_logits_t(const XT* x, const float* router_w, const float* bias, int T, int H, int E,
+                                   float* logits_out, hipStream_t s) {
+  if (T >= 8)
+    launch(router_logits_kernel<XT, 8>, dim3(E), 256, 0, s, x, router_w, bias, T, H, E, logits_out);
+  else if (T >= 2)
+    launch(router_logits_kernel<XT, 2>, dim3(E), 256, 0, s, x, router_w, bias, T, H, E, logits_out);
+  else
+    launch(router_logits_kernel<XT, 1>, dim3(E), 256, 0, s, x, router_w, bias, T, H, E, logits_out);
+}
+
+static void launch_router_logits_kernel(const void* x, int x_dtype, const float* router_w, const float* bias, int T,
+                                        int H, int E, float* logits_out, hipStream_t s) {
+  if (x_dtype == MOE_DTYPE_F32)
+    launch_router_logits_t((const float*)x, router_w, bias, T, H, E, logits_out, s);
+  else
+    launch_router_logits_t((const uint16_t*)x, router_w, bias, T, H, E, logits_out, s);
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ src,
@@ -176,11 +178,7 @@ int validate_route_args(const char* fn, const void* x, int x_dtype, const float*
 int launch_router_logits(moe_ctx* ctx, const void* x, int x_dtype, const float* router_w, const float* bias, int T,
                          int H, int E, float* logits_out, hipStream_t s) {
   KernelTimer timer(ctx, "router_logits", s);
-  dim3 grid(E);
-  if (x_dtype == MOE_DTYPE_F32)
-    launch(router_logits_kernel<float>, grid, 256, 0, s, (const float*)x, router_w, bias, T, H, E, logits_out);
-  else
-    launch(router_logits_kernel<uint16_t>, grid, 256, 0, s, (const uint16_t*)x, router_w, bias, T, H, E, logits_out);
+  launch_router_logits_kernel(x, x_dtype, router_w, bias, T, H, E, logits_out, s);
   return check_launch("router_logits_kernel");
 }
 
@@ -191,14 +189,9 @@ static int launch_route(moe_ctx* ctx, const void* x, int x_dtype, const float* r
   const float* src = logits_in;
   const float* tk_bias = bias;
   if (!logits_in) {
-    dim3 grid(E);
     {
       KernelTimer timer(ctx, "router_logits", s);
-      if (x_dtype == MOE_DTYPE_F32)
-        launch(router_logits_kernel<float>, grid, 256, 0, s, (const float*)x, router_w, bias, T, H, E, logits_out);
-      else
-        launch(router_logits_kernel<uint16_t>, grid, 256, 0, s, (const uint16_t*)x, router_w, bias, T, H, E,
-                                                            logits_out);
+      launch_router_logits_kernel(x, x_dtype, router_w, bias, T, H, E, logits_out, s);
     }
     if ((rc = check_launch("router_logits_kernel"))) return rc;
     src = logits_out;
@@ -275,12 +268,7 @@ int route_permute_impl(moe_ctx* ctx, const void* x, int x_dtype, const float* ro
   if (!logits_in) {
     {
       KernelTimer timer(ctx, "router_logits", s);
-      dim3 grid(E);
-      if (x_dtype == MOE_DTYPE_F32)
-        launch(router_logits_kernel<float>, grid, 256, 0, s, (const float*)x, router_w, bias, T, H, E, logits_out);
-      else
-        launch(router_logits_kernel<uint16_t>, grid, 256, 0, s, (const uint16_t*)x, router_w, bias, T, H, E,
-                                                            logits_out);
+      launch_router_logits_kernel(x, x_dtype, router_w, bias, T, H, E, logits_out, s);
     }
     if ((rc = check_launch("router_logits_kernel"))) return rc;
     src = logits_out;
