@@ -169,7 +169,31 @@ constexpr int kDownLdsFloats = 2048;    // y tile kept in LDS for the combine wh
 constexpr int kDownStageFloats = 1024;  // per-wave staging of one h row when I fits
 constexpr int kStageVec = kDownStageFloats / (4 * kWave);  // float4 per lane
 
-// One h row (I <= kDownStageFloats floats) in registers, on its way to LDS.
+// Staged h rows are swizzled in LDS: within each 32-float block b, float4 j
+// sits in slot (j + b) mod 8.  The lanes of a row group read blocks lg +
+// LPR*i at the same j; plain, those are 128 B apart and hit the same banks,
+// swizzled they fall in 8 different 16-byte slots.
+__device__ __forceinline__ int hswz(int c) {  // float index c (a multiple of 4) -> LDS position
+  const int b = c >> 5, j = (c >> 2) & 7;
+  return (b << 5) | (((j + b) & 7) << 2);
+}
+
+// The lane's BPL activation blocks from a swizzled LDS row.
+template <int LPR, int BPL>
+__device__ __forceinline__ void load_act_swz(const float* row, int lg, float (&xv)[BPL][32]) {
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = lg + LPR * i;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(row + (b << 5) + (((j + b) & 7) << 2));
+      xv[i][4 * j] = v.x; xv[i][4 * j + 1] = v.y; xv[i][4 * j + 2] = v.z; xv[i][4 * j + 3] = v.w;
+    }
+  }
+}
+
+// One h row (I <= kDownStageFloats floats) in registers, on its way to LDS
+// (stored swizzled, see hswz).
 struct HRowRegs {
   float4 v[kStageVec];
   // Lanes past the row end re-read its last 4 floats (in bounds) and skip
@@ -185,7 +209,7 @@ struct HRowRegs {
 #pragma unroll
     for (int i = 0; i < kStageVec; ++i) {
       const int c = (lane + kWave * i) * 4;
-      if (c < I) *reinterpret_cast<float4*>(dst + c) = v[i];
+      if (c < I) *reinterpret_cast<float4*>(dst + hswz(c)) = v[i];
     }
   }
 };

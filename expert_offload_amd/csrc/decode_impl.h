@@ -183,14 +183,14 @@ __global__ __launch_bounds__(kDownWaves * kWave) void ffn_down_decode(FfnParams 
         hr.load(p.hbuf + (size_t)pbeg * p.I, p.I, lane);
         tile.load(rows, lg);
         hr.store(hrow, p.I, lane);
-        load_act<LPR, BPL>(hrow, lg, xv);
+        load_act_swz<LPR, BPL>(hrow, lg, xv);
         float acc[RPL];
         tile.dot(xv, acc);
         MOE_DOWN_FINISH(0);
         for (int s = 1; s < n_e; ++s) {
           hr.load(p.hbuf + (size_t)(pbeg + s) * p.I, p.I, lane);
           hr.store(hrow, p.I, lane);
-          load_act<LPR, BPL>(hrow, lg, xv);
+          load_act_swz<LPR, BPL>(hrow, lg, xv);
           tile.dot(xv, acc);
           MOE_DOWN_FINISH(s);
         }
