@@ -117,42 +117,69 @@ struct RowTile {
   __device__ __forceinline__ void dot(const float (&xv)[BPL][32], float (&acc)[RPL]) {
     float sx[BPL];
 #pragma unroll
-    for (int i = 0; i < BPL; ++i) sx[i] = Q::kMin ? sum32(xv[i]) : sum32(xv[i]) * Q::kOff;
+    for (int i = 0; i < BPL; ++i) sx[i] = block_sx(xv[i]);
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       acc[r] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) {
+      for (int i = 0; i < BPL; ++i) acc[r] = block_dot(r, i, xv[i], sx[i], acc[r]);
+    }
+  }
+
+  // The same sums for one row, with each activation block read from a
+  // swizzled LDS row (see hswz) right before its use, so only 32
+  // activations are live at a time; bit-identical to dot.
+  __device__ __forceinline__ void dot_lds_swz(const float* row, int lg, float (&acc)[RPL]) {
+    static_assert(RPL == 1, "one row per lane");
+    acc[0] = 0.0f;
 #pragma unroll
-        for (int q = 0; q < Q::kWords; ++q) asm volatile("" : "+v"(w[r][i][q]));
-        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (QT == MOE_QTYPE_Q8_0) {
+    for (int i = 0; i < BPL; ++i) {
+      float xb[32];
+      const int b = lg + LPR * i;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint32_t u = w[r][i][q] ^ 0x80808080u;
+      for (int j = 0; j < 8; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(row + (b << 5) + (((j + b) & 7) << 2));
+        xb[4 * j] = v.x; xb[4 * j + 1] = v.y; xb[4 * j + 2] = v.z; xb[4 * j + 3] = v.w;
+      }
+      acc[0] = block_dot(0, i, xb, block_sx(xb), acc[0]);
+    }
+  }
+
+  __device__ __forceinline__ static float block_sx(const float (&x)[32]) {
+    return Q::kMin ? sum32(x) : sum32(x) * Q::kOff;
+  }
+
+  // acc + this lane's block i of row r against x: d * (u . x - sx) or
+  // d * (u . x) + m * sx, with sx from block_sx.
+  __device__ __forceinline__ float block_dot(int r, int i, const float (&x)[32], float sx, float acc) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) part[j] = fmaf((float)((u >> (8 * j)) & 0xFFu), xv[i][4 * q + j], part[j]);
-          }
-        } else {
+    for (int q = 0; q < Q::kWords; ++q) asm volatile("" : "+v"(w[r][i][q]));
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (QT == MOE_QTYPE_Q8_0) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t lo = w[r][i][q] & 0x0F0F0F0Fu, hi = (w[r][i][q] >> 4) & 0x0F0F0F0Fu;
-            if constexpr (Q::kQh) {
-              lo |= spread_fifth_bits(qh[r][i] >> (4 * q));
-              hi |= spread_fifth_bits(qh[r][i] >> (16 + 4 * q));
-            }
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t u = w[r][i][q] ^ 0x80808080u;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              part[j] = fmaf((float)((lo >> (8 * j)) & 0xFFu), xv[i][4 * q + j], part[j]);
-              part[j] = fmaf((float)((hi >> (8 * j)) & 0xFFu), xv[i][16 + 4 * q + j], part[j]);
-            }
-          }
+        for (int j = 0; j < 4; ++j) part[j] = fmaf((float)((u >> (8 * j)) & 0xFFu), x[4 * q + j], part[j]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t lo = w[r][i][q] & 0x0F0F0F0Fu, hi = (w[r][i][q] >> 4) & 0x0F0F0F0Fu;
+        if constexpr (Q::kQh) {
+          lo |= spread_fifth_bits(qh[r][i] >> (4 * q));
+          hi |= spread_fifth_bits(qh[r][i] >> (16 + 4 * q));
         }
-        const float su = (part[0] + part[1]) + (part[2] + part[3]);
-        if constexpr (Q::kMin) acc[r] = fmaf(d[r][i], su, fmaf(m[r][i], sx[i], acc[r]));
-        else acc[r] = fmaf(d[r][i], su - sx[i], acc[r]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          part[j] = fmaf((float)((lo >> (8 * j)) & 0xFFu), x[4 * q + j], part[j]);
+          part[j] = fmaf((float)((hi >> (8 * j)) & 0xFFu), x[16 + 4 * q + j], part[j]);
+        }
       }
     }
+    const float su = (part[0] + part[1]) + (part[2] + part[3]);
+    if constexpr (Q::kMin) return fmaf(d[r][i], su, fmaf(m[r][i], sx, acc));
+    else return fmaf(d[r][i], su - sx, acc);
   }
 };
 

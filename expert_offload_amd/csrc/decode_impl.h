@@ -124,20 +124,31 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
 // y[t*k + j] over those rows (j ascending, as moe_combine does).  No data
 // crosses workgroups, so no device-wide fences are needed.
 
+// Wavefronts per down workgroup: 16 where one row per lane and activations
+// streamed from LDS keep a wavefront within 128 registers (four per SIMD),
+// else 8.
 template <int QT, int LPR, int BPL, int RPL>
-__global__ __launch_bounds__(kDownWaves * kWave) void ffn_down_decode(FfnParams p) {
+constexpr int down_waves() {
+  constexpr bool stream = kWave / LPR > 1 && kQK * LPR * BPL <= kDownStageFloats && RPL == 1;
+  return stream && !QTraits<QT>::kQh ? 16 : kDownWaves;
+}
+
+template <int QT, int LPR, int BPL, int RPL>
+__global__ __launch_bounds__((down_waves<QT, LPR, BPL, RPL>() * kWave)) void ffn_down_decode(FfnParams p) {
   constexpr int RPP = kWave / LPR, RW = RPP * RPL;
+  constexpr int NWV = down_waves<QT, LPR, BPL, RPL>();
   __shared__ float s_y[kDownLdsFloats];
-  __shared__ float s_h[kDownWaves][kDownStageFloats];
+  __shared__ float s_h[NWV][kDownStageFloats];
   __shared__ CtlLds ctl;
-  stage_ctl<kDownWaves * kWave>(p, ctl, p.out != nullptr);
+  stage_ctl<NWV * kWave>(p, ctl, p.out != nullptr);
   const int* pairs = ctl.pairs;
   const float* topk_w = ctl.w;
   const bool lds_y = p.T * p.k * RW <= kDownLdsFloats;
   // With LPR < 64 the 64/LPR lane groups own the same columns of h: each h
   // row is read from memory once (issued before the weights) into the
   // wavefront's LDS row, and the groups read their blocks from there.
-  const bool stage_h = RPP > 1 && p.I <= kDownStageFloats;
+  // (the kernel for LPR lanes of BPL blocks serves I = 32 * LPR * BPL only)
+  constexpr bool stage_h = RPP > 1 && kQK * LPR * BPL <= kDownStageFloats;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   float* hrow = s_h[wave];
   const int g = lane / LPR, lg = lane % LPR;
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(kDownWaves * kWave) void ffn_down_decode(FfnParams 
   const size_t rbytes = row_bytes(QT, p.I);
   for (int tile_i = blockIdx.x; tile_i < n_tiles; tile_i += gridDim.x) {
     const int h0 = tile_i * RW;
-    for (int a = wave; a < n_active; a += kDownWaves) {
+    for (int a = wave; a < n_active; a += NWV) {
       const int e = ctl.active[1 + a];
       if (p.mask && !p.mask[e]) continue;
       const int slot = ctl.slots[e];
@@ -178,20 +189,26 @@ __global__ __launch_bounds__(kDownWaves * kWave) void ffn_down_decode(FfnParams 
   } while (0)
       RowTile<QT, LPR, BPL, RPL> tile;
       float xv[BPL][32];
-      if (stage_h) {
+      if constexpr (stage_h) {
         HRowRegs hr;
         hr.load(p.hbuf + (size_t)pbeg * p.I, p.I, lane);
         tile.load(rows, lg);
         hr.store(hrow, p.I, lane);
-        load_act_swz<LPR, BPL>(hrow, lg, xv);
+        // one row per lane: activations straight from LDS, a block at a time
+        auto dot_h = [&](float (&acc)[RPL]) {
+          if constexpr (RPL == 1) tile.dot_lds_swz(hrow, lg, acc);
+          else {
+            load_act_swz<LPR, BPL>(hrow, lg, xv);
+            tile.dot(xv, acc);
+          }
+        };
         float acc[RPL];
-        tile.dot(xv, acc);
+        dot_h(acc);
         MOE_DOWN_FINISH(0);
         for (int s = 1; s < n_e; ++s) {
           hr.load(p.hbuf + (size_t)(pbeg + s) * p.I, p.I, lane);
           hr.store(hrow, p.I, lane);
-          load_act_swz<LPR, BPL>(hrow, lg, xv);
-          tile.dot(xv, acc);
+          dot_h(acc);
           MOE_DOWN_FINISH(s);
         }
       } else {
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(kDownWaves * kWave) void ffn_down_decode(FfnParams 
     }
     if (p.out) {
       __syncthreads();
-      for (int idx = threadIdx.x; idx < p.T * RW; idx += kDownWaves * kWave) {
+      for (int idx = threadIdx.x; idx < p.T * RW; idx += NWV * kWave) {
         const int t = idx / RW, r = idx - t * RW;
         float acc = 0.0f;
         for (int j = 0; j < p.k; ++j) {
@@ -261,7 +278,8 @@ static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStrea
 }
 template <int QT, int LPR, int BPL>
 static void launch_down(const FfnParams& p, int grid, hipStream_t s) {
-  launch(ffn_down_decode<QT, LPR, BPL, down_rows_per_lane<QT, LPR, BPL>()>, grid, kDownWaves * kWave, 0, s, p);
+  constexpr int rpl = down_rows_per_lane<QT, LPR, BPL>();
+  launch(ffn_down_decode<QT, LPR, BPL, rpl>, grid, down_waves<QT, LPR, BPL, rpl>() * kWave, 0, s, p);
 }
 template <int QT, int LPR, int BPL>
 static constexpr int down_rows_per_tile() {
