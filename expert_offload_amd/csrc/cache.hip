@@ -60,14 +60,36 @@ __global__ void slot_move_kernel(const uint4* src, uint4* dst, const int2* moves
   }
 }
 
-// Rows of y_pairs computed on the host: pair p's row is copied from the
-// staging rows when its expert is marked in host_mask.
+// Rows of y_pairs computed on the host: pair p's row is read from src
+// (coherent pinned host memory, [P][H]) when its expert is a host miss.
 __global__ void host_rows_kernel(const float4* __restrict__ src, const int32_t* __restrict__ host_mask,
                                  const int32_t* __restrict__ ids, float4* __restrict__ y, int H4) {
   const int p = blockIdx.y;
   if (!host_mask[ids[p]]) return;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < H4; i += gridDim.x * blockDim.x)
     y[(size_t)p * H4 + i] = src[(size_t)p * H4 + i];
+}
+
+// The layer's expert masks (resident, copied misses, host misses) travel
+// as bits in the kernel arguments and are expanded on the device, so no
+// copy-engine transfer, which could queue behind expert copies still in
+// flight on another stream, stands between the lookup and the FFN.
+struct MaskBits {
+  int E;
+  uint32_t bits[3][kMaxE / 32];
+};
+
+__global__ void mask_write_kernel(int32_t* __restrict__ mask, MaskBits m) {
+  for (int i = threadIdx.x; i < 3 * m.E; i += blockDim.x) {
+    const int j = i / m.E, e = i - j * m.E;
+    mask[i] = (m.bits[j][e >> 5] >> (e & 31)) & 1u;
+  }
+}
+
+// The layer's tokens into coherent pinned host memory for the host
+// executor, written by the GPU itself (no copy-engine transfer).
+__global__ void rows_to_host_kernel(const float4* __restrict__ src, float4* __restrict__ dst, int n4) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) dst[i] = src[i];
 }
 
 constexpr int kEventRing = 256;
@@ -115,7 +137,7 @@ struct moe_cache {
   int host_threads = 1;
   float* h_x = nullptr;   // pinned [kCtlStagePairs][H]: the layer's tokens
   float* h_y = nullptr;   // pinned [kCtlStagePairs][H]: host-computed pair rows
-  float* d_yh = nullptr;  // device [kCtlStagePairs][H]
+  float* d_yh = nullptr;  // device [kCtlStagePairs][H]: destination of the copy-rate calibration
   std::vector<float> h_scratch;  // [kCtlStagePairs][I]
   hipEvent_t copy_t0 = nullptr, copy_t1 = nullptr;  // around one layer's copies
   int timed_copies = 0;                             // copies between them, not yet read
@@ -548,8 +570,9 @@ int cache_set_miss_policy(moe_cache* c, int policy, int host_threads) {
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_error(e, "hipSetDevice");
     const size_t rows = (size_t)kCtlStagePairs * c->H;
-    if ((e = hipHostMalloc((void**)&c->h_x, sizeof(float) * rows, hipHostMallocDefault)) != hipSuccess ||
-        (e = hipHostMalloc((void**)&c->h_y, sizeof(float) * rows, hipHostMallocDefault)) != hipSuccess ||
+    // coherent: the GPU writes h_x and reads h_y in place
+    if ((e = hipHostMalloc((void**)&c->h_x, sizeof(float) * rows, hipHostMallocCoherent)) != hipSuccess ||
+        (e = hipHostMalloc((void**)&c->h_y, sizeof(float) * rows, hipHostMallocCoherent)) != hipSuccess ||
         (e = hipMalloc(&c->d_yh, sizeof(float) * rows)) != hipSuccess ||
         (e = hipEventCreate(&c->copy_t0)) != hipSuccess || (e = hipEventCreate(&c->copy_t1)) != hipSuccess) {
       if (c->h_x) (void)hipHostFree(c->h_x);
@@ -636,9 +659,11 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
   if (rc) return rc;
   hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
   hipError_t e;
-  if (host_ok && (e = hipMemcpyAsync(c->h_x, x, sizeof(float) * (size_t)T * c->H, hipMemcpyDeviceToHost, cs)) !=
-                     hipSuccess)
-    return hip_error(e, "hipMemcpyAsync(x)");
+  if (host_ok) {
+    const int n4 = T * c->H / 4;
+    launch(rows_to_host_kernel, std::min(64, (n4 + 255) / 256), 256, 0, cs, (const float4*)x, (float4*)c->h_x, n4);
+    if ((rc = check_launch("rows_to_host_kernel"))) return rc;
+  }
   if ((e = hipEventRecord(c->ids_ready, cs)) != hipSuccess) return hip_error(e, "hipEventRecord(ids)");
   // wait for the flag, not for the kernel's end; the event bounds the wait:
   // once it has completed the flag must be up
@@ -748,8 +773,15 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
     if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
     return cache_mark_layer_done(c, layer, compute_stream);
   }
-  if ((e = hipMemcpyAsync(c->d_mask, hm, sizeof(int32_t) * 3 * E, hipMemcpyHostToDevice, cs)) != hipSuccess)
-    return hip_error(e, "hipMemcpyAsync(masks)");
+  {
+    MaskBits mb{};
+    mb.E = E;
+    for (int j = 0; j < 3; ++j)
+      for (int id = 0; id < E; ++id)
+        if (hm[j * E + id]) mb.bits[j][id >> 5] |= 1u << (id & 31);
+    launch(mask_write_kernel, 1, 256, 0, cs, c->d_mask, mb);
+    if ((rc = check_launch("mask_write_kernel"))) return rc;
+  }
   if (any_hit) {  // the resident experts run while the misses are copied
     a.expert_mask = c->d_mask;
     if ((rc = moe_expert_ffn(ctx, &a, compute_stream))) return rc;
@@ -809,11 +841,8 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
                                c->h_y, c->h_scratch.data(), c->host_threads, true)))
       return rc;
     update_rate(c->rate_host, n_host * (double)c->slot_bytes / (now_s() - t0));
-    if ((e = hipMemcpyAsync(c->d_yh, c->h_y, sizeof(float) * (size_t)P * c->H, hipMemcpyHostToDevice, cs)) !=
-        hipSuccess)
-      return hip_error(e, "hipMemcpyAsync(host rows)");
     const int H4 = c->H / 4;
-    launch(host_rows_kernel, dim3((H4 + 255) / 256, P), 256, 0, cs, (const float4*)c->d_yh,
+    launch(host_rows_kernel, dim3((H4 + 255) / 256, P), 256, 0, cs, (const float4*)c->h_y,
            (const int32_t*)(c->d_mask + 2 * E), (const int32_t*)topk_ids, (float4*)y_pairs, H4);
     if ((rc = check_launch("host_rows_kernel"))) return rc;
   }
