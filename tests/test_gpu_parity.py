@@ -115,7 +115,9 @@ def test_topk_bias_and_nan(ctx):
 
 
 @pytest.mark.parametrize("name,T", [("tiny_q8_0", 4), ("decode_q8_0_h2048_e128", 16),
-                                    ("wide_q4_0_h2048_e512", 64)])
+                                    ("wide_q4_0_h2048_e512", 64), ("tiny_q8_0", 1), ("tiny_q8_0", 3),
+                                    ("decode_q8_0_h2048_e128", 13), ("decode_q8_0_h2048_e128", 100),
+                                    ("wide_q4_0_h2048_e512", 71)])
 def test_router_computed(ctx, name, T):
     note(f"router computed {name} T={T}")
     wl = gi.workload(name)
@@ -137,6 +139,29 @@ def test_router_computed(ctx, name, T):
     np.testing.assert_array_equal(got_ids[ok], ref_ids[ok])
     assert (~ok).sum() <= max(1, T // 100), f"{(~ok).sum()} near-tie tokens"
     assert np.abs(w.cpu().numpy()[ok] - ref_w[ok]).max() <= WEIGHT_TOL
+
+
+def test_router_logits_batch_invariant(ctx):
+    """The router kernel takes several tokens per pass (a partial last pass
+    repeats a token); each token's logits are bit-identical to those of the
+    token routed alone, for batch sizes across the pass widths and past the
+    64-token chunk."""
+    wl = gi.workload("decode_q8_0_h2048_e128")
+    x = gi.activations(wl, 77)
+    wr = dev(gi.router_weight(wl))
+
+    def logits(rows):
+        T = rows.shape[0]
+        lo = torch.empty((T, wl.E), dtype=torch.float32, device=DEV)
+        ids = torch.empty((T, wl.k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, wl.k), dtype=torch.float32, device=DEV)
+        moe.moe_route(ctx, dev(rows), wr, None, None, T, wl.H, wl.E, wl.k, lo, ids, w)
+        torch.cuda.synchronize()
+        return lo.cpu().numpy()
+
+    alone = np.stack([logits(x[t:t + 1])[0] for t in range(x.shape[0])])
+    for T in (2, 3, 7, 8, 9, 15, 64, 65, 77):
+        np.testing.assert_array_equal(logits(x[:T]), alone[:T])
 
 
 # ------------------------------------------------------------------ permute
