@@ -1,5 +1,5 @@
 // Building blocks of the decode dequant-GEMV kernels: raw block loads,
-// the offset-trick block dot product, the transposed butterfly that folds
+// the block dot product, the transposed butterfly that folds
 // per-lane row sums, activation staging, and the shape rules (rows per lane
 // within a register budget).
 //
@@ -12,10 +12,13 @@
 // transposed butterfly (RPL - 1 + log2(LPR / RPL) shuffles instead of
 // RPL * log2(LPR)).
 //
-// Block arithmetic.  With u the stored byte (Q8_0: q + 128 after flipping
-// the sign bit; Q4_0: the nibble q), sum_k w_k x_k = d * (sum_k u_k x_k -
-// OFF * sum_k x_k), OFF = 128 or 8; sum_k x_k is formed once per block and
-// token and shared by the lane's RPL rows.
+// Block arithmetic.  With u the unsigned code (Q8_0: q + 128 after
+// flipping the sign bit), sum_k w_k x_k = d * (sum_k u_k x_k - OFF * sum_k
+// x_k), OFF = 128 (Q8_0), 8 (Q4_0) or 16 (Q5_0); Q4_1 / Q5_1: d * sum_k
+// u_k x_k + m * sum_k x_k.  sum_k x_k is formed once per block and token
+// and shared by the lane's RPL rows.  The down kernel takes Q8_0 as
+// d * sum_k q_k x_k instead, each signed byte converted in one
+// instruction (RowTile's SGN).
 #pragma once
 
 #include "device_common.h"
@@ -87,9 +90,13 @@ __device__ __forceinline__ void fold_rows(float (&v)[M], int lane) {
 
 // Rows of one lane's GEMV: RPL rows x BPL blocks of raw codes, fifth bits,
 // scales and offsets (the last two only for the types that have them).
-template <int QT, int LPR, int BPL, int RPL>
+// SGN (Q8_0 only): convert the signed codes directly instead of adding the
+// offset back; the down kernel measured faster so, the gate/up kernel
+// slower (the two forms round differently, each is used by one kernel).
+template <int QT, int LPR, int BPL, int RPL, bool SGN = false>
 struct RowTile {
   using Q = QTraits<QT>;
+  static constexpr bool kSigned = SGN && QT == MOE_QTYPE_Q8_0;
   uint32_t w[RPL][BPL][Q::kWords];
   uint32_t qh[RPL][BPL];
   float d[RPL][BPL];
@@ -106,8 +113,9 @@ struct RowTile {
       }
   }
 
-  // acc[r] = sum over the lane's blocks of d * (u . x - OFF * sum x), or
-  // d * (u . x) + m * sum x for the types with an offset m, with the lane's
+  // acc[r] = sum over the lane's blocks of d * (u . x - OFF * sum x) (or
+  // d * (q . x) with SGN), or d * (u . x) + m * sum x for the types with
+  // an offset m, with the lane's
   // activation blocks already in xv.  Rows are finished one at a time in
   // load order, so the wait before row r covers only the loads up to row r
   // and row r's math overlaps the later rows' transfers.  Each row's codes
@@ -146,7 +154,8 @@ struct RowTile {
   }
 
   __device__ __forceinline__ static float block_sx(const float (&x)[32]) {
-    return Q::kMin ? sum32(x) : sum32(x) * Q::kOff;
+    if constexpr (kSigned) return 0.0f;  // signed codes: no offset term
+    else return Q::kMin ? sum32(x) : sum32(x) * Q::kOff;
   }
 
   // acc + this lane's block i of row r against x: d * (u . x - sx) or
@@ -155,10 +164,19 @@ struct RowTile {
 #pragma unroll
     for (int q = 0; q < Q::kWords; ++q) asm volatile("" : "+v"(w[r][i][q]));
     float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (QT == MOE_QTYPE_Q8_0) {
+    if constexpr (kSigned) {
+      // each signed byte converts in one instruction (byte-select sign
+      // extension), so no offset is folded in
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const uint32_t u = w[r][i][q] ^ 0x80808080u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          part[j] = fmaf((float)(int8_t)(w[r][i][q] >> (8 * j)), x[4 * q + j], part[j]);
+      }
+    } else if constexpr (QT == MOE_QTYPE_Q8_0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t u = w[r][i][q] ^ 0x80808080u;  // q + 128 in every byte
 #pragma unroll
         for (int j = 0; j < 4; ++j) part[j] = fmaf((float)((u >> (8 * j)) & 0xFFu), x[4 * q + j], part[j]);
       }

@@ -187,7 +187,7 @@ __global__ __launch_bounds__((down_waves<QT, LPR, BPL, RPL>() * kWave)) void ffn
       if (lds_y) s_y[pair_ * RW + rr] = acc[0];             \
     }                                                       \
   } while (0)
-      RowTile<QT, LPR, BPL, RPL> tile;
+      RowTile<QT, LPR, BPL, RPL, true> tile;
       float xv[BPL][32];
       if constexpr (stage_h) {
         HRowRegs hr;
