@@ -260,12 +260,24 @@ inline bool gemv_shape(int cols, GemvShape* s) {
 }
 
 
+// Rows per lane of the gate/up kernel without routing inside (batches
+// past the routing variant's pairs): twice the register budget (up to 16),
+// so each activation block, its sum and the per-pair fold serve twice the
+// rows.
+template <int QT, int LPR, int BPL>
+static constexpr int gateup_batch_rpl() {
+  constexpr int RPL0 = rows_per_lane<QT, BPL>();
+  constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
+  return 2 * RPL <= LPR && 2 * RPL <= 16 ? 2 * RPL : RPL;
+}
+
 template <int QT, int LPR, int BPL>
 static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStream_t s, const RouteArgs* ra) {
   constexpr int RPL0 = rows_per_lane<QT, BPL>();
   constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
   if (!ra) {
-    launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 0>, grid, 256, 0, s, p, x, RouteArgs{});
+    constexpr int RPLB = gateup_batch_rpl<QT, LPR, BPL>();
+    launch(ffn_gateup_decode<QT, LPR, BPL, RPLB, 0>, grid, 256, 0, s, p, x, RouteArgs{});
     return;
   }
   if constexpr (LPR == 64) {  // the routing variant exists for these shapes (decode_route_supported)
@@ -299,6 +311,16 @@ static int down_rows_rt(GemvShape sh) {
   MOE_RPT(64, 1) MOE_RPT(64, 2) MOE_RPT(64, 3) MOE_RPT(32, 1) MOE_RPT(32, 2) MOE_RPT(32, 3)
   MOE_RPT(16, 1) MOE_RPT(16, 2) MOE_RPT(16, 3) MOE_RPT(8, 1) MOE_RPT(8, 2) MOE_RPT(8, 3)
 #undef MOE_RPT
+  return 0;
+}
+
+template <int QT>
+static int batch_rows_per_wave_rt(GemvShape sh) {
+#define MOE_RPW(L, B) \
+  if (sh.lpr == L && sh.bpl == B) return (kWave / L) * gateup_batch_rpl<QT, L, B>();
+  MOE_RPW(64, 1) MOE_RPW(64, 2) MOE_RPW(64, 3) MOE_RPW(32, 1) MOE_RPW(32, 2) MOE_RPW(32, 3)
+  MOE_RPW(16, 1) MOE_RPW(16, 2) MOE_RPW(16, 3) MOE_RPW(8, 1) MOE_RPW(8, 2) MOE_RPW(8, 3)
+#undef MOE_RPW
   return 0;
 }
 
@@ -337,7 +359,8 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
   gemv_shape(p.I, &dn);
   const int max_active = std::min(p.E, p.T * p.k);
   const int cap = 16 * ctx->num_cus;
-  const int rw_gu = rows_per_wave_rt<QT>(gu), rt_dn = down_rows_rt<QT>(dn);
+  const int rw_gu = route ? rows_per_wave_rt<QT>(gu) : batch_rows_per_wave_rt<QT>(gu);
+  const int rt_dn = down_rows_rt<QT>(dn);
   const long long items_gu = (long long)max_active * (p.I / (rw_gu / 2));
   const int grid_gu = (int)std::max(1LL, std::min<long long>(cap, (items_gu + 3) / 4));
   const int grid_dn = std::max(1, p.H / rt_dn);
