@@ -260,10 +260,12 @@ inline bool gemv_shape(int cols, GemvShape* s) {
 }
 
 
-// Rows per lane of the gate/up kernel without routing inside (batches
-// past the routing variant's pairs): twice the register budget (up to 16),
-// so each activation block, its sum and the per-pair fold serve twice the
-// rows.
+// Rows per lane of the gate/up kernel without routing inside, for 8 tokens
+// and more (gateup_wide_rows): twice the register budget (up to 16), so
+// each activation block, its sum and the per-pair fold serve twice the
+// rows.  Fewer tokens keep the narrower rows: their few experts need the
+// wider spread of work items.
+inline bool gateup_wide_rows(int T, bool route) { return !route && T >= 8; }
 template <int QT, int LPR, int BPL>
 static constexpr int gateup_batch_rpl() {
   constexpr int RPL0 = rows_per_lane<QT, BPL>();
@@ -277,7 +279,8 @@ static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStrea
   constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
   if (!ra) {
     constexpr int RPLB = gateup_batch_rpl<QT, LPR, BPL>();
-    launch(ffn_gateup_decode<QT, LPR, BPL, RPLB, 0>, grid, 256, 0, s, p, x, RouteArgs{});
+    if (gateup_wide_rows(p.T, false)) launch(ffn_gateup_decode<QT, LPR, BPL, RPLB, 0>, grid, 256, 0, s, p, x, RouteArgs{});
+    else launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 0>, grid, 256, 0, s, p, x, RouteArgs{});
     return;
   }
   if constexpr (LPR == 64) {  // the routing variant exists for these shapes (decode_route_supported)
@@ -359,7 +362,8 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
   gemv_shape(p.I, &dn);
   const int max_active = std::min(p.E, p.T * p.k);
   const int cap = 16 * ctx->num_cus;
-  const int rw_gu = route ? rows_per_wave_rt<QT>(gu) : batch_rows_per_wave_rt<QT>(gu);
+  const int rw_gu =
+      gateup_wide_rows(p.T, route != nullptr) ? batch_rows_per_wave_rt<QT>(gu) : rows_per_wave_rt<QT>(gu);
   const int rt_dn = down_rows_rt<QT>(dn);
   const long long items_gu = (long long)max_active * (p.I / (rw_gu / 2));
   const int grid_gu = (int)std::max(1LL, std::min<long long>(cap, (items_gu + 3) / 4));
