@@ -441,3 +441,22 @@ def test_host_copy_policy_keeps_the_lru(ctx):
     for key, cp in copied.items():
         assert set(cp) <= computed[key] and not (set(cp) & host[key])
     assert stats[1] >= stats[0] > 0
+
+
+def test_widest_cache_masks_match_oracle(ctx):
+    """1024 experts, the most a cache takes: the hit / copied / host masks,
+    which travel to the device as bits, cover ids across every word, under
+    the copy, host and host-now-copy-behind policies in turn; outputs within
+    the decode tolerance of the oracle and misses as its LRU has them."""
+    wl = gi.Workload(9, "cache_widest_q4_0", H=256, E=1024, k=8, I=256, qtype="q4_0", batches=(1,),
+                     layers=1, router="trace", cache_fraction=0.06, steps=12, trace_keep_p=0.5,
+                     trace_zipf_s=1.0)
+    pool, blocks = host_pool(wl)
+    plan = {0: L.MISS_COPY, 4: L.MISS_HOST, 8: L.MISS_HOST_COPY}
+    trace, host, copied, computed, misses, worst, stats = _run_policies(ctx, wl, pool, blocks, 64, plan, 12)
+    note(f"   widest cache: worst max rel err {worst:.2e}; copied {stats[0]}, host {stats[1]}")
+    assert worst <= 1e-3
+    assert stats[0] > 0 and stats[1] > 0
+    assert (trace >= 512).any() and (trace < 512).any()
+    want, _ = oracle.lru_simulate(trace, 64, host=host)
+    np.testing.assert_array_equal(misses, (~want).sum(axis=2))
