@@ -361,7 +361,10 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
   gemv_shape(p.H, &gu);
   gemv_shape(p.I, &dn);
   const int max_active = std::min(p.E, p.T * p.k);
-  const int cap = 16 * ctx->num_cus;
+  // the routed kernel repeats the top-k in every workgroup: no more
+  // workgroups than are resident at once (three per CU), which then take
+  // further items in turn
+  const int cap = (route ? 3 : 16) * ctx->num_cus;
   const int rw_gu =
       gateup_wide_rows(p.T, route != nullptr) ? batch_rows_per_wave_rt<QT>(gu) : rows_per_wave_rt<QT>(gu);
   const int rt_dn = down_rows_rt<QT>(dn);
