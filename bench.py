@@ -596,8 +596,8 @@ def cpu_baseline(wl, T, budget_s):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported on this build "
-              "(multi-GPU sharding is a design note only)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the layer runs on one GPU; how it would shard is described, not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
     import expert_offload_amd as moe
