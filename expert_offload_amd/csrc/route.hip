@@ -129,21 +129,23 @@ __global__ __launch_bounds__(kTopkPermuteThreads) void topk_permute_kernel(
     int32_t seq) {
   __shared__ TopkPermuteLds s;
   __shared__ TopkScratch sc[kTopkPermuteThreads / kWave];
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   constexpr int waves = kTopkPermuteThreads / kWave;
   for (int t = wave; t < T; t += waves)
     wave_topk(src + (size_t)t * E, bias, E, k, logits_out ? logits_out + (size_t)t * E : nullptr,
               ids + (size_t)t * k, w + (size_t)t * k, s.ids + t * k, nullptr, nullptr, &sc[wave]);
   __syncthreads();
   // a copy of the ids straight into host memory for a caller that waits for
-  // them (the expert cache's lookup), instead of a separate read-back
-  if (ids_host) {  // uniform: a kernel argument
-    for (int i = threadIdx.x; i < T * k; i += kTopkPermuteThreads) ids_host[i] = s.ids[i];
-    // every id reaches host memory before the flag does: a host that waits
-    // for seq can start its lookup while this kernel still permutes
+  // them (the expert cache's lookup), instead of a separate read-back;
+  static_assert(kTopkPermuteThreads >= 2 * kWave, "a second wavefront publishes the ids");
+  if (ids_host && wave == 1) {
+    // wavefront 1 publishes while wavefront 0 groups the pairs: every id
+    // reaches host memory (the fence waits for this wavefront's stores)
+    // before the flag does, so a host that waits for seq can start its
+    // lookup while this kernel still permutes
+    for (int i = lane; i < T * k; i += kWave) ids_host[i] = s.ids[i];
     __threadfence_system();
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(ids_flag, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (lane == 0) __hip_atomic_store(ids_flag, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   if (T * k <= 1024) {
     if (wave == 0) wave_permute(s.ids, T * k, E, offsets, sorted_pairs, pair_pos, active, err, s.perm.cnt, s.perm.cur);
