@@ -51,10 +51,22 @@ __global__ __launch_bounds__(kMaxE) void permute_scan_kernel(const int32_t* __re
                                                              int32_t* __restrict__ active) {
   __shared__ int tot[kMaxE], off[kMaxE], flag[kMaxE], fpos[kMaxE], wsum[kMaxE / kWave];
   const int e = threadIdx.x;
+  // up to kScanRegs chunks: every count loaded at once and kept in
+  // registers for the second pass (no re-read)
+  constexpr int kScanRegs = 64;
+  const bool in_regs = n_chunks <= kScanRegs;
+  int v[kScanRegs];
   int run = 0;
   if (e < E) {
+    if (in_regs) {
+#pragma unroll
+      for (int c = 0; c < kScanRegs; ++c) v[c] = c < n_chunks ? counts[(size_t)c * E + e] : 0;
+#pragma unroll
+      for (int c = 0; c < kScanRegs; ++c) run += v[c];
+    } else {
 #pragma unroll 16
-    for (int c = 0; c < n_chunks; ++c) run += counts[(size_t)c * E + e];
+      for (int c = 0; c < n_chunks; ++c) run += counts[(size_t)c * E + e];
+    }
   }
   tot[e] = e < E ? run : 0;
   flag[e] = e < E && run > 0;
@@ -65,11 +77,19 @@ __global__ __launch_bounds__(kMaxE) void permute_scan_kernel(const int32_t* __re
     offsets[e] = off[e];
     if (tot[e] > 0) active[1 + fpos[e]] = e;
     int base = off[e];
+    if (in_regs) {
+#pragma unroll
+      for (int c = 0; c < kScanRegs; ++c) {
+        if (c < n_chunks) bases[(size_t)c * E + e] = base;
+        base += v[c];
+      }
+    } else {
 #pragma unroll 16
-    for (int c = 0; c < n_chunks; ++c) {
-      const int v = counts[(size_t)c * E + e];
-      bases[(size_t)c * E + e] = base;
-      base += v;
+      for (int c = 0; c < n_chunks; ++c) {
+        const int cv = counts[(size_t)c * E + e];
+        bases[(size_t)c * E + e] = base;
+        base += cv;
+      }
     }
   }
   if (e == 0) {
