@@ -24,6 +24,11 @@ Decision precision.  Top-k selection is an integer decision taken on fp32
 logits, the precision the GPU kernel decides in: ``topk_select`` casts its
 input to float32 before ordering.  Everything else is float64.
 
+NaN logits.  The pages do not mention them.  Here a NaN logit reads as
+-inf in every routing step (selection, softmax, top-k gap): it is never
+chosen over a number, ties with -inf (lower id first), and has
+probability 0.
+
 Parity pins.  Every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, brute force or independent simulations.  The full
 layer output at large sizes has no external values to compare against; it is
@@ -134,9 +139,18 @@ def router_logits(x: np.ndarray, router_w: np.ndarray,
     return l
 
 
+def nan_as_minus_inf(l: np.ndarray) -> np.ndarray:
+    """A NaN logit reads as -inf: it is never chosen over a number and its
+    probability is 0.  The pages say nothing about NaN router logits; this
+    is the reading under which every routing step stays defined (a NaN
+    would otherwise poison the softmax of the whole row)."""
+    l = np.asarray(l)
+    return np.where(np.isnan(l), -np.inf, l).astype(l.dtype)
+
+
 def softmax(l: np.ndarray) -> np.ndarray:
-    """Row softmax, max-shifted for range."""
-    l = np.asarray(l, dtype=np.float64)
+    """Row softmax, max-shifted for range; NaN logits count as -inf."""
+    l = nan_as_minus_inf(np.asarray(l, dtype=np.float64))
     z = np.exp(l - l.max(axis=-1, keepdims=True))
     return z / z.sum(axis=-1, keepdims=True)
 
@@ -145,9 +159,10 @@ def topk_select(l: np.ndarray, k: int) -> np.ndarray:
     """Ids of the k largest fp32 logits per row, ordered (logit desc, id asc).
 
     Selecting on logits equals selecting on their softmax (a monotone map)
-    and avoids false ties where exp() rounds two logits to one value.
+    and avoids false ties where exp() rounds two logits to one value.  NaN
+    counts as -inf (so it ties with -inf and loses to every number).
     """
-    l32 = np.asarray(l, dtype=np.float32)
+    l32 = nan_as_minus_inf(np.asarray(l, dtype=np.float32))
     order = np.argsort(-l32, axis=-1, kind="stable")  # equal keys keep id order
     return order[..., :k].astype(np.int32)
 
@@ -166,11 +181,16 @@ def route(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def topk_gap(l: np.ndarray, k: int) -> np.ndarray:
-    """Per row: k-th largest minus (k+1)-th largest logit (inf when k == E)."""
-    s = -np.sort(-np.asarray(l, dtype=np.float64), axis=-1)
+    """Per row: k-th largest minus (k+1)-th largest logit (inf when k == E).
+
+    NaN counts as -inf; two equal values (two -inf included) have gap 0.
+    """
+    s = -np.sort(-nan_as_minus_inf(np.asarray(l, dtype=np.float64)), axis=-1)
     if k >= s.shape[-1]:
         return np.full(s.shape[:-1], np.inf)
-    return s[..., k - 1] - s[..., k]
+    a, b = s[..., k - 1], s[..., k]
+    with np.errstate(invalid="ignore"):
+        return np.where(a == b, 0.0, a - b)
 
 
 # --------------------------------------------------------------------------

@@ -276,6 +276,45 @@ def test_topk_decides_in_fp32():
     assert oracle.topk_select(np.array([[a, b]]), 1)[0].tolist() == [0]
 
 
+def test_topk_gap_brute_force():
+    """topk_gap = k-th minus (k+1)-th largest logit, against Python's own
+    sort of each row; ties give 0, k = E gives inf."""
+    rng = np.random.default_rng(23)
+    for trial in range(200):
+        E = int(rng.integers(2, 12))
+        k = int(rng.integers(1, E + 1))
+        row = rng.standard_normal(E)
+        if trial % 4 == 0:
+            row = rng.integers(-2, 3, E).astype(np.float64)  # exact ties
+        desc = sorted(row.tolist(), reverse=True)
+        want = math.inf if k == E else desc[k - 1] - desc[k]
+        assert oracle.topk_gap(row[None, :], k)[0] == want, (row, k)
+    # hand-worked rows
+    l = np.array([[1.0, 5.0, 3.0, 4.0], [2.0, 2.0, 1.0, 0.0]])
+    assert oracle.topk_gap(l, 1).tolist() == [1.0, 0.0]
+    assert oracle.topk_gap(l, 2).tolist() == [1.0, 1.0]
+    assert oracle.topk_gap(l, 3).tolist() == [2.0, 1.0]
+    assert oracle.topk_gap(l, 4).tolist() == [math.inf, math.inf]
+
+
+def test_nan_logits_read_as_minus_inf():
+    """A NaN logit is never chosen over a number, ties with -inf (lower id
+    first) and has probability 0; expected ids and weights worked by hand."""
+    nan, inf = float("nan"), float("inf")
+    l = np.array([[0.5, nan, 0.25, -inf, 0.25, nan]], dtype=np.float32)
+    assert oracle.topk_select(l, 3)[0].tolist() == [0, 2, 4]
+    assert oracle.topk_select(l, 6)[0].tolist() == [0, 2, 4, 1, 3, 5]
+    ids, w = oracle.route(l, 3)
+    e = math.exp(-0.25)  # exp(0.25 - 0.5)
+    np.testing.assert_allclose(w[0], [1 / (1 + 2 * e), e / (1 + 2 * e), e / (1 + 2 * e)], rtol=1e-15)
+    p = oracle.softmax(l.astype(np.float64))[0]
+    assert p[1] == 0.0 and p[3] == 0.0 and p[5] == 0.0
+    np.testing.assert_allclose(p.sum(), 1.0, rtol=1e-15)
+    # the gap treats NaN as -inf too: 0.25 - (-inf), and two -inf tie at 0
+    assert oracle.topk_gap(l, 3)[0] == inf
+    assert oracle.topk_gap(l, 4)[0] == 0.0
+
+
 def test_renormalised_weights():
     rng = np.random.default_rng(19)
     l = rng.standard_normal((50, 16)) * 3
@@ -355,6 +394,34 @@ def test_single_expert_k1_is_dense_ffn(qt):
     for t in range(T):
         want = _dense_ffn_loops(x[t].astype(np.float64), wg, wu, wd)
         np.testing.assert_allclose(res["out"][t], want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+def test_layer_k_above_one_is_per_token_dense_sum(qt):
+    """k >= 2: every token's output equals, token by token, the sum over
+    its k chosen experts (logit desc, id asc) of exp-weighted dense SwiGLU
+    FFNs computed by explicit loops, with the weights worked from the logits
+    by math.exp: no grouping, gathering or scattering involved."""
+    rng = np.random.default_rng(41)
+    H, I, E, k, T = 64, 96, 6, 3, 5
+    quant = gi.quantize_q8_0 if qt == "q8_0" else gi.quantize_q4_0
+    banks = [tuple(quant((rng.standard_normal(sh) * 0.1).astype(np.float32)) for sh in ((I, H), (I, H), (H, I)))
+             for _ in range(E)]
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    logits = rng.standard_normal((T, E))
+    logits[1, [1, 4]] = logits[1, 2]  # a tie at the top: lower ids first
+    res = oracle.moe_layer(x, qt, lambda e: banks[e], k, logits=logits)
+    deq = [tuple(oracle.dequant(qt, b) for b in bank) for bank in banks]
+    for t in range(T):
+        chosen = sorted(range(E), key=lambda e: (-float(np.float32(logits[t, e])), e))[:k]
+        assert res["ids"][t].tolist() == chosen
+        z = [math.exp(logits[t, e] - logits[t, chosen[0]]) for e in chosen]
+        want = np.zeros(H)
+        for j, e in enumerate(chosen):
+            y = _dense_ffn_loops(x[t].astype(np.float64), *deq[e])
+            np.testing.assert_allclose(res["y_pairs"][t * k + j], y, rtol=1e-12, atol=1e-13)
+            want = want + (z[j] / math.fsum(z)) * y
+        np.testing.assert_allclose(res["out"][t], want, rtol=1e-12, atol=1e-13)
 
 
 def test_combine_one_hot_is_gather():
