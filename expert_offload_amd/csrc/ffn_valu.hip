@@ -1,6 +1,7 @@
-// Portable expert-FFN kernels on the vector ALUs (fp32 activations or bf16
-// activations widened to fp32, fp32 accumulation): the reference schedule
-// every tuned kernel of this library is compared against.
+// Expert-FFN kernels on the vector ALUs (fp32 activations or bf16
+// activations widened to fp32, fp32 accumulation) for the shapes the tuned
+// kernels do not take: decode batches of more than 1024 (token, expert)
+// pairs and prefill with fp32 activations.
 //
 // Work is split into (active expert, row tile) items; each item streams its
 // rows' quant blocks once per group of up to 8 of the expert's pairs.

@@ -7,8 +7,8 @@
 // (X Wu^T) with X the expert's gathered token rows, then y = h Wd^T.
 //
 // Tiles.  A workgroup (4 wavefronts) computes a 256 x 128 output tile of one
-// expert with v_mfma_f32_32x32x16_bf16.  Each wavefront owns 64 rows and all
-// 128 columns (2 x 4 MFMA tiles, 128 accumulators per lane), so:
+// expert with v_mfma_f32_16x16x32_bf16.  Each wavefront owns 64 rows and all
+// 128 columns (4 x 8 blocks of 16 x 16, 128 accumulators per lane), so:
 //  * activation rows are private to a wavefront and go from global memory
 //    (L2) straight into MFMA operand registers, the next K step's loads
 //    issued while the current step's MFMAs run;

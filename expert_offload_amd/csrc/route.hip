@@ -140,11 +140,15 @@ __global__ __launch_bounds__(kTopkPermuteThreads) void topk_permute_kernel(
   static_assert(kTopkPermuteThreads >= 2 * kWave, "a second wavefront publishes the ids");
   if (ids_host && wave == 1) {
     // wavefront 1 publishes while wavefront 0 groups the pairs: every id
-    // reaches host memory (the fence waits for this wavefront's stores)
-    // before the flag does, so a host that waits for seq can start its
-    // lookup while this kernel still permutes
+    // reaches host memory before the flag does, so a host that waits for
+    // seq can start its lookup while this kernel still permutes.  Each
+    // lane's system fence waits for the wavefront's outstanding stores (the
+    // memory counter is per wavefront, so it covers all 64 lanes' stores);
+    // the wave barrier keeps lane 0's flag store after every lane's fence
+    // even if a later change lets lanes of this wavefront diverge.
     for (int i = lane; i < T * k; i += kWave) ids_host[i] = s.ids[i];
     __threadfence_system();
+    __builtin_amdgcn_wave_barrier();
     if (lane == 0) __hip_atomic_store(ids_flag, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   if (T * k <= 1024) {

@@ -11,7 +11,7 @@ from expert_offload_amd import layer
 from gen import inputs as gi
 import oracle
 
-from gpu_util import DEV, ResidentLayer, bf16_tensor, dev, max_rel_err, note
+from gpu_util import DEV, ResidentLayer, bf16_tensor, check_routed_layer, dev, max_rel_err, note
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def _outputs(ctx, rl, T, x, wr, fused):
                   router_w=dev(wr), fused=fused)
     torch.cuda.synchronize()
     moe.moe_ctx_check(ctx)
-    return {n: getattr(buf, n).cpu().numpy() for n in ("ids", "w", "y", "out")}
+    return {n: getattr(buf, n).cpu().numpy() for n in ("logits", "ids", "w", "y", "out")}
 
 
 @pytest.mark.parametrize("T", [1, 4, 16])
@@ -87,11 +87,8 @@ def test_decode_layer(ctx, typed_layer, T):
     for key in two:
         np.testing.assert_array_equal(one[key], two[key], err_msg=key)
     ref = oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, router_w=wr)
-    ok = ref["gap"] >= 1e-5
-    np.testing.assert_array_equal(one["ids"][ok], ref["ids"][ok])
-    err = max_rel_err(one["out"][ok], ref["out"][ok])
-    note(f"   out max rel err {err:.2e}")
-    assert err <= DECODE_TOL
+    check_routed_layer(one["ids"], one["w"], one["logits"], one["y"], one["out"], ref, DECODE_TOL, T,
+                       lambda lo: oracle.moe_layer(x, wl.qtype, rl.get_blocks, wl.k, logits=lo))
 
 
 @pytest.mark.parametrize("T", [37, 300])

@@ -460,3 +460,43 @@ def test_widest_cache_masks_match_oracle(ctx):
     assert (trace >= 512).any() and (trace < 512).any()
     want, _ = oracle.lru_simulate(trace, 64, host=host)
     np.testing.assert_array_equal(misses, (~want).sum(axis=2))
+
+
+def test_lru_full_expert_cache_trace(ctx):
+    """The expert-cache workload's whole trace (8 layers, 256 experts,
+    top-8, 2048 single-token steps, 816 slots = 40% of each layer's
+    experts) through cache_decode_layer, the call the benchmark makes per
+    layer, with experts of a small size (the LRU's decisions do not depend
+    on it): every lookup's hit or miss equals the oracle's LRU, and the
+    cache's counts equal the oracle's."""
+    import dataclasses
+    big = gi.workload("cache_q4_0_h4096_e256")
+    wl = dataclasses.replace(big, H=256, I=256)
+    trace = gi.cache_trace(big)
+    steps = trace.shape[0]
+    n_slots = int(big.cache_fraction * big.E) * big.layers
+    note(f"full expert-cache trace: {steps} steps x {big.layers} layers, {n_slots} slots")
+    sb = moe.moe_slot_bytes(L.QTYPE[wl.qtype], wl.H, wl.I)
+    pool = torch.zeros(wl.layers * wl.E * sb, dtype=torch.uint8, pin_memory=True)
+    logits = np.stack([gi.cache_trace_logits(big, trace, s) for s in range(steps)])
+    order = oracle.topk_select(logits, big.k)  # the router's order of each (step, layer)'s ids
+    lg = dev(logits)
+    x = torch.zeros((1, wl.H), dtype=torch.float32, device=DEV)
+    cl = layer.CachedLayers(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, n_slots, pool)
+    hits = np.zeros(order.shape, dtype=bool)
+    for s in range(steps):
+        for l in range(wl.layers):
+            cl.layer(l, x, lg[s, l:l + 1])
+            copied, on_host, _ = cl.last_misses()
+            assert len(on_host) == 0
+            hits[s, l] = ~np.isin(order[s, l], copied)
+        if (s + 1) % 512 == 0:
+            note(f"   step {s + 1}")
+    torch.cuda.synchronize()
+    moe.moe_ctx_check(ctx)
+    want, _ = oracle.lru_simulate(order, n_slots)
+    np.testing.assert_array_equal(hits, want)
+    h, m = cl.stats()
+    assert h == int(want.sum()) and m == int((~want).sum())
+    note(f"   hit rate {h / (h + m):.4f} ({m} misses), equal to the oracle's on every lookup")
+    cl.close()
