@@ -37,7 +37,7 @@ EXPORTS = (
     "moe_route_permute_workspace_size", "moe_route_permute", "moe_decode_layer", "cache_decode_layer",
     "prefill_stream_create", "prefill_stream_layer", "prefill_stream_stats", "prefill_stream_destroy",
     "moe_host_expert_ffn", "moe_host_has_avx512", "cache_set_miss_policy", "cache_miss_stats",
-    "cache_last_misses",
+    "cache_last_misses", "moe_decode_layer_static", "moe_static_scratch_bytes",
 )
 
 
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         "moe_expert_ffn_workspace_size": (i, [ctypes.POINTER(moe_ffn_args), szp]),
         "moe_expert_ffn": (i, [vp, ctypes.POINTER(moe_ffn_args), vp]),
         "moe_decode_layer": (i, [vp, ctypes.POINTER(moe_ffn_args), vp, vp, vp, vp, vp, vp, vp]),
+        "moe_decode_layer_static": (i, [vp, ctypes.POINTER(moe_ffn_args), vp, vp, vp, vp, vp, vp, vp]),
+        "moe_static_scratch_bytes": (sz, []),
         "moe_combine": (i, [vp, vp, vp, i, i, i, vp, vp]),
         "moe_dequantize": (i, [vp, i, vp, i, i, i, vp, vp]),
         "cache_slot_table_create": (i, [i, i, i, i, i, i, vp, vp, ctypes.POINTER(vp)]),
@@ -313,6 +315,17 @@ def moe_decode_layer(ctx: Ctx, args: moe_ffn_args, router_w, bias, logits_in, lo
     _check(lib().moe_decode_layer(ctx.handle, ctypes.byref(args), _dev_ptr(router_w), _dev_ptr(bias),
                                   _dev_ptr(logits_in), _dev_ptr(logits_out), _dev_ptr(topk_ids),
                                   _dev_ptr(pair_pos), _stream(stream)), "moe_decode_layer")
+
+
+def moe_decode_layer_static(ctx: Ctx, args: moe_ffn_args, router_w, bias, logits_in, logits_out, topk_ids,
+                            pair_pos, stream=None) -> None:
+    _check(lib().moe_decode_layer_static(ctx.handle, ctypes.byref(args), _dev_ptr(router_w), _dev_ptr(bias),
+                                         _dev_ptr(logits_in), _dev_ptr(logits_out), _dev_ptr(topk_ids),
+                                         _dev_ptr(pair_pos), _stream(stream)), "moe_decode_layer_static")
+
+
+def moe_static_scratch_bytes() -> int:
+    return int(lib().moe_static_scratch_bytes())
 
 
 def moe_combine(ctx: Ctx, y_pairs, topk_w, T: int, k: int, H: int, out, stream=None) -> None:

@@ -121,6 +121,12 @@ int moe_ctx_create(int device, moe_ctx** out) {
     delete c;
     return hip_error(e, "hipMemset(error word)");
   }
+  int rc = static_scratch_init(device, &c->d_scratch);
+  if (rc) {
+    (void)hipFree(c->d_err);
+    delete c;
+    return rc;
+  }
   *out = c;
   return MOE_OK;
 }

@@ -20,6 +20,7 @@ struct moe_ctx {
   int device;
   int num_cus;
   int* d_err;  // sticky device error word: 0, (expert id + 1), or INT_MIN
+  void* d_scratch = nullptr;  // this device's static scratch array (moe_decode_layer_static)
   bool timing = false;
   std::vector<moe_timing_rec> recs;
   std::vector<hipEvent_t> spare_events;
@@ -67,6 +68,9 @@ int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3
 void clear_error();
 int hip_error(hipError_t e, const char* what);
 int ensure_device(const moe_ctx* ctx);
+// Device address of the static scratch array on `device` (current), looked
+// up once per device.
+int static_scratch_init(int device, void** out);
 int check_launch(const char* kernel);
 
 // ------------------------------------------------------- device layout

@@ -78,7 +78,8 @@ def forward(ctx: L.Ctx, buf: LayerBuffers, pool_base: int, slot_bytes: int, n_sl
 
     ``fused``: True = moe_route_permute, then moe_expert_ffn with the
     combine folded in (two calls); "layer" = moe_decode_layer (one call);
-    otherwise the four entry points one after another.
+    "static" = moe_decode_layer_static (one call, no workspace); otherwise
+    the four entry points one after another.
     """
     T, H, I, E, k = buf.T, buf.H, buf.I, buf.E, buf.k
     if fused == "layer":
@@ -87,6 +88,13 @@ def forward(ctx: L.Ctx, buf: LayerBuffers, pool_base: int, slot_bytes: int, n_sl
                                ws=buf.ws, ws_bytes=buf.ws.numel(), x_dtype=buf.x_dtype,
                                topk_w=buf.w, out=buf.out)
         L.moe_decode_layer(ctx, args, router_w, bias, logits_in, buf.logits, buf.ids, buf.pair_pos, stream=stream)
+        return buf.out
+    if fused == "static":  # moe_decode_layer_static: the library's own scratch, no workspace passed
+        args = L.make_ffn_args(pool_base, slot_bytes, n_slots, buf.q, H, I, T, k, E, slot_table, x,
+                               buf.offsets, buf.sorted_pairs, buf.active, buf.y, buf.mode,
+                               ws=None, ws_bytes=0, x_dtype=buf.x_dtype, topk_w=buf.w, out=buf.out)
+        L.moe_decode_layer_static(ctx, args, router_w, bias, logits_in, buf.logits, buf.ids, buf.pair_pos,
+                                  stream=stream)
         return buf.out
     if fused and expert_mask is None:
         L.moe_route_permute(ctx, x, router_w, bias, logits_in, T, H, E, k, buf.logits, buf.ids, buf.w,

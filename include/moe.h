@@ -257,6 +257,29 @@ int moe_decode_layer(moe_ctx* ctx, const moe_ffn_args* args,
                      const float* logits_in, float* logits_out,
                      int32_t* topk_ids, int32_t* pair_pos, void* stream);
 
+/* moe_decode_layer_static: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The same layer as moe_decode_layer, through the same
+ * kernels and with the same results, but args.ws / args.ws_bytes are
+ * ignored: the workspace is a static device array of the library,
+ * moe_static_scratch_bytes() bytes (8 MiB) on each GPU it runs on, held
+ * until the process ends.  The caller still passes every input and output.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine; with the context's kernel timing switched on the timer may
+ * create events).  It needs T*k*I*4 bytes of workspace (the decode h rows);
+ * more -> MOE_ERR_WORKSPACE, checked on the host before any launch.  Every
+ * call on one GPU shares that GPU's array and leaves its contents as they
+ * were, so calls that overlap on one GPU (on different streams, or from
+ * different threads) race: order them on one stream.  Nothing in the array
+ * needs to start at zero (every element read is first written by the same
+ * call).  Errors otherwise as moe_decode_layer. */
+size_t moe_static_scratch_bytes(void);
+int moe_decode_layer_static(moe_ctx* ctx, const moe_ffn_args* args,
+                            const float* router_w, const float* bias,
+                            const float* logits_in, float* logits_out,
+                            int32_t* topk_ids, int32_t* pair_pos,
+                            void* stream);
+
 /* --------------------------------------------------------------- combine
  * out[t][:] = sum over j ascending of topk_w[t][j] * y_pairs[t*k + j][:]
  * (device fp32; out [T][H]). */
