@@ -20,6 +20,8 @@ Usage::
     python -m expert_offload_amd.rocprof_summary stats DIR --out FILE --command CMD
     python -m expert_offload_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR --kernel NAME
         --calib-bytes N --out FILE --command CMD
+    python -m expert_offload_amd.rocprof_summary counters DIR [DIR ...] --kernel NAME [--kernel NAME]
+        --out FILE --command CMD
 """
 from __future__ import annotations
 
@@ -152,6 +154,56 @@ def write_traffic(fetch_dir: str, write_dir: str, kernel: str, calib_bytes: int,
         f.write(f"source_hash: {source_hash(kernel)}\n")
 
 
+SIMD_NUM, CU_NUM = 1024, 256  # MI355X: 256 compute units of 4 SIMDs
+
+
+def write_counters(dirs: List[str], kernels: List[str], out: str, command: str) -> None:
+    """Per-dispatch averages of every counter collected in `dirs` (one
+    rocprofv3 --pmc run each) for the kernels whose names contain one of
+    `kernels`, with the derived figures the counters allow:
+      MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs)
+      VALU busy % = 4 * SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE * SIMDs)
+      MFMA FLOP   = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512
+      L2 hit %    = TCC_HIT / (TCC_HIT + TCC_MISS)
+    (SIMD count of MI355X: 1024)."""
+    per: Dict[str, Dict[str, List[float]]] = {}
+    for d in dirs:
+        with open(_find(d, "counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                name = _short(r["Kernel_Name"])
+                if not any(k in name for k in kernels):
+                    continue
+                per.setdefault(name, {}).setdefault((d, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    with open(out, "w") as f:
+        f.write("rocprofv3 counters per dispatch\n")
+        f.write(f"command: {command}\n\n")
+        for name in sorted(per):
+            f.write(f"{name}\n")
+            avg: Dict[str, float] = {}
+            for (d, c), v in sorted(per[name].items()):
+                a = sum(v) / len(v)
+                key = c if c != "GRBM_GUI_ACTIVE" else f"GRBM_GUI_ACTIVE[{os.path.basename(d.rstrip('/'))}]"
+                avg[key] = a
+                f.write(f"  {key:58s} {a:18.1f}   ({len(v)} dispatches)\n")
+
+            def gui(counter):
+                for d, c in per[name]:
+                    if c == counter:
+                        g = per[name].get((d, "GRBM_GUI_ACTIVE"))
+                        return sum(g) / len(g) if g else None
+                return None
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and gui("SQ_VALU_MFMA_BUSY_CYCLES"):
+                f.write(f"  MFMA busy: {100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui('SQ_VALU_MFMA_BUSY_CYCLES') * SIMD_NUM):.1f}%\n")
+            if "SQ_ACTIVE_INST_VALU" in avg and gui("SQ_ACTIVE_INST_VALU"):
+                f.write(f"  VALU busy: {100 * 4 * avg['SQ_ACTIVE_INST_VALU'] / (gui('SQ_ACTIVE_INST_VALU') * SIMD_NUM):.1f}%\n")
+            if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+                f.write(f"  bf16 MFMA FLOP per dispatch: {avg['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g}\n")
+            if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+                h, m = avg["TCC_HIT_sum"], avg["TCC_MISS_sum"]
+                f.write(f"  L2 hit rate: {100 * h / max(h + m, 1):.1f}%\n")
+            f.write("\n")
+
+
 def traffic_bytes(kernel: str, path: str) -> Optional[float]:
     """Recorded HBM bytes per launch, or None if absent or the sources changed."""
     if kernel not in KERNEL_SOURCES or not os.path.exists(path):
@@ -181,9 +233,16 @@ def main() -> None:
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--command", required=True)
     a = p.parse_args()
     if a.what == "stats":
         write_stats(a.dir, a.out, a.command)
+    elif a.what == "counters":
+        write_counters(a.dirs, a.kernel, a.out, a.command)
     else:
         write_traffic(a.fetch_dir, a.write_dir, a.kernel, a.calib_bytes, a.out, a.command)
 
