@@ -22,7 +22,54 @@ struct CtlLds {
   int slots[kMaxE];
   int pairs[kCtlMaxPairs];
   float w[kCtlMaxPairs];
+  int runs[kMaxE];      // pair runs of active expert a (stage_runs)
+  int run_base[kMaxE];  // runs before active expert a
+  int scan_wave[16];
 };
+
+// Pair runs.  With more than kRunMinTokens tokens a work item takes at most
+// kRunPairs consecutive pairs of one expert, so an expert that many tokens
+// chose (a skewed router) spreads over several items instead of one
+// wavefront looping over all its tokens.  With fewer tokens run a is active
+// expert a: no expert can have many pairs (a token names an expert once),
+// and the scan in every workgroup's prologue would cost more than it saves
+// (16 tokens of 128 experts: 4 us per kernel).
+constexpr int kRunPairs = 8;
+constexpr int kRunMinTokens = 16;
+
+struct PairRun {
+  int e, pbeg, n;  // expert, first grouped pair of the run, pairs in it
+};
+
+template <int NT>
+__device__ __forceinline__ int stage_runs(const FfnParams& p, CtlLds& s, int n_active) {
+  if (p.T <= kRunMinTokens) return n_active;
+  for (int a = threadIdx.x; a < n_active; a += NT) {
+    const int e = s.active[1 + a];
+    s.runs[a] = (s.offsets[e + 1] - s.offsets[e] + kRunPairs - 1) / kRunPairs;
+  }
+  __syncthreads();
+  return block_exclusive_scan<NT>(s.runs, s.run_base, n_active, s.scan_wave);
+}
+
+// Run r (wavefront-uniform) -> its expert and pairs.
+__device__ __forceinline__ PairRun pair_run(const FfnParams& p, const CtlLds& s, int n_active, int r) {
+  int a = r, first = 0;
+  if (p.T > kRunMinTokens) {  // last active expert with run_base <= r (run_base strictly increases)
+    int lo = 0, hi = n_active - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s.run_base[mid] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    a = lo;
+    first = (r - s.run_base[a]) * kRunPairs;
+  }
+  const int e = s.active[1 + a];
+  const int pbeg = s.offsets[e];
+  const int left = s.offsets[e + 1] - pbeg - first;
+  return {e, pbeg + first, p.T > kRunMinTokens ? min(kRunPairs, left) : left};
+}
 
 // The decode kernels run only when T*k <= kCtlMaxPairs.
 template <int NT>

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
     n_active = route_active(rlds, p.T, p.E);
   } else {
     stage_ctl<256>(p, ctl, false);
-    n_active = ctl.active[0];
+    n_active = stage_runs<256>(p, ctl, ctl.active[0]);  // pair runs (one per expert up to kRunPairs tokens)
   }
   const int* pairs = ctl.pairs;
   constexpr int STRIDE = RPL >= 2 ? LPR / RPL : LPR;  // lane distance gate row -> up row
@@ -55,9 +55,10 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
       n_e = ic.n_e;
       pm = ic.pairs;
     } else {
-      e = ctl.active[1 + a];
-      pbeg = ctl.offsets[e];
-      n_e = ctl.offsets[e + 1] - pbeg;
+      const PairRun run = pair_run(p, ctl, ctl.active[0], a);
+      e = run.e;
+      pbeg = run.pbeg;
+      n_e = run.n;
     }
     // pair s of the expert, s = 0, 1, ... in turn
     int s_next = 0;
@@ -156,15 +157,17 @@ __global__ __launch_bounds__((down_waves<QT, LPR, BPL, RPL>() * kWave)) void ffn
   const bool writer = (lg % (LPR / RPL)) == 0;
   const int n_tiles = p.H / RW;
   const int n_active = ctl.active[0];
+  const int n_runs = stage_runs<NWV * kWave>(p, ctl, n_active);  // pair runs of at most kRunPairs pairs
   const size_t down_off = slot_down_off(QT, p.H, p.I);
   const size_t rbytes = row_bytes(QT, p.I);
   for (int tile_i = blockIdx.x; tile_i < n_tiles; tile_i += gridDim.x) {
     const int h0 = tile_i * RW;
-    for (int a = wave; a < n_active; a += NWV) {
-      const int e = ctl.active[1 + a];
+    for (int r = wave; r < n_runs; r += NWV) {
+      const PairRun run = pair_run(p, ctl, n_active, r);
+      const int e = run.e;
       if (p.mask && !p.mask[e]) continue;
       const int slot = ctl.slots[e];
-      const int pbeg = ctl.offsets[e], n_e = ctl.offsets[e + 1] - pbeg;
+      const int pbeg = run.pbeg, n_e = run.n;
       if (slot < 0 || slot >= p.n_slots) {
         if (lane == 0) atomicCAS(p.err, 0, e + 1);
         for (int s = lane; s < n_e * RW; s += kWave) {

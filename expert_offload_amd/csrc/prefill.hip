@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void prefill_tiles_kernel(const int32_t* __res
 // raw codes and scale in registers, then dequantised to bf16 into LDS.
 // Q4_0 keeps elements 0..15 in the low nibbles and 16..31 in the high
 // nibbles of the block's 16 bytes; Q8_0 half h is bytes 16h..16h+15.
-template <int QT>
+template <int QT, bool FAST = false>
 struct WStage {
   uint32_t w[4];
   uint32_t qh;
@@ -101,6 +101,23 @@ struct WStage {
         const uint32_t u = w[i] ^ 0x80808080u;  // q + 128 in every byte
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[i / 2][(i & 1) * 4 + j] = (__bf16)fmaf(d, (float)((u >> (8 * j)) & 0xFFu), off);
+      }
+    } else if (FAST && !qtype_has_min(QT)) {
+      // code u (at most 5 bits) -> the float 128 + u by placing u in the
+      // mantissa of 128.0 (one byte permute), then fma(128 + u, d, -(128 +
+      // OFF) d) = d (u - OFF), exact as in the path below: (128 + OFF) d
+      // has at most 16 significant bits
+      const float c = -(128.0f + qtype_code_off(QT)) * d;
+      const int sh = 4 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t nib = (w[i] >> sh) & 0x0F0F0F0Fu;
+        if constexpr (qtype_has_qh(QT)) nib |= spread_fifth_bits(qh >> (16 * h + 4 * i));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t bits = __builtin_amdgcn_perm(0x43434343u, nib, 0x04000C0Cu | ((uint32_t)j << 16));
+          o[i / 2][(i & 1) * 4 + j] = (__bf16)fmaf(__uint_as_float(bits), d, c);
+        }
       }
     } else {
       const float off = qtype_has_min(QT) ? m : -qtype_code_off(QT) * d;
@@ -128,7 +145,10 @@ struct WStage {
 // rows would leave the others without MFMA work: every wavefront takes the
 // same rows and two of the eight 16-column blocks (gate/up: gate block
 // `wave` and its up block `wave + 4`, so SwiGLU stays in the wavefront).
-template <int QT, bool GATEUP, int NW, bool SPLIT>
+// FL bit 0: the MFMA phase of a step at raised wave priority, so of the two
+// workgroups on a CU the one with MFMAs to issue is served first while the
+// other dequantises; bit 1: WStage's byte-permute dequantisation.
+template <int QT, bool GATEUP, int NW, bool SPLIT, int FL = 0>
 __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* __restrict__ x, int2 tl, int nt_i,
                                              __bf16* __restrict__ hbuf, __bf16 (&sB)[2][kTN][kLdB],
                                              int (&s_pair)[kWaveRows * NW]) {
@@ -202,17 +222,18 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) a[mt][ks] = *reinterpret_cast<const bf16x8*>(arow[mt] + koff + 32 * ks);
   };
-  auto load_w = [&](WStage<QT> (&st)[kUnits], int kc) {
+  using WS = WStage<QT, (FL & 2) != 0>;
+  auto load_w = [&](WS (&st)[kUnits], int kc) {
     const int b = 2 * min(kc, nk - 1) + bblk;
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) st[u].load(wrow, b, (v0 + u) & 1);
   };
-  auto store_w = [&](const WStage<QT> (&st)[kUnits], __bf16* dst) {
+  auto store_w = [&](const WS (&st)[kUnits], __bf16* dst) {
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) st[u].store(dst + 16 * u, (v0 + u) & 1);
   };
   load_a(a0, 0);
-  WStage<QT> st0[kUnits], st1[kUnits];
+  WS st0[kUnits], st1[kUnits];
   load_w(st0, 0);
   load_w(st1, 1);
   store_w(st0, sdst0);
@@ -225,7 +246,7 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
   // Prefetch indices are clamped to the last step instead of branched on:
   // near the end the repeated loads and the staging into the idle buffer
   // are never read.
-  auto step = [&](int kc, const __bf16 (*sb)[kLdB], __bf16* sdst, WStage<QT> (&nxt)[kUnits],
+  auto step = [&](int kc, const __bf16 (*sb)[kLdB], __bf16* sdst, WS (&nxt)[kUnits],
                   const bf16x8 (&a)[4][2], bf16x8 (&an)[4][2]) {
     load_a(an, kc + 1);
     store_w(nxt, sdst);
@@ -242,6 +263,7 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
         }
       }
     } else if (active) {
+      if constexpr (FL & 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -257,6 +279,7 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
               acc[mt][4 * nh + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b[q], acc[mt][4 * nh + q], 0, 0, 0);
         }
       }
+      if constexpr (FL & 1) __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
   };
@@ -309,7 +332,7 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
 // One launch over both lists: the tiles, then the small tiles (so the
 // small ones are dispatched last, into the big ones' tail).  Each branch is
 // a whole tile, so the two register allocations never overlap.
-template <int QT, bool GATEUP, int NW>
+template <int QT, bool GATEUP, int NW, int FL = 0>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, const __bf16* __restrict__ x,
                                                                   const int2* __restrict__ tiles,
                                                                   const int* __restrict__ count, int ntn,
@@ -321,8 +344,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, c
   const int nt_i = j % ntn;
   const int n_big = count[0];
   if (mt_i >= n_big + count[1]) return;
-  if (mt_i < n_big) prefill_tile<QT, GATEUP, NW, false>(p, x, tiles[mt_i], nt_i, hbuf, sB, s_pair);
-  else prefill_tile<QT, GATEUP, NW, true>(p, x, tiles[mt_i], nt_i, hbuf, sB, s_pair);
+  if (mt_i < n_big) prefill_tile<QT, GATEUP, NW, false, FL>(p, x, tiles[mt_i], nt_i, hbuf, sB, s_pair);
+  else prefill_tile<QT, GATEUP, NW, true, FL>(p, x, tiles[mt_i], nt_i, hbuf, sB, s_pair);
 }
 
 bool prefill_mfma_supported(int H, int I) {
@@ -334,6 +357,10 @@ bool prefill_mfma_supported(int H, int I) {
 // expert of a 4096-token batch) measured slower than four: with one
 // workgroup per CU every barrier idles the matrix cores.
 constexpr int kPrefillWaves = 4;
+// MFMA phase at raised wave priority (bit 0) and the byte-permute
+// dequantisation of the offset types (bit 1): bit-identical results,
+// gate/up 359 -> 349 us at 4096 tokens.
+constexpr int kPrefillFlags = 3;
 constexpr int kPrefillRows = kWaveRows * kPrefillWaves;
 
 static int prefill_max_tiles(size_t P, int E) { return (int)(P / kPrefillRows) + E + 1; }
@@ -348,8 +375,8 @@ static void launch_prefill_gemm(const FfnParams& p, unsigned grid, hipStream_t s
                                 const int* count, int ntn, __bf16* hbuf) {
 #define MOE_PF(Q)                                                                                          \
   case Q:                                                                                                  \
-    launch(prefill_gemm_kernel<Q, GATEUP, kPrefillWaves>, grid, 64 * kPrefillWaves, 0, s, p, x, tiles, count, ntn, \
-           hbuf);                                                                                          \
+    launch(prefill_gemm_kernel<Q, GATEUP, kPrefillWaves, kPrefillFlags>, grid, 64 * kPrefillWaves, 0, s, p, x, tiles, \
+           count, ntn, hbuf);                                                                              \
     break;
   switch (p.qtype) {
     MOE_PF(MOE_QTYPE_Q8_0)

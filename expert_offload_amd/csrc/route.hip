@@ -115,6 +115,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ src
 constexpr int kFusedMaxPairs = 4096;
 
 constexpr int kTopkPermuteThreads = 512;
+constexpr int kFusedMaxTokens = 2 * kTopkPermuteThreads / kWave;
 
 struct TopkPermuteLds {
   int ids[kFusedMaxPairs];
@@ -261,7 +262,11 @@ int route_permute_impl(moe_ctx* ctx, const void* x, int x_dtype, const float* ro
   if ((rc = ensure_device(ctx))) return rc;
   if (!ids_host != !ids_flag) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: host ids need their flag");
   hipStream_t s = (hipStream_t)stream;
-  if ((long long)T * k > kFusedMaxPairs) {  // large batches: separate kernels
+  // Large batches, and more tokens than the fused kernel's wavefronts take
+  // two at a time (it selects token by token in each wavefront; the
+  // separate top-k kernel spreads the tokens over many workgroups): separate
+  // kernels.  The host copy of the ids needs the fused kernel.
+  if ((long long)T * k > kFusedMaxPairs || (T > kFusedMaxTokens && !ids_host)) {
     if (ids_host || ids_flag) return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: a host copy of the ids needs T*k <= %d",
                                    kFusedMaxPairs);
     rc = launch_route(ctx, x, x_dtype, router_w, bias, logits_in, T, H, E, k, logits_out, topk_ids, topk_w, s);

@@ -252,8 +252,11 @@ def decode_layer():
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("T", [1, 4, 16, 17, 100])
 def test_decode_q8_0_layer(ctx, decode_layer, T, fused):
+    """Decode layers at the benchmark's batch sizes, and past 16 tokens,
+    where an expert's pairs are split into runs of at most 8 and the top-k
+    runs in its own kernel ahead of the grouping."""
     note(f"decode q8_0 layer T={T} fused={fused}")
     wl = decode_layer.wl
     x, wr = gi.activations(wl, T), gi.router_weight(wl, 0)
