@@ -54,7 +54,8 @@ __all__ = [
 ]
 
 QK = 32
-BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24}
+BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24,
+               "q4_k": 18}  # bytes per 32 weights (Q4_K: 144 per super-block of 256)
 
 # substream "kind" field
 KIND = {
@@ -260,8 +261,66 @@ def quantize_q5_1(w: np.ndarray) -> np.ndarray:
     return out
 
 
+def _round_half_away_f32(v: np.ndarray) -> np.ndarray:
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    return np.where(v >= 0, np.floor(v + 0.5), np.ceil(v - 0.5))
+
+
+def pack_q4_k(d: np.ndarray, dmin: np.ndarray, sc: np.ndarray, mn: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Q4_K super-blocks from their fields: d, dmin fp32 [...] (stored as
+    fp16), 6-bit scales and mins [..., 8], codes [..., 8, 32] in 0..15 ->
+    uint8 [..., 144]: d, dmin, 12 bytes of packed scales and mins, 128 bytes
+    of nibbles (sub-block 2i low and 2i+1 high in bytes 32i .. 32i+31)."""
+    sc = np.asarray(sc).astype(np.uint8)
+    mn = np.asarray(mn).astype(np.uint8)
+    q = np.asarray(q).astype(np.uint8)
+    out = np.empty(sc.shape[:-1] + (144,), dtype=np.uint8)
+    out[..., 0:2] = _fp16_bytes(np.asarray(d, dtype=np.float32))
+    out[..., 2:4] = _fp16_bytes(np.asarray(dmin, dtype=np.float32))
+    for j in range(4):
+        out[..., 4 + j] = (sc[..., j] & 63) | ((sc[..., j + 4] >> 4) << 6)
+        out[..., 8 + j] = (mn[..., j] & 63) | ((mn[..., j + 4] >> 4) << 6)
+        out[..., 12 + j] = (sc[..., j + 4] & 0x0F) | ((mn[..., j + 4] & 0x0F) << 4)
+    for i in range(4):
+        out[..., 16 + 32 * i:48 + 32 * i] = (q[..., 2 * i, :] & 0x0F) | ((q[..., 2 * i + 1, :] & 0x0F) << 4)
+    return out
+
+
+def quantize_q4_k(w: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K] -> uint8 [rows, K/256, 144] ggml Q4_K super-blocks.
+
+    Harness quantiser (both sides read the same bytes): per sub-block of 32
+    the offset m = max(0, -min) and the step s = (max + m) / 15; per
+    super-block d = max step / 63 and dmin = max offset / 63, stored as fp16;
+    6-bit scale and min codes round(s / d), round(m / dmin); weight codes
+    round((w + dmin * min) / (d * scale)) clamped to 0..15 (rounding half away
+    from zero, in fp32)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    sb = w.reshape(rows, K // 256, 8, 32)
+    off = np.maximum(-sb.min(axis=3), np.float32(0)).astype(np.float32)
+    step = ((sb.max(axis=3) + off) / np.float32(15)).astype(np.float32)
+    d = (step.max(axis=2) / np.float32(63)).astype(np.float16).astype(np.float32)
+    dmin = (off.max(axis=2) / np.float32(63)).astype(np.float16).astype(np.float32)
+
+    def codes(v, s, top):
+        out = np.zeros(v.shape, dtype=np.float64)
+        nz = np.broadcast_to(s != 0, v.shape)
+        ratio = np.zeros(v.shape, dtype=np.float32)
+        ratio[nz] = (np.broadcast_to(v, v.shape)[nz] / np.broadcast_to(s, v.shape)[nz]).astype(np.float32)
+        out[nz] = _round_half_away_f32(ratio[nz])
+        return np.clip(out, 0, top).astype(np.uint8)
+
+    sc = codes(step, d[..., None], 63)
+    mn = codes(off, dmin[..., None], 63)
+    eff_d = (d[..., None] * sc.astype(np.float32)).astype(np.float32)
+    eff_m = (dmin[..., None] * mn.astype(np.float32)).astype(np.float32)
+    q = codes((sb + eff_m[..., None]).astype(np.float32), eff_d[..., None], 15)
+    return pack_q4_k(d, dmin, sc, mn, q)
+
+
 _QUANT = {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0, "q4_1": quantize_q4_1, "q5_0": quantize_q5_0,
-          "q5_1": quantize_q5_1}
+          "q5_1": quantize_q5_1, "q4_k": quantize_q4_k}
 
 
 # --------------------------------------------------------------------------

@@ -11,8 +11,8 @@ pool in host memory and uses VRAM as an expert cache
 ("FreeToken github moe: Setup Guide & MoE Runtime Comparison", introduction;
 "FreeToken Inference Engine: 3x Speed Boost for MoE Models", section "From
 Static Allocation to Dynamic Scheduling").  The expert banks are ggml
-blocks of the standard types (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0) held in one
-slot pool of one type (FreeToken fork README, sections "Quant types" and
+blocks of the standard types (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0) and the
+Q4_K K-quant held in one slot pool of one type (FreeToken fork README, sections "Quant types" and
 "Known limits").  Each token activates only a
 subset of the experts (setup guide, introduction).  The steps below are the
 plainest reading of that layer: softmax over expert logits, keep the k
@@ -44,8 +44,8 @@ QK = 32  # weights per block, every format here
 
 
 # --------------------------------------------------------------------------
-# 1. block dequantisation (ggml Q8_0 / Q4_0 / Q4_1 / Q5_0 / Q5_1; FreeToken fork
-#    README, "Quant types": the standard ggml types)
+# 1. block dequantisation (ggml Q8_0 / Q4_0 / Q4_1 / Q5_0 / Q5_1 and Q4_K;
+#    FreeToken fork README, "Quant types": the standard and K-quant rows)
 # --------------------------------------------------------------------------
 def _block_scale(blocks: np.ndarray) -> np.ndarray:
     """fp16 little-endian scale in bytes 0..1 of every block, as float64."""
@@ -117,8 +117,50 @@ def dequant_q5_1(blocks: np.ndarray) -> np.ndarray:
     return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK)
 
 
+QK_K = 256  # weights per K-quant super-block
+
+
+def q4_k_scales_mins(sc12: np.ndarray):
+    """The 12 packed bytes of a Q4_K super-block -> (scales, mins), int64
+    [..., 8], each a 6-bit field of sub-block j = 0..7.  Sub-blocks 0-3:
+    the low six bits of byte j (scale) and of byte j + 4 (min).  Sub-blocks
+    4-7: byte j + 4 gives the low four bits (scale in its low nibble, min
+    in its high nibble), and the top two bits of byte j - 4 (scale) and of
+    byte j (min) give bits 4-5."""
+    b = np.asarray(sc12).astype(np.int64)
+    sc = np.empty(b.shape[:-1] + (8,), dtype=np.int64)
+    mn = np.empty(b.shape[:-1] + (8,), dtype=np.int64)
+    for j in range(4):
+        sc[..., j] = b[..., j] & 63
+        mn[..., j] = b[..., j + 4] & 63
+    for j in range(4, 8):
+        sc[..., j] = (b[..., j + 4] & 0x0F) | ((b[..., j - 4] >> 6) << 4)
+        mn[..., j] = (b[..., j + 4] >> 4) | ((b[..., j] >> 6) << 4)
+    return sc, mn
+
+
+def dequant_q4_k(blocks: np.ndarray) -> np.ndarray:
+    """uint8 [..., nsb, 144] -> float64 [..., nsb*256] (ggml Q4_K, a K-quant
+    of the FreeToken fork README's "Quant types" table).  A super-block of
+    256 weights: fp16 d, fp16 dmin, 12 bytes of 6-bit scales and mins of its
+    8 sub-blocks of 32, then 128 bytes of nibbles.  Bytes 32i .. 32i+31 hold
+    sub-block 2i in their low nibbles and sub-block 2i+1 in their high
+    nibbles, element l of either sub-block in byte 32i + l.  Weight l of
+    sub-block j: d * scale_j * q - dmin * min_j."""
+    d, dmin = _half(blocks, 0), _half(blocks, 2)
+    sc, mn = q4_k_scales_mins(blocks[..., 4:16])
+    qs = blocks[..., 16:144].astype(np.int64)
+    q = np.empty(blocks.shape[:-1] + (8, 32), dtype=np.int64)
+    for i in range(4):
+        chunk = qs[..., 32 * i:32 * i + 32]
+        q[..., 2 * i, :] = chunk & 0x0F
+        q[..., 2 * i + 1, :] = chunk >> 4
+    w = (d[..., None, None] * sc[..., None]) * q - (dmin[..., None] * mn)[..., None]
+    return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK_K)
+
+
 _DEQUANT = {"q8_0": dequant_q8_0, "q4_0": dequant_q4_0, "q4_1": dequant_q4_1, "q5_0": dequant_q5_0,
-            "q5_1": dequant_q5_1}
+            "q5_1": dequant_q5_1, "q4_k": dequant_q4_k}
 
 
 def dequant(qtype: str, blocks: np.ndarray) -> np.ndarray:

@@ -168,6 +168,78 @@ def test_quantiser_error_bound_affine(qt):
     assert (err <= bound * 1.01 + 2 * np.abs(b).max(axis=2) * 2.0 ** -10).all()
 
 
+GOLDEN_Q4_K = os.path.join(os.path.dirname(__file__), "golden", "hand_superblock_q4_k.txt")
+
+
+def _golden_q4_k():
+    f = {}
+    for line in open(GOLDEN_Q4_K):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            f[k.strip()] = v.split()
+    return f
+
+
+def _hand_superblock_q4_k():
+    """The golden super-block's bytes, built here from the field rules."""
+    f = _golden_q4_k()
+    b = [0x00, 0x3C, 0x00, 0x38] + [int(h, 16) for h in f["scales"]]
+    for i in range(4):
+        b += [((l + i) & 15) | (((3 * l + i) & 15) << 4) for l in range(32)]
+    return np.array(b, dtype=np.uint8)
+
+
+def test_dequant_q4_k_hand_superblock():
+    """Hand-built Q4_K super-block: the 6-bit scale and min fields and
+    selected weights worked out by hand from the format (golden file)."""
+    f = _golden_q4_k()
+    blk = _hand_superblock_q4_k()
+    sc, mn = oracle.q4_k_scales_mins(blk[4:16])
+    assert sc.tolist() == [int(v) for v in f["expected_scales"]]
+    assert mn.tolist() == [int(v) for v in f["expected_mins"]]
+    got = oracle.dequant("q4_k", blk[None, None, :])[0]
+    assert got.shape == (256,)
+    for item in f["weights"]:
+        idx, val = item.split(":")
+        assert got[int(idx)] == float(val), (idx, got[int(idx)], val)
+
+
+def test_dequant_q4_k_brute_force():
+    """Every code at every position of every sub-block, with scale and min
+    codes over the full 6-bit range (high bits set and clear), against the
+    exact d * scale * q - dmin * min; the super-blocks are packed by the
+    harness packer (field rules written independently of the oracle)."""
+    rng = np.random.default_rng(13)
+    for d_bits, m_bits in [(0x3C00, 0x3800), (0x2E66, 0x0001), (0x7BFF, 0x03FF), (0x0001, 0x7BFF)]:
+        dv, mv = Fraction(fp16_bits_to_float(d_bits)), Fraction(fp16_bits_to_float(m_bits))
+        for trial in range(6):
+            sc = rng.integers(0, 64, 8)
+            mn = rng.integers(0, 64, 8)
+            sc[trial % 8], mn[(trial + 3) % 8] = 63, 0
+            q = (np.arange(256).reshape(8, 32) * (trial + 1) + trial) % 16
+            blk = gi.pack_q4_k(np.float32(fp16_bits_to_float(d_bits)), np.float32(fp16_bits_to_float(m_bits)),
+                               sc, mn, q)
+            assert int(blk[0]) | int(blk[1]) << 8 == d_bits and int(blk[2]) | int(blk[3]) << 8 == m_bits
+            got = oracle.dequant("q4_k", blk[None, None, :])[0]
+            for j in range(8):
+                for l in range(32):
+                    want = dv * int(sc[j]) * int(q[j, l]) - mv * int(mn[j])
+                    assert Fraction(float(got[32 * j + l])) == want, (j, l)
+
+
+def test_quantiser_error_bound_q4_k():
+    """The harness Q4_K quantiser stays within about a step of its input:
+    half a code step plus the 6-bit rounding of scale and min."""
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    got = oracle.dequant("q4_k", gi.quantize_q4_k(w))
+    sb = w.reshape(6, 2, 8, 32).astype(np.float64)
+    step = (sb.max(axis=3) - np.minimum(sb.min(axis=3), 0)) / 15
+    err = np.abs(got - w).reshape(6, 2, 8, 32).max(axis=3)
+    assert (err <= 1.5 * step.max(axis=2)[..., None]).all()
+
+
 def test_dequant_layout_rows_and_blocks():
     """Blocks run along the input dimension; rows stack (shape [rows, nblk*32])."""
     rng = np.random.default_rng(3)
@@ -377,12 +449,12 @@ def test_silu_special_values():
     assert abs(oracle.silu(np.array([z]))[0] - z / (1 + math.exp(-z))) < 1e-16
 
 
-@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0", "q4_k"])
 def test_single_expert_k1_is_dense_ffn(qt):
     """E = 1, k = 1: the layer is the dense SwiGLU FFN of that expert (w = 1)."""
     rng = np.random.default_rng(29)
-    H, I, T = 64, 96, 3
-    quant = gi.quantize_q8_0 if qt == "q8_0" else gi.quantize_q4_0
+    H, I, T = (64, 96, 3) if qt != "q4_k" else (256, 256, 2)
+    quant = {"q8_0": gi.quantize_q8_0, "q4_0": gi.quantize_q4_0, "q4_k": gi.quantize_q4_k}[qt]
     blocks = (quant((rng.standard_normal((I, H)) * 0.1).astype(np.float32)),
               quant((rng.standard_normal((I, H)) * 0.1).astype(np.float32)),
               quant((rng.standard_normal((H, I)) * 0.1).astype(np.float32)))
