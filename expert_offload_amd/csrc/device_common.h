@@ -76,14 +76,35 @@ template <int QT>
 __device__ __forceinline__ const uint8_t* block_quants(const uint8_t* row, int b) {
   return row + (size_t)(b >> 3) * group_bytes(QT) + (b & 7) * quant_bytes_per_block(QT);
 }
+// Q4_K's 6-bit scale and min codes of sub-block j from its 12 packed bytes
+// sc: j < 4 in the low six bits of bytes j and j + 4; j >= 4 in the two
+// nibbles of byte j + 4 with bits 4-5 in the top two bits of bytes j - 4 and j.
+__device__ __forceinline__ int q4k_scale_code(const uint8_t* sc, int j) {
+  return j < 4 ? (sc[j] & 63) : ((sc[j + 4] & 15) | ((sc[j - 4] >> 6) << 4));
+}
+__device__ __forceinline__ int q4k_min_code(const uint8_t* sc, int j) {
+  return j < 4 ? (sc[j + 4] & 63) : ((sc[j + 4] >> 4) | ((sc[j] >> 6) << 4));
+}
+
+// Q4_K: d * scale_j and -dmin * min_j are exact in fp32 (an 11-bit scale
+// times a 6-bit code).
 template <int QT>
 __device__ __forceinline__ float block_scale(const uint8_t* row, int b) {
   const uint8_t* g = row + (size_t)(b >> 3) * group_bytes(QT);
-  return __half2float(*reinterpret_cast<const __half*>(g + group_d_off(QT) + 2 * (b & 7)));
+  if constexpr (qtype_is_k(QT)) {
+    const float d = __half2float(*reinterpret_cast<const __half*>(g + group_d_off(QT)));
+    return d * (float)q4k_scale_code(g + group_ksc_off(QT), b & 7);
+  } else {
+    return __half2float(*reinterpret_cast<const __half*>(g + group_d_off(QT) + 2 * (b & 7)));
+  }
 }
 template <int QT>
 __device__ __forceinline__ float block_min(const uint8_t* row, int b) {
-  if constexpr (qtype_has_min(QT)) {
+  if constexpr (qtype_is_k(QT)) {
+    const uint8_t* g = row + (size_t)(b >> 3) * group_bytes(QT);
+    const float dmin = __half2float(*reinterpret_cast<const __half*>(g + group_m_off(QT)));
+    return -(dmin * (float)q4k_min_code(g + group_ksc_off(QT), b & 7));
+  } else if constexpr (qtype_has_min(QT)) {
     const uint8_t* g = row + (size_t)(b >> 3) * group_bytes(QT);
     return __half2float(*reinterpret_cast<const __half*>(g + group_m_off(QT) + 2 * (b & 7)));
   } else {
@@ -108,7 +129,7 @@ __device__ __forceinline__ uint32_t spread_fifth_bits(uint32_t t) {
 
 // The 32 codes of block `b` as floats in logical element order: the signed
 // code q (w = d * q) for Q8_0 (int8), Q4_0 (u - 8), Q5_0 (u - 16); the
-// unsigned code u (w = d * u + m) for Q4_1 and Q5_1.
+// unsigned code u (w = d * u + m) for Q4_1, Q5_1 and Q4_K.
 template <int QT>
 __device__ __forceinline__ void block_codes(const uint8_t* row, int b, float (&q)[32]) {
   const uint8_t* p = block_quants<QT>(row, b);

@@ -47,6 +47,7 @@ int launch_ffn_decode_q4_0(moe_ctx* ctx, const FfnParams& p, const float* x, hip
 int launch_ffn_decode_q4_1(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
 int launch_ffn_decode_q5_0(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
 int launch_ffn_decode_q5_1(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
+int launch_ffn_decode_q4_k(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
 int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s,
                       const RouteArgs* route = nullptr);
 bool prefill_mfma_supported(int H, int I);

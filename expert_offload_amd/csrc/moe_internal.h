@@ -85,8 +85,12 @@ __host__ __device__ constexpr int quant_bytes_per_block(int qtype) {
   return qtype == MOE_QTYPE_Q8_0 ? 32 : 16;
 }
 __host__ __device__ constexpr bool qtype_has_min(int qtype) {  // w = d*q + m
-  return qtype == MOE_QTYPE_Q4_1 || qtype == MOE_QTYPE_Q5_1;
+  return qtype == MOE_QTYPE_Q4_1 || qtype == MOE_QTYPE_Q5_1 || qtype == MOE_QTYPE_Q4_K;
 }
+// Q4_K: one super-block of 256 weights per group; its 8 sub-blocks' scales
+// d * scale_j and offsets -dmin * min_j come from the super-block's fp16 d,
+// dmin and 6-bit codes.
+__host__ __device__ constexpr bool qtype_is_k(int qtype) { return qtype == MOE_QTYPE_Q4_K; }
 __host__ __device__ constexpr bool qtype_has_qh(int qtype) {  // fifth code bits
   return qtype == MOE_QTYPE_Q5_0 || qtype == MOE_QTYPE_Q5_1;
 }
@@ -94,14 +98,24 @@ __host__ __device__ constexpr bool qtype_has_qh(int qtype) {  // fifth code bits
 __host__ __device__ constexpr int ggml_block_bytes(int qtype) {
   return 2 + (qtype_has_min(qtype) ? 2 : 0) + (qtype_has_qh(qtype) ? 4 : 0) + quant_bytes_per_block(qtype);
 }
-__host__ __device__ constexpr int group_bytes(int qtype) { return kGroupBlocks * ggml_block_bytes(qtype); }
-// Offsets inside a group: quant bytes at 0, then fifth-bit words, scales d,
-// offsets m.
-__host__ __device__ constexpr int group_qh_off(int qtype) { return kGroupBlocks * quant_bytes_per_block(qtype); }
-__host__ __device__ constexpr int group_d_off(int qtype) {
-  return group_qh_off(qtype) + (qtype_has_qh(qtype) ? 4 * kGroupBlocks : 0);
+// Q4_K: the ggml super-block is 144 bytes (fp16 d, fp16 dmin, 12 bytes of
+// 6-bit scales and mins, 128 bytes of nibbles), the same bytes per group.
+constexpr int kQ4KBytes = 144;
+__host__ __device__ constexpr int group_bytes(int qtype) {
+  return qtype_is_k(qtype) ? kQ4KBytes : kGroupBlocks * ggml_block_bytes(qtype);
 }
-__host__ __device__ constexpr int group_m_off(int qtype) { return group_d_off(qtype) + 2 * kGroupBlocks; }
+// Offsets inside a group: quant bytes at 0, then fifth-bit words, scales d,
+// offsets m.  Q4_K: quant bytes (per sub-block, nibble order of the 32-weight
+// types), the 12 scale bytes, d, dmin.
+__host__ __device__ constexpr int group_qh_off(int qtype) { return kGroupBlocks * quant_bytes_per_block(qtype); }
+__host__ __device__ constexpr int group_ksc_off(int qtype) { return kGroupBlocks * quant_bytes_per_block(qtype); }
+__host__ __device__ constexpr int group_d_off(int qtype) {
+  return qtype_is_k(qtype) ? group_ksc_off(qtype) + 12
+                           : group_qh_off(qtype) + (qtype_has_qh(qtype) ? 4 * kGroupBlocks : 0);
+}
+__host__ __device__ constexpr int group_m_off(int qtype) {
+  return group_d_off(qtype) + (qtype_is_k(qtype) ? 2 : 2 * kGroupBlocks);
+}
 // The stored code u (Q8_0: q + 128; 4-bit: the nibble; 5-bit: nibble + 16 *
 // fifth bit) maps to w = d*u - OFF*d, or d*u + m for the types with m.
 __host__ __device__ constexpr float qtype_code_off(int qtype) {
@@ -127,7 +141,7 @@ __host__ __device__ constexpr size_t slot_bytes_of(int qtype, int H, int I) {
 
 inline bool qtype_supported(int qtype) {
   return qtype == MOE_QTYPE_Q8_0 || qtype == MOE_QTYPE_Q4_0 || qtype == MOE_QTYPE_Q4_1 || qtype == MOE_QTYPE_Q5_0 ||
-         qtype == MOE_QTYPE_Q5_1;
+         qtype == MOE_QTYPE_Q5_1 || qtype == MOE_QTYPE_Q4_K;
 }
 inline const char* qtype_name(int qtype) {
   switch (qtype) {
@@ -136,6 +150,7 @@ inline const char* qtype_name(int qtype) {
     case MOE_QTYPE_Q4_1: return "Q4_1";
     case MOE_QTYPE_Q5_0: return "Q5_0";
     case MOE_QTYPE_Q5_1: return "Q5_1";
+    case MOE_QTYPE_Q4_K: return "Q4_K";
     default: return "?";
   }
 }

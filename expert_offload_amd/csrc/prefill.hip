@@ -384,6 +384,7 @@ static void launch_prefill_gemm(const FfnParams& p, unsigned grid, hipStream_t s
     MOE_PF(MOE_QTYPE_Q4_1)
     MOE_PF(MOE_QTYPE_Q5_0)
     MOE_PF(MOE_QTYPE_Q5_1)
+    MOE_PF(MOE_QTYPE_Q4_K)
     default: break;
   }
 #undef MOE_PF

@@ -7,7 +7,7 @@
  * MoE Runtime Comparison", introduction; "FreeToken Inference Engine: 3x
  * Speed Boost for MoE Models", section "From Static Allocation to Dynamic
  * Scheduling").  Expert banks are ggml blocks of the standard types
- * (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0) in one GPU slot
+ * (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0) or the K-quant Q4_K in one GPU slot
  * pool of a single type (FreeToken fork README, "Quant types" and "Known
  * limits"); decode and prefill use different kernel families there (matrix
  * x vector for decode, matrix x matrix for prefill, same section).  One
@@ -67,7 +67,8 @@ enum {
   MOE_QTYPE_Q4_1 = 3,
   MOE_QTYPE_Q5_0 = 6,
   MOE_QTYPE_Q5_1 = 7,
-  MOE_QTYPE_Q8_0 = 8
+  MOE_QTYPE_Q8_0 = 8,
+  MOE_QTYPE_Q4_K = 12
 };
 
 /* Activation dtypes. */
@@ -127,6 +128,14 @@ int moe_ctx_kernel_time(moe_ctx* ctx, const char* kernel, int* count,
  *       w = d*q + m, q in 0..31.
  * Nibble byte j holds element j (low nibble) and element j+16 (high
  * nibble); bit j of the little-endian fifth-bit word is bit 4 of element j.
+ * The K-quant Q4_K (the fork README's "K-quants" row) is a super-block of
+ * 256 weights (144 B): fp16 d, fp16 dmin, 12 bytes of 6-bit scale and min
+ * codes of its 8 sub-blocks of 32 (sub-block j < 4: scale = byte j & 63,
+ * min = byte j+4 & 63; j >= 4: scale = (byte j+4 & 15) | (byte j-4 >> 6)
+ * << 4, min = (byte j+4 >> 4) | (byte j >> 6) << 4), 128 nibble bytes
+ * (bytes 32i..32i+31: sub-block 2i low nibbles, 2i+1 high, element l in
+ * byte 32i + l); weight l of sub-block j = d * scale_j * q - dmin * min_j.
+ * moe_qtype_info reports its super-block (256, 144).
  * Unknown qtype -> MOE_ERR_UNSUPPORTED_QTYPE and the outputs untouched. */
 int moe_qtype_info(int qtype, int* block_elems, int* block_bytes);
 
@@ -137,7 +146,9 @@ int moe_qtype_info(int qtype, int* block_elems, int* block_bytes);
  * blocks' quant bytes (ggml order, 8*32 B for Q8_0, 8*16 B otherwise),
  * then for Q5_0 / Q5_1 their 8 fifth-bit words (32 B), then their 8 fp16
  * scales d (16 B), then for Q4_1 / Q5_1 their 8 fp16 offsets m (16 B), so
- * every group is 16-B aligned.
+ * every group is 16-B aligned.  A Q4_K group is one super-block (144 B):
+ * its 8 sub-blocks' 16 quant bytes each (nibble order as above: byte j
+ * holds elements j and j+16 of the sub-block), the 12 scale bytes, d, dmin.
  * The pinned host pool holds experts in this same layout, so staging an
  * expert into VRAM is one verbatim copy ("FreeToken Inference Engine",
  * FTW paragraph: load straight into the engine's layout, no repacking).

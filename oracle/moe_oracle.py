@@ -287,21 +287,86 @@ def expert_ffn(x_rows: np.ndarray, wg: np.ndarray, wu: np.ndarray,
 
 
 def moe_ffn_pairs(x: np.ndarray, ids: np.ndarray, E: int, qtype: str,
-                  get_blocks) -> np.ndarray:
+                  get_blocks, act_q8: bool = False) -> np.ndarray:
     """y_pairs [T*k, H]: FFN output of every pair p = t*k + j in pair order.
 
     ``get_blocks(e)`` returns the ggml blocks (gate, up, down) of expert e.
+    ``act_q8``: the int8-activation FFN (expert_ffn_q8a) instead.
     """
     T, k = ids.shape
+    x32 = np.asarray(x, dtype=np.float32)
     x = np.asarray(x, dtype=np.float64)
     offsets, sorted_pairs, _, active = permute(ids, E)
     y = np.zeros((T * k, x.shape[1]), dtype=np.float64)
     for e in active:
         pairs = sorted_pairs[offsets[e]:offsets[e + 1]]
         gb, ub, db = get_blocks(int(e))
+        if act_q8:
+            y[pairs] = expert_ffn_q8a(x32[pairs // k], qtype, gb, ub, db)
+            continue
         wg, wu, wd = dequant(qtype, gb), dequant(qtype, ub), dequant(qtype, db)
         y[pairs] = expert_ffn(x[pairs // k], wg, wu, wd)
     return y
+
+
+# --------------------------------------------------------------------------
+# 7b. decode with int8 activations: the fork README's W4A8 scheme
+#     ("DeepSeek-V4-Flash" section: 4-bit weights against 8-bit activations
+#     in the decode kernels, not bit-comparable with an fp32 reference)
+# --------------------------------------------------------------------------
+def quantize_act_q8(x: np.ndarray):
+    """fp32 [..., K] -> (codes int64 [..., K] in -127..127, scales fp32
+    [..., K/32]).  Per block of 32: s = max |x| / 127 and the code x / s
+    rounded half away from zero, both divisions in fp32; s = 0 gives codes
+    0.  (The pages give no formula; this is the plainest symmetric int8
+    block quantiser.)"""
+    x32 = np.asarray(x, dtype=np.float32)
+    b = x32.reshape(*x32.shape[:-1], -1, QK)
+    s = (np.abs(b).max(axis=-1) / np.float32(127)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1), s)
+    ratio = (b / safe[..., None]).astype(np.float32).astype(np.float64)
+    q = np.where(ratio >= 0, np.floor(ratio + 0.5), np.ceil(ratio - 0.5))
+    q = np.where((s == 0)[..., None], 0.0, np.clip(q, -127, 127)).astype(np.int64)
+    return q.reshape(x32.shape), s
+
+
+def block_codes_scales(qtype: str, blocks: np.ndarray):
+    """(signed codes int64 [..., nblk, 32], scales float64 [..., nblk]) of
+    the types whose weight is d * code: Q8_0 (code q) and Q4_0 (code q - 8)."""
+    d = _block_scale(blocks)
+    if qtype == "q8_0":
+        codes = np.ascontiguousarray(blocks[..., 2:34]).view(np.int8).astype(np.int64)
+    elif qtype == "q4_0":
+        nib = blocks[..., 2:18]
+        codes = np.concatenate([nib & 0x0F, nib >> 4], axis=-1).astype(np.int64) - 8
+    else:
+        raise ValueError(f"int8-activation decode takes Q8_0 and Q4_0 banks, not {qtype!r}")
+    return codes, d
+
+
+def matvec_q8a(codes: np.ndarray, d: np.ndarray, aq: np.ndarray, a_s: np.ndarray) -> np.ndarray:
+    """rows [R, nblk, 32] codes with scales [R, nblk] against one quantised
+    activation row (codes [nblk*32], scales [nblk]):
+    y_r = sum_b d[r, b] * a_s[b] * (sum_j codes[r, b, j] * aq[b, j]),
+    the inner sums exact integers."""
+    inner = (codes * aq.reshape(1, -1, QK)).sum(axis=-1)
+    return (d * a_s.astype(np.float64)[None, :] * inner).sum(axis=-1)
+
+
+def expert_ffn_q8a(x_rows: np.ndarray, qtype: str, gate_blocks, up_blocks, down_blocks) -> np.ndarray:
+    """SwiGLU FFN of one expert with int8 block activations: x quantised,
+    g and u by matvec_q8a, h = silu(g) u, h rounded to fp32 (the precision
+    the h rows are kept in) and quantised, y by matvec_q8a."""
+    gc, gd = block_codes_scales(qtype, gate_blocks)
+    uc, ud = block_codes_scales(qtype, up_blocks)
+    dc, dd = block_codes_scales(qtype, down_blocks)
+    out = []
+    for x in np.asarray(x_rows, dtype=np.float32):
+        xq, xs = quantize_act_q8(x)
+        g, u = matvec_q8a(gc, gd, xq, xs), matvec_q8a(uc, ud, xq, xs)
+        hq, hs = quantize_act_q8((silu(g) * u).astype(np.float32))
+        out.append(matvec_q8a(dc, dd, hq, hs))
+    return np.array(out).reshape(-1, dc.shape[0])
 
 
 def combine(y_pairs: np.ndarray, w: np.ndarray) -> np.ndarray:
@@ -317,17 +382,19 @@ def combine(y_pairs: np.ndarray, w: np.ndarray) -> np.ndarray:
 def moe_layer(x: np.ndarray, qtype: str, get_blocks, k: int, *,
               router_w: Optional[np.ndarray] = None,
               bias: Optional[np.ndarray] = None,
-              logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+              logits: Optional[np.ndarray] = None,
+              act_q8: bool = False) -> Dict[str, np.ndarray]:
     """Whole layer: route -> permute -> expert FFN -> combine.
 
     Router logits are computed from x and Wr, or taken as given.  Returns
     a dict with logits, ids, w, y_pairs, out and the top-k logit gap.
+    ``act_q8``: the expert FFN with int8 block activations.
     """
     if logits is None:
         logits = router_logits(x, router_w, bias)
     logits = np.asarray(logits, dtype=np.float64)
     ids, w = route(logits, k)
-    y = moe_ffn_pairs(x, ids, logits.shape[1], qtype, get_blocks)
+    y = moe_ffn_pairs(x, ids, logits.shape[1], qtype, get_blocks, act_q8=act_q8)
     return {"logits": logits, "ids": ids, "w": w, "y_pairs": y,
             "out": combine(y, w), "gap": topk_gap(logits, k)}
 

@@ -37,8 +37,9 @@ def test_qtype_table():
     assert moe.moe_qtype_info(L.QTYPE["q4_1"]) == (32, 20)
     assert moe.moe_qtype_info(L.QTYPE["q5_0"]) == (32, 22)
     assert moe.moe_qtype_info(L.QTYPE["q5_1"]) == (32, 24)
-    assert L.QTYPE == {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8}  # ggml's type numbers
-    for bad in (0, 1, 4, 5, 9, 10, 12, 14, -1, 99):
+    assert moe.moe_qtype_info(L.QTYPE["q4_k"]) == (256, 144)  # one super-block
+    assert L.QTYPE == {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12}  # ggml's type numbers
+    for bad in (0, 1, 4, 5, 9, 10, 11, 13, 14, -1, 99):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_qtype_info(bad)
         assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"
@@ -53,8 +54,11 @@ def test_unsupported_qtype_leaves_outputs_untouched():
 
 @pytest.mark.parametrize("qt,H,I", [("q8_0", 256, 512), ("q8_0", 2048, 768), ("q4_0", 2048, 768),
                                     ("q4_0", 2048, 512), ("q4_0", 4096, 2048), ("q4_1", 2048, 768),
-                                    ("q5_0", 2048, 768), ("q5_1", 4096, 2048)])
+                                    ("q5_0", 2048, 768), ("q5_1", 4096, 2048), ("q4_k", 2048, 768)])
 def test_slot_bytes_equal_ggml_bytes(qt, H, I):
+    if qt == "q4_k":  # 144 bytes per super-block of 256 weights
+        assert moe.moe_slot_bytes(L.QTYPE[qt], H, I) == 3 * H * I // 256 * 144
+        return
     per_block = {"q8_0": 34, "q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24}[qt]
     assert moe.moe_slot_bytes(L.QTYPE[qt], H, I) == 3 * H * I // 32 * per_block
 
@@ -97,12 +101,30 @@ def _unpack_doc_layout(qt, rows, cols, packed):
     return out
 
 
-@pytest.mark.parametrize("qt", ["q8_0", "q4_0", "q4_1", "q5_0", "q5_1"])
+def _unpack_doc_layout_q4_k(rows, cols, packed):
+    """Read the documented Q4_K device groups back into ggml super-blocks:
+    per group 8 sub-blocks of 16 quant bytes (element j low, j + 16 high in
+    byte j), the 12 scale bytes, d, dmin; a ggml super-block is d, dmin,
+    scales, then 4 x 32 bytes holding sub-blocks 2i (low) and 2i+1 (high)."""
+    out = np.empty((rows, cols // 256, 144), dtype=np.uint8)
+    for r in range(rows):
+        for g in range(cols // 256):
+            grp = packed[(r * (cols // 256) + g) * 144:(r * (cols // 256) + g + 1) * 144]
+            sb = out[r, g]
+            sb[0:2], sb[2:4], sb[4:16] = grp[140:142], grp[142:144], grp[128:140]
+            codes = [[(grp[16 * b + (l % 16)] >> (4 * (l // 16))) & 15 for l in range(32)] for b in range(8)]
+            for i in range(4):
+                sb[16 + 32 * i:48 + 32 * i] = [codes[2 * i][l] | (codes[2 * i + 1][l] << 4) for l in range(32)]
+    return out
+
+
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0", "q4_1", "q5_0", "q5_1", "q4_k"])
 def test_pack_expert_layout(qt):
     H, I = 512, 256
     rng = np.random.default_rng(1)
     quant = {"q8_0": gi.quantize_q8_0, "q4_0": gi.quantize_q4_0, "q4_1": gi.quantize_q4_1,
-             "q5_0": gi.quantize_q5_0, "q5_1": gi.quantize_q5_1}[qt]
+             "q5_0": gi.quantize_q5_0, "q5_1": gi.quantize_q5_1, "q4_k": gi.quantize_q4_k}[qt]
+    unpack = _unpack_doc_layout_q4_k if qt == "q4_k" else (lambda r, c, p: _unpack_doc_layout(qt, r, c, p))
     g = quant(rng.standard_normal((I, H)).astype(np.float32))
     u = quant(rng.standard_normal((I, H)).astype(np.float32))
     d = quant(rng.standard_normal((H, I)).astype(np.float32))
@@ -110,9 +132,9 @@ def test_pack_expert_layout(qt):
     packed = pack_expert(qt, H, I, g, u, d)
     n1 = g.size
     assert packed.size == g.size + u.size + d.size
-    np.testing.assert_array_equal(_unpack_doc_layout(qt, I, H, packed[:n1]), g)
-    np.testing.assert_array_equal(_unpack_doc_layout(qt, I, H, packed[n1:2 * n1]), u)
-    np.testing.assert_array_equal(_unpack_doc_layout(qt, H, I, packed[2 * n1:]), d)
+    np.testing.assert_array_equal(unpack(I, H, packed[:n1]), g)
+    np.testing.assert_array_equal(unpack(I, H, packed[n1:2 * n1]), u)
+    np.testing.assert_array_equal(unpack(H, I, packed[2 * n1:]), d)
 
 
 def test_pack_expert_small_destination():
@@ -148,7 +170,7 @@ def test_workspace_queries():
     args = L.moe_ffn_args(qtype=8, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, n_slots=128,
                           slot_bytes=moe.moe_slot_bytes(8, 2048, 768))
     assert moe.moe_expert_ffn_workspace_size(args) >= 16 * 8 * 768 * 4
-    bad = L.moe_ffn_args(qtype=12, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, slot_bytes=1)
+    bad = L.moe_ffn_args(qtype=13, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, slot_bytes=1)
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_expert_ffn_workspace_size(bad)
     assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"

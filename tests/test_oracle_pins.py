@@ -496,6 +496,80 @@ def test_layer_k_above_one_is_per_token_dense_sum(qt):
         np.testing.assert_allclose(res["out"][t], want, rtol=1e-12, atol=1e-13)
 
 
+def test_quantize_act_q8_hand_blocks():
+    """int8 block activations worked by hand: s = max|x| / 127, codes round
+    half away from zero, an all-zero block has s = 0 and codes 0."""
+    x = np.zeros(96, dtype=np.float32)
+    x[0:6] = [0.5, -0.5, 1.5, 2.4999, -127.0, 127.0]   # s = 1
+    x[32:36] = [63.5, 0.25, -0.25, 0.74]                # s = 0.5: 127, 1 (0.5 away), -1, 1 (1.48)
+    q, s = oracle.quantize_act_q8(x)
+    assert s.tolist() == [1.0, 0.5, 0.0]
+    assert q[0:6].tolist() == [1, -1, 2, 2, -127, 127]
+    assert q[32:36].tolist() == [127, 1, -1, 1]
+    assert (q[64:] == 0).all()
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((4, 256)).astype(np.float32) * 3
+    q, s = oracle.quantize_act_q8(v)
+    assert np.abs(q).max() <= 127 and (np.abs(q).reshape(4, 8, 32).max(axis=2) == 127).all()
+    err = np.abs(q.reshape(4, 8, 32) * s[..., None].astype(np.float64) - v.reshape(4, 8, 32))
+    assert (err <= 0.5 * s[..., None] * (1 + 1e-6)).all()
+
+
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0"])
+def test_matvec_q8a_exact_on_representable_activations(qt):
+    """Activations that are integers with a +-127 in every block quantise
+    exactly (s = 1), so the int8-activation product equals the plain product
+    with the dequantised weights."""
+    rng = np.random.default_rng(7)
+    quant = gi.quantize_q8_0 if qt == "q8_0" else gi.quantize_q4_0
+    blocks = quant((rng.standard_normal((40, 128)) * 0.05).astype(np.float32))
+    x = rng.integers(-126, 127, 128).astype(np.float32)
+    x[::32] = 127.0
+    x[5::32] = -127.0
+    xq, xs = oracle.quantize_act_q8(x)
+    assert (xs == 1).all() and (xq == x).all()
+    codes, d = oracle.block_codes_scales(qt, blocks)
+    got = oracle.matvec_q8a(codes, d, xq, xs)
+    np.testing.assert_allclose(got, oracle.dequant(qt, blocks) @ x.astype(np.float64), rtol=1e-13, atol=1e-13)
+
+
+def test_expert_ffn_q8a_loops_and_closeness():
+    """The int8-activation FFN equals the same steps written as plain loops
+    on a tiny expert, and stays within 2e-2 (max relative) of the float FFN."""
+    rng = np.random.default_rng(9)
+    H, I = 64, 96
+    banks = [gi.quantize_q4_0((rng.standard_normal(sh) * 0.1).astype(np.float32)) for sh in ((I, H), (I, H), (H, I))]
+    x = rng.standard_normal((2, H)).astype(np.float32)
+    got = oracle.expert_ffn_q8a(x, "q4_0", *banks)
+    deq = [oracle.dequant("q4_0", b) for b in banks]
+
+    def qrow(v):
+        v = np.asarray(v, dtype=np.float32)
+        out_q, out_s = [], []
+        for b0 in range(0, len(v), 32):
+            blk = v[b0:b0 + 32]
+            s = np.float32(np.abs(blk).max() / np.float32(127))
+            for val in blk:
+                r = float(np.float32(val / s)) if s != 0 else 0.0
+                out_q.append(0 if s == 0 else int(math.copysign(math.floor(abs(r) + 0.5), r)))
+            out_s.append(float(s))
+        return out_q, out_s
+
+    def mv(bk, vq, vs):
+        codes, d = oracle.block_codes_scales("q4_0", bk)
+        return [math.fsum(float(d[r, b]) * vs[b] * sum(int(codes[r, b, j]) * vq[32 * b + j] for j in range(32))
+                          for b in range(codes.shape[1])) for r in range(codes.shape[0])]
+
+    for t in range(2):
+        xq, xs = qrow(x[t])
+        g, u = mv(banks[0], xq, xs), mv(banks[1], xq, xs)
+        h = [gi_ / (1 + math.exp(-gi_)) * ui for gi_, ui in zip(g, u)]
+        hq, hs = qrow(h)
+        np.testing.assert_allclose(got[t], mv(banks[2], hq, hs), rtol=1e-12, atol=1e-12)
+    ref = oracle.expert_ffn(x, *deq)
+    assert np.abs(got - ref).max() / np.abs(ref).max() <= 2e-2
+
+
 def test_combine_one_hot_is_gather():
     rng = np.random.default_rng(31)
     T, k, H = 5, 3, 4  # T != k so a transposed index fails
