@@ -111,10 +111,12 @@ class DecodeStack:
         self.bias = None if bias is None else torch.from_numpy(bias).cuda()
         self.np = np
 
+    mode = 0  # MOE_MODE_DECODE; MOE_MODE_DECODE_Q8A for int8 activations
+
     def buffers(self, T):
         from expert_offload_amd import layer
         wl = self.wl
-        return [layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device="cuda")
+        return [layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device="cuda", mode=self.mode)
                 for _ in range(self.L)]
 
     def run(self, bufs, x, stream=None):
@@ -158,7 +160,8 @@ def time_graph(stack, T, steps, warmup):
     return x, bufs, wall, ev[0].elapsed_time(ev[-1])
 
 
-def kernel_profile(stack, x, bufs, reps=5):
+def kernel_profile(stack, x, bufs, reps=5, names=("router_logits", "topk_permute", "topk", "permute", "ffn_gateup",
+                                                  "ffn_down", "combine")):
     """Per-kernel average durations from the library's event timing (eager)."""
     import torch
     import expert_offload_amd as moe
@@ -172,7 +175,7 @@ def kernel_profile(stack, x, bufs, reps=5):
             stack.run(bufs, x)
     s.synchronize()
     out = {}
-    for name in ("router_logits", "topk_permute", "topk", "permute", "ffn_gateup", "ffn_down", "combine"):
+    for name in names:
         n, ms = moe.moe_ctx_kernel_time(stack.ctx, name)
         if n:
             out[name] = (n, ms)
@@ -346,11 +349,23 @@ def wide_extra(ctx, layers=8, steps=30, warmup=5, distinct=128):
         t_valu = flops / (VALU_F32_PEAK_TFLOPS * 1e12)
         res["ffn_bound"] = "hbm" if t_hbm >= t_valu else "valu (fp32)"
         res["ffn_floor_us"] = {"hbm": t_hbm * 1e6, "valu_fp32": t_valu * 1e6}
+        # the same layers with int8 activations (MOE_MODE_DECODE_Q8A)
+        from expert_offload_amd import _lib as L
+        stack.mode = L.MODE_DECODE_Q8A
+        xq, bq, wq, _ = time_graph(stack, T, steps, warmup)
+        kq = kernel_profile(stack, xq, bq, names=("router_logits", "topk_permute", "topk", "permute", "quant_act",
+                                                   "ffn_gateup", "ffn_down"))
+        stack.mode = 0
+        q_us = wq * 1e3 / steps / layers * 1e3
+        res["int8_activations"] = {"layer_us": q_us, "tokens_per_s_per_layer": T / (q_us * 1e-6),
+                                   "kernel_us": {n: ms_ / c * 1e3 for n, (c, ms_) in kq.items()}}
         out[str(T)] = res
         log(f"wide T={T}: {layer_us:.1f} us/layer ({res['tokens_per_s_per_layer']:.0f} tok/s per layer), "
             f"{res['mean_active_experts']:.1f} experts, layer {res['layer_hbm_gbs']:.0f} GB/s; kernels "
-            + ", ".join(f"{k_} {v:.1f}" for k_, v in kus.items()) + f" us; FFN bound {res['ffn_bound']}")
-        del bufs, x
+            + ", ".join(f"{k_} {v:.1f}" for k_, v in kus.items()) + f" us; FFN bound {res['ffn_bound']}; "
+            f"int8 activations {q_us:.1f} us/layer ("
+            + ", ".join(f"{k_} {v:.1f}" for k_, v in res["int8_activations"]["kernel_us"].items()) + " us)")
+        del bufs, x, bq, xq
     del stack
     torch.cuda.empty_cache()
     return out

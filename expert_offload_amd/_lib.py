@@ -23,7 +23,7 @@ ERRORS = {
 }
 QTYPE = {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12}
 DTYPE_F32, DTYPE_BF16 = 0, 1
-MODE_DECODE, MODE_PREFILL = 0, 1
+MODE_DECODE, MODE_PREFILL, MODE_DECODE_Q8A = 0, 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = (

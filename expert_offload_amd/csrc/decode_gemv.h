@@ -153,6 +153,37 @@ struct RowTile {
     }
   }
 
+  // int8 activations (MOE_MODE_DECODE_Q8A): acc[r] = sum over the lane's
+  // blocks of (d * s) * (integer sum of weight code x activation code), the
+  // integer sums by 4-way int8 dot products (Q4_0: codes u - 8 as
+  // sum(u q) - 8 sum(q); Q8_0: the signed codes as stored).
+  template <typename A>
+  __device__ __forceinline__ void dot_q8(const A& a, float (&acc)[RPL]) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      acc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+#pragma unroll
+        for (int q = 0; q < Q::kWords; ++q) asm volatile("" : "+v"(w[r][i][q]));
+        int isum = 0;
+        if constexpr (QT == MOE_QTYPE_Q8_0) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) isum = __builtin_amdgcn_sdot4((int)w[r][i][q], (int)a.q[i][q], isum, false);
+        } else {
+          static_assert(QT == MOE_QTYPE_Q4_0, "int8 activations take Q4_0 and Q8_0 codes");
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            isum = __builtin_amdgcn_sdot4((int)(w[r][i][q] & 0x0F0F0F0Fu), (int)a.q[i][q], isum, false);
+            isum = __builtin_amdgcn_sdot4((int)((w[r][i][q] >> 4) & 0x0F0F0F0Fu), (int)a.q[i][4 + q], isum, false);
+          }
+          isum -= 8 * a.sum[i];
+        }
+        acc[r] = fmaf(d[r][i] * a.s[i], (float)isum, acc[r]);
+      }
+    }
+  }
+
   __device__ __forceinline__ static float block_sx(const float (&x)[32]) {
     if constexpr (kSigned) return 0.0f;  // signed codes: no offset term
     else return Q::kMin ? sum32(x) : sum32(x) * Q::kOff;
@@ -198,6 +229,28 @@ struct RowTile {
     const float su = (part[0] + part[1]) + (part[2] + part[3]);
     if constexpr (Q::kMin) return fmaf(d[r][i], su, fmaf(m[r][i], sx, acc));
     else return fmaf(d[r][i], su - sx, acc);
+  }
+};
+
+// The lane's BPL int8 activation blocks of one row (MOE_MODE_DECODE_Q8A):
+// 32 codes as 8 words (word q = elements 4q .. 4q+3), the block scale and
+// the sum of its codes.
+template <int LPR, int BPL>
+struct ActQ8 {
+  uint32_t q[BPL][8];
+  float s[BPL];
+  int sum[BPL];
+  __device__ __forceinline__ void load(const int8_t* codes, const float* scales, const int* sums, int lg) {
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const int b = lg + LPR * i;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(codes + (size_t)b * kQK);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(codes + (size_t)b * kQK + 16);
+      q[i][0] = v0.x; q[i][1] = v0.y; q[i][2] = v0.z; q[i][3] = v0.w;
+      q[i][4] = v1.x; q[i][5] = v1.y; q[i][6] = v1.z; q[i][7] = v1.w;
+      s[i] = scales[b];
+      sum[i] = sums[b];
+    }
   }
 };
 

@@ -19,7 +19,8 @@ namespace moe {
 // its rows interleave gate and up: row 2m = gate(i0 + m), 2m + 1 = up(i0 + m).
 // RNS = 0: control data from moe_permute's results; RNS > 0: routing in the
 // kernel, with ceil(E / 64) <= RNS logits per lane in the top-k.
-template <int QT, int LPR, int BPL, int RPL, int RNS>
+// AQ: int8 activations (MOE_MODE_DECODE_Q8A), from p.xq / p.xs / p.xsum.
+template <int QT, int LPR, int BPL, int RPL, int RNS, bool AQ = false>
 __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const float* __restrict__ x, RouteArgs ra) {
   constexpr bool ROUTE = RNS > 0;
   constexpr int RPP = kWave / LPR, RW = RPP * RPL, NI = RW / 2;
@@ -86,13 +87,6 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
       const int rw = g * RPL + r;
       rows[r] = base + ((rw & 1) ? up_off : gate_off) + (size_t)(i0 + rw / 2) * rbytes;
     }
-    // the first token's activations go out before the weights (L2 hits), and
-    // the first token is peeled out of the loop so its row-by-row waits cover
-    // only the weight loads issued so far
-    float xv[BPL][32];
-    load_act<LPR, BPL>(x + (size_t)(next_pair() / p.k) * p.H, lg, xv);
-    RowTile<QT, LPR, BPL, RPL> tile;
-    tile.load(rows, lg);
     auto finish = [&](int s, float (&acc)[RPL]) {
       fold_rows<LPR / 2, RPL, RPL>(acc, lane);
       const float u = __shfl_down(acc[0], STRIDE, kWave);
@@ -101,16 +95,40 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
         p.hbuf[(size_t)(pbeg + s) * p.I + i0 + rr / 2] = gv / (1.0f + expf(-gv)) * u;
       }
     };
-    {
-      float acc[RPL];
-      tile.dot(xv, acc);
-      finish(0, acc);
-    }
-    for (int s = 1; s < n_e; ++s) {
+    RowTile<QT, LPR, BPL, RPL> tile;
+    if constexpr (AQ) {
+      const int nb = p.H / kQK;
+      ActQ8<LPR, BPL> a;
+      int tok = next_pair() / p.k;
+      a.load(p.xq + (size_t)tok * p.H, p.xs + (size_t)tok * nb, p.xsum + (size_t)tok * nb, lg);
+      tile.load(rows, lg);
+      for (int s = 0; s < n_e; ++s) {
+        if (s) {
+          tok = next_pair() / p.k;
+          a.load(p.xq + (size_t)tok * p.H, p.xs + (size_t)tok * nb, p.xsum + (size_t)tok * nb, lg);
+        }
+        float acc[RPL];
+        tile.dot_q8(a, acc);
+        finish(s, acc);
+      }
+    } else {
+      // the first token's activations go out before the weights (L2 hits),
+      // and the first token is peeled out of the loop so its row-by-row
+      // waits cover only the weight loads issued so far
+      float xv[BPL][32];
       load_act<LPR, BPL>(x + (size_t)(next_pair() / p.k) * p.H, lg, xv);
-      float acc[RPL];
-      tile.dot(xv, acc);
-      finish(s, acc);
+      tile.load(rows, lg);
+      {
+        float acc[RPL];
+        tile.dot(xv, acc);
+        finish(0, acc);
+      }
+      for (int s = 1; s < n_e; ++s) {
+        load_act<LPR, BPL>(x + (size_t)(next_pair() / p.k) * p.H, lg, xv);
+        float acc[RPL];
+        tile.dot(xv, acc);
+        finish(s, acc);
+      }
     }
   }
   if constexpr (ROUTE) {
@@ -134,7 +152,7 @@ constexpr int down_waves() {
   return stream && !QTraits<QT>::kQh ? 16 : kDownWaves;
 }
 
-template <int QT, int LPR, int BPL, int RPL>
+template <int QT, int LPR, int BPL, int RPL, bool AQ = false>
 __global__ __launch_bounds__((down_waves<QT, LPR, BPL, RPL>() * kWave)) void ffn_down_decode(FfnParams p) {
   constexpr int RPP = kWave / LPR, RW = RPP * RPL;
   constexpr int NWV = down_waves<QT, LPR, BPL, RPL>();
@@ -149,7 +167,7 @@ __global__ __launch_bounds__((down_waves<QT, LPR, BPL, RPL>() * kWave)) void ffn
   // row is read from memory once (issued before the weights) into the
   // wavefront's LDS row, and the groups read their blocks from there.
   // (the kernel for LPR lanes of BPL blocks serves I = 32 * LPR * BPL only)
-  constexpr bool stage_h = RPP > 1 && kQK * LPR * BPL <= kDownStageFloats;
+  constexpr bool stage_h = !AQ && RPP > 1 && kQK * LPR * BPL <= kDownStageFloats;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   float* hrow = s_h[wave];
   const int g = lane / LPR, lg = lane % LPR;
@@ -214,6 +232,19 @@ __global__ __launch_bounds__((down_waves<QT, LPR, BPL, RPL>() * kWave)) void ffn
           dot_h(acc);
           MOE_DOWN_FINISH(s);
         }
+      } else if constexpr (AQ) {
+        const int nb = p.I / kQK;
+        ActQ8<LPR, BPL> a;
+        a.load(p.hq + (size_t)pbeg * p.I, p.hs + (size_t)pbeg * nb, p.hsum + (size_t)pbeg * nb, lg);
+        tile.load(rows, lg);
+        float acc[RPL];
+        tile.dot_q8(a, acc);
+        MOE_DOWN_FINISH(0);
+        for (int s = 1; s < n_e; ++s) {
+          a.load(p.hq + (size_t)(pbeg + s) * p.I, p.hs + (size_t)(pbeg + s) * nb, p.hsum + (size_t)(pbeg + s) * nb, lg);
+          tile.dot_q8(a, acc);
+          MOE_DOWN_FINISH(s);
+        }
       } else {
         load_act<LPR, BPL>(p.hbuf + (size_t)pbeg * p.I, lg, xv);
         tile.load(rows, lg);
@@ -276,14 +307,16 @@ static constexpr int gateup_batch_rpl() {
   return 2 * RPL <= LPR && 2 * RPL <= 16 ? 2 * RPL : RPL;
 }
 
-template <int QT, int LPR, int BPL>
+template <int QT, int LPR, int BPL, bool AQ = false>
 static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStream_t s, const RouteArgs* ra) {
   constexpr int RPL0 = rows_per_lane<QT, BPL>();
   constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
-  if (!ra) {
+  if (AQ || !ra) {
     constexpr int RPLB = gateup_batch_rpl<QT, LPR, BPL>();
-    if (gateup_wide_rows(p.T, false)) launch(ffn_gateup_decode<QT, LPR, BPL, RPLB, 0>, grid, 256, 0, s, p, x, RouteArgs{});
-    else launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 0>, grid, 256, 0, s, p, x, RouteArgs{});
+    if (gateup_wide_rows(p.T, false))
+      launch(ffn_gateup_decode<QT, LPR, BPL, RPLB, 0, AQ>, grid, 256, 0, s, p, x, RouteArgs{});
+    else
+      launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 0, AQ>, grid, 256, 0, s, p, x, RouteArgs{});
     return;
   }
   if constexpr (LPR == 64) {  // the routing variant exists for these shapes (decode_route_supported)
@@ -294,10 +327,10 @@ static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStrea
     else launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 16>, grid, 256, 0, s, p, x, *ra);
   }
 }
-template <int QT, int LPR, int BPL>
+template <int QT, int LPR, int BPL, bool AQ = false>
 static void launch_down(const FfnParams& p, int grid, hipStream_t s) {
   constexpr int rpl = down_rows_per_lane<QT, LPR, BPL>();
-  launch(ffn_down_decode<QT, LPR, BPL, rpl>, grid, down_waves<QT, LPR, BPL, rpl>() * kWave, 0, s, p);
+  launch(ffn_down_decode<QT, LPR, BPL, rpl, AQ>, grid, down_waves<QT, LPR, BPL, rpl>() * kWave, 0, s, p);
 }
 template <int QT, int LPR, int BPL>
 static constexpr int down_rows_per_tile() {
@@ -340,19 +373,19 @@ static int rows_per_wave_rt(GemvShape sh) {
   return 0;
 }
 
-template <int QT>
+template <int QT, bool AQ = false>
 static void dispatch_gateup(GemvShape sh, const FfnParams& p, const float* x, int grid, hipStream_t s,
                             const RouteArgs* ra) {
 #define MOE_GU(L, B) \
-  if (sh.lpr == L && sh.bpl == B) return launch_gateup<QT, L, B>(p, x, grid, s, ra);
+  if (sh.lpr == L && sh.bpl == B) return launch_gateup<QT, L, B, AQ>(p, x, grid, s, ra);
   MOE_GU(64, 1) MOE_GU(64, 2) MOE_GU(64, 3) MOE_GU(32, 1) MOE_GU(32, 2) MOE_GU(32, 3)
   MOE_GU(16, 1) MOE_GU(16, 2) MOE_GU(16, 3) MOE_GU(8, 1) MOE_GU(8, 2) MOE_GU(8, 3)
 #undef MOE_GU
 }
-template <int QT>
+template <int QT, bool AQ = false>
 static void dispatch_down(GemvShape sh, const FfnParams& p, int grid, hipStream_t s) {
 #define MOE_DN(L, B) \
-  if (sh.lpr == L && sh.bpl == B) return launch_down<QT, L, B>(p, grid, s);
+  if (sh.lpr == L && sh.bpl == B) return launch_down<QT, L, B, AQ>(p, grid, s);
   MOE_DN(64, 1) MOE_DN(64, 2) MOE_DN(64, 3) MOE_DN(32, 1) MOE_DN(32, 2) MOE_DN(32, 3)
   MOE_DN(16, 1) MOE_DN(16, 2) MOE_DN(16, 3) MOE_DN(8, 1) MOE_DN(8, 2) MOE_DN(8, 3)
 #undef MOE_DN
@@ -374,11 +407,29 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
   const long long items_gu = (long long)max_active * (p.I / (rw_gu / 2));
   const int grid_gu = (int)std::max(1LL, std::min<long long>(cap, (items_gu + 3) / 4));
   const int grid_dn = std::max(1, p.H / rt_dn);
+  int rc;
+  if (p.xq) {  // int8 activations: quantise x, gate/up, quantise the h rows, down
+    if constexpr (QT == MOE_QTYPE_Q4_0 || QT == MOE_QTYPE_Q8_0) {
+      if ((rc = launch_quant_act(ctx, x, (long long)p.T * p.H / kQK, p.xq, p.xs, p.xsum, s))) return rc;
+      {
+        KernelTimer timer(ctx, "ffn_gateup", s);
+        dispatch_gateup<QT, true>(gu, p, x, grid_gu, s, nullptr);
+      }
+      if ((rc = check_launch("ffn_gateup_decode"))) return rc;
+      if ((rc = launch_quant_act(ctx, p.hbuf, (long long)p.T * p.k * p.I / kQK, p.hq, p.hs, p.hsum, s))) return rc;
+      {
+        KernelTimer timer(ctx, "ffn_down", s);
+        dispatch_down<QT, true>(dn, p, grid_dn, s);
+      }
+      return check_launch("ffn_down_decode");
+    }
+    return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "int8-activation decode: block type %d", QT);
+  }
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
     dispatch_gateup<QT>(gu, p, x, grid_gu, s, route);
   }
-  int rc = check_launch("ffn_gateup_decode");
+  rc = check_launch("ffn_gateup_decode");
   if (rc) return rc;
   {
     KernelTimer timer(ctx, "ffn_down", s);

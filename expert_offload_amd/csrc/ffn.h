@@ -21,6 +21,14 @@ struct FfnParams {
   int* err;
   const float* topk_w;  // [T][k] (fused combine only)
   float* out;           // [T][H] or NULL: fused combine target
+  // int8 activations (MOE_MODE_DECODE_Q8A), else NULL: per 32-block codes,
+  // scales and code sums of x [T][H] and of the h rows [T*k][I] (grouped)
+  int8_t* xq;
+  float* xs;
+  int* xsum;
+  int8_t* hq;
+  float* hs;
+  int* hsum;
 };
 
 // Routing done inside the decode gate/up kernel (small batches, T*k <= 64):
@@ -50,6 +58,10 @@ int launch_ffn_decode_q5_1(moe_ctx* ctx, const FfnParams& p, const float* x, hip
 int launch_ffn_decode_q4_k(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
 int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s,
                       const RouteArgs* route = nullptr);
+// int8 block quantisation of n_blocks blocks of 32 floats at src (rows laid
+// end to end): codes q, scales s = max|v| / 127 and code sums.
+int launch_quant_act(moe_ctx* ctx, const float* src, long long n_blocks, int8_t* q, float* s, int* qsum,
+                     hipStream_t stream);
 bool prefill_mfma_supported(int H, int I);
 size_t prefill_ws_bytes(int T, int k, int I, int E);
 int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws, hipStream_t s);

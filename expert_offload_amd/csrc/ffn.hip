@@ -8,8 +8,26 @@ namespace moe {
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace: decode keeps h as T*k x I fp32 in grouped (sorted) pair order;
-// prefill keeps a tile list and h as bf16.  One size covers both.
+// prefill keeps a tile list and h as bf16.  One size covers both.  The
+// int8-activation decode adds, after h, the codes, scales and code sums of
+// x and of h (256-byte aligned regions).
+struct Q8aLayout {
+  size_t xq, xs, xsum, hq, hs, hsum, end;
+};
+static Q8aLayout q8a_layout(const moe_ffn_args* a) {
+  const size_t P = (size_t)a->T * a->k, xb = (size_t)a->T * a->H / kQK, hb = P * a->I / kQK;
+  Q8aLayout l;
+  l.xq = align_up(P * a->I * sizeof(float), 256);
+  l.xs = align_up(l.xq + (size_t)a->T * a->H, 256);
+  l.xsum = align_up(l.xs + xb * sizeof(float), 256);
+  l.hq = align_up(l.xsum + xb * sizeof(int), 256);
+  l.hs = align_up(l.hq + P * a->I, 256);
+  l.hsum = align_up(l.hs + hb * sizeof(float), 256);
+  l.end = align_up(l.hsum + hb * sizeof(int), 256);
+  return l;
+}
 static size_t ffn_ws_bytes(const moe_ffn_args* a) {
+  if (a->mode == MOE_MODE_DECODE_Q8A) return q8a_layout(a).end;
   const size_t dec = align_up((size_t)a->T * a->k * a->I * sizeof(float), 256);
   const size_t pre = align_up(prefill_ws_bytes(a->T, a->k, a->I, a->E), 256);
   return dec > pre ? dec : pre;
@@ -25,12 +43,21 @@ static int validate_ffn(const moe_ffn_args* a, bool need_buffers) {
   if (a->T < 0 || a->E < 1 || a->E > kMaxE || a->k < 1 || a->k > a->E)
     return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: need T >= 0, 1 <= k <= E <= %d (T=%d k=%d E=%d)",
                      kMaxE, a->T, a->k, a->E);
-  if (a->mode != MOE_MODE_DECODE && a->mode != MOE_MODE_PREFILL)
+  if (a->mode != MOE_MODE_DECODE && a->mode != MOE_MODE_PREFILL && a->mode != MOE_MODE_DECODE_Q8A)
     return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: mode %d unknown", a->mode);
   if (a->x_dtype != MOE_DTYPE_F32 && a->x_dtype != MOE_DTYPE_BF16)
     return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: x_dtype %d unknown", a->x_dtype);
-  if (a->mode == MOE_MODE_DECODE && a->x_dtype != MOE_DTYPE_F32)
-    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: decode mode takes fp32 activations");
+  if (a->mode != MOE_MODE_PREFILL && a->x_dtype != MOE_DTYPE_F32)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: decode modes take fp32 activations");
+  if (a->mode == MOE_MODE_DECODE_Q8A) {
+    if (a->qtype != MOE_QTYPE_Q4_0 && a->qtype != MOE_QTYPE_Q8_0)
+      return set_error(MOE_ERR_UNSUPPORTED_QTYPE,
+                       "moe_expert_ffn: int8-activation decode takes Q4_0 and Q8_0 banks, not %s (type %d)",
+                       qtype_name(a->qtype), a->qtype);
+    if (!decode_gemv_supported(a->H, a->I, a->T, a->k))
+      return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: int8-activation decode needs T*k <= 1024 (T=%d k=%d)",
+                       a->T, a->k);
+  }
   if (a->slot_bytes < slot_bytes_of(a->qtype, a->H, a->I))
     return set_error(MOE_ERR_INVALID_ARG, "moe_expert_ffn: slot_bytes %zu below one %s expert (%zu)",
                      a->slot_bytes, qtype_name(a->qtype), slot_bytes_of(a->qtype, a->H, a->I));
@@ -87,6 +114,19 @@ static FfnParams ffn_params(const moe_ctx* ctx, const moe_ffn_args* a) {
   p.err = ctx->d_err;
   p.topk_w = a->topk_w;
   p.out = a->out;
+  p.xq = p.hq = nullptr;
+  p.xs = p.hs = nullptr;
+  p.xsum = p.hsum = nullptr;
+  if (a->mode == MOE_MODE_DECODE_Q8A) {
+    const Q8aLayout l = q8a_layout(a);
+    char* ws = (char*)a->ws;
+    p.xq = (int8_t*)(ws + l.xq);
+    p.xs = (float*)(ws + l.xs);
+    p.xsum = (int*)(ws + l.xsum);
+    p.hq = (int8_t*)(ws + l.hq);
+    p.hs = (float*)(ws + l.hs);
+    p.hsum = (int*)(ws + l.hsum);
+  }
   return p;
 }
 
@@ -99,7 +139,7 @@ extern "C" int moe_expert_ffn(moe_ctx* ctx, const moe_ffn_args* a, void* stream)
   if ((rc = ensure_device(ctx))) return rc;
   FfnParams p = ffn_params(ctx, a);
   hipStream_t s = (hipStream_t)stream;
-  if (a->mode == MOE_MODE_DECODE && decode_gemv_supported(a->H, a->I, a->T, a->k))
+  if (a->mode == MOE_MODE_DECODE_Q8A || (a->mode == MOE_MODE_DECODE && decode_gemv_supported(a->H, a->I, a->T, a->k)))
     return launch_ffn_decode(ctx, p, (const float*)a->x, s);
   p.out = nullptr;
   if (a->mode == MOE_MODE_PREFILL && a->x_dtype == MOE_DTYPE_BF16 && prefill_mfma_supported(a->H, a->I))
@@ -115,8 +155,8 @@ extern "C" int moe_decode_layer(moe_ctx* ctx, const moe_ffn_args* a, const float
                                 void* stream) {
   clear_error();
   if (!ctx || !a) return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: ctx or args is NULL");
-  if (a->mode != MOE_MODE_DECODE)
-    return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: args.mode must be MOE_MODE_DECODE");
+  if (a->mode != MOE_MODE_DECODE && a->mode != MOE_MODE_DECODE_Q8A)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: args.mode must be MOE_MODE_DECODE or _DECODE_Q8A");
   if (!a->topk_w || !a->out)
     return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: args.topk_w and args.out are required");
   if (a->expert_mask) return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: args.expert_mask must be NULL");
@@ -134,7 +174,7 @@ extern "C" int moe_decode_layer(moe_ctx* ctx, const moe_ffn_args* a, const float
   if (!pair_pos) return set_error(MOE_ERR_INVALID_ARG, "moe_decode_layer: pair_pos is NULL");
   if ((rc = ensure_device(ctx))) return rc;
   hipStream_t s = (hipStream_t)stream;
-  if (!decode_route_supported(a->H, a->I, a->T, a->k)) {
+  if (a->mode == MOE_MODE_DECODE_Q8A || !decode_route_supported(a->H, a->I, a->T, a->k)) {
     rc = moe_route_permute(ctx, a->x, a->x_dtype, router_w, bias, logits_in, a->T, a->H, a->E, a->k, logits_out,
                            topk_ids, topk_w, offsets, sorted, pair_pos, active, nullptr, 0, stream);
     if (rc) return rc;

@@ -78,7 +78,16 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  * and fp32 accumulation, or grouped matrix x matrix prefill with bf16
  * operands on the matrix cores and fp32 accumulation (fork README, "Quant
  * types": separate decode and prefill kernels per block type). */
-enum { MOE_MODE_DECODE = 0, MOE_MODE_PREFILL = 1 };
+enum { MOE_MODE_DECODE = 0, MOE_MODE_PREFILL = 1, MOE_MODE_DECODE_Q8A = 2 };
+/* MOE_MODE_DECODE_Q8A: decode with 8-bit activations against the raw
+ * 4- or 8-bit weight codes (the fork README's W4A8 decode scheme, section
+ * "DeepSeek-V4-Flash", which states that it cannot agree bit for bit with
+ * a float reference).  x (fp32) and then the h rows are quantised per
+ * block of 32: s = max|v| / 127, code = v / s rounded half away from zero
+ * (both divisions in fp32; s = 0 gives codes 0); every block dot product is
+ * an exact integer sum of code products scaled by d * s in fp32.  Q4_0 and
+ * Q8_0 banks only (others -> MOE_ERR_UNSUPPORTED_QTYPE), T*k <= 1024.  The
+ * workspace (moe_expert_ffn_workspace_size) also holds the quantised rows. */
 
 /* What cache_decode_layer does with an expert that is not in VRAM:
  * MOE_MISS_COPY copies it in (it becomes resident); MOE_MISS_HOST computes
@@ -109,7 +118,7 @@ int moe_ctx_check(moe_ctx* ctx, void* stream);
  * not timed); enabling or disabling discards earlier records.  moe_ctx_kernel_time waits for the
  * recorded launches of `kernel` (names: "router_logits", "topk", "permute",
  * "ffn_gateup", "ffn_down", "combine", "dequant", "topk_permute",
- * "permute_count", "permute_scan", "permute_scatter") and
+ * "permute_count", "permute_scan", "permute_scatter", "quant_act") and
  * returns their number
  * and summed duration in milliseconds. */
 int moe_ctx_set_timing(moe_ctx* ctx, int enable);
@@ -238,7 +247,7 @@ typedef struct moe_ffn_args {
   const int32_t* active;          /* device [E+1] from moe_permute */
   const int32_t* expert_mask;     /* device [E] or NULL (= all) */
   float* y_pairs;                 /* device fp32 [T*k][H], pair order */
-  int mode;                       /* MOE_MODE_DECODE or MOE_MODE_PREFILL */
+  int mode;                       /* MOE_MODE_DECODE, _PREFILL or _DECODE_Q8A */
   void* ws;                       /* device workspace (256-B aligned) */
   size_t ws_bytes;
   const float* topk_w;            /* device [T][k]; with out: fused combine */

@@ -183,3 +183,21 @@ def test_null_context_is_an_error():
     assert lib.moe_combine(None, None, None, 1, 2, 256, None, None) == -1
     assert lib.moe_ctx_check(None, None) == -1
     assert "ctx is NULL" in moe.moe_last_error()
+
+
+def test_q8a_mode_refusals():
+    """Int8-activation decode: banks of a type without signed codes, and
+    batches past 1024 pairs, are refused on the host with the documented
+    errors."""
+    wl = gi.workload("tiny_q8_0")
+    for qt, T, want in (("q4_1", 4, "MOE_ERR_UNSUPPORTED_QTYPE"), ("q4_k", 4, "MOE_ERR_UNSUPPORTED_QTYPE"),
+                        ("q8_0", 600, "MOE_ERR_INVALID_ARG")):
+        args = L.moe_ffn_args(qtype=L.QTYPE[qt], H=wl.H, I=wl.I, T=T, k=wl.k, E=wl.E, mode=L.MODE_DECODE_Q8A,
+                              x_dtype=L.DTYPE_F32, n_slots=1, slot_bytes=moe.moe_slot_bytes(L.QTYPE[qt], wl.H, wl.I))
+        with pytest.raises(moe.MoeError) as ei:
+            L.moe_expert_ffn_workspace_size(args)
+        assert ei.value.name == want, (qt, T, ei.value.name)
+    ok = L.moe_ffn_args(qtype=L.QTYPE["q8_0"], H=wl.H, I=wl.I, T=4, k=wl.k, E=wl.E, mode=L.MODE_DECODE_Q8A,
+                        x_dtype=L.DTYPE_F32, n_slots=1, slot_bytes=moe.moe_slot_bytes(L.QTYPE["q8_0"], wl.H, wl.I))
+    # h rows, then codes, scales and code sums of x and of h
+    assert L.moe_expert_ffn_workspace_size(ok) >= 4 * wl.k * wl.I * 4 + 4 * wl.H + 4 * wl.k * wl.I
