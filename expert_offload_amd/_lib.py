@@ -13,7 +13,9 @@ from typing import Optional, Sequence, Tuple
 
 import torch  # noqa: F401  (must precede loading libmoe)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIB_PATH selects another build of the library (the host-sanitizer
+# build that the CPU tests load under AddressSanitizer)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK = 0
 ERRORS = {

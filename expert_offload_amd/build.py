@@ -52,17 +52,36 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link libmoe.so.  Returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer build of the
+# library (libmoe_asan.so) for the CPU tests of its host code: every
+# sanitizer flag applies to the host compilation only (-Xarch_host); device
+# code is built as usual.
+ASAN_LIB_PATH = os.path.join(HERE, "libmoe_asan.so")
+ASAN_BUILD_DIR = os.path.join(ROOT, "_build_asan")
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The compiler's shared ASan runtime (to preload into the interpreter)."""
+    return _run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"]).strip()
+
+
+def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
+    """Compile every source and link libmoe.so (libmoe_asan.so with
+    sanitize).  Returns the library path."""
+    bdir = ASAN_BUILD_DIR if sanitize else BUILD_DIR
+    lib_path = ASAN_LIB_PATH if sanitize else LIB_PATH
+    extra = SANITIZE_HOST if sanitize else []
+    os.makedirs(bdir, exist_ok=True)
     srcs = sources()
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
         if src.endswith(".hip"):
-            cmd = [HIPCC, "-c", "-x", "hip", src, "-o", obj] + COMMON_FLAGS + HIP_FLAGS
+            cmd = [HIPCC, "-c", "-x", "hip", src, "-o", obj] + COMMON_FLAGS + HIP_FLAGS + extra
         else:
-            cmd = [HIPCC, "-c", src, "-o", obj] + COMMON_FLAGS
+            cmd = [HIPCC, "-c", src, "-o", obj] + COMMON_FLAGS + extra
         out = _run(cmd)
         if verbose and out.strip():
             print(out)
@@ -71,17 +90,18 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         objs = list(ex.map(compile_one, srcs))
     tlib = _torch_lib_dir()
-    tmp = LIB_PATH + ".tmp"
-    cmd = [CLANGXX, "-shared", "-fPIC", "-o", tmp] + objs + [
-        "-L", tlib, "-l:libamdhip64.so", "-Wl,-rpath," + tlib, "-Wl,--no-undefined",
+    tmp = lib_path + ".tmp"
+    link_san = ["-fsanitize=address,undefined", "-shared-libasan"] if sanitize else []
+    cmd = [CLANGXX, "-shared", "-fPIC", "-o", tmp] + objs + link_san + [
+        "-L", tlib, "-l:libamdhip64.so", "-Wl,-rpath," + tlib,
         "-lstdc++", "-lm", "-lpthread",
-    ]
+    ] + ([] if sanitize else ["-Wl,--no-undefined"])
     out = _run(cmd)
     if verbose and out.strip():
         print(out)
-    shutil.move(tmp, LIB_PATH)
-    return LIB_PATH
+    shutil.move(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

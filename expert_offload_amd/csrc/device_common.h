@@ -86,6 +86,22 @@ __device__ __forceinline__ int q4k_min_code(const uint8_t* sc, int j) {
   return j < 4 ? (sc[j + 4] & 63) : ((sc[j + 4] >> 4) | ((sc[j] >> 6) << 4));
 }
 
+// Q4_K sub-block b's scale d * scale_b and offset -dmin * min_b from one
+// 16-byte load of the group's tail (12 scale bytes, d, dmin).
+__device__ __forceinline__ void q4k_block_dm(const uint8_t* row, int b, float& d, float& m) {
+  const uint8_t* g = row + (size_t)(b >> 3) * kQ4KBytes;
+  const uint4 t = *reinterpret_cast<const uint4*>(g + group_ksc_off(MOE_QTYPE_Q4_K));
+  const uint32_t w[3] = {t.x, t.y, t.z};
+  const int j = b & 7;
+  auto byte = [&](int i) -> int { return (int)((w[i >> 2] >> (8 * (i & 3))) & 0xFFu); };
+  const int sc = j < 4 ? (byte(j) & 63) : ((byte(j + 4) & 15) | ((byte(j - 4) >> 6) << 4));
+  const int mn = j < 4 ? (byte(j + 4) & 63) : ((byte(j + 4) >> 4) | ((byte(j) >> 6) << 4));
+  const float dd = __half2float(__ushort_as_half((unsigned short)(t.w & 0xFFFFu)));
+  const float dm = __half2float(__ushort_as_half((unsigned short)(t.w >> 16)));
+  d = dd * (float)sc;
+  m = -(dm * (float)mn);
+}
+
 // Q4_K: d * scale_j and -dmin * min_j are exact in fp32 (an 11-bit scale
 // times a 6-bit code).
 template <int QT>

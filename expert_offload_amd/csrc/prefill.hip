@@ -84,6 +84,10 @@ struct WStage {
     const uint8_t* q = block_quants<QT>(row, b) + (QT == MOE_QTYPE_Q8_0 ? 16 * h : 0);
     const uint4 v = *reinterpret_cast<const uint4*>(q);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    if constexpr (qtype_is_k(QT)) {
+      q4k_block_dm(row, b, d, m);
+      return;
+    }
     d = block_scale<QT>(row, b);
     if constexpr (qtype_has_min(QT)) m = block_min<QT>(row, b);
     if constexpr (qtype_has_qh(QT)) qh = block_qh<QT>(row, b);
@@ -359,7 +363,12 @@ bool prefill_mfma_supported(int H, int I) {
 constexpr int kPrefillWaves = 4;
 // MFMA phase at raised wave priority (bit 0) and the byte-permute
 // dequantisation of the offset types (bit 1): bit-identical results,
-// gate/up 359 -> 349 us at 4096 tokens.
+// gate/up 359 -> 349 us at 4096 tokens.  Tried and dropped: staging one
+// row per thread so the LDS writes are free of bank conflicts (the weight
+// loads then spread over twice the rows; gate/up 350 -> 374 us), and one
+// workgroup per CU with the dequantisation interleaved into the MFMAs by
+// scheduling hints (the compiler moved accumulators through AGPRs; 359 ->
+// 499 us).
 constexpr int kPrefillFlags = 3;
 constexpr int kPrefillRows = kWaveRows * kPrefillWaves;
 
