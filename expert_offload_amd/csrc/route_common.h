@@ -63,16 +63,16 @@ __device__ __forceinline__ void wave_topk_select(float (&v)[NS], bool (&ok)[NS],
 }
 
 // ------------------------------------------------- threshold selection
-// tau, the smallest of G >= k group maxima (groups of 64 / G lanes), is at
-// most the k-th largest logit: the G maxima are G different logits, all
-// >= tau.  So every member of the top k is >= tau, and a logit below tau
-// outranks no logit >= tau.  The candidates (logits >= tau, usually about
-// twice k) are compacted into LDS and ranked among themselves: the rank of
-// a candidate is the number of candidates whose (logit, id) comes first
-// (larger logit, or equal logit and smaller id), and a rank below k is its
-// place in the output.  A few DPP steps and one pass of broadcast reads
-// replace the k rounds of wave_topk_select, which remains the path when
-// more than kTopkCand logits tie at or above tau.
+// tau, the k-th largest of G >= k group maxima (groups of 64 / G lanes), is
+// at most the k-th largest logit: the k largest maxima are k different
+// logits, all >= tau.  So every member of the top k is >= tau, and a logit
+// below tau outranks no logit >= tau.  The candidates (logits >= tau,
+// usually about twice k) are compacted into LDS and ranked among
+// themselves: the rank of a candidate is the number of candidates whose
+// (logit, id) comes first (larger logit, or equal logit and smaller id),
+// and a rank below k is its place in the output.  A few DPP steps and two
+// passes of broadcast reads replace the k rounds of wave_topk_select, which
+// remains the path when more than kTopkCand logits lie at or above tau.
 constexpr int kTopkCand = 128;
 struct TopkScratch {
   uint64_t cand[kTopkCand];
@@ -112,21 +112,28 @@ __device__ __forceinline__ bool wave_select_thresh(const float (&v)[NS], const b
 #pragma unroll
   for (int i = 0; i < NS; ++i)
     if (ok[i]) m = fmaxf(m, v[i]);
-  // group maxima over 8, 4, 2 or 1 lanes: 8, 16, 32 or 64 groups >= k
-  if (k <= 32) m = fmaxf(m, dpp_f32<kDppXor1>(m));
-  if (k <= 16) m = fmaxf(m, dpp_f32<kDppXor2>(m));
-  if (k <= 8) m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
-  float tau = fminf(m, dpp_f32<kDppXor1>(m));
-  tau = fminf(tau, dpp_f32<kDppXor2>(tau));
-  tau = fminf(tau, dpp_f32<kDppHalfMirror>(tau));
-  tau = fminf(tau, dpp_f32<kDppMirror>(tau));
-  {
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau), 48));
-    tau = fminf(fminf(r0, r1), fminf(r2, r3));
+  // group maxima over 8, 4, 2 or 1 lanes: G = 8, 16, 32 or 64 groups >= k
+  int gs = 1;
+  if (k <= 32) { m = fmaxf(m, dpp_f32<kDppXor1>(m)); gs = 2; }
+  if (k <= 16) { m = fmaxf(m, dpp_f32<kDppXor2>(m)); gs = 4; }
+  if (k <= 8) { m = fmaxf(m, dpp_f32<kDppHalfMirror>(m)); gs = 8; }
+  // tau = the k-th largest of the G group maxima (the smallest maximum is
+  // also a bound, but a far lower one when a bias skews the logits: 40 to
+  // 80 candidates instead of about 20 with E = 512, k = 10).  Ranks among
+  // the maxima (ties to the lower group) go through LDS.
+  const int G = kWave / gs;
+  float* gmax = reinterpret_cast<float*>(sc.cand);
+  if (lane % gs == 0) gmax[lane / gs] = m;
+  wave_lds_sync();
+  int rank = 0;
+  const int g = lane / gs;
+  for (int j = 0; j < G; ++j) {
+    const float mj = gmax[j];
+    rank += (mj > m || (mj == m && j < g)) ? 1 : 0;
   }
+  const uint64_t at = __ballot(lane % gs == 0 && rank == k - 1);
+  const float tau = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), (int)__builtin_ctzll(at)));
+  wave_lds_sync();
   uint64_t bm[NS];
   int n = 0;
 #pragma unroll
