@@ -49,6 +49,14 @@ KERNEL_SOURCES = {
 CALIB_PATTERNS = ("copyBuffer", "neg_kernel")
 
 
+def _family(kernel: str) -> str:
+    """The KERNEL_SOURCES entry a kernel name or name prefix belongs to."""
+    for fam in KERNEL_SOURCES:
+        if fam in kernel:
+            return fam
+    raise KeyError(f"no source list for kernel {kernel}")
+
+
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -151,21 +159,24 @@ def write_traffic(fetch_dir: str, write_dir: str, kernel: str, calib_bytes: int,
         f.write(f"{kf}: {nf} dispatches, FETCH_SIZE {vf:.1f} KiB/dispatch -> {rd:.0f} B read\n")
         f.write(f"{kw}: {nw} dispatches, WRITE_SIZE {vw:.1f} KiB/dispatch -> {wr:.0f} B written\n")
         f.write(f"traffic_bytes_per_launch: {rd + wr:.0f}\n")
-        f.write(f"source_hash: {source_hash(kernel)}\n")
+        f.write(f"source_hash: {source_hash(_family(kernel))}\n")
 
 
-SIMD_NUM, CU_NUM = 1024, 256  # MI355X: 256 compute units of 4 SIMDs
+SIMD_NUM, CU_NUM, XCD_NUM = 1024, 256, 8  # MI355X: 256 compute units of 4 SIMDs in 8 XCDs
 
 
 def write_counters(dirs: List[str], kernels: List[str], out: str, command: str) -> None:
     """Per-dispatch averages of every counter collected in `dirs` (one
     rocprofv3 --pmc run each) for the kernels whose names contain one of
     `kernels`, with the derived figures the counters allow:
-      MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs)
-      VALU busy % = 4 * SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE * SIMDs)
+      cycles      = GRBM_GUI_ACTIVE / XCDs (the counter is summed over the
+                    8 XCDs; the quotient matches the kernel's duration
+                    times the clock)
+      MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * SIMDs)
+      VALU busy % = 4 * SQ_ACTIVE_INST_VALU / (cycles * SIMDs)
       MFMA FLOP   = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512
       L2 hit %    = TCC_HIT / (TCC_HIT + TCC_MISS)
-    (SIMD count of MI355X: 1024)."""
+    (MI355X: 1024 SIMDs in 8 XCDs)."""
     per: Dict[str, Dict[str, List[float]]] = {}
     for d in dirs:
         with open(_find(d, "counter_collection.csv")) as f:
@@ -190,8 +201,12 @@ def write_counters(dirs: List[str], kernels: List[str], out: str, command: str) 
                 for d, c in per[name]:
                     if c == counter:
                         g = per[name].get((d, "GRBM_GUI_ACTIVE"))
-                        return sum(g) / len(g) if g else None
+                        return sum(g) / len(g) / XCD_NUM if g else None
                 return None
+            for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_ANY"):
+                if c in avg and gui(c):
+                    f.write(f"  cycles (GRBM_GUI_ACTIVE / {XCD_NUM}) in the {c} run: {gui(c):.0f}\n")
+                    break
             if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and gui("SQ_VALU_MFMA_BUSY_CYCLES"):
                 f.write(f"  MFMA busy: {100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui('SQ_VALU_MFMA_BUSY_CYCLES') * SIMD_NUM):.1f}%\n")
             if "SQ_ACTIVE_INST_VALU" in avg and gui("SQ_ACTIVE_INST_VALU"):
