@@ -308,20 +308,15 @@ static constexpr int gateup_batch_rpl() {
 }
 
 template <int QT, int LPR, int BPL, bool AQ = false>
-static void launch_gateup(moe_ctx* ctx, const FfnParams& p, const float* x, int grid, hipStream_t s,
-                          const RouteArgs* ra) {
+static void launch_gateup(const FfnParams& p, const float* x, int grid, hipStream_t s, const RouteArgs* ra) {
   constexpr int RPL0 = rows_per_lane<QT, BPL>();
   constexpr int RPL = RPL0 > LPR ? LPR : RPL0;
   if (AQ || !ra) {
-    // no more workgroups than are resident at once: each stages the
-    // control data once and then takes work items in turn, instead of
-    // later generations of workgroups each staging it again before their
-    // first weight load
     constexpr int RPLB = gateup_batch_rpl<QT, LPR, BPL>();
-    auto kern = gateup_wide_rows(p.T, false) ? ffn_gateup_decode<QT, LPR, BPL, RPLB, 0, AQ>
-                                             : ffn_gateup_decode<QT, LPR, BPL, RPL, 0, AQ>;
-    const int res = resident_per_cu(kern, 256) * ctx->num_cus;
-    launch(kern, res > 0 ? std::min(grid, res) : grid, 256, 0, s, p, x, RouteArgs{});
+    if (gateup_wide_rows(p.T, false))
+      launch(ffn_gateup_decode<QT, LPR, BPL, RPLB, 0, AQ>, grid, 256, 0, s, p, x, RouteArgs{});
+    else
+      launch(ffn_gateup_decode<QT, LPR, BPL, RPL, 0, AQ>, grid, 256, 0, s, p, x, RouteArgs{});
     return;
   }
   if constexpr (LPR == 64) {  // the routing variant exists for these shapes (decode_route_supported)
@@ -379,10 +374,10 @@ static int rows_per_wave_rt(GemvShape sh) {
 }
 
 template <int QT, bool AQ = false>
-static void dispatch_gateup(moe_ctx* ctx, GemvShape sh, const FfnParams& p, const float* x, int grid, hipStream_t s,
+static void dispatch_gateup(GemvShape sh, const FfnParams& p, const float* x, int grid, hipStream_t s,
                             const RouteArgs* ra) {
 #define MOE_GU(L, B) \
-  if (sh.lpr == L && sh.bpl == B) return launch_gateup<QT, L, B, AQ>(ctx, p, x, grid, s, ra);
+  if (sh.lpr == L && sh.bpl == B) return launch_gateup<QT, L, B, AQ>(p, x, grid, s, ra);
   MOE_GU(64, 1) MOE_GU(64, 2) MOE_GU(64, 3) MOE_GU(32, 1) MOE_GU(32, 2) MOE_GU(32, 3)
   MOE_GU(16, 1) MOE_GU(16, 2) MOE_GU(16, 3) MOE_GU(8, 1) MOE_GU(8, 2) MOE_GU(8, 3)
 #undef MOE_GU
@@ -418,7 +413,7 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
       if ((rc = launch_quant_act(ctx, x, (long long)p.T * p.H / kQK, p.xq, p.xs, p.xsum, s))) return rc;
       {
         KernelTimer timer(ctx, "ffn_gateup", s);
-        dispatch_gateup<QT, true>(ctx, gu, p, x, grid_gu, s, nullptr);
+        dispatch_gateup<QT, true>(gu, p, x, grid_gu, s, nullptr);
       }
       if ((rc = check_launch("ffn_gateup_decode"))) return rc;
       if ((rc = launch_quant_act(ctx, p.hbuf, (long long)p.T * p.k * p.I / kQK, p.hq, p.hs, p.hsum, s))) return rc;
@@ -432,7 +427,7 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
   }
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
-    dispatch_gateup<QT>(ctx, gu, p, x, grid_gu, s, route);
+    dispatch_gateup<QT>(gu, p, x, grid_gu, s, route);
   }
   rc = check_launch("ffn_gateup_decode");
   if (rc) return rc;

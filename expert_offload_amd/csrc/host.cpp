@@ -3,8 +3,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
-#include <unordered_map>
 
 #include "moe_internal.h"
 
@@ -93,25 +91,6 @@ KernelTimer* KernelTimer::armed() {
 }  // namespace moe
 
 using namespace moe;
-
-namespace moe {
-
-int resident_per_cu(const void* kern, int threads) {
-  static std::mutex mu;
-  static std::unordered_map<const void*, int> cache;
-  std::lock_guard<std::mutex> lock(mu);
-  const auto it = cache.find(kern);
-  if (it != cache.end()) return it->second;
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess) {
-    (void)hipGetLastError();
-    n = 0;
-  }
-  cache.emplace(kern, n);
-  return n;
-}
-
-}  // namespace moe
 
 extern "C" {
 

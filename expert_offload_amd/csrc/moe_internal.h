@@ -63,15 +63,6 @@ inline void launch(void (*kern)(P...), dim3 grid, dim3 block, uint32_t lds, hipS
   }
 }
 
-// Workgroups of `threads` threads of kernel `kern` that one compute unit
-// holds at once (hipOccupancyMaxActiveBlocksPerMultiprocessor, looked up
-// once per kernel); 0 if the query fails.
-int resident_per_cu(const void* kern, int threads);
-template <typename... P>
-inline int resident_per_cu(void (*kern)(P...), int threads) {
-  return resident_per_cu(reinterpret_cast<const void*>(kern), threads);
-}
-
 // ---------------------------------------------------------------- errors
 int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
