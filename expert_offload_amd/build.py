@@ -93,7 +93,7 @@ def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
     tmp = lib_path + ".tmp"
     link_san = ["-fsanitize=address,undefined", "-shared-libasan"] if sanitize else []
     cmd = [CLANGXX, "-shared", "-fPIC", "-o", tmp] + objs + link_san + [
-        "-L", tlib, "-l:libamdhip64.so", "-Wl,-rpath," + tlib,
+        "-L", tlib, "-l:libamdhip64.so", "-l:libhsa-runtime64.so", "-Wl,-rpath," + tlib,
         "-lstdc++", "-lm", "-lpthread",
     ] + ([] if sanitize else ["-Wl,--no-undefined"])
     out = _run(cmd)

@@ -27,6 +27,9 @@
 #include <unordered_map>
 #include <vector>
 
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
+
 #include "device_common.h"
 #include "ffn.h"
 
@@ -146,11 +149,90 @@ struct moe_cache {
   std::vector<int32_t> last_copy, last_host;
   int last_host_only = 0;  // the first of last_host that were not inserted
   std::deque<int> inflight;  // copy_events of background copies, oldest first
+  // MOE_MISS_HOST_COPY's background copies go through the HSA runtime's
+  // asynchronous copy with a completion signal the host polls, not through a
+  // HIP stream: an event recorded on a copy stream becomes a barrier packet
+  // on that stream's hardware queue, and when the caller's compute stream
+  // shares the queue (HIP shares a few queues among all streams) its
+  // kernels would wait for the copy.  Set up with the policy; if it cannot
+  // be, those copies take the copy stream.
+  bool hsa_ok = false;
+  hsa_agent_t hsa_gpu{}, hsa_cpu{};
+  hsa_signal_t hsa_sig[kEventRing] = {};
+  int next_sig = 0;
+  std::vector<int> slot_sig;  // slot -> hsa_sig of its last background copy, or -1
+  std::deque<int> inflight_sig;
 };
 
 // Background copies allowed in flight under MOE_MISS_HOST_COPY; a miss
 // beyond them is computed on the host and not inserted.
 constexpr int kCopyBacklog = 8;
+
+static bool sig_done(const moe_cache* c, int si) { return hsa_signal_load_scacquire(c->hsa_sig[si]) == 0; }
+static void sig_wait(const moe_cache* c, int si) {
+  while (hsa_signal_wait_scacquire(c->hsa_sig[si], HSA_SIGNAL_CONDITION_EQ, 0, UINT64_MAX, HSA_WAIT_STATE_BLOCKED) != 0) {
+  }
+}
+// Every background copy has landed (before the pool is moved or freed).
+static void wait_all_sigs(moe_cache* c) {
+  if (!c->hsa_ok) return;
+  for (int i = 0; i < kEventRing; ++i) sig_wait(c, i);
+  c->inflight_sig.clear();
+  std::fill(c->slot_sig.begin(), c->slot_sig.end(), -1);
+}
+
+struct AgentSearch {
+  int domain, bus, device;
+  hsa_agent_t gpu{}, cpu{};
+  bool have_gpu = false, have_cpu = false;
+};
+static hsa_status_t find_agents(hsa_agent_t a, void* data) {
+  auto* q = static_cast<AgentSearch*>(data);
+  hsa_device_type_t type;
+  if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &type) != HSA_STATUS_SUCCESS) return HSA_STATUS_SUCCESS;
+  if (type == HSA_DEVICE_TYPE_CPU && !q->have_cpu) {
+    q->cpu = a;
+    q->have_cpu = true;
+  } else if (type == HSA_DEVICE_TYPE_GPU && !q->have_gpu) {
+    uint32_t bdf = 0, domain = 0;
+    if (hsa_agent_get_info(a, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_BDFID, &bdf) == HSA_STATUS_SUCCESS &&
+        hsa_agent_get_info(a, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_DOMAIN, &domain) == HSA_STATUS_SUCCESS &&
+        (int)domain == q->domain && (int)(bdf >> 8) == q->bus && (int)((bdf >> 3) & 31) == q->device) {
+      q->gpu = a;
+      q->have_gpu = true;
+    }
+  }
+  return HSA_STATUS_SUCCESS;
+}
+
+// The HSA agents of the cache's device and of the host, and the signals.
+static void hsa_setup(moe_cache* c) {
+  if (c->hsa_ok) return;
+  AgentSearch q{};
+  if (hipDeviceGetAttribute(&q.domain, hipDeviceAttributePciDomainID, c->device) != hipSuccess ||
+      hipDeviceGetAttribute(&q.bus, hipDeviceAttributePciBusId, c->device) != hipSuccess ||
+      hipDeviceGetAttribute(&q.device, hipDeviceAttributePciDeviceId, c->device) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  if (hsa_init() != HSA_STATUS_SUCCESS) return;
+  if (hsa_iterate_agents(find_agents, &q) != HSA_STATUS_SUCCESS || !q.have_gpu || !q.have_cpu) {
+    hsa_shut_down();
+    return;
+  }
+  int made = 0;
+  for (; made < kEventRing; ++made)
+    if (hsa_signal_create(0, 0, nullptr, &c->hsa_sig[made]) != HSA_STATUS_SUCCESS) break;
+  if (made < kEventRing) {
+    for (int i = 0; i < made; ++i) hsa_signal_destroy(c->hsa_sig[i]);
+    hsa_shut_down();
+    return;
+  }
+  c->hsa_gpu = q.gpu;
+  c->hsa_cpu = q.cpu;
+  c->slot_sig.assign(c->slot_key.size(), -1);
+  c->hsa_ok = true;
+}
 
 static int pop_free(moe_cache* c) {
   if (c->free_head >= c->free_fifo.size()) return -1;
@@ -236,6 +318,11 @@ int cache_slot_table_destroy(moe_cache* c) {
   clear_error();
   if (!c) return MOE_OK;
   (void)hipDeviceSynchronize();
+  if (c->hsa_ok) {
+    wait_all_sigs(c);
+    for (int i = 0; i < kEventRing; ++i) hsa_signal_destroy(c->hsa_sig[i]);
+    hsa_shut_down();
+  }
   for (int i = 0; i < kEventRing; ++i) {
     if (c->events[i]) (void)hipEventDestroy(c->events[i]);
     if (c->copy_events[i]) (void)hipEventDestroy(c->copy_events[i]);
@@ -388,6 +475,11 @@ static int issue_copy(moe_cache* c, int key, moe_cache::Pending pd, hipStream_t 
                       bool compute_waits) {
   hipError_t e = hipSetDevice(c->device);
   if (e != hipSuccess) return hip_error(e, "hipSetDevice");
+  // a background copy into the slot (HSA, no stream to wait on) comes first
+  if (c->hsa_ok && c->slot_sig[pd.slot] >= 0) {
+    sig_wait(c, c->slot_sig[pd.slot]);
+    c->slot_sig[pd.slot] = -1;
+  }
   // an earlier copy into the slot (possibly on another stream) comes first
   if (c->slot_ready[pd.slot] >= 0 &&
       (e = hipStreamWaitEvent(cs, c->copy_events[c->slot_ready[pd.slot]], 0)) != hipSuccess)
@@ -407,6 +499,48 @@ static int issue_copy(moe_cache* c, int key, moe_cache::Pending pd, hipStream_t 
   c->slot_ready[pd.slot] = ce;
   if (compute_waits && (e = hipStreamWaitEvent(ks, done, 0)) != hipSuccess)
     return hip_error(e, "hipStreamWaitEvent(compute)");
+  TableUpdate u{};
+  u.idx[u.n] = key; u.val[u.n] = pd.slot; ++u.n;
+  if (pd.victim_key >= 0 && c->table[pd.victim_key] < 0) {
+    u.idx[u.n] = pd.victim_key; u.val[u.n] = -1; ++u.n;
+  }
+  launch(table_update_kernel, 1, 64, 0, ks, c->d_table, u);
+  return check_launch("table_update_kernel");
+}
+
+// A background copy of key into its destination slot through the HSA
+// runtime (completion signal polled by the host), then the slot table
+// update on compute stream ks.  The slot's earlier copy is a dependency of
+// the copy itself; its earlier readers have finished, which the host
+// checks (the LRU evicts only keys of earlier layers, whose kernels precede
+// this layer's routing, already complete).  No kernel may read the slot
+// before the signal reads zero.
+static int issue_copy_hsa(moe_cache* c, int key, moe_cache::Pending pd, hipStream_t ks) {
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_error(e, "hipSetDevice");
+  if (c->slot_ready[pd.slot] >= 0) {  // an earlier copy on a stream
+    if ((e = hipEventSynchronize(c->copy_events[c->slot_ready[pd.slot]])) != hipSuccess)
+      return hip_error(e, "hipEventSynchronize(earlier copy)");
+    c->slot_ready[pd.slot] = -1;
+  }
+  if (c->slot_event[pd.slot] >= 0 && (e = hipEventSynchronize(c->events[c->slot_event[pd.slot]])) != hipSuccess)
+    return hip_error(e, "hipEventSynchronize(reader)");
+  const int si = c->next_sig;
+  c->next_sig = (c->next_sig + 1) % kEventRing;
+  sig_wait(c, si);  // the ring is far longer than the backlog: normally done
+  hsa_signal_t dep[1];
+  uint32_t n_dep = 0;
+  if (c->slot_sig[pd.slot] >= 0 && !sig_done(c, c->slot_sig[pd.slot])) dep[n_dep++] = c->hsa_sig[c->slot_sig[pd.slot]];
+  hsa_signal_store_screlease(c->hsa_sig[si], 1);
+  const hsa_status_t st = hsa_amd_memory_async_copy(c->d_pool + (size_t)pd.slot * c->slot_bytes, c->hsa_gpu,
+                                                    c->h_pool + (size_t)key * c->slot_bytes, c->hsa_cpu,
+                                                    c->slot_bytes, n_dep, n_dep ? dep : nullptr, c->hsa_sig[si]);
+  if (st != HSA_STATUS_SUCCESS) {
+    hsa_signal_store_screlease(c->hsa_sig[si], 0);
+    return set_error(MOE_ERR_HIP, "hsa_amd_memory_async_copy(expert) failed (status %d)", (int)st);
+  }
+  c->slot_sig[pd.slot] = si;
+  c->inflight_sig.push_back(si);
   TableUpdate u{};
   u.idx[u.n] = key; u.val[u.n] = pd.slot; ++u.n;
   if (pd.victim_key >= 0 && c->table[pd.victim_key] < 0) {
@@ -476,7 +610,9 @@ int cache_slot_table_resize(moe_cache* c, int n_slots, void* d_pool, void* strea
   hipError_t e = hipSetDevice(c->device);
   if (e != hipSuccess) return hip_error(e, "hipSetDevice");
   // every earlier reader of the pool and every expert copy, on any stream
+  // or through the HSA runtime
   if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_error(e, "hipDeviceSynchronize");
+  wait_all_sigs(c);
   hipStream_t st = (hipStream_t)stream;
   int2* d_moves = nullptr;
   if (!moves.empty()) {
@@ -508,6 +644,7 @@ int cache_slot_table_resize(moe_cache* c, int n_slots, void* d_pool, void* strea
   c->slot_key.swap(slot_key);
   c->slot_event.assign(count, -1);
   c->slot_ready.assign(count, -1);
+  if (c->hsa_ok) c->slot_sig.assign(count, -1);
   c->free_fifo.clear();
   c->free_head = 0;
   for (int s = 0; s < count; ++s)
@@ -566,6 +703,16 @@ int cache_set_miss_policy(moe_cache* c, int policy, int host_threads) {
     return set_error(MOE_ERR_INVALID_ARG, "cache_set_miss_policy: policy %d unknown", policy);
   if (host_threads < 0) return set_error(MOE_ERR_INVALID_ARG, "cache_set_miss_policy: host_threads=%d", host_threads);
   c->host_threads = host_threads == 0 ? default_host_threads() : host_threads;
+  if (c->policy == MOE_MISS_HOST_COPY && policy != MOE_MISS_HOST_COPY) {
+    // the other policies read a resident slot without checking that its
+    // copy has landed: let every background copy land first
+    hipError_t e = hipSetDevice(c->device);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_error(e, "cache_set_miss_policy: background copies");
+    wait_all_sigs(c);
+    c->inflight.clear();
+    std::fill(c->slot_ready.begin(), c->slot_ready.end(), -1);
+  }
   if (policy != MOE_MISS_COPY && !c->h_x) {
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_error(e, "hipSetDevice");
@@ -586,6 +733,7 @@ int cache_set_miss_policy(moe_cache* c, int policy, int host_threads) {
     }
     c->h_scratch.assign((size_t)kCtlStagePairs * c->I, 0.0f);
   }
+  if (policy == MOE_MISS_HOST_COPY) hsa_setup(c);
   if (policy == MOE_MISS_QSTAR && (c->rate_pcie <= 0.0 || c->rate_host <= 0.0)) {
     int rc = calibrate_rates(c);
     if (rc) return rc;
@@ -701,7 +849,8 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
   } else if (c->policy == MOE_MISS_HOST_COPY) {
     while (!c->inflight.empty() && hipEventQuery(c->copy_events[c->inflight.front()]) == hipSuccess)
       c->inflight.pop_front();
-    const int room = std::max(0, kCopyBacklog - (int)c->inflight.size());
+    while (!c->inflight_sig.empty() && sig_done(c, c->inflight_sig.front())) c->inflight_sig.pop_front();
+    const int room = std::max(0, kCopyBacklog - (int)c->inflight.size() - (int)c->inflight_sig.size());
     n_host = std::max(0, (int)missing.size() - room);  // host only: not inserted
   }
   c->last_host.assign(missing.end() - n_host, missing.end());
@@ -724,10 +873,17 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
       if (std::find(c->last_host.begin(), c->last_host.end(), id) != c->last_host.end()) continue;
       const int slot = c->table[layer * E + id];
       if (slot < 0) continue;
+      bool landed = true;
+      if (c->hsa_ok && c->slot_sig[slot] >= 0) {
+        if (sig_done(c, c->slot_sig[slot])) c->slot_sig[slot] = -1;
+        else landed = false;
+      }
       const int r = c->slot_ready[slot];
-      if (r < 0) continue;
-      if (hipEventQuery(c->copy_events[r]) == hipSuccess) c->slot_ready[slot] = -1;
-      else c->last_host.push_back(id);
+      if (r >= 0) {
+        if (hipEventQuery(c->copy_events[r]) == hipSuccess) c->slot_ready[slot] = -1;
+        else landed = false;
+      }
+      if (!landed) c->last_host.push_back(id);
     }
     n_host = (int)c->last_host.size();
   }
@@ -793,6 +949,10 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x, co
       if (it == c->pending.end()) continue;
       const moe_cache::Pending pd = it->second;
       c->pending.erase(it);
+      if (c->hsa_ok) {
+        if ((rc = issue_copy_hsa(c, key, pd, cs))) return rc;
+        continue;
+      }
       if ((rc = issue_copy(c, key, pd, ps, cs, false))) return rc;
       c->inflight.push_back(c->slot_ready[pd.slot]);
     }

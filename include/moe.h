@@ -498,11 +498,15 @@ int moe_host_has_avx512(void);
  * MOE_MISS_HOST_COPY (not on the pages; it keeps the cache learning while
  * the host takes the misses): this layer computes every missing expert on
  * the host; the first ones (router order), up to 8 background copies in
- * flight, are also inserted and copied as with MOE_MISS_COPY, but on
- * copy_stream only, with nothing on compute_stream waiting for them; the
- * rest are left out of the cache as with MOE_MISS_HOST.  A later hit on an
- * expert whose copy has not completed (its event, checked on the host at
- * lookup) is computed on the host as well.  Use one copy_stream per cache.
+ * flight, are also inserted and copied as with MOE_MISS_COPY, but with
+ * nothing on compute_stream waiting for them: through the HSA runtime's
+ * asynchronous copy with a completion signal the host polls (so no packet
+ * on any stream's hardware queue waits for the copy), or on copy_stream if
+ * that cannot be set up; the rest are left out of the cache as with
+ * MOE_MISS_HOST.  A later hit on an expert whose copy has not completed
+ * (checked on the host at lookup) is computed on the host as well.  Use
+ * one copy_stream per cache.  Leaving this policy (for another) waits for
+ * every background copy; until then use cache_decode_layer only.
  *
  * cache_miss_stats: experts copied and computed on the host so far, and
  * the current rate estimates (GB/s; 0 before any measurement).
