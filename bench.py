@@ -161,7 +161,7 @@ def time_graph(stack, T, steps, warmup):
 
 
 def kernel_profile(stack, x, bufs, reps=5, names=("router_logits", "topk_permute", "topk", "permute", "ffn_gateup",
-                                                  "ffn_down", "combine")):
+                                                  "ffn_gateup_mfma", "ffn_down", "ffn_down_mfma", "combine")):
     """Per-kernel average durations from the library's event timing (eager)."""
     import torch
     import expert_offload_amd as moe
@@ -331,23 +331,26 @@ def wide_extra(ctx, layers=8, steps=30, warmup=5, distinct=128):
         layer_bytes = sum(decode_layer_bytes(wl, T, a) for a in na) / len(na)
         flops = 2.0 * T * wl.k * 3 * wl.H * wl.I
         kus = {name: ms_ / n * 1e3 for name, (n, ms_) in prof.items()}
-        ffn_us = kus.get("ffn_gateup", 0) + kus.get("ffn_down", 0)
+        ffn_us = sum(kus.get(n_, 0) for n_ in ("ffn_gateup", "ffn_gateup_mfma", "ffn_down", "ffn_down_mfma"))
         res = {"tokens": T, "tokens_per_s_per_layer": T / (layer_us * 1e-6), "layer_us": layer_us,
                "median_layer_us": stack.last_replay_ms["median"] / layers * 1e3,
                "mean_active_experts": sum(na) / len(na), "layer_bytes": layer_bytes,
                "layer_hbm_gbs": layer_bytes / (layer_us * 1e-6) / 1e9,
                "layer_hbm_frac": layer_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                "kernel_us": kus,
-               "gateup_hbm_frac": kb["ffn_gateup"] / (kus["ffn_gateup"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
-               "down_hbm_frac": kb["ffn_down"] / (kus["ffn_down"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                "ffn_flops": flops,
-               "ffn_valu_tflops": flops / (ffn_us * 1e-6) / 1e12,
-               "ffn_valu_frac": flops / (ffn_us * 1e-6) / 1e12 / VALU_F32_PEAK_TFLOPS,
+               # the fp32 FFN arithmetic over the GEMV and matrix-core kernels together
+               "ffn_fp32_tflops": flops / (ffn_us * 1e-6) / 1e12,
+               "ffn_fp32_frac": flops / (ffn_us * 1e-6) / 1e12 / VALU_F32_PEAK_TFLOPS,
                "ffn_hbm_frac": (kb["ffn_gateup"] + kb["ffn_down"]) / (ffn_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
-        # which roofline binds: the larger of the two times at peak
+        for part in ("gateup", "down"):  # both kernels of a part (matrix-core experts, the others)
+            t_ = kus.get("ffn_" + part, 0) + kus.get("ffn_%s_mfma" % part, 0)
+            res[part + "_hbm_frac"] = kb["ffn_" + part] / (t_ * 1e-6) / 1e9 / HBM_PEAK_GBS
+        # which roofline binds: the larger of the two times at peak (the fp32
+        # peak is the same for the VALU and the fp32 matrix cores)
         t_hbm = (kb["ffn_gateup"] + kb["ffn_down"]) / (HBM_PEAK_GBS * 1e9)
         t_valu = flops / (VALU_F32_PEAK_TFLOPS * 1e12)
-        res["ffn_bound"] = "hbm" if t_hbm >= t_valu else "valu (fp32)"
+        res["ffn_bound"] = "hbm" if t_hbm >= t_valu else "fp32 arithmetic"
         res["ffn_floor_us"] = {"hbm": t_hbm * 1e6, "valu_fp32": t_valu * 1e6}
         # the same layers with int8 activations (MOE_MODE_DECODE_Q8A)
         from expert_offload_amd import _lib as L

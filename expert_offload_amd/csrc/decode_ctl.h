@@ -46,16 +46,23 @@ __device__ __forceinline__ int stage_runs(const FfnParams& p, CtlLds& s, int n_a
   if (p.T <= kRunMinTokens) return n_active;
   for (int a = threadIdx.x; a < n_active; a += NT) {
     const int e = s.active[1 + a];
-    s.runs[a] = (s.offsets[e + 1] - s.offsets[e] + kRunPairs - 1) / kRunPairs;
+    const int n = s.offsets[e + 1] - s.offsets[e];
+    s.runs[a] = p.mfma_min && n >= p.mfma_min ? 0 : (n + kRunPairs - 1) / kRunPairs;  // matrix-core experts: none
   }
   __syncthreads();
   return block_exclusive_scan<NT>(s.runs, s.run_base, n_active, s.scan_wave);
 }
 
-// Run r (wavefront-uniform) -> its expert and pairs.
+// Whether expert e runs on the matrix cores instead (FfnParams mfma_min).
+__device__ __forceinline__ bool mfma_expert(const FfnParams& p, const CtlLds& s, int e) {
+  return p.mfma_min && s.offsets[e + 1] - s.offsets[e] >= p.mfma_min;
+}
+
+// Run r (wavefront-uniform) -> its expert and pairs.  (Runs of zero pairs,
+// for matrix-core experts, never come out: run_base only repeats there.)
 __device__ __forceinline__ PairRun pair_run(const FfnParams& p, const CtlLds& s, int n_active, int r) {
   int a = r, first = 0;
-  if (p.T > kRunMinTokens) {  // last active expert with run_base <= r (run_base strictly increases)
+  if (p.T > kRunMinTokens) {  // last active expert with run_base <= r
     int lo = 0, hi = n_active - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;

@@ -11,6 +11,7 @@
 #include "decode_ctl.h"
 #include "decode_gemv.h"
 #include "route_common.h"
+#include "decode_mfma.h"
 
 namespace moe {
 
@@ -60,6 +61,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_decode(FfnParams p, const floa
       e = run.e;
       pbeg = run.pbeg;
       n_e = run.n;
+      if (mfma_expert(p, ctl, e)) continue;  // on the matrix cores
     }
     // pair s of the expert, s = 0, 1, ... in turn
     int s_next = 0;
@@ -162,7 +164,8 @@ __global__ __launch_bounds__((down_waves<QT, LPR, BPL, RPL>() * kWave)) void ffn
   stage_ctl<NWV * kWave>(p, ctl, p.out != nullptr);
   const int* pairs = ctl.pairs;
   const float* topk_w = ctl.w;
-  const bool lds_y = p.T * p.k * RW <= kDownLdsFloats;
+  // (with matrix-core experts, their y rows are read back from memory)
+  const bool lds_y = p.T * p.k * RW <= kDownLdsFloats && !p.mfma_min;
   // With LPR < 64 the 64/LPR lane groups own the same columns of h: each h
   // row is read from memory once (issued before the weights) into the
   // wavefront's LDS row, and the groups read their blocks from there.
@@ -184,6 +187,7 @@ __global__ __launch_bounds__((down_waves<QT, LPR, BPL, RPL>() * kWave)) void ffn
       const PairRun run = pair_run(p, ctl, n_active, r);
       const int e = run.e;
       if (p.mask && !p.mask[e]) continue;
+      if (mfma_expert(p, ctl, e)) continue;  // its y rows come from the matrix-core kernel
       const int slot = ctl.slots[e];
       const int pbeg = run.pbeg, n_e = run.n;
       if (slot < 0 || slot >= p.n_slots) {
@@ -425,15 +429,34 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
     }
     return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "int8-activation decode: block type %d", QT);
   }
+  // experts with many tokens of the batch on the matrix cores (fp32)
+  FfnParams q = p;
+  const bool mix = mfma_decode_type(QT) && !route && p.T >= kMfmaMinBatch;
+  const int grid_mx = 4 * ctx->num_cus;  // persistent: items in turn
+  if (mix) {
+    q.mfma_min = kMfmaMinPairs;
+    if constexpr (mfma_decode_type(QT)) {
+      KernelTimer timer(ctx, "ffn_gateup_mfma", s);
+      launch(ffn_gateup_mfma<QT>, grid_mx, 256, 0, s, q, x);
+    }
+    if ((rc = check_launch("ffn_gateup_mfma"))) return rc;
+  }
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
-    dispatch_gateup<QT>(gu, p, x, grid_gu, s, route);
+    dispatch_gateup<QT>(gu, q, x, grid_gu, s, route);
   }
   rc = check_launch("ffn_gateup_decode");
   if (rc) return rc;
+  if (mix) {
+    if constexpr (mfma_decode_type(QT)) {
+      KernelTimer timer(ctx, "ffn_down_mfma", s);
+      launch(ffn_down_mfma<QT>, grid_mx, 256, 0, s, q);
+    }
+    if ((rc = check_launch("ffn_down_mfma"))) return rc;
+  }
   {
     KernelTimer timer(ctx, "ffn_down", s);
-    dispatch_down<QT>(dn, p, grid_dn, s);
+    dispatch_down<QT>(dn, q, grid_dn, s);
   }
   return check_launch("ffn_down_decode");
 }

@@ -29,6 +29,9 @@ struct FfnParams {
   int8_t* hq;
   float* hs;
   int* hsum;
+  // experts with at least this many pairs run on the matrix cores (their
+  // own kernels), and the GEMV kernels skip them; 0: none
+  int mfma_min = 0;
 };
 
 // Routing done inside the decode gate/up kernel (small batches, T*k <= 64):

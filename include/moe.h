@@ -118,7 +118,8 @@ int moe_ctx_check(moe_ctx* ctx, void* stream);
  * not timed); enabling or disabling discards earlier records.  moe_ctx_kernel_time waits for the
  * recorded launches of `kernel` (names: "router_logits", "topk", "permute",
  * "ffn_gateup", "ffn_down", "combine", "dequant", "topk_permute",
- * "permute_count", "permute_scan", "permute_scatter", "quant_act") and
+ * "permute_count", "permute_scan", "permute_scatter", "quant_act",
+ * "ffn_gateup_mfma", "ffn_down_mfma") and
  * returns their number
  * and summed duration in milliseconds. */
 int moe_ctx_set_timing(moe_ctx* ctx, int enable);
