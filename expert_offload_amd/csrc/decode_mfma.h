@@ -82,18 +82,24 @@ struct BRaw {
     if constexpr (QT == MOE_QTYPE_Q8_0) w1 = *reinterpret_cast<const uint32_t*>(q + 16 + 4 * g);
     d = *reinterpret_cast<const uint16_t*>(grp + group_d_off(QT) + 2 * (b & 7));
   }
-  // weight of set s, element q (exact: an fp16 scale times a small integer)
+  // weight of set s, element q: d * u - off * d for the stored code u (Q8_0:
+  // q + 128, Q4_0: the nibble), one fused multiply-add of exact operands whose
+  // exact result d * (u - off) is an fp32 number, so it is exact.
   __device__ __forceinline__ void dequant(float (&v)[2][4]) const {
     const float dd = __half2float(__ushort_as_half((unsigned short)d));
+    const float off = -qtype_code_off(QT) * dd;
+    uint32_t c0, c1;
+    if constexpr (QT == MOE_QTYPE_Q8_0) {
+      c0 = w0 ^ 0x80808080u;
+      c1 = w1 ^ 0x80808080u;
+    } else {
+      c0 = w0 & 0x0F0F0F0Fu;
+      c1 = (w0 >> 4) & 0x0F0F0F0Fu;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if constexpr (QT == MOE_QTYPE_Q8_0) {
-        v[0][q] = dd * (float)(int8_t)(w0 >> (8 * q));
-        v[1][q] = dd * (float)(int8_t)(w1 >> (8 * q));
-      } else {
-        v[0][q] = dd * (float)((int)((w0 >> (8 * q)) & 0xFu) - 8);
-        v[1][q] = dd * (float)((int)((w0 >> (8 * q + 4)) & 0xFu) - 8);
-      }
+      v[0][q] = fmaf(dd, (float)((c0 >> (8 * q)) & 0xFFu), off);
+      v[1][q] = fmaf(dd, (float)((c1 >> (8 * q)) & 0xFFu), off);
     }
   }
 };
@@ -183,7 +189,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma(FfnParams p, const float*
   stage_ctl<256>(p, ctl, false);
   const int n_active = ctl.active[0];
   const int n_tiles = stage_mfma_tiles<256>(p, ctl, mc, n_active);
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6, g = lane / 16, j = lane % 16;
+  const int lane = threadIdx.x & (kWave - 1), g = lane / 16, j = lane % 16;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_chunks = p.I / 16;
   const int items = n_tiles * n_chunks;
   const size_t gate_off = slot_gate_off(QT, p.H, p.I), up_off = slot_up_off(QT, p.H, p.I);
@@ -233,7 +240,8 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnParams p) {
   stage_ctl<256>(p, ctl, false);
   const int n_active = ctl.active[0];
   const int n_tiles = stage_mfma_tiles<256>(p, ctl, mc, n_active);
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6, g = lane / 16, j = lane % 16;
+  const int lane = threadIdx.x & (kWave - 1), g = lane / 16, j = lane % 16;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_chunks = p.H / 32;
   const int items = n_tiles * n_chunks;
   const size_t down_off = slot_down_off(QT, p.H, p.I);
