@@ -437,7 +437,7 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
     q.mfma_min = kMfmaMinPairs;
     if constexpr (mfma_decode_type(QT)) {
       KernelTimer timer(ctx, "ffn_gateup_mfma", s);
-      launch(ffn_gateup_mfma<QT>, grid_mx, 256, 0, s, q, x);
+      launch(ffn_gateup_mfma<QT>, grid_mx, kMfmaThreads, 0, s, q, x);
     }
     if ((rc = check_launch("ffn_gateup_mfma"))) return rc;
   }
@@ -450,7 +450,7 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
   if (mix) {
     if constexpr (mfma_decode_type(QT)) {
       KernelTimer timer(ctx, "ffn_down_mfma", s);
-      launch(ffn_down_mfma<QT>, grid_mx, 256, 0, s, q);
+      launch(ffn_down_mfma<QT>, grid_mx, kMfmaThreads, 0, s, q);
     }
     if ((rc = check_launch("ffn_down_mfma"))) return rc;
   }

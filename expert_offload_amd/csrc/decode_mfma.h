@@ -152,6 +152,7 @@ __device__ __forceinline__ void mfma_rows(const float* arow, bool arow_ok, const
 // K blocks in four consecutive ranges and their partial sums meet in LDS,
 // added in wavefront order (so the result does not depend on timing).
 constexpr int kSplitK = 4;
+constexpr int kMfmaThreads = kWave * kSplitK;  // threads of a matrix-core workgroup
 struct SplitLds {
   float part[kSplitK][2][4][kWave];
 };
@@ -182,13 +183,13 @@ __device__ __forceinline__ void split_reduce(SplitLds& sl, mf32x4 (&acc)[2], int
 
 // gate/up + SwiGLU: item = (tile, 16 intermediate indices), one per workgroup.
 template <int QT>
-__global__ __launch_bounds__(256) void ffn_gateup_mfma(FfnParams p, const float* __restrict__ x) {
+__global__ __launch_bounds__(kMfmaThreads) void ffn_gateup_mfma(FfnParams p, const float* __restrict__ x) {
   __shared__ CtlLds ctl;
   __shared__ MfmaCtl mc;
   __shared__ SplitLds sl;
-  stage_ctl<256>(p, ctl, false);
+  stage_ctl<kMfmaThreads>(p, ctl, false);
   const int n_active = ctl.active[0];
-  const int n_tiles = stage_mfma_tiles<256>(p, ctl, mc, n_active);
+  const int n_tiles = stage_mfma_tiles<kMfmaThreads>(p, ctl, mc, n_active);
   const int lane = threadIdx.x & (kWave - 1), g = lane / 16, j = lane % 16;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_chunks = p.I / 16;
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma(FfnParams p, const float*
     const int slot = ctl.slots[e];
     if (slot < 0 || slot >= p.n_slots) {
       if (threadIdx.x == 0) atomicCAS(p.err, 0, e + 1);
-      for (int s = threadIdx.x; s < rows * 16; s += 256) p.hbuf[(size_t)(pbeg + s / 16) * p.I + i0 + s % 16] = NAN;
+      for (int s = threadIdx.x; s < rows * 16; s += kMfmaThreads) p.hbuf[(size_t)(pbeg + s / 16) * p.I + i0 + s % 16] = NAN;
       continue;
     }
     const bool ok = j < rows;  // this lane's A row (pair j of the tile)
@@ -233,13 +234,13 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma(FfnParams p, const float*
 
 // down: item = (tile, 32 output columns), one per workgroup; y rows in pair order.
 template <int QT>
-__global__ __launch_bounds__(256) void ffn_down_mfma(FfnParams p) {
+__global__ __launch_bounds__(kMfmaThreads) void ffn_down_mfma(FfnParams p) {
   __shared__ CtlLds ctl;
   __shared__ MfmaCtl mc;
   __shared__ SplitLds sl;
-  stage_ctl<256>(p, ctl, false);
+  stage_ctl<kMfmaThreads>(p, ctl, false);
   const int n_active = ctl.active[0];
-  const int n_tiles = stage_mfma_tiles<256>(p, ctl, mc, n_active);
+  const int n_tiles = stage_mfma_tiles<kMfmaThreads>(p, ctl, mc, n_active);
   const int lane = threadIdx.x & (kWave - 1), g = lane / 16, j = lane % 16;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_chunks = p.H / 32;
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnParams p) {
     const int slot = ctl.slots[e];
     if (slot < 0 || slot >= p.n_slots) {
       if (threadIdx.x == 0) atomicCAS(p.err, 0, e + 1);
-      for (int s = threadIdx.x; s < rows * 32; s += 256) p.y[(size_t)ctl.pairs[pbeg + s / 32] * p.H + h0 + s % 32] = NAN;
+      for (int s = threadIdx.x; s < rows * 32; s += kMfmaThreads) p.y[(size_t)ctl.pairs[pbeg + s / 32] * p.H + h0 + s % 32] = NAN;
       continue;
     }
     const bool ok = j < rows;

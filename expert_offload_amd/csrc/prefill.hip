@@ -6,23 +6,33 @@
 // matrix-matrix kernels with prefill).  Per expert: h = silu(X Wg^T) *
 // (X Wu^T) with X the expert's gathered token rows, then y = h Wd^T.
 //
-// Tiles.  A workgroup (4 wavefronts) computes a 256 x 128 output tile of one
-// expert with v_mfma_f32_16x16x32_bf16.  Each wavefront owns 64 rows and all
-// 128 columns (4 x 8 blocks of 16 x 16, 128 accumulators per lane), so:
-//  * activation rows are private to a wavefront and go from global memory
-//    (L2) straight into MFMA operand registers, the next K step's loads
-//    issued while the current step's MFMAs run;
-//  * the weight tile is shared by the four wavefronts through LDS: each
-//    thread dequantises one 32-weight block per K step (bf16 = round to
-//    nearest even of d * q, exact in fp32 before rounding) into one of two
-//    LDS buffers while the MFMAs read the other, one barrier per K step, and
-//    the blocks' global loads are issued two K steps ahead.
+// Tiles.  A workgroup of eight wavefronts in two groups of four computes
+// one row tile of an expert (256 token rows) against two column tiles of 128
+// outputs, group g on column tile 2 j + g, with v_mfma_f32_16x16x32_bf16; K
+// steps of 64.  Each wavefront owns 64 rows x 128 columns (4 x 8 blocks of
+// 16 x 16, 128 accumulators per lane).
+//  * The activation tile of a K step (256 rows, bf16) sits in LDS, double
+//    buffered, and both groups read it: each activation row is fetched from
+//    L2 once per 256 output columns.  The fetch uses whole 128-byte lines
+//    (eight lanes per row), two stages before the rows are written to LDS.
+//  * Each group dequantises its own weight tile (bf16 = round to nearest even
+//    of d * q, exact in fp32 before rounding) into its own double-buffered
+//    LDS tile, the blocks' global loads issued two K steps ahead.
+//  * A K step of a group is an MFMA phase and a staging phase, each ended by
+//    a workgroup barrier, and group 1 runs one phase behind group 0: on every
+//    SIMD one wavefront issues matrix instructions while the other stages.
 // Gate/up tiles hold 64 gate rows and the 64 up rows of the same
 // intermediate indices, so SwiGLU is applied in the accumulator registers.
+// An expert's last tile of at most 64 rows (a tail) is computed by all four
+// wavefronts of a group on the same rows, each taking two of the eight
+// 16-column blocks (a gate block and its up block), so the tail does not
+// leave three wavefronts without MFMA work.
 //
 // Workgroups are dispatched to the 8 XCDs round-robin; the index mapping
 // puts all column tiles of one row tile on one XCD so its activation rows
 // are read into that XCD's L2 once.
+#include <type_traits>
+
 #include "device_common.h"
 #include "ffn.h"
 #include "route_common.h"
@@ -37,6 +47,8 @@ constexpr int kTN = 128;       // output columns per tile
 constexpr int kTK = 64;        // K step
 constexpr int kLdB = kTK + 8;  // LDS row stride of the weight tile (bf16)
 constexpr int kXcds = 8;
+// dequantisation form of the two-group kernel (bit 1: byte permute)
+constexpr int kPrefillFlagsPp = 2;
 
 // ------------------------------------------------------------ tile list
 // One workgroup: for every expert with pairs (and not masked out), its
@@ -140,59 +152,68 @@ struct WStage {
 };
 
 // ------------------------------------------------------ grouped GEMM
-// GATEUP: A = gathered token rows of x (bf16 [T][H]), B = 64 gate + 64 up
-// rows, epilogue h = silu(g) * u into hbuf (bf16, grouped order [T*k][I]).
-// Down: A = hbuf rows (grouped order), B = 128 rows of Wd, epilogue y
-// (fp32, pair order [T*k][H]).  NW wavefronts, 64 rows each.
-// One tile (expert e, first row m0; column tile nt_i).  SPLIT: a small
-// tile (at most 64 rows, an expert's last rows), where one wavefront of
-// rows would leave the others without MFMA work: every wavefront takes the
-// same rows and two of the eight 16-column blocks (gate/up: gate block
-// `wave` and its up block `wave + 4`, so SwiGLU stays in the wavefront).
-// FL bit 0: the MFMA phase of a step at raised wave priority, so of the two
-// workgroups on a CU the one with MFMAs to issue is served first while the
-// other dequantises; bit 1: WStage's byte-permute dequantisation.
-template <int QT, bool GATEUP, int NW, bool SPLIT, int FL = 0>
-__device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* __restrict__ x, int2 tl, int nt_i,
-                                             __bf16* __restrict__ hbuf, __bf16 (&sB)[2][kTN][kLdB],
-                                             int (&s_pair)[kWaveRows * NW]) {
-  constexpr int kThreads = 64 * NW, kRows = kWaveRows * NW;
-  constexpr int kUnits = 2 * 2 * kTN / kThreads;  // half blocks staged per thread and K step
+// One row tile against column tiles 2 ntp and 2 ntp + 1, as group G (0 or 1)
+// of the workgroup: G selects the column tile, the half of the activation
+// rows this group stages, and the group's phase (group 1 one behind).
+constexpr int kPpRows = 4 * kWaveRows;  // rows of a tile
+constexpr int kLdA = kTK + 8;           // LDS row stride of the activation tile (bf16)
+
+struct PpLds {
+  __bf16 a[2][kPpRows][kLdA];
+  __bf16 b[2][2][kTN][kLdB];  // [group][buffer]
+  int pair[kPpRows];
+};
+
+template <int QT, bool GATEUP, bool SPLIT, int G>
+__device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* __restrict__ x, int2 tl, int ntp,
+                                        __bf16* __restrict__ hbuf, PpLds& L) {
+  constexpr int kUnits = 2;  // half blocks staged per thread and K step: 128 rows x 2 blocks x 2 halves / 256
+  const int tid = threadIdx.x, ltid = tid & 255;
+  const int lane = tid & (kWave - 1), wave = ltid >> 6, quad = lane >> 4;
   const int e = tl.x, m0 = tl.y;
   const int pbeg = p.offsets[e];
-  const int rows = min(kRows, p.offsets[e + 1] - pbeg - m0);
+  const int rows = min(kPpRows, p.offsets[e + 1] - pbeg - m0);
   const int slot = p.slot_table[e];
   const int K = GATEUP ? p.H : p.I;
+  const int nt_i = 2 * ntp + G;
   const int n0 = GATEUP ? nt_i * (kTN / 2) : nt_i * kTN;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6, half = lane >> 5;
-  for (int r = tid; r < kRows; r += kThreads) s_pair[r] = r < rows ? p.sorted_pairs[pbeg + m0 + r] : 0;
+  for (int r = tid; r < kPpRows; r += 512) L.pair[r] = r < rows ? p.sorted_pairs[pbeg + m0 + r] : 0;
   __syncthreads();
-  if (slot < 0 || slot >= p.n_slots) {
+  if (slot < 0 || slot >= p.n_slots) {  // both groups see the same expert
     if (tid == 0) atomicCAS(p.err, 0, e + 1);
     if constexpr (GATEUP) {
-      for (int idx = tid; idx < rows * (kTN / 2); idx += kThreads)
+      for (int idx = ltid; idx < rows * (kTN / 2); idx += 256)
         hbuf[(size_t)(pbeg + m0 + idx / (kTN / 2)) * p.I + n0 + idx % (kTN / 2)] = (__bf16)NAN;
     } else {
-      for (int idx = tid; idx < rows * kTN; idx += kThreads)
-        p.y[(size_t)s_pair[idx / kTN] * p.H + n0 + idx % kTN] = NAN;
+      for (int idx = ltid; idx < rows * kTN; idx += 256)
+        p.y[(size_t)L.pair[idx / kTN] * p.H + n0 + idx % kTN] = NAN;
     }
     return;
   }
-  // activation rows of this lane: MFMA row block mt holds rows 16 mt + lane % 16
-  // (rows past the tile's end read row 0; their results are dropped)
-  const int quad = lane >> 4;
-  const __bf16* arow[4];
-  const int row0 = SPLIT ? 0 : kWaveRows * wave;
+  const int nk = K / kTK;  // even (checked on the host)
+  // activation staging: this group's half of the rows, eight lanes per row
+  // (16 bytes each), 32 rows per round, four rounds; rows past the tile read row 0
+  const int a_chunk = ltid & 7;
+  const __bf16* asrc[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int m = row0 + 16 * mt + (lane & 15);
-    const int mm = m < rows ? m : 0;
-    arow[mt] = GATEUP ? x + (size_t)(s_pair[mm] / p.k) * p.H + 8 * quad
-                      : hbuf + (size_t)(pbeg + m0 + mm) * p.I + 8 * quad;
+  for (int i = 0; i < 4; ++i) {
+    const int r = 128 * G + (ltid >> 3) + 32 * i;
+    const int rr = r < rows ? r : 0;
+    asrc[i] = (GATEUP ? x + (size_t)(L.pair[rr] / p.k) * p.H : hbuf + (size_t)(pbeg + m0 + rr) * p.I) + 8 * a_chunk;
   }
-  const bool active = row0 < rows;
-  // weight staging: unit v = tid * kUnits + u is row v / 4, block (v / 2) % 2, half v % 2
-  const int v0 = tid * kUnits;
+  bf16x8 areg[2][4];
+  auto load_a = [&](bf16x8 (&ar)[4], int kc) {
+    const size_t koff = (size_t)min(kc, nk - 1) * kTK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = *reinterpret_cast<const bf16x8*>(asrc[i] + koff);
+  };
+  auto store_a = [&](const bf16x8 (&ar)[4], int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<bf16x8*>(&L.a[buf][128 * G + (ltid >> 3) + 32 * i][8 * a_chunk]) = ar[i];
+  };
+  // weight staging: unit v = ltid * kUnits + u is row v / 4, block (v / 2) % 2, half v % 2
+  const int v0 = ltid * kUnits;
   const int brow = v0 >> 2, bblk = (v0 >> 1) & 1;
   const uint8_t* slotp = p.pool + (size_t)slot * p.slot_bytes;
   const uint8_t* wrow;
@@ -202,122 +223,122 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
   else
     wrow = slotp + slot_down_off(QT, p.H, p.I) + (size_t)(n0 + brow) * row_bytes(QT, p.I);
   const int scol = 32 * bblk + 16 * (v0 & 1);
-  __bf16* const sdst0 = &sB[0][brow][scol];
-  __bf16* const sdst1 = &sB[1][brow][scol];
+  using WS = WStage<QT, (kPrefillFlagsPp & 2) != 0>;
+  WS st[2][kUnits];
+  auto load_w = [&](WS (&s_)[kUnits], int kc) {
+    const int b = 2 * min(kc, nk - 1) + bblk;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) s_[u].load(wrow, b, (v0 + u) & 1);
+  };
+  auto store_w = [&](const WS (&s_)[kUnits], int buf) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) s_[u].store(&L.b[G][buf][brow][scol] + 16 * u, (v0 + u) & 1);
+  };
+  // prologue: activation step 0 (and step 1 for group 1, whose first stage
+  // writes step 2), weight step 0; registers for the first two stages
+  load_a(areg[0], 0);
+  load_w(st[0], 0);
+  load_w(st[1], 1);
+  store_a(areg[0], 0);
+  if constexpr (G == 1) {
+    load_a(areg[1], 1);
+    store_a(areg[1], 1);
+  }
+  store_w(st[0], 0);
+  load_w(st[0], 2);
+  // the stage writing activation step j + G holds it in set (j + G) & 1
+  load_a(areg[(1 + G) & 1], 1 + G);
+  load_a(areg[(2 + G) & 1], 2 + G);
+  __syncthreads();
 
-  // 4 x 8 blocks of 16 x 16 accumulators (rows 16 mt + 4 (lane / 16) + r, column 16 nt + lane % 16)
   f32x4 acc[4][8];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{};
-  // activation fragments (row block, 32-wide K half of the step): two
-  // register sets, the next step's loads issued at the top of the current
-  // step (before the weight prefetch, so waiting for them never waits for
-  // a younger load).  Every wavefront loads, even one with no rows in this
-  // tile (its rows read row 0): a load under a branch makes the compiler's
-  // wait counts assume the path without it.
-  bf16x8 a0[4][2], a1[4][2];
-  const int nk = K / kTK;  // even (checked on the host)
-  auto load_a = [&](bf16x8 (&a)[4][2], int kc) {
-    const size_t koff = (size_t)min(kc, nk - 1) * kTK;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) a[mt][ks] = *reinterpret_cast<const bf16x8*>(arow[mt] + koff + 32 * ks);
+  const int row0 = SPLIT ? 0 : kWaveRows * wave;
+  const bool active = row0 < rows;
+  auto phase_end = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
-  using WS = WStage<QT, (FL & 2) != 0>;
-  auto load_w = [&](WS (&st)[kUnits], int kc) {
-    const int b = 2 * min(kc, nk - 1) + bblk;
-#pragma unroll
-    for (int u = 0; u < kUnits; ++u) st[u].load(wrow, b, (v0 + u) & 1);
-  };
-  auto store_w = [&](const WS (&st)[kUnits], __bf16* dst) {
-#pragma unroll
-    for (int u = 0; u < kUnits; ++u) st[u].store(dst + 16 * u, (v0 + u) & 1);
-  };
-  load_a(a0, 0);
-  WS st0[kUnits], st1[kUnits];
-  load_w(st0, 0);
-  load_w(st1, 1);
-  store_w(st0, sdst0);
-  load_w(st0, 2);
-  __syncthreads();
-
-  // One K step on buffer `sb` with activations `a`: load the next step's
-  // activations into `an`, stage step kc+1 from `nxt` into the other LDS
-  // buffer and reload `nxt` with step kc+3, then the MFMAs of step kc.
-  // Prefetch indices are clamped to the last step instead of branched on:
-  // near the end the repeated loads and the staging into the idle buffer
-  // are never read.
-  auto step = [&](int kc, const __bf16 (*sb)[kLdB], __bf16* sdst, WS (&nxt)[kUnits],
-                  const bf16x8 (&a)[4][2], bf16x8 (&an)[4][2]) {
-    load_a(an, kc + 1);
-    store_w(nxt, sdst);
-    load_w(nxt, kc + 3);
-    if constexpr (SPLIT) {
+  auto mfma_phase = [&](int buf) {
+    if (active) {
+      __builtin_amdgcn_s_setprio(1);
+      const __bf16 (*sa)[kLdA] = L.a[buf];
+      const __bf16 (*sb)[kLdB] = L.b[G][buf];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&sb[16 * wave + (lane & 15)][32 * ks + 8 * quad]);
-        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sb[16 * (wave + 4) + (lane & 15)][32 * ks + 8 * quad]);
+        bf16x8 a[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b0, acc[mt][0], 0, 0, 0);
-          acc[mt][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b1, acc[mt][4], 0, 0, 0);
-        }
-      }
-    } else if (active) {
-      if constexpr (FL & 1) __builtin_amdgcn_s_setprio(1);
+        for (int mt = 0; mt < 4; ++mt)
+          a[mt] = *reinterpret_cast<const bf16x8*>(&sa[row0 + 16 * mt + (lane & 15)][32 * ks + 8 * quad]);
+        if constexpr (SPLIT) {
+          const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&sb[16 * wave + (lane & 15)][32 * ks + 8 * quad]);
+          const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sb[16 * (wave + 4) + (lane & 15)][32 * ks + 8 * quad]);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+          for (int mt = 0; mt < 4; ++mt) {
+            acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b0, acc[mt][0], 0, 0, 0);
+            acc[mt][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b1, acc[mt][4], 0, 0, 0);
+          }
+        } else {
 #pragma unroll
-        for (int nh = 0; nh < 2; ++nh) {
-          bf16x8 b[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            b[q] = *reinterpret_cast<const bf16x8*>(&sb[16 * (4 * nh + q) + (lane & 15)][32 * ks + 8 * quad]);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+          for (int nh = 0; nh < 2; ++nh) {
+            bf16x8 b[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              acc[mt][4 * nh + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b[q], acc[mt][4 * nh + q], 0, 0, 0);
+              b[q] = *reinterpret_cast<const bf16x8*>(&sb[16 * (4 * nh + q) + (lane & 15)][32 * ks + 8 * quad]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc[mt][4 * nh + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[q], acc[mt][4 * nh + q], 0, 0, 0);
+          }
         }
       }
-      if constexpr (FL & 1) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
     }
-    __syncthreads();
+    phase_end();
   };
+  // stage j (parity P = j & 1): weights of step j into buffer P from st[P]
+  // (then st[P] <- step j + 2); activation step j + G into buffer
+  // (j + G) & 1 from its register set (then that set <- step j + G + 2)
+  auto stage_phase = [&](int j, auto P) {
+    constexpr int kP = decltype(P)::value, kS = (kP + G) & 1;
+    store_w(st[kP], kP);
+    load_w(st[kP], j + 2);
+    store_a(areg[kS], kS);
+    load_a(areg[kS], j + G + 2);
+    phase_end();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if constexpr (G == 1) phase_end();
   for (int kc = 0; kc < nk; kc += 2) {
-    step(kc, sB[0], sdst1, st1, a0, a1);
-    step(kc + 1, sB[1], sdst0, st0, a1, a0);
+    mfma_phase(0);
+    stage_phase(kc + 1, P1{});
+    mfma_phase(1);
+    stage_phase(kc + 2, P0{});
   }
+  if constexpr (G == 0) phase_end();
   if (!active) return;
-  if constexpr (SPLIT) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 16 * mt + 4 * quad + r;
-        if (m >= rows) continue;
-        if constexpr (GATEUP) {
-          const float g = acc[mt][0][r], u = acc[mt][4][r];
-          hbuf[(size_t)(pbeg + m0 + m) * p.I + n0 + 16 * wave + (lane & 15)] = (__bf16)(g / (1.0f + expf(-g)) * u);
-        } else {
-          float* yrow = p.y + (size_t)s_pair[m] * p.H + n0 + (lane & 15);
-          yrow[16 * wave] = acc[mt][0][r];
-          yrow[16 * (wave + 4)] = acc[mt][4][r];
-        }
-      }
-    }
-    return;
-  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = kWaveRows * wave + 16 * mt + 4 * quad + r;
+      const int m = row0 + 16 * mt + 4 * quad + r;
       if (m >= rows) continue;
-      if constexpr (GATEUP) {
+      if constexpr (SPLIT) {
+        if constexpr (GATEUP) {
+          const float g = acc[mt][0][r], u = acc[mt][4][r];
+          hbuf[(size_t)(pbeg + m0 + m) * p.I + n0 + 16 * wave + (lane & 15)] = (__bf16)(g / (1.0f + expf(-g)) * u);
+        } else {
+          float* yrow = p.y + (size_t)L.pair[m] * p.H + n0 + (lane & 15);
+          yrow[16 * wave] = acc[mt][0][r];
+          yrow[16 * (wave + 4)] = acc[mt][4][r];
+        }
+      } else if constexpr (GATEUP) {
         __bf16* hrow = hbuf + (size_t)(pbeg + m0 + m) * p.I + n0 + (lane & 15);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -325,7 +346,7 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
           hrow[16 * nt] = (__bf16)(g / (1.0f + expf(-g)) * u);
         }
       } else {
-        float* yrow = p.y + (size_t)s_pair[m] * p.H + n0 + (lane & 15);
+        float* yrow = p.y + (size_t)L.pair[m] * p.H + n0 + (lane & 15);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) yrow[16 * nt] = acc[mt][nt][r];
       }
@@ -333,44 +354,46 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
   }
 }
 
-// One launch over both lists: the tiles, then the small tiles (so the
-// small ones are dispatched last, into the big ones' tail).  Each branch is
-// a whole tile, so the two register allocations never overlap.
-template <int QT, bool GATEUP, int NW, int FL = 0>
-__global__ __launch_bounds__(64 * NW, 2) void prefill_gemm_kernel(FfnParams p, const __bf16* __restrict__ x,
-                                                                  const int2* __restrict__ tiles,
-                                                                  const int* __restrict__ count, int ntn,
-                                                                  __bf16* __restrict__ hbuf) {
-  __shared__ __attribute__((aligned(16))) __bf16 sB[2][kTN][kLdB];
-  __shared__ int s_pair[kWaveRows * NW];
+// One launch over both tile lists: the full tiles, then the tails (so the
+// tails are dispatched last, into the full tiles' wake).  Each branch is a
+// whole tile, so the register allocations never overlap.
+template <int QT, bool GATEUP>
+__global__ __launch_bounds__(512, 1) void prefill_gemm_kernel(FfnParams p, const __bf16* __restrict__ x,
+                                                          const int2* __restrict__ tiles, const int* __restrict__ count,
+                                                          int ntn, __bf16* __restrict__ hbuf) {
+  __shared__ __attribute__((aligned(16))) PpLds L;
+  const int nth = ntn / 2;
   const int j = blockIdx.x / kXcds;
-  const int mt_i = kXcds * (j / ntn) + (int)(blockIdx.x % kXcds);
-  const int nt_i = j % ntn;
+  const int mt_i = kXcds * (j / nth) + (int)(blockIdx.x % kXcds);
+  const int ntp = j % nth;
   const int n_big = count[0];
   if (mt_i >= n_big + count[1]) return;
-  if (mt_i < n_big) prefill_tile<QT, GATEUP, NW, false, FL>(p, x, tiles[mt_i], nt_i, hbuf, sB, s_pair);
-  else prefill_tile<QT, GATEUP, NW, true, FL>(p, x, tiles[mt_i], nt_i, hbuf, sB, s_pair);
+  const bool g1 = threadIdx.x >= 256;
+  if (mt_i < n_big) {
+    if (g1) prefill_tile<QT, GATEUP, false, 1>(p, x, tiles[mt_i], ntp, hbuf, L);
+    else prefill_tile<QT, GATEUP, false, 0>(p, x, tiles[mt_i], ntp, hbuf, L);
+  } else {
+    if (g1) prefill_tile<QT, GATEUP, true, 1>(p, x, tiles[mt_i], ntp, hbuf, L);
+    else prefill_tile<QT, GATEUP, true, 0>(p, x, tiles[mt_i], ntp, hbuf, L);
+  }
 }
 
 bool prefill_mfma_supported(int H, int I) {
-  // column tiles of 128 (down) and 64 (gate/up), and an even number of K steps
-  return H % (2 * kTK) == 0 && I % (2 * kTK) == 0 && H % kTN == 0;
+  // column tiles of 128 (down) and 64 (gate/up) in pairs, and an even number
+  // of K steps (a multiple of 256 for H and I, as the block layout has)
+  return H % (2 * kTN) == 0 && I % (2 * kTN) == 0;
 }
 
-// Wavefronts per workgroup (64 rows each).  Eight (512 rows, one tile per
-// expert of a 4096-token batch) measured slower than four: with one
-// workgroup per CU every barrier idles the matrix cores.
-constexpr int kPrefillWaves = 4;
-// MFMA phase at raised wave priority (bit 0) and the byte-permute
-// dequantisation of the offset types (bit 1): bit-identical results,
-// gate/up 359 -> 349 us at 4096 tokens.  Tried and dropped: staging one
-// row per thread so the LDS writes are free of bank conflicts (the weight
-// loads then spread over twice the rows; gate/up 350 -> 374 us), and one
-// workgroup per CU with the dequantisation interleaved into the MFMAs by
-// scheduling hints (the compiler moved accumulators through AGPRs; 359 ->
-// 499 us).
-constexpr int kPrefillFlags = 3;
-constexpr int kPrefillRows = kWaveRows * kPrefillWaves;
+// Tried and dropped on the way here (4096-token layer, gate/up): a single
+// group of four wavefronts per workgroup, two workgroups per CU, activation
+// rows straight into registers (the previous kernel: 354 us against 302
+// us), with the MFMA phase at raised priority and the byte-permute
+// dequantisation (359 -> 349 us there, both kept here); eight wavefronts on
+// 512 rows, slower with one workgroup per CU; the same eight on two column
+// tiles in step, without phases (390 us); phases with the activation rows
+// in registers rather than LDS (387-392 us); the dequantisation interleaved
+// into the MFMAs by scheduling hints (366 us).
+constexpr int kPrefillRows = kPpRows;
 
 static int prefill_max_tiles(size_t P, int E) { return (int)(P / kPrefillRows) + E + 1; }
 
@@ -382,10 +405,9 @@ size_t prefill_ws_bytes(int T, int k, int I, int E) {
 template <bool GATEUP>
 static void launch_prefill_gemm(const FfnParams& p, unsigned grid, hipStream_t s, const __bf16* x, const int2* tiles,
                                 const int* count, int ntn, __bf16* hbuf) {
-#define MOE_PF(Q)                                                                                          \
-  case Q:                                                                                                  \
-    launch(prefill_gemm_kernel<Q, GATEUP, kPrefillWaves, kPrefillFlags>, grid, 64 * kPrefillWaves, 0, s, p, x, tiles, \
-           count, ntn, hbuf);                                                                              \
+#define MOE_PF(Q)                                                                                \
+  case Q:                                                                                        \
+    launch(prefill_gemm_kernel<Q, GATEUP>, grid, 512, 0, s, p, x, tiles, count, ntn, hbuf);      \
     break;
   switch (p.qtype) {
     MOE_PF(MOE_QTYPE_Q8_0)
@@ -416,13 +438,13 @@ int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
     const int ntn = p.I / (kTN / 2);
-    launch_prefill_gemm<true>(p, kXcds * row_groups * (unsigned)ntn, s, xb, tiles, count, ntn, hbuf);
+    launch_prefill_gemm<true>(p, kXcds * row_groups * (unsigned)(ntn / 2), s, xb, tiles, count, ntn, hbuf);
   }
   if ((rc = check_launch("prefill_gemm_kernel"))) return rc;
   {
     KernelTimer timer(ctx, "ffn_down", s);
     const int ntn = p.H / kTN;
-    launch_prefill_gemm<false>(p, kXcds * row_groups * (unsigned)ntn, s, xb, tiles, count, ntn, hbuf);
+    launch_prefill_gemm<false>(p, kXcds * row_groups * (unsigned)(ntn / 2), s, xb, tiles, count, ntn, hbuf);
   }
   return check_launch("prefill_gemm_kernel");
 }
