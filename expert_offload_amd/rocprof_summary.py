@@ -37,7 +37,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 # Sources each profiled kernel family is compiled from.
-_DECODE = ["csrc/decode_gemv.h", "csrc/decode_ctl.h", "csrc/route_common.h", "csrc/ffn.h",
+_DECODE = ["csrc/decode_gemv.h", "csrc/decode_ctl.h", "csrc/decode_mfma.h", "csrc/route_common.h", "csrc/ffn.h",
            "csrc/device_common.h", "csrc/moe_internal.h"]
 KERNEL_SOURCES = {
     "ffn_gateup_decode": ["csrc/decode_impl.h", "csrc/decode_q8_0.hip"] + _DECODE,
