@@ -170,6 +170,32 @@ def test_router_logits_batch_invariant(ctx):
         np.testing.assert_array_equal(logits(x[:T]), alone[:T])
 
 
+def test_router_logits_experts_per_workgroup(ctx):
+    """Past 16 tokens a router workgroup takes four experts; with 10 experts
+    the last workgroup holds two past the end (loaded from the last expert's
+    row, never written).  Logits against the oracle, and each token's logits
+    bit-identical to the token routed alone."""
+    wl = gi.Workload(61, "router_h256_e10", H=256, E=10, k=2, I=256, qtype="q8_0", batches=(40,))
+    x = gi.activations(wl, 40)
+    wr = gi.router_weight(wl)
+
+    def logits(rows):
+        T = rows.shape[0]
+        lo = torch.full((T, wl.E), float("nan"), dtype=torch.float32, device=DEV)
+        ids = torch.empty((T, wl.k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, wl.k), dtype=torch.float32, device=DEV)
+        moe.moe_route(ctx, dev(rows), dev(wr), None, None, T, wl.H, wl.E, wl.k, lo, ids, w)
+        torch.cuda.synchronize()
+        return lo.cpu().numpy()
+
+    got = logits(x)
+    ref = oracle.router_logits(x, wr, None)
+    assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+    alone = np.stack([logits(x[t:t + 1])[0] for t in range(x.shape[0])])
+    for T in (17, 33, 40):
+        np.testing.assert_array_equal(logits(x[:T]), alone[:T])
+
+
 # ------------------------------------------------------------------ permute
 @pytest.mark.parametrize("with_ws", [False, True])
 @pytest.mark.parametrize("T,k,E", [(0, 2, 8), (1, 1, 1), (4, 2, 8), (16, 8, 128), (64, 10, 512),
