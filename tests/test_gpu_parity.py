@@ -440,6 +440,35 @@ def test_prefill_full_compare(ctx, prefill_layer, T):
     _check_layer(buf, out, ref, PREFILL_TOL, T)
 
 
+@pytest.mark.parametrize("T", [300, 2048])
+def test_prefill_not_resident_expert(ctx, prefill_layer, T):
+    """An expert whose slot is -1 in the prefill GEMM: reported by id, its
+    tokens' outputs NaN, every other token finite.  300 tokens reach the
+    tail tiles (at most 64 rows), 2048 the full-tile branch (about 128 rows
+    per expert); both groups of a workgroup take the missing-slot exit
+    together."""
+    wl = prefill_layer.wl
+    logits, xbits, x32 = _prefill_inputs(wl, T)
+    ids = oracle.topk_select(logits, wl.k)
+    counts = np.bincount(ids.reshape(-1), minlength=wl.E)
+    victim = int(np.argmax(counts))
+    note(f"prefill not-resident T={T}: expert {victim} with {counts[victim]} pairs")
+    table = prefill_layer.slot_table.clone()
+    table[victim] = -1
+    from gpu_util import bf16_tensor
+    buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV, mode=L.MODE_PREFILL,
+                             x_dtype=L.DTYPE_BF16)
+    out = layer.forward(ctx, buf, prefill_layer.pool.base(), prefill_layer.pool.slot_bytes,
+                        prefill_layer.pool.n_slots, table, bf16_tensor(xbits), logits_in=dev(logits)).cpu().numpy()
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_ctx_check(ctx)
+    assert ei.value.name == "MOE_ERR_NOT_RESIDENT" and f"expert {victim}" in str(ei.value)
+    moe.moe_ctx_check(ctx)
+    uses = (ids == victim).any(axis=1)
+    assert np.isnan(out[uses]).all(axis=1).all()
+    assert np.isfinite(out[~uses]).all()
+
+
 @pytest.mark.parametrize("case", ["decode-four-calls", "decode-one-call", "prefill-fp32"])
 def test_valu_ffn_paths(ctx, decode_layer, prefill_layer, case):
     """Shapes the tuned kernels do not take run the VALU kernels: decode
