@@ -47,8 +47,10 @@ constexpr int kTN = 128;       // output columns per tile
 constexpr int kTK = 64;        // K step
 constexpr int kLdB = kTK + 8;  // LDS row stride of the weight tile (bf16)
 constexpr int kXcds = 8;
-// dequantisation form of the two-group kernel (bit 1: byte permute)
-constexpr int kPrefillFlagsPp = 2;
+// the byte-permute dequantisation of the offset types (WStage FAST): the
+// same bits as the conversion path, gate/up 359 -> 349 us at 4096 tokens
+// when it was measured on a one-group version of this kernel
+constexpr bool kDequantPermute = true;
 
 // ------------------------------------------------------------ tile list
 // One workgroup: for every expert with pairs (and not masked out), its
@@ -155,29 +157,29 @@ struct WStage {
 // One row tile against column tiles 2 ntp and 2 ntp + 1, as group G (0 or 1)
 // of the workgroup: G selects the column tile, the half of the activation
 // rows this group stages, and the group's phase (group 1 one behind).
-constexpr int kPpRows = 4 * kWaveRows;  // rows of a tile
+constexpr int kTileRows = 4 * kWaveRows;  // rows of a tile
 constexpr int kLdA = kTK + 8;           // LDS row stride of the activation tile (bf16)
 
-struct PpLds {
-  __bf16 a[2][kPpRows][kLdA];
+struct TileLds {
+  __bf16 a[2][kTileRows][kLdA];
   __bf16 b[2][2][kTN][kLdB];  // [group][buffer]
-  int pair[kPpRows];
+  int pair[kTileRows];
 };
 
 template <int QT, bool GATEUP, bool SPLIT, int G>
 __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* __restrict__ x, int2 tl, int ntp,
-                                        __bf16* __restrict__ hbuf, PpLds& L) {
+                                        __bf16* __restrict__ hbuf, TileLds& L) {
   constexpr int kUnits = 2;  // half blocks staged per thread and K step: 128 rows x 2 blocks x 2 halves / 256
   const int tid = threadIdx.x, ltid = tid & 255;
   const int lane = tid & (kWave - 1), wave = ltid >> 6, quad = lane >> 4;
   const int e = tl.x, m0 = tl.y;
   const int pbeg = p.offsets[e];
-  const int rows = min(kPpRows, p.offsets[e + 1] - pbeg - m0);
+  const int rows = min(kTileRows, p.offsets[e + 1] - pbeg - m0);
   const int slot = p.slot_table[e];
   const int K = GATEUP ? p.H : p.I;
   const int nt_i = 2 * ntp + G;
   const int n0 = GATEUP ? nt_i * (kTN / 2) : nt_i * kTN;
-  for (int r = tid; r < kPpRows; r += 512) L.pair[r] = r < rows ? p.sorted_pairs[pbeg + m0 + r] : 0;
+  for (int r = tid; r < kTileRows; r += 512) L.pair[r] = r < rows ? p.sorted_pairs[pbeg + m0 + r] : 0;
   __syncthreads();
   if (slot < 0 || slot >= p.n_slots) {  // both groups see the same expert
     if (tid == 0) atomicCAS(p.err, 0, e + 1);
@@ -223,7 +225,7 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
   else
     wrow = slotp + slot_down_off(QT, p.H, p.I) + (size_t)(n0 + brow) * row_bytes(QT, p.I);
   const int scol = 32 * bblk + 16 * (v0 & 1);
-  using WS = WStage<QT, (kPrefillFlagsPp & 2) != 0>;
+  using WS = WStage<QT, kDequantPermute>;
   WS st[2][kUnits];
   auto load_w = [&](WS (&s_)[kUnits], int kc) {
     const int b = 2 * min(kc, nk - 1) + bblk;
@@ -361,7 +363,7 @@ template <int QT, bool GATEUP>
 __global__ __launch_bounds__(512, 1) void prefill_gemm_kernel(FfnParams p, const __bf16* __restrict__ x,
                                                           const int2* __restrict__ tiles, const int* __restrict__ count,
                                                           int ntn, __bf16* __restrict__ hbuf) {
-  __shared__ __attribute__((aligned(16))) PpLds L;
+  __shared__ __attribute__((aligned(16))) TileLds L;
   const int nth = ntn / 2;
   const int j = blockIdx.x / kXcds;
   const int mt_i = kXcds * (j / nth) + (int)(blockIdx.x % kXcds);
@@ -393,9 +395,7 @@ bool prefill_mfma_supported(int H, int I) {
 // tiles in step, without phases (390 us); phases with the activation rows
 // in registers rather than LDS (387-392 us); the dequantisation interleaved
 // into the MFMAs by scheduling hints (366 us).
-constexpr int kPrefillRows = kPpRows;
-
-static int prefill_max_tiles(size_t P, int E) { return (int)(P / kPrefillRows) + E + 1; }
+static int prefill_max_tiles(size_t P, int E) { return (int)(P / kTileRows) + E + 1; }
 
 size_t prefill_ws_bytes(int T, int k, int I, int E) {
   const size_t P = (size_t)T * k;
@@ -430,7 +430,7 @@ int launch_ffn_prefill(moe_ctx* ctx, const FfnParams& p, const void* x, void* ws
   const unsigned row_groups = (unsigned)((max_tiles + kXcds - 1) / kXcds);
   {
     KernelTimer timer(ctx, "prefill_tiles", s);
-    launch(prefill_tiles_kernel, 1, 256, 0, s, p.offsets, p.mask, p.E, kPrefillRows, kWaveRows, tiles, count);
+    launch(prefill_tiles_kernel, 1, 256, 0, s, p.offsets, p.mask, p.E, kTileRows, kWaveRows, tiles, count);
   }
   int rc = check_launch("prefill_tiles_kernel");
   if (rc) return rc;
