@@ -107,45 +107,60 @@ struct BRaw {
 // acc[c] += rows' activations (A, 16 x K from `arow`) times the weight rows
 // brow[c] (16 columns each) over blocks b_beg .. b_end - 1.  The loads run
 // kDepth blocks ahead of the matrix instructions, in a ring of registers
-// indexed at compile time.
+// indexed at compile time; every load is issued on every path (no branch
+// around a load), so the wait before each block counts only the loads
+// issued after it and the ring stays in flight (a ring whose loads sat
+// under branches waited for all of them at the loop head: 75 -> 73 us for
+// gate/up and 42 -> 39 us for down at 64 tokens of 512 experts).
 constexpr int kDepth = 4;
 template <int QT, int NB>
-__device__ __forceinline__ void mfma_rows(const float* arow, bool arow_ok, const uint8_t* const (&brow)[NB],
-                                          int b_beg, int b_end, int g, mf32x4 (&acc)[NB]) {
+__device__ __forceinline__ void mfma_rows(const float* arow, const uint8_t* const (&brow)[NB], int b_beg, int b_end,
+                                          int g, mf32x4 (&acc)[NB]) {
+  if (b_beg >= b_end) return;
   float4 a0[kDepth], a1[kDepth];
   BRaw<QT> raw[kDepth][NB];
+  // every load unconditional (rows past the tile read a valid row; block
+  // indices past the range clamp), so the wait before a block counts only
+  // the loads issued after it
   auto load = [&](int u, int b) {
-    if (arow_ok) {
-      a0[u] = *reinterpret_cast<const float4*>(arow + 32 * b + 4 * g);
-      a1[u] = *reinterpret_cast<const float4*>(arow + 32 * b + 16 + 4 * g);
-    } else {
-      a0[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      a1[u] = a0[u];
-    }
+    b = min(b, b_end - 1);
+    a0[u] = *reinterpret_cast<const float4*>(arow + 32 * b + 4 * g);
+    a1[u] = *reinterpret_cast<const float4*>(arow + 32 * b + 16 + 4 * g);
 #pragma unroll
     for (int c = 0; c < NB; ++c) raw[u][c].load(brow[c], b, g);
   };
+  auto block = [&](int u) {
+    const float av[2][4] = {{a0[u].x, a0[u].y, a0[u].z, a0[u].w}, {a1[u].x, a1[u].y, a1[u].z, a1[u].w}};
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u)
-    if (b_beg + u < b_end) load(u, b_beg + u);
-  for (int b0 = b_beg; b0 < b_end; b0 += kDepth) {
+    for (int c = 0; c < NB; ++c) {
+      float wv[2][4];
+      raw[u][c].dequant(wv);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s][q], wv[s][q], acc[c], 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) {
+    load(u, b_beg + u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int b0 = b_beg;
+  // full groups whose successors exist: consume a slot, refill it
+  for (; b0 + kDepth < b_end; b0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      if (b0 + u >= b_end) break;
-      const float av[2][4] = {{a0[u].x, a0[u].y, a0[u].z, a0[u].w}, {a1[u].x, a1[u].y, a1[u].z, a1[u].w}};
-#pragma unroll
-      for (int c = 0; c < NB; ++c) {
-        float wv[2][4];
-        raw[u][c].dequant(wv);
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s][q], wv[s][q], acc[c], 0, 0, 0);
-      }
-      if (b0 + kDepth + u < b_end) load(u, b0 + kDepth + u);
+      block(u);
+      load(u, b0 + kDepth + u);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the last group: no more loads
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u)
+    if (b0 + u < b_end) block(u);
 }
 
 // A workgroup takes one tile item at a time; its four wavefronts split the
@@ -211,13 +226,14 @@ __global__ __launch_bounds__(kMfmaThreads) void ffn_gateup_mfma(FfnParams p, con
       for (int s = threadIdx.x; s < rows * 16; s += kMfmaThreads) p.hbuf[(size_t)(pbeg + s / 16) * p.I + i0 + s % 16] = NAN;
       continue;
     }
-    const bool ok = j < rows;  // this lane's A row (pair j of the tile)
-    const int pair = ctl.pairs[pbeg + (ok ? j : 0)];
+    // this lane's A row: pair j of the tile (rows past the tile read pair 0's
+    // row; their outputs are not stored)
+    const int pair = ctl.pairs[pbeg + (j < rows ? j : 0)];
     const float* arow = x + (size_t)(pair / p.k) * p.H;
     const uint8_t* base = p.pool + (size_t)slot * p.slot_bytes;
     const uint8_t* brow[2] = {base + gate_off + (size_t)(i0 + j) * rbytes, base + up_off + (size_t)(i0 + j) * rbytes};
     mf32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    mfma_rows<QT, 2>(arow, ok, brow, b_beg, b_end, g, acc);
+    mfma_rows<QT, 2>(arow, brow, b_beg, b_end, g, acc);
     split_reduce(sl, acc, w, lane);
     if (w == 0) {
 #pragma unroll
@@ -262,12 +278,11 @@ __global__ __launch_bounds__(kMfmaThreads) void ffn_down_mfma(FfnParams p) {
       for (int s = threadIdx.x; s < rows * 32; s += kMfmaThreads) p.y[(size_t)ctl.pairs[pbeg + s / 32] * p.H + h0 + s % 32] = NAN;
       continue;
     }
-    const bool ok = j < rows;
-    const float* arow = p.hbuf + (size_t)(pbeg + (ok ? j : 0)) * p.I;
+    const float* arow = p.hbuf + (size_t)(pbeg + (j < rows ? j : 0)) * p.I;
     const uint8_t* base = p.pool + (size_t)slot * p.slot_bytes + down_off;
     const uint8_t* brow[2] = {base + (size_t)(h0 + j) * rbytes, base + (size_t)(h0 + 16 + j) * rbytes};
     mf32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    mfma_rows<QT, 2>(arow, ok, brow, b_beg, b_end, g, acc);
+    mfma_rows<QT, 2>(arow, brow, b_beg, b_end, g, acc);
     split_reduce(sl, acc, w, lane);
     if (w == 0) {
 #pragma unroll
