@@ -202,7 +202,8 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
   }
   const int nk = K / kTK;  // even (checked on the host)
   // activation staging: this group's half of the rows, eight lanes per row
-  // (16 bytes each), 32 rows per round, four rounds; rows past the tile read row 0
+  // (16 bytes each), 32 rows per round, four rounds; rows past the tile are
+  // neither fetched nor written (their products land in rows never stored)
   const int a_chunk = ltid & 7;
   const __bf16* asrc[4];
 #pragma unroll
@@ -212,15 +213,17 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
     asrc[i] = (GATEUP ? x + (size_t)(L.pair[rr] / p.k) * p.H : hbuf + (size_t)(pbeg + m0 + rr) * p.I) + 8 * a_chunk;
   }
   bf16x8 areg[2][4];
+  const int a_rows = rows - 128 * G - (ltid >> 3);  // this lane's row r is staged when 32 i < a_rows
   auto load_a = [&](bf16x8 (&ar)[4], int kc) {
     const size_t koff = (size_t)min(kc, nk - 1) * kTK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ar[i] = *reinterpret_cast<const bf16x8*>(asrc[i] + koff);
+    for (int i = 0; i < 4; ++i)
+      if (32 * i < a_rows) ar[i] = *reinterpret_cast<const bf16x8*>(asrc[i] + koff);
   };
   auto store_a = [&](const bf16x8 (&ar)[4], int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<bf16x8*>(&L.a[buf][128 * G + (ltid >> 3) + 32 * i][8 * a_chunk]) = ar[i];
+      if (32 * i < a_rows) *reinterpret_cast<bf16x8*>(&L.a[buf][128 * G + (ltid >> 3) + 32 * i][8 * a_chunk]) = ar[i];
   };
   // weight staging: unit v = ltid * kUnits + u is row v / 4, block (v / 2) % 2, half v % 2
   const int v0 = ltid * kUnits;
@@ -268,6 +271,7 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{};
   const int row0 = SPLIT ? 0 : kWaveRows * wave;
   const bool active = row0 < rows;
+  const int split_mt = (rows + 15) >> 4;  // a tail's 16-row blocks holding rows
   auto phase_end = [] {
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -289,6 +293,7 @@ __device__ __forceinline__ void prefill_tile(const FfnParams& p, const __bf16* _
           const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sb[16 * (wave + 4) + (lane & 15)][32 * ks + 8 * quad]);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
+            if (mt >= split_mt) break;  // 16-row blocks past the tail
             acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b0, acc[mt][0], 0, 0, 0);
             acc[mt][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b1, acc[mt][4], 0, 0, 0);
           }
