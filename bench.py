@@ -273,7 +273,44 @@ def prefill_extra(ctx, steps=10, warmup=3, qtype=None):
         run()
     ev1.record()
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
+    ms_eager = ev0.elapsed_time(ev1) / steps
+    # The same layer as a HIP graph, as a serving loop would issue it (no
+    # launch gaps between its kernels).  Every replay's output is checked bit
+    # for bit against the eager one, with eager forwards between replays.
+    out_eager = buf.out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    graph_ok = True
+    for _ in range(3):
+        buf.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        graph_ok &= bool(torch.equal(buf.out, out_eager))
+        run()
+        torch.cuda.synchronize()
+        graph_ok &= bool(torch.equal(buf.out, out_eager))
+    if not graph_ok:
+        raise RuntimeError("prefill layer: a graph replay differs from the eager forward")
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    graph_ok &= bool(torch.equal(buf.out, out_eager))
+    if not graph_ok:
+        raise RuntimeError("prefill layer: a graph replay differs from the eager forward")
     moe.moe_ctx_set_timing(ctx, True)
     for _ in range(3):
         run()
@@ -293,6 +330,8 @@ def prefill_extra(ctx, steps=10, warmup=3, qtype=None):
     gu_tflops = gate_up_flops / (gu_ms * 1e-3) / 1e12 if gu_ms else None
     return {
         "workload": wl.name, "tokens": T, "layer_ms": ms, "tokens_per_s": T / (ms * 1e-3),
+        "timing": "hip graph of the layer, replayed; every replay equal bit for bit to the eager forward",
+        "median_layer_ms": per[steps // 2], "layer_ms_eager": ms_eager, "tokens_per_s_eager": T / (ms_eager * 1e-3),
         "kernel_ms": kt, "ffn_tflops": tflops, "ffn_frac_bf16_peak": tflops / BF16_PEAK_TFLOPS if tflops else None,
         "gateup_tflops": gu_tflops,
         "flops_per_layer": flops,
