@@ -440,6 +440,53 @@ def test_prefill_full_compare(ctx, prefill_layer, T):
     _check_layer(buf, out, ref, PREFILL_TOL, T)
 
 
+def test_prefill_layer_graph_replays(ctx, prefill_layer):
+    """The prefill layer (routing on given logits, permutation, both grouped
+    GEMMs, combine) captured as one HIP graph, as the bench replays it: every
+    replay, with the outputs poisoned before it and an eager forward after
+    it, equals the eager forward bit for bit, and the eager forward is within
+    the prefill tolerance of the oracle.  1000 tokens: partial tiles and
+    tails."""
+    wl, T = prefill_layer.wl, 1000
+    note(f"prefill graph replays T={T}")
+    logits, xbits, x32 = _prefill_inputs(wl, T)
+    from gpu_util import bf16_tensor
+    xd, ld = bf16_tensor(xbits), dev(logits)
+    buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV, mode=L.MODE_PREFILL,
+                             x_dtype=L.DTYPE_BF16)
+
+    def run():
+        layer.forward(ctx, buf, prefill_layer.pool.base(), prefill_layer.pool.slot_bytes, prefill_layer.pool.n_slots,
+                      prefill_layer.slot_table, xd, logits_in=ld)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    s.synchronize()
+    moe.moe_ctx_check(ctx)
+    eager = {n: getattr(buf, n).clone() for n in ("ids", "w", "offsets", "sorted_pairs", "y", "out")}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for rep in range(3):
+        for n in ("w", "y", "out"):
+            getattr(buf, n).fill_(float("nan"))
+        buf.ids.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        moe.moe_ctx_check(ctx)
+        for n, want in eager.items():
+            assert torch.equal(getattr(buf, n), want), f"replay {rep}: {n} differs from the eager forward"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(buf.out, eager["out"])
+    ref = oracle.moe_layer(x32, wl.qtype, prefill_layer.get_blocks, wl.k, logits=logits)
+    np.testing.assert_array_equal(buf.ids.cpu().numpy(), ref["ids"])
+    _check_layer(buf, buf.out.cpu().numpy(), ref, PREFILL_TOL, T)
+
+
 @pytest.mark.parametrize("T", [300, 2048])
 def test_prefill_not_resident_expert(ctx, prefill_layer, T):
     """An expert whose slot is -1 in the prefill GEMM: reported by id, its
