@@ -18,14 +18,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (h >= H) return;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int j = 0; j < k; ++j) {
-      const float wj = wt[j];
-      const float4 v = *reinterpret_cast<const float4*>(yt + (size_t)j * H + h);
+    auto add = [&](float wj, const float4& v) {
       acc.x = fmaf(wj, v.x, acc.x);
       acc.y = fmaf(wj, v.y, acc.y);
       acc.z = fmaf(wj, v.z, acc.z);
       acc.w = fmaf(wj, v.w, acc.w);
-    }
+    };
+    // the first (up to) eight pairs' rows are all requested before the
+    // first product, so their latencies overlap; the sum keeps j ascending
+    constexpr int kAhead = 8;
+    float4 v[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (j < k) v[j] = *reinterpret_cast<const float4*>(yt + (size_t)j * H + h);
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (j < k) add(wt[j], v[j]);
+    for (int j = kAhead; j < k; ++j) add(wt[j], *reinterpret_cast<const float4*>(yt + (size_t)j * H + h));
     *reinterpret_cast<float4*>(out + (size_t)t * H + h) = acc;
   } else {
     const int h = blockIdx.x * 256 + threadIdx.x;
