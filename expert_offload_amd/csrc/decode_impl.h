@@ -429,17 +429,31 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
     }
     return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "int8-activation decode: block type %d", QT);
   }
-  // experts with many tokens of the batch on the matrix cores (fp32)
+  // experts with many tokens of the batch on the matrix cores (fp32): their
+  // gate/up and down kernels run on the context's side stream, beside the
+  // GEMV gate/up of the other experts (they share no data), and are joined
+  // before the down GEMV kernel, whose combine reads their y rows
   FfnParams q = p;
   const bool mix = mfma_decode_type(QT) && !route && p.T >= kMfmaMinBatch;
   const int grid_mx = 4 * ctx->num_cus;  // persistent: items in turn
+  hipStream_t ms = s;
   if (mix) {
     q.mfma_min = kMfmaMinPairs;
+    hipError_t e;
+    if ((e = hipEventRecord(ctx->fork_ev, s)) != hipSuccess) return hip_error(e, "hipEventRecord(fork)");
+    if ((e = hipStreamWaitEvent(ctx->side, ctx->fork_ev, 0)) != hipSuccess) return hip_error(e, "hipStreamWaitEvent(fork)");
+    ms = ctx->side;
     if constexpr (mfma_decode_type(QT)) {
-      KernelTimer timer(ctx, "ffn_gateup_mfma", s);
-      launch(ffn_gateup_mfma<QT>, grid_mx, kMfmaThreads, 0, s, q, x);
+      KernelTimer timer(ctx, "ffn_gateup_mfma", ms);
+      launch(ffn_gateup_mfma<QT>, grid_mx, kMfmaThreads, 0, ms, q, x);
     }
     if ((rc = check_launch("ffn_gateup_mfma"))) return rc;
+    if constexpr (mfma_decode_type(QT)) {
+      KernelTimer timer(ctx, "ffn_down_mfma", ms);
+      launch(ffn_down_mfma<QT>, grid_mx, kMfmaThreads, 0, ms, q);
+    }
+    if ((rc = check_launch("ffn_down_mfma"))) return rc;
+    if ((e = hipEventRecord(ctx->join_ev, ms)) != hipSuccess) return hip_error(e, "hipEventRecord(join)");
   }
   {
     KernelTimer timer(ctx, "ffn_gateup", s);
@@ -448,11 +462,8 @@ int launch_ffn_decode_t(moe_ctx* ctx, const FfnParams& p, const float* x, hipStr
   rc = check_launch("ffn_gateup_decode");
   if (rc) return rc;
   if (mix) {
-    if constexpr (mfma_decode_type(QT)) {
-      KernelTimer timer(ctx, "ffn_down_mfma", s);
-      launch(ffn_down_mfma<QT>, grid_mx, kMfmaThreads, 0, s, q);
-    }
-    if ((rc = check_launch("ffn_down_mfma"))) return rc;
+    hipError_t e;
+    if ((e = hipStreamWaitEvent(s, ctx->join_ev, 0)) != hipSuccess) return hip_error(e, "hipStreamWaitEvent(join)");
   }
   {
     KernelTimer timer(ctx, "ffn_down", s);

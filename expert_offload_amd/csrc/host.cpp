@@ -127,6 +127,16 @@ int moe_ctx_create(int device, moe_ctx** out) {
     delete c;
     return rc;
   }
+  if ((e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming)) != hipSuccess) {
+    if (c->join_ev) (void)hipEventDestroy(c->join_ev);
+    if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
+    if (c->side) (void)hipStreamDestroy(c->side);
+    (void)hipFree(c->d_err);
+    delete c;
+    return hip_error(e, "moe_ctx_create: side stream and events");
+  }
   *out = c;
   return MOE_OK;
 }
@@ -172,6 +182,9 @@ int moe_ctx_destroy(moe_ctx* ctx) {
     (void)hipEventDestroy(r.stop);
   }
   for (auto e : ctx->spare_events) (void)hipEventDestroy(e);
+  if (ctx->join_ev) (void)hipEventDestroy(ctx->join_ev);
+  if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
+  if (ctx->side) (void)hipStreamDestroy(ctx->side);
   if (ctx->d_err) (void)hipFree(ctx->d_err);
   delete ctx;
   return MOE_OK;

@@ -24,6 +24,10 @@ struct moe_ctx {
   bool timing = false;
   std::vector<moe_timing_rec> recs;
   std::vector<hipEvent_t> spare_events;
+  // a second stream (default priority) on which kernels independent of the
+  // caller's stream's next ones run, forked and joined with these events
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
 };
 
 namespace moe {

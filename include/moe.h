@@ -104,9 +104,15 @@ const char* moe_last_error(void);
 
 /* ---------------------------------------------------------------- context
  * moe_ctx_create: binds device `device`, allocates the 4-byte device error
- * word.  moe_ctx_check: waits for `stream`, reads and clears the error word;
+ * word, and creates a second stream (default priority, non-blocking) with
+ * two events: decode batches of 32 or more tokens run the matrix-core
+ * experts' kernels there, forked from and joined back into the caller's
+ * stream within the call (this also holds under HIP graph capture).  Calls
+ * that share a context are issued from one host thread at a time.
+ * moe_ctx_check: waits for `stream`, reads and clears the error word;
  * returns MOE_ERR_NOT_RESIDENT if a kernel met a slot of -1 since the last
- * check (the message names the expert).  moe_ctx_destroy frees the word. */
+ * check (the message names the expert).  moe_ctx_destroy frees the word,
+ * the stream and the events. */
 int moe_ctx_create(int device, moe_ctx** out);
 int moe_ctx_destroy(moe_ctx* ctx);
 int moe_ctx_check(moe_ctx* ctx, void* stream);
