@@ -116,3 +116,45 @@ def test_mfma_expert_without_slot(ctx, mlayer):
     assert np.isnan(got["y"][rows]).all()
     others = np.nonzero(ids != 1)[0]
     assert not np.isnan(got["y"][others]).any()
+
+
+def test_mfma_layer_graph_replays(ctx, mlayer):
+    """The 64-token layer with matrix-core experts, whose kernels the library
+    forks onto its side stream and joins back within the call, captured as a
+    HIP graph (the fork and join become graph edges): every replay, with the
+    outputs poisoned before it and an eager call after it, equals the eager
+    call bit for bit."""
+    wl = mlayer.wl
+    T = 64
+    x, lg = dev(gi.activations(wl, T)), dev(_logits(T, wl.E, wl.k))
+    buf = layer.LayerBuffers(T, wl.H, wl.I, wl.E, wl.k, wl.qtype, device=DEV)
+
+    def run():
+        layer.forward(ctx, buf, mlayer.pool.base(), mlayer.pool.slot_bytes, mlayer.pool.n_slots, mlayer.slot_table,
+                      x, logits_in=lg, fused="layer")
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    s.synchronize()
+    moe.moe_ctx_check(ctx)
+    names = ("ids", "w", "y", "out")
+    eager = {n: getattr(buf, n).clone() for n in names}
+    assert not torch.isnan(eager["out"]).any()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for rep in range(3):
+        for n in ("w", "y", "out"):
+            getattr(buf, n).fill_(float("nan"))
+        buf.ids.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        moe.moe_ctx_check(ctx)
+        for n in names:
+            assert torch.equal(getattr(buf, n), eager[n]), f"replay {rep}: {n} differs from the eager call"
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(buf.out, eager["out"])
