@@ -205,18 +205,28 @@ static hsa_status_t find_agents(hsa_agent_t a, void* data) {
   return HSA_STATUS_SUCCESS;
 }
 
+namespace moe {
+bool hsa_agents_of(int device, hsa_agent_t* gpu, hsa_agent_t* cpu) {
+  AgentSearch q{};
+  if (hipDeviceGetAttribute(&q.domain, hipDeviceAttributePciDomainID, device) != hipSuccess ||
+      hipDeviceGetAttribute(&q.bus, hipDeviceAttributePciBusId, device) != hipSuccess ||
+      hipDeviceGetAttribute(&q.device, hipDeviceAttributePciDeviceId, device) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (hsa_iterate_agents(find_agents, &q) != HSA_STATUS_SUCCESS || !q.have_gpu || !q.have_cpu) return false;
+  *gpu = q.gpu;
+  *cpu = q.cpu;
+  return true;
+}
+}  // namespace moe
+
 // The HSA agents of the cache's device and of the host, and the signals.
 static void hsa_setup(moe_cache* c) {
   if (c->hsa_ok) return;
-  AgentSearch q{};
-  if (hipDeviceGetAttribute(&q.domain, hipDeviceAttributePciDomainID, c->device) != hipSuccess ||
-      hipDeviceGetAttribute(&q.bus, hipDeviceAttributePciBusId, c->device) != hipSuccess ||
-      hipDeviceGetAttribute(&q.device, hipDeviceAttributePciDeviceId, c->device) != hipSuccess) {
-    (void)hipGetLastError();
-    return;
-  }
   if (hsa_init() != HSA_STATUS_SUCCESS) return;
-  if (hsa_iterate_agents(find_agents, &q) != HSA_STATUS_SUCCESS || !q.have_gpu || !q.have_cpu) {
+  hsa_agent_t gpu{}, cpu{};
+  if (!hsa_agents_of(c->device, &gpu, &cpu)) {
     hsa_shut_down();
     return;
   }
@@ -228,8 +238,8 @@ static void hsa_setup(moe_cache* c) {
     hsa_shut_down();
     return;
   }
-  c->hsa_gpu = q.gpu;
-  c->hsa_cpu = q.cpu;
+  c->hsa_gpu = gpu;
+  c->hsa_cpu = cpu;
   c->slot_sig.assign(c->slot_key.size(), -1);
   c->hsa_ok = true;
 }

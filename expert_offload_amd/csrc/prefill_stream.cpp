@@ -9,12 +9,24 @@
 //
 // Per call for layer l: if no buffer holds l, it is copied now into the
 // buffer the previous layer did not use (demand load).  The routing runs on
-// the compute stream at once (it needs no expert bytes), the compute stream
-// then waits for l's copy and runs the FFN and the combine out of that
-// buffer, and a done-event marks the buffer free.  Then layer l+1 is copied
-// into the other buffer on the copy stream, after the layer that last read
-// that buffer has finished.
+// the compute stream at once (it needs no expert bytes), then the FFN and
+// the combine run out of that buffer once l's copy has landed, and a
+// done-event marks the buffer free.  Then layer l+1 is copied into the
+// other buffer, after the layer that last read that buffer has finished.
+//
+// The copies are HSA asynchronous copies (the DMA engines, with one
+// completion signal per buffer), waited for on the host: they put no packet
+// into any HIP queue, so the copy and the compute overlap however HIP maps
+// streams onto hardware queues (two streams that share one queue run their
+// work in order).  The cost is that a call returns only once its layer's
+// copy has landed and the next layer's copy has been issued, i.e. after
+// the previous layer's FFN.  Without the HSA runtime, or with
+// MOE_STREAM_HIP_COPY set in the environment at create time, the copies are
+// hipMemcpyAsync calls on the caller's copy stream ordered by events.
+#include <cstdlib>
 #include <vector>
+
+#include <hsa/hsa_ext_amd.h>
 
 #include "moe_internal.h"
 
@@ -32,9 +44,59 @@ struct moe_prefill_stream {
   hipEvent_t copy_ev[2] = {}, done_ev[2] = {};
   int last_buf = -1;
   int64_t loads = 0, demand_loads = 0;
+  bool hsa_ok = false;  // copies through the HSA runtime
+  hsa_agent_t hsa_gpu{}, hsa_cpu{};
+  hsa_signal_t sig[2] = {};  // 1 while a copy into the buffer is in flight
 };
 
+static void sig_wait(const moe_prefill_stream* s, int b) {
+  while (hsa_signal_wait_scacquire(s->sig[b], HSA_SIGNAL_CONDITION_EQ, 0, UINT64_MAX, HSA_WAIT_STATE_BLOCKED) != 0) {
+  }
+}
+
+static void hsa_setup(moe_prefill_stream* s) {
+  const char* env = std::getenv("MOE_STREAM_HIP_COPY");
+  if (env && *env && *env != '0') return;
+  if (hsa_init() != HSA_STATUS_SUCCESS) return;
+  if (!hsa_agents_of(s->device, &s->hsa_gpu, &s->hsa_cpu)) {
+    hsa_shut_down();
+    return;
+  }
+  if (hsa_signal_create(0, 0, nullptr, &s->sig[0]) != HSA_STATUS_SUCCESS) {
+    hsa_shut_down();
+    return;
+  }
+  if (hsa_signal_create(0, 0, nullptr, &s->sig[1]) != HSA_STATUS_SUCCESS) {
+    hsa_signal_destroy(s->sig[0]);
+    hsa_shut_down();
+    return;
+  }
+  s->hsa_ok = true;
+}
+
+static int load_layer_hsa(moe_prefill_stream* s, int b, int layer) {
+  hipError_t e;
+  // after the last reader of the buffer and after an earlier copy into it
+  if (s->used[b] && (e = hipEventSynchronize(s->done_ev[b])) != hipSuccess)
+    return hip_error(e, "hipEventSynchronize(buffer free)");
+  sig_wait(s, b);
+  hsa_signal_store_screlease(s->sig[b], 1);
+  const hsa_status_t st =
+      hsa_amd_memory_async_copy(s->d_bufs + (size_t)b * s->layer_bytes, s->hsa_gpu,
+                                s->h_pool + (size_t)layer * s->layer_bytes, s->hsa_cpu, s->layer_bytes, 0, nullptr,
+                                s->sig[b]);
+  if (st != HSA_STATUS_SUCCESS) {
+    hsa_signal_store_screlease(s->sig[b], 0);
+    s->buf_layer[b] = -1;
+    return set_error(MOE_ERR_HIP, "hsa_amd_memory_async_copy(layer experts) failed (status %d)", (int)st);
+  }
+  s->buf_layer[b] = layer;
+  ++s->loads;
+  return MOE_OK;
+}
+
 static int load_layer(moe_prefill_stream* s, int b, int layer, hipStream_t cs) {
+  if (s->hsa_ok) return load_layer_hsa(s, b, layer);
   hipError_t e;
   // after the last reader of the buffer, and after an earlier copy into it
   // that may sit on another copy stream
@@ -99,6 +161,7 @@ int prefill_stream_create(int L, int E, int qtype, int H, int I, void* d_bufs, c
       return hip_error(e, "hipEventCreate");
     }
   }
+  hsa_setup(s);
   *out = s;
   return MOE_OK;
 }
@@ -107,6 +170,13 @@ int prefill_stream_destroy(moe_prefill_stream* s) {
   clear_error();
   if (!s) return MOE_OK;
   (void)hipDeviceSynchronize();
+  if (s->hsa_ok) {
+    for (int b = 0; b < 2; ++b) {
+      sig_wait(s, b);
+      hsa_signal_destroy(s->sig[b]);
+    }
+    hsa_shut_down();
+  }
   for (int b = 0; b < 2; ++b) {
     if (s->copy_ev[b]) (void)hipEventDestroy(s->copy_ev[b]);
     if (s->done_ev[b]) (void)hipEventDestroy(s->done_ev[b]);
@@ -158,7 +228,10 @@ int prefill_stream_layer(moe_prefill_stream* s, moe_ctx* ctx, int layer, const m
                          const_cast<int32_t*>(args->expert_offsets), const_cast<int32_t*>(args->sorted_pairs),
                          pair_pos, const_cast<int32_t*>(args->active), route_ws, route_ws_bytes, compute_stream);
   if (rc) return rc;
-  if ((e = hipStreamWaitEvent(ks, s->copy_ev[b], 0)) != hipSuccess) return hip_error(e, "hipStreamWaitEvent(copy)");
+  if (s->hsa_ok)
+    sig_wait(s, b);
+  else if ((e = hipStreamWaitEvent(ks, s->copy_ev[b], 0)) != hipSuccess)
+    return hip_error(e, "hipStreamWaitEvent(copy)");
   moe_ffn_args a = *args;
   a.pool_base = s->d_bufs + (size_t)b * s->layer_bytes;
   a.slot_bytes = s->slot_bytes;

@@ -424,7 +424,8 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x,
  *   h_pool   pinned host memory, experts [L][E] in the device slot layout
  *            (the expert cache's host pool layout), caller-owned; not
  *            pinned -> MOE_ERR_NOT_PINNED.
- * The stream object owns an identity slot table and four events.
+ * The stream object owns an identity slot table, four events and two HSA
+ * signals.
  *
  * prefill_stream_layer: one layer's forward with its experts streamed.  If
  * no buffer holds `layer` it is copied now (a demand load, counted) into
@@ -437,10 +438,20 @@ int cache_decode_layer(moe_cache* c, moe_ctx* ctx, int layer, const float* x,
  * set and no expert_mask; args.pool_base, slot_bytes, n_slots and
  * slot_table are ignored, and args.H, I, E and qtype must equal the
  * stream's).  Then layer + 1, if it exists and is not held, is copied into
- * the other buffer with hipMemcpyAsync on copy_stream, after the last layer
- * that read that buffer has finished on its compute stream.  Calls in
- * layer order keep PCIe busy back to back; any order is correct.  Errors
- * as in the calls it makes.
+ * the other buffer, after the last layer that read that buffer has
+ * finished on its compute stream.  Calls in layer order keep PCIe busy back
+ * to back; any order is correct.  Errors as in the calls it makes.
+ * The copies are HSA asynchronous copies (DMA engines, completion signals
+ * waited for on the host), which enter no HIP queue and so overlap the
+ * compute whatever hardware queues HIP gives the streams; copy_stream is
+ * then unused, and the call blocks the host until its layer's copy has
+ * landed and until the previous call's layer has finished (before it
+ * issues the next copy).  Such calls cannot be captured in a HIP graph.
+ * Where the HSA runtime is unavailable, or MOE_STREAM_HIP_COPY is set to
+ * a nonzero value when the stream is created, the copies are
+ * hipMemcpyAsync calls on copy_stream ordered by events instead, and the
+ * call does not block.  Either way d_bufs and h_pool must outlive
+ * prefill_stream_destroy, which waits for every copy.
  *
  * prefill_stream_stats: layer copies issued in total and how many of them
  * were demand loads (not prefetched by the previous call). */

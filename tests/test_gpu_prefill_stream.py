@@ -1,6 +1,8 @@
 """Prefill layer streaming on the GPU: layers whose experts stream from a
 pinned host pool through two device buffers (prefill_stream_*) give the
-oracle's outputs, bit for bit the resident path's, in any call order."""
+oracle's outputs, bit for bit the resident path's, in any call order, with
+the copies as HSA asynchronous copies (the default) and as hipMemcpyAsync
+on the copy stream (MOE_STREAM_HIP_COPY=1 at create time)."""
 import numpy as np
 import pytest
 import torch
@@ -52,11 +54,14 @@ def resident_out(ctx, wl, blocks, l, T, xd, logits):
     return out.cpu().numpy()
 
 
-def test_streamed_layers_match_oracle(ctx):
+@pytest.mark.parametrize("copies", ["hsa", "hip"])
+def test_streamed_layers_match_oracle(ctx, copies, monkeypatch):
     """Three layers called in order twice, then out of order: every call of a
     layer gives the same bytes, equal to the resident path and within the
     prefill tolerance of the oracle; prefetches and demand loads are those
-    the dual-buffer schedule implies."""
+    the dual-buffer schedule implies.  The layers' experts differ, so a
+    buffer refilled while stale bytes of its previous layer were still
+    visible to the kernels would show here."""
     wl = SMALL
     T = wl.batches[0]
     pool, blocks = host_pool(wl)
@@ -64,7 +69,10 @@ def test_streamed_layers_match_oracle(ctx):
     x32, xd = gi.bf16_bits_to_f32(xbits), bf16_tensor(xbits)
     logits = [gi.given_logits(wl, T, l) for l in range(wl.layers)]
     logits_d = [dev(g) for g in logits]
+    if copies == "hip":
+        monkeypatch.setenv("MOE_STREAM_HIP_COPY", "1")
     sp = layer.StreamedPrefill(ctx, wl.qtype, wl.H, wl.I, wl.E, wl.k, wl.layers, T, pool)
+    monkeypatch.delenv("MOE_STREAM_HIP_COPY", raising=False)
     order = [0, 1, 2, 0, 1, 2, 2, 0, 1]
     outs, ids = [], []
     for l in order:
