@@ -31,6 +31,7 @@
 #include <hsa/hsa_ext_amd.h>
 
 #include "device_common.h"
+#include "hsa_copy.h"
 #include "ffn.h"
 
 namespace moe {

@@ -3,7 +3,6 @@
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
-#include <hsa/hsa.h>
 
 #include <cstddef>
 #include <cstdint>
@@ -174,12 +173,5 @@ int host_experts_ffn(int qtype, int H, int I, int n_exp, const uint8_t* const* s
                      const int* const* tok, const int* const* yrow, const float* x, float* y, float* h,
                      int threads, bool vector);
 int default_host_threads();
-
-// ------------------------------------------------------------ HSA copies
-// The HSA agents of HIP device `device` (matched by PCI domain, bus and
-// device) and of the host (the first CPU agent), for
-// hsa_amd_memory_async_copy.  The caller has called hsa_init.  False if
-// either is not found.
-bool hsa_agents_of(int device, hsa_agent_t* gpu, hsa_agent_t* cpu);
 
 }  // namespace moe

@@ -26,8 +26,7 @@
 #include <cstdlib>
 #include <vector>
 
-#include <hsa/hsa_ext_amd.h>
-
+#include "hsa_copy.h"
 #include "moe_internal.h"
 
 using namespace moe;
