@@ -22,7 +22,7 @@ Also reported on the same line:
   wide          wide-expert decode (hidden 2048, 512 experts, top-10,
                 intermediate 512, Q4_0, Zipf-biased router) at 1 and 64
                 tokens over 8 layer copies; HBM and fp32-VALU rooflines
-  block_types   every block type (Q8_0, Q5_1, Q5_0, Q4_1, Q4_0, Q4_K) on the
+  block_types   every block type (Q8_0, Q5_1, Q5_0, Q4_1, Q4_0, Q4_K, Q5_K) on the
                 decode shape (8 layers, T=1) and on the prefill layer
   cache         expert-cache decode: 8 layers (hidden 4096, 256 experts,
                 top-8, intermediate 2048, Q4_0) served from a pinned host
@@ -212,7 +212,7 @@ def types_extra(ctx, layers=8, steps=40, warmup=5):
     import torch
     from gen import inputs as gi
     out = {}
-    for qt in ("q8_0", "q5_1", "q5_0", "q4_1", "q4_0", "q4_k"):
+    for qt in ("q8_0", "q5_1", "q5_0", "q4_1", "q4_0", "q4_k", "q5_k"):
         wl = dataclasses.replace(gi.workload("decode_q8_0_h2048_e128"), qtype=qt, name=f"decode_{qt}_h2048_e128")
         stack = DecodeStack(ctx, wl, layers, distinct=32)
         x, bufs, _, gpu_ms = time_graph(stack, 1, steps, warmup)

@@ -134,6 +134,7 @@ extern "C" int moe_dequantize(moe_ctx* ctx, int qtype, const void* packed, int r
     MOE_DQ(MOE_QTYPE_Q5_0)
     MOE_DQ(MOE_QTYPE_Q5_1)
     MOE_DQ(MOE_QTYPE_Q4_K)
+    MOE_DQ(MOE_QTYPE_Q5_K)
     default: break;
   }
 #undef MOE_DQ

@@ -23,6 +23,7 @@ int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStrea
     case MOE_QTYPE_Q5_0: return launch_ffn_decode_q5_0(ctx, p, x, s, route);
     case MOE_QTYPE_Q5_1: return launch_ffn_decode_q5_1(ctx, p, x, s, route);
     case MOE_QTYPE_Q4_K: return launch_ffn_decode_q4_k(ctx, p, x, s, route);
+    case MOE_QTYPE_Q5_K: return launch_ffn_decode_q5_k(ctx, p, x, s, route);
     default: return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "decode: block type %d", p.qtype);
   }
 }

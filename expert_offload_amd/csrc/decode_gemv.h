@@ -110,7 +110,8 @@ struct RowTile {
         if constexpr (qtype_is_k(QT)) {  // codes, then scale and offset from one load
           const uint4 v = *reinterpret_cast<const uint4*>(block_quants<QT>(rows[r], lg + LPR * i));
           w[r][i][0] = v.x; w[r][i][1] = v.y; w[r][i][2] = v.z; w[r][i][3] = v.w;
-          q4k_block_dm(rows[r], lg + LPR * i, d[r][i], m[r][i]);
+          q4k_block_dm<QT>(rows[r], lg + LPR * i, d[r][i], m[r][i]);
+          if constexpr (Q::kQh) qh[r][i] = block_qh<QT>(rows[r], lg + LPR * i);
           continue;
         }
         load_block_raw<QT>(rows[r], lg + LPR * i, w[r][i], d[r][i]);

@@ -86,11 +86,13 @@ __device__ __forceinline__ int q4k_min_code(const uint8_t* sc, int j) {
   return j < 4 ? (sc[j + 4] & 63) : ((sc[j + 4] >> 4) | ((sc[j] >> 6) << 4));
 }
 
-// Q4_K sub-block b's scale d * scale_b and offset -dmin * min_b from one
+// K-quant sub-block b's scale d * scale_b and offset -dmin * min_b from one
 // 16-byte load of the group's tail (12 scale bytes, d, dmin).
+template <int QT>
 __device__ __forceinline__ void q4k_block_dm(const uint8_t* row, int b, float& d, float& m) {
-  const uint8_t* g = row + (size_t)(b >> 3) * kQ4KBytes;
-  const uint4 t = *reinterpret_cast<const uint4*>(g + group_ksc_off(MOE_QTYPE_Q4_K));
+  static_assert(qtype_is_k(QT) && group_ksc_off(QT) % 16 == 0 && group_bytes(QT) % 16 == 0, "16-byte tail load");
+  const uint8_t* g = row + (size_t)(b >> 3) * group_bytes(QT);
+  const uint4 t = *reinterpret_cast<const uint4*>(g + group_ksc_off(QT));
   const uint32_t w[3] = {t.x, t.y, t.z};
   const int j = b & 7;
   auto byte = [&](int i) -> int { return (int)((w[i >> 2] >> (8 * (i & 3))) & 0xFFu); };
@@ -102,7 +104,7 @@ __device__ __forceinline__ void q4k_block_dm(const uint8_t* row, int b, float& d
   m = -(dm * (float)mn);
 }
 
-// Q4_K: d * scale_j and -dmin * min_j are exact in fp32 (an 11-bit scale
+// K-quants: d * scale_j and -dmin * min_j are exact in fp32 (an 11-bit scale
 // times a 6-bit code).
 template <int QT>
 __device__ __forceinline__ float block_scale(const uint8_t* row, int b) {
@@ -145,7 +147,7 @@ __device__ __forceinline__ uint32_t spread_fifth_bits(uint32_t t) {
 
 // The 32 codes of block `b` as floats in logical element order: the signed
 // code q (w = d * q) for Q8_0 (int8), Q4_0 (u - 8), Q5_0 (u - 16); the
-// unsigned code u (w = d * u + m) for Q4_1, Q5_1 and Q4_K.
+// unsigned code u (w = d * u + m) for Q4_1, Q5_1, Q4_K and Q5_K.
 template <int QT>
 __device__ __forceinline__ void block_codes(const uint8_t* row, int b, float (&q)[32]) {
   const uint8_t* p = block_quants<QT>(row, b);

@@ -59,6 +59,7 @@ int launch_ffn_decode_q4_1(moe_ctx* ctx, const FfnParams& p, const float* x, hip
 int launch_ffn_decode_q5_0(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
 int launch_ffn_decode_q5_1(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
 int launch_ffn_decode_q4_k(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
+int launch_ffn_decode_q5_k(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s, const RouteArgs* route);
 int launch_ffn_decode(moe_ctx* ctx, const FfnParams& p, const float* x, hipStream_t s,
                       const RouteArgs* route = nullptr);
 // int8 block quantisation of n_blocks blocks of 32 floats at src (rows laid

@@ -196,6 +196,7 @@ int launch_ffn_valu(moe_ctx* ctx, const FfnParams& p, const void* x, int x_dtype
     case MOE_QTYPE_Q5_0: return launch_ffn_valu_t<MOE_QTYPE_Q5_0>(ctx, p, x, x_dtype, s);
     case MOE_QTYPE_Q5_1: return launch_ffn_valu_t<MOE_QTYPE_Q5_1>(ctx, p, x, x_dtype, s);
     case MOE_QTYPE_Q4_K: return launch_ffn_valu_t<MOE_QTYPE_Q4_K>(ctx, p, x, x_dtype, s);
+    case MOE_QTYPE_Q5_K: return launch_ffn_valu_t<MOE_QTYPE_Q5_K>(ctx, p, x, x_dtype, s);
     default: return set_error(MOE_ERR_UNSUPPORTED_QTYPE, "expert FFN: block type %d", p.qtype);
   }
 }

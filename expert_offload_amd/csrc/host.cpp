@@ -217,10 +217,11 @@ int moe_qtype_info(int qtype, int* block_elems, int* block_bytes) {
   clear_error();
   if (!qtype_supported(qtype))
     return set_error(MOE_ERR_UNSUPPORTED_QTYPE,
-                     "block type %d is not supported (Q4_0=%d, Q4_1=%d, Q5_0=%d, Q5_1=%d, Q8_0=%d, Q4_K=%d)", qtype,
-                     MOE_QTYPE_Q4_0, MOE_QTYPE_Q4_1, MOE_QTYPE_Q5_0, MOE_QTYPE_Q5_1, MOE_QTYPE_Q8_0, MOE_QTYPE_Q4_K);
+                     "block type %d is not supported (Q4_0=%d, Q4_1=%d, Q5_0=%d, Q5_1=%d, Q8_0=%d, Q4_K=%d, Q5_K=%d)",
+                     qtype, MOE_QTYPE_Q4_0, MOE_QTYPE_Q4_1, MOE_QTYPE_Q5_0, MOE_QTYPE_Q5_1, MOE_QTYPE_Q8_0, MOE_QTYPE_Q4_K,
+                     MOE_QTYPE_Q5_K);
   if (block_elems) *block_elems = qtype_is_k(qtype) ? kGroupWeights : kQK;
-  if (block_bytes) *block_bytes = qtype_is_k(qtype) ? kQ4KBytes : ggml_block_bytes(qtype);
+  if (block_bytes) *block_bytes = qtype_is_k(qtype) ? k_superblock_bytes(qtype) : ggml_block_bytes(qtype);
   return MOE_OK;
 }
 
@@ -242,17 +243,22 @@ int moe_slot_bytes(int qtype, int H, int I, size_t* out_bytes) {
   return MOE_OK;
 }
 
-// ggml Q4_K super-blocks [rows][cols/256] -> device groups: sub-block b's 32
-// codes (ggml: bytes 32 (b/2) + l, low nibble for even b, high for odd) as 16
-// bytes with element j in the low and element j + 16 in the high nibble of
-// byte j, then the 12 scale bytes, d and dmin unchanged.
-static void pack_matrix_q4_k(int rows, int cols, const uint8_t* src, uint8_t* dst) {
+// ggml K-quant super-blocks [rows][cols/256] -> device groups: sub-block
+// b's 32 codes (ggml: bytes 32 (b/2) + l of the nibbles, low nibble for even
+// b, high for odd) as 16 bytes with element j in the low and element j + 16
+// in the high nibble of byte j; Q5_K: then sub-block b's fifth bits (ggml:
+// bit b of qh byte l) as a word with bit l for element l; then the 12 scale
+// bytes, d and dmin unchanged.
+static void pack_matrix_k(int qtype, int rows, int cols, const uint8_t* src, uint8_t* dst) {
   const int groups = cols / kGroupWeights;
+  const int sbb = k_superblock_bytes(qtype);
+  const bool has_qh = qtype_has_qh(qtype);
+  const int qs_in = 16 + (has_qh ? 32 : 0);  // ggml: d, dmin, scales, [qh,] qs
   for (int r = 0; r < rows; ++r) {
     for (int g = 0; g < groups; ++g) {
-      const uint8_t* sb = src + ((size_t)r * groups + g) * kQ4KBytes;
-      uint8_t* d = dst + (size_t)r * row_bytes(MOE_QTYPE_Q4_K, cols) + (size_t)g * kQ4KBytes;
-      const uint8_t* qs = sb + 16;
+      const uint8_t* sb = src + ((size_t)r * groups + g) * sbb;
+      uint8_t* d = dst + (size_t)r * row_bytes(qtype, cols) + (size_t)g * group_bytes(qtype);
+      const uint8_t* qs = sb + qs_in;
       for (int b = 0; b < kGroupBlocks; ++b) {
         uint8_t code[32];
         for (int l = 0; l < 32; ++l) {
@@ -260,10 +266,15 @@ static void pack_matrix_q4_k(int rows, int cols, const uint8_t* src, uint8_t* ds
           code[l] = (b & 1) ? (v >> 4) : (v & 0x0F);
         }
         for (int j = 0; j < 16; ++j) d[16 * b + j] = (uint8_t)(code[j] | (code[j + 16] << 4));
+        if (has_qh) {
+          uint32_t word = 0;
+          for (int l = 0; l < 32; ++l) word |= (uint32_t)((sb[16 + l] >> b) & 1) << l;
+          std::memcpy(d + group_qh_off(qtype) + 4 * b, &word, 4);
+        }
       }
-      std::memcpy(d + group_ksc_off(MOE_QTYPE_Q4_K), sb + 4, 12);
-      std::memcpy(d + group_d_off(MOE_QTYPE_Q4_K), sb, 2);
-      std::memcpy(d + group_m_off(MOE_QTYPE_Q4_K), sb + 2, 2);
+      std::memcpy(d + group_ksc_off(qtype), sb + 4, 12);
+      std::memcpy(d + group_d_off(qtype), sb, 2);
+      std::memcpy(d + group_m_off(qtype), sb + 2, 2);
     }
   }
 }
@@ -271,7 +282,7 @@ static void pack_matrix_q4_k(int rows, int cols, const uint8_t* src, uint8_t* ds
 // ggml blocks [rows][cols/32] -> device layout (groups of 8 blocks: quant
 // bytes, fifth-bit words, scales d, offsets m).
 static void pack_matrix(int qtype, int rows, int cols, const uint8_t* src, uint8_t* dst) {
-  if (qtype_is_k(qtype)) return pack_matrix_q4_k(rows, cols, src, dst);
+  if (qtype_is_k(qtype)) return pack_matrix_k(qtype, rows, cols, src, dst);
   const int qb = quant_bytes_per_block(qtype);
   const int bb = ggml_block_bytes(qtype);
   const bool has_m = qtype_has_min(qtype), has_qh = qtype_has_qh(qtype);

@@ -77,11 +77,11 @@ inline uint32_t load_u32(const uint8_t* p) {
   return v;
 }
 
-// Q4_K: the 8 sub-blocks' scales d * scale_j and offsets -dmin * min_j of a
-// group (exact in fp32), from the super-block's fp16 d, dmin and the 6-bit
-// codes in its 12 packed bytes.
-inline void q4_k_group_scales(const uint8_t* grp, float (&d)[8], float (&m)[8]) {
-  constexpr int QT = MOE_QTYPE_Q4_K;
+// K-quants: the 8 sub-blocks' scales d * scale_j and offsets -dmin * min_j
+// of a group (exact in fp32), from the super-block's fp16 d, dmin and the
+// 6-bit codes in its 12 packed bytes.
+template <int QT>
+inline void k_group_scales(const uint8_t* grp, float (&d)[8], float (&m)[8]) {
   const uint8_t* sc = grp + group_ksc_off(QT);
   const float dd = half_to_float(load_u16(grp + group_d_off(QT)));
   const float dm = half_to_float(load_u16(grp + group_m_off(QT)));
@@ -101,7 +101,7 @@ float row_dot_scalar(const uint8_t* row, const float* x, const float* xs, int co
   for (int g = 0; g < cols / kGroupWeights; ++g) {
     const uint8_t* grp = row + (size_t)g * group_bytes(QT);
     float kd[8], km[8];
-    if constexpr (qtype_is_k(QT)) q4_k_group_scales(grp, kd, km);
+    if constexpr (qtype_is_k(QT)) k_group_scales<QT>(grp, kd, km);
     for (int b = 0; b < kGroupBlocks; ++b) {
       const float d = qtype_is_k(QT) ? kd[b] : half_to_float(load_u16(grp + group_d_off(QT) + 2 * b));
       const uint8_t* q = grp + b * qb;
@@ -140,7 +140,7 @@ __attribute__((target("avx512f,avx512bw,avx512vl,f16c"))) float row_dot_avx512(c
     alignas(32) float d[8];
     if constexpr (qtype_is_k(QT)) {
       float km[8];
-      q4_k_group_scales(grp, d, km);
+      k_group_scales<QT>(grp, d, km);
       macc += _mm256_reduce_add_ps_(_mm256_mul_ps(_mm256_loadu_ps(km), _mm256_loadu_ps(xs + g * kGroupBlocks)));
     } else {
       const __m256 d8 = _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i*>(grp + group_d_off(QT))));
@@ -200,6 +200,7 @@ RowDot row_dot_for(int qtype, bool vector) {
     case MOE_QTYPE_Q5_0: return vector ? row_dot_avx512<MOE_QTYPE_Q5_0> : row_dot_scalar<MOE_QTYPE_Q5_0>;
     case MOE_QTYPE_Q5_1: return vector ? row_dot_avx512<MOE_QTYPE_Q5_1> : row_dot_scalar<MOE_QTYPE_Q5_1>;
     case MOE_QTYPE_Q4_K: return vector ? row_dot_avx512<MOE_QTYPE_Q4_K> : row_dot_scalar<MOE_QTYPE_Q4_K>;
+    case MOE_QTYPE_Q5_K: return vector ? row_dot_avx512<MOE_QTYPE_Q5_K> : row_dot_scalar<MOE_QTYPE_Q5_K>;
     default: return vector ? row_dot_avx512<MOE_QTYPE_Q4_0> : row_dot_scalar<MOE_QTYPE_Q4_0>;
   }
 }

@@ -89,30 +89,37 @@ __host__ __device__ constexpr int quant_bytes_per_block(int qtype) {
   return qtype == MOE_QTYPE_Q8_0 ? 32 : 16;
 }
 __host__ __device__ constexpr bool qtype_has_min(int qtype) {  // w = d*q + m
-  return qtype == MOE_QTYPE_Q4_1 || qtype == MOE_QTYPE_Q5_1 || qtype == MOE_QTYPE_Q4_K;
+  return qtype == MOE_QTYPE_Q4_1 || qtype == MOE_QTYPE_Q5_1 || qtype == MOE_QTYPE_Q4_K || qtype == MOE_QTYPE_Q5_K;
 }
-// Q4_K: one super-block of 256 weights per group; its 8 sub-blocks' scales
-// d * scale_j and offsets -dmin * min_j come from the super-block's fp16 d,
-// dmin and 6-bit codes.
-__host__ __device__ constexpr bool qtype_is_k(int qtype) { return qtype == MOE_QTYPE_Q4_K; }
+// Q4_K, Q5_K: one super-block of 256 weights per group; its 8 sub-blocks'
+// scales d * scale_j and offsets -dmin * min_j come from the super-block's
+// fp16 d, dmin and 6-bit codes.
+__host__ __device__ constexpr bool qtype_is_k(int qtype) {
+  return qtype == MOE_QTYPE_Q4_K || qtype == MOE_QTYPE_Q5_K;
+}
 __host__ __device__ constexpr bool qtype_has_qh(int qtype) {  // fifth code bits
-  return qtype == MOE_QTYPE_Q5_0 || qtype == MOE_QTYPE_Q5_1;
+  return qtype == MOE_QTYPE_Q5_0 || qtype == MOE_QTYPE_Q5_1 || qtype == MOE_QTYPE_Q5_K;
 }
 // ggml block bytes: fp16 d, [fp16 m], [4 B fifth bits], quant bytes.
 __host__ __device__ constexpr int ggml_block_bytes(int qtype) {
   return 2 + (qtype_has_min(qtype) ? 2 : 0) + (qtype_has_qh(qtype) ? 4 : 0) + quant_bytes_per_block(qtype);
 }
-// Q4_K: the ggml super-block is 144 bytes (fp16 d, fp16 dmin, 12 bytes of
-// 6-bit scales and mins, 128 bytes of nibbles), the same bytes per group.
-constexpr int kQ4KBytes = 144;
+// K-quant super-blocks: Q4_K 144 bytes (fp16 d, fp16 dmin, 12 bytes of
+// 6-bit scales and mins, 128 bytes of nibbles); Q5_K 176 (the same and 32
+// bytes of fifth bits).  A group holds the same bytes.
+__host__ __device__ constexpr int k_superblock_bytes(int qtype) {
+  return 4 + 12 + kGroupWeights / 2 + (qtype_has_qh(qtype) ? kGroupWeights / 8 : 0);
+}
 __host__ __device__ constexpr int group_bytes(int qtype) {
-  return qtype_is_k(qtype) ? kQ4KBytes : kGroupBlocks * ggml_block_bytes(qtype);
+  return qtype_is_k(qtype) ? k_superblock_bytes(qtype) : kGroupBlocks * ggml_block_bytes(qtype);
 }
 // Offsets inside a group: quant bytes at 0, then fifth-bit words, scales d,
-// offsets m.  Q4_K: quant bytes (per sub-block, nibble order of the 32-weight
-// types), the 12 scale bytes, d, dmin.
+// offsets m.  K-quants: quant bytes (per sub-block, nibble order of the
+// 32-weight types), [fifth-bit words,] the 12 scale bytes, d, dmin.
 __host__ __device__ constexpr int group_qh_off(int qtype) { return kGroupBlocks * quant_bytes_per_block(qtype); }
-__host__ __device__ constexpr int group_ksc_off(int qtype) { return kGroupBlocks * quant_bytes_per_block(qtype); }
+__host__ __device__ constexpr int group_ksc_off(int qtype) {
+  return group_qh_off(qtype) + (qtype_has_qh(qtype) ? 4 * kGroupBlocks : 0);
+}
 __host__ __device__ constexpr int group_d_off(int qtype) {
   return qtype_is_k(qtype) ? group_ksc_off(qtype) + 12
                            : group_qh_off(qtype) + (qtype_has_qh(qtype) ? 4 * kGroupBlocks : 0);
@@ -145,7 +152,7 @@ __host__ __device__ constexpr size_t slot_bytes_of(int qtype, int H, int I) {
 
 inline bool qtype_supported(int qtype) {
   return qtype == MOE_QTYPE_Q8_0 || qtype == MOE_QTYPE_Q4_0 || qtype == MOE_QTYPE_Q4_1 || qtype == MOE_QTYPE_Q5_0 ||
-         qtype == MOE_QTYPE_Q5_1 || qtype == MOE_QTYPE_Q4_K;
+         qtype == MOE_QTYPE_Q5_1 || qtype == MOE_QTYPE_Q4_K || qtype == MOE_QTYPE_Q5_K;
 }
 inline const char* qtype_name(int qtype) {
   switch (qtype) {
@@ -155,6 +162,7 @@ inline const char* qtype_name(int qtype) {
     case MOE_QTYPE_Q5_0: return "Q5_0";
     case MOE_QTYPE_Q5_1: return "Q5_1";
     case MOE_QTYPE_Q4_K: return "Q4_K";
+    case MOE_QTYPE_Q5_K: return "Q5_K";
     default: return "?";
   }
 }

@@ -99,7 +99,8 @@ struct WStage {
     const uint4 v = *reinterpret_cast<const uint4*>(q);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     if constexpr (qtype_is_k(QT)) {
-      q4k_block_dm(row, b, d, m);
+      q4k_block_dm<QT>(row, b, d, m);
+      if constexpr (qtype_has_qh(QT)) qh = block_qh<QT>(row, b);
       return;
     }
     d = block_scale<QT>(row, b);
@@ -429,6 +430,7 @@ static void launch_prefill_gemm(const FfnParams& p, unsigned grid, hipStream_t s
     MOE_PF(MOE_QTYPE_Q5_0)
     MOE_PF(MOE_QTYPE_Q5_1)
     MOE_PF(MOE_QTYPE_Q4_K)
+    MOE_PF(MOE_QTYPE_Q5_K)
     default: break;
   }
 #undef MOE_PF

@@ -55,7 +55,7 @@ __all__ = [
 
 QK = 32
 BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24,
-               "q4_k": 18}  # bytes per 32 weights (Q4_K: 144 per super-block of 256)
+               "q4_k": 18, "q5_k": 22}  # bytes per 32 weights (Q4_K: 144, Q5_K: 176 per super-block of 256)
 
 # substream "kind" field
 KIND = {
@@ -286,20 +286,31 @@ def pack_q4_k(d: np.ndarray, dmin: np.ndarray, sc: np.ndarray, mn: np.ndarray, q
     return out
 
 
-def quantize_q4_k(w: np.ndarray) -> np.ndarray:
-    """fp32 [rows, K] -> uint8 [rows, K/256, 144] ggml Q4_K super-blocks.
+def pack_q5_k(d: np.ndarray, dmin: np.ndarray, sc: np.ndarray, mn: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Q5_K super-blocks from their fields (as pack_q4_k, codes in 0..31)
+    -> uint8 [..., 176]: d, dmin, the 12 scale bytes, 32 bytes qh (bit j of
+    byte l = bit 4 of element l of sub-block j), 128 bytes of low nibbles
+    laid out as in Q4_K."""
+    q = np.asarray(q).astype(np.uint8)
+    k4 = pack_q4_k(d, dmin, sc, mn, q & 0x0F)
+    out = np.empty(k4.shape[:-1] + (176,), dtype=np.uint8)
+    out[..., 0:16] = k4[..., 0:16]
+    hi = (q >> 4) & 1  # [..., 8, 32]
+    qh = np.zeros(q.shape[:-2] + (32,), dtype=np.uint8)
+    for j in range(8):
+        qh |= (hi[..., j, :] << j).astype(np.uint8)
+    out[..., 16:48] = qh
+    out[..., 48:176] = k4[..., 16:144]
+    return out
 
-    Harness quantiser (both sides read the same bytes): per sub-block of 32
-    the offset m = max(0, -min) and the step s = (max + m) / 15; per
-    super-block d = max step / 63 and dmin = max offset / 63, stored as fp16;
-    6-bit scale and min codes round(s / d), round(m / dmin); weight codes
-    round((w + dmin * min) / (d * scale)) clamped to 0..15 (rounding half away
-    from zero, in fp32)."""
+
+def _quantize_k(w: np.ndarray, top: int):
+    """Fields of K-quant super-blocks with weight codes in 0..top."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, K = w.shape
     sb = w.reshape(rows, K // 256, 8, 32)
     off = np.maximum(-sb.min(axis=3), np.float32(0)).astype(np.float32)
-    step = ((sb.max(axis=3) + off) / np.float32(15)).astype(np.float32)
+    step = ((sb.max(axis=3) + off) / np.float32(top)).astype(np.float32)
     d = (step.max(axis=2) / np.float32(63)).astype(np.float16).astype(np.float32)
     dmin = (off.max(axis=2) / np.float32(63)).astype(np.float16).astype(np.float32)
 
@@ -315,12 +326,30 @@ def quantize_q4_k(w: np.ndarray) -> np.ndarray:
     mn = codes(off, dmin[..., None], 63)
     eff_d = (d[..., None] * sc.astype(np.float32)).astype(np.float32)
     eff_m = (dmin[..., None] * mn.astype(np.float32)).astype(np.float32)
-    q = codes((sb + eff_m[..., None]).astype(np.float32), eff_d[..., None], 15)
-    return pack_q4_k(d, dmin, sc, mn, q)
+    q = codes((sb + eff_m[..., None]).astype(np.float32), eff_d[..., None], top)
+    return d, dmin, sc, mn, q
+
+
+def quantize_q4_k(w: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K] -> uint8 [rows, K/256, 144] ggml Q4_K super-blocks.
+
+    Harness quantiser (both sides read the same bytes): per sub-block of 32
+    the offset m = max(0, -min) and the step s = (max + m) / 15; per
+    super-block d = max step / 63 and dmin = max offset / 63, stored as fp16;
+    6-bit scale and min codes round(s / d), round(m / dmin); weight codes
+    round((w + dmin * min) / (d * scale)) clamped to 0..15 (rounding half away
+    from zero, in fp32)."""
+    return pack_q4_k(*_quantize_k(w, 15))
+
+
+def quantize_q5_k(w: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K] -> uint8 [rows, K/256, 176] ggml Q5_K super-blocks:
+    quantize_q4_k's recipe with steps (max + m) / 31 and codes in 0..31."""
+    return pack_q5_k(*_quantize_k(w, 31))
 
 
 _QUANT = {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0, "q4_1": quantize_q4_1, "q5_0": quantize_q5_0,
-          "q5_1": quantize_q5_1, "q4_k": quantize_q4_k}
+          "q5_1": quantize_q5_1, "q4_k": quantize_q4_k, "q5_k": quantize_q5_k}
 
 
 # --------------------------------------------------------------------------

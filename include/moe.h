@@ -7,7 +7,7 @@
  * MoE Runtime Comparison", introduction; "FreeToken Inference Engine: 3x
  * Speed Boost for MoE Models", section "From Static Allocation to Dynamic
  * Scheduling").  Expert banks are ggml blocks of the standard types
- * (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0) or the K-quant Q4_K in one GPU slot
+ * (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0) or the K-quants Q4_K, Q5_K in one GPU slot
  * pool of a single type (FreeToken fork README, "Quant types" and "Known
  * limits"); decode and prefill use different kernel families there (matrix
  * x vector for decode, matrix x matrix for prefill, same section).  One
@@ -68,7 +68,8 @@ enum {
   MOE_QTYPE_Q5_0 = 6,
   MOE_QTYPE_Q5_1 = 7,
   MOE_QTYPE_Q8_0 = 8,
-  MOE_QTYPE_Q4_K = 12
+  MOE_QTYPE_Q4_K = 12,
+  MOE_QTYPE_Q5_K = 13
 };
 
 /* Activation dtypes. */
@@ -152,6 +153,10 @@ int moe_ctx_kernel_time(moe_ctx* ctx, const char* kernel, int* count,
  * (bytes 32i..32i+31: sub-block 2i low nibbles, 2i+1 high, element l in
  * byte 32i + l); weight l of sub-block j = d * scale_j * q - dmin * min_j.
  * moe_qtype_info reports its super-block (256, 144).
+ * Q5_K is Q4_K with a fifth code bit (176 B): fp16 d, fp16 dmin, the same
+ * 12 scale bytes, 32 bytes qh, 128 nibble bytes as in Q4_K; bit j of qh
+ * byte l is bit 4 of element l of sub-block j, so q in 0..31 and weight l
+ * of sub-block j = d * scale_j * q - dmin * min_j; super-block (256, 176).
  * Unknown qtype -> MOE_ERR_UNSUPPORTED_QTYPE and the outputs untouched. */
 int moe_qtype_info(int qtype, int* block_elems, int* block_bytes);
 
@@ -165,6 +170,9 @@ int moe_qtype_info(int qtype, int* block_elems, int* block_bytes);
  * every group is 16-B aligned.  A Q4_K group is one super-block (144 B):
  * its 8 sub-blocks' 16 quant bytes each (nibble order as above: byte j
  * holds elements j and j+16 of the sub-block), the 12 scale bytes, d, dmin.
+ * A Q5_K group (176 B) is the same with the 8 sub-blocks' fifth-bit words
+ * (32 B, bit j for element j, as in Q5_0) between the quant bytes and the
+ * scale bytes.
  * The pinned host pool holds experts in this same layout, so staging an
  * expert into VRAM is one verbatim copy ("FreeToken Inference Engine",
  * FTW paragraph: load straight into the engine's layout, no repacking).

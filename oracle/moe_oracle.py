@@ -159,8 +159,28 @@ def dequant_q4_k(blocks: np.ndarray) -> np.ndarray:
     return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK_K)
 
 
+def dequant_q5_k(blocks: np.ndarray) -> np.ndarray:
+    """uint8 [..., nsb, 176] -> float64 [..., nsb*256] (ggml Q5_K, the
+    five-bit K-quant of the same "Quant types" table).  Q4_K's super-block
+    with 32 bytes qh between the scale bytes and the nibbles: fp16 d, fp16
+    dmin, 12 scale bytes, qh, 128 nibble bytes.  Code q of element l of
+    sub-block j = its nibble (as in Q4_K) + 16 * bit j of qh byte l, in
+    0..31; weight = d * scale_j * q - dmin * min_j."""
+    d, dmin = _half(blocks, 0), _half(blocks, 2)
+    sc, mn = q4_k_scales_mins(blocks[..., 4:16])
+    qh = blocks[..., 16:48].astype(np.int64)
+    qs = blocks[..., 48:176].astype(np.int64)
+    q = np.empty(blocks.shape[:-1] + (8, 32), dtype=np.int64)
+    for j in range(8):
+        chunk = qs[..., 32 * (j // 2):32 * (j // 2) + 32]
+        nib = chunk >> 4 if j % 2 else chunk & 0x0F
+        q[..., j, :] = nib + 16 * ((qh >> j) & 1)
+    w = (d[..., None, None] * sc[..., None]) * q - (dmin[..., None] * mn)[..., None]
+    return w.reshape(*blocks.shape[:-2], blocks.shape[-2] * QK_K)
+
+
 _DEQUANT = {"q8_0": dequant_q8_0, "q4_0": dequant_q4_0, "q4_1": dequant_q4_1, "q5_0": dequant_q5_0,
-            "q5_1": dequant_q5_1, "q4_k": dequant_q4_k}
+            "q5_1": dequant_q5_1, "q4_k": dequant_q4_k, "q5_k": dequant_q5_k}
 
 
 def dequant(qtype: str, blocks: np.ndarray) -> np.ndarray:

@@ -1,5 +1,5 @@
-"""The other standard block types (Q4_1, Q5_0, Q5_1) and the K-quant Q4_K
-on the GPU: exact dequantisation, and decode (GEMV) and prefill (bf16 MFMA)
+"""The other standard block types (Q4_1, Q5_0, Q5_1) and the K-quants Q4_K,
+Q5_K on the GPU: exact dequantisation, and decode (GEMV) and prefill (bf16 MFMA)
 layers against the oracle, through the same entry points as Q4_0 / Q8_0."""
 import numpy as np
 import pytest
@@ -15,9 +15,10 @@ from gpu_util import DEV, ResidentLayer, bf16_tensor, check_routed_layer, dev, m
 
 pytestmark = pytest.mark.gpu
 
-TYPES = ["q4_1", "q5_0", "q5_1", "q4_k"]
+TYPES = ["q4_1", "q5_0", "q5_1", "q4_k", "q5_k"]
 DECODE_TOL, PREFILL_TOL = 1e-3, 2e-2
-QUANT = {"q4_1": gi.quantize_q4_1, "q5_0": gi.quantize_q5_0, "q5_1": gi.quantize_q5_1, "q4_k": gi.quantize_q4_k}
+QUANT = {"q4_1": gi.quantize_q4_1, "q5_0": gi.quantize_q5_0, "q5_1": gi.quantize_q5_1, "q4_k": gi.quantize_q4_k,
+         "q5_k": gi.quantize_q5_k}
 
 
 @pytest.fixture(scope="module")
@@ -42,6 +43,23 @@ def test_dequantize_q4_k_hand_superblock(ctx):
         idx, val = item.split(":")
         assert got[int(idx)] == float(val), (idx, got[int(idx)], val)
     np.testing.assert_array_equal(got, oracle.dequant("q4_k", blk)[0].astype(np.float32))
+
+
+def test_dequantize_q5_k_hand_superblock(ctx):
+    """The hand-built Q5_K super-block of the oracle's pins (fifth bits set
+    and clear) through the library's packer and device decoding."""
+    from test_oracle_pins import _golden_q5_k, _hand_superblock_q5_k
+    blk = _hand_superblock_q5_k().reshape(1, 1, 176)
+    packed = np.empty(176, dtype=np.uint8)
+    moe.moe_pack_matrix(L.QTYPE["q5_k"], 1, 256, blk, packed)
+    out = torch.full((1, 256), float("nan"), dtype=torch.float32, device=DEV)
+    moe.moe_dequantize(ctx, L.QTYPE["q5_k"], dev(packed), 1, 256, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0]
+    for item in _golden_q5_k()["weights"]:
+        idx, val = item.split(":")
+        assert got[int(idx)] == float(val), (idx, got[int(idx)], val)
+    np.testing.assert_array_equal(got, oracle.dequant("q5_k", blk)[0].astype(np.float32))
 
 
 @pytest.mark.parametrize("qt", TYPES)

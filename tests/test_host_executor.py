@@ -26,6 +26,7 @@ CASES = [
     gi.Workload(25, "host_q5_0", H=256, E=2, k=1, I=512, qtype="q5_0", batches=(2,)),
     gi.Workload(26, "host_q5_1", H=512, E=2, k=1, I=768, qtype="q5_1", batches=(3,)),
     gi.Workload(27, "host_q4_k", H=512, E=2, k=1, I=768, qtype="q4_k", batches=(3,)),
+    gi.Workload(28, "host_q5_k", H=512, E=2, k=1, I=768, qtype="q5_k", batches=(3,)),
 ]
 
 

@@ -38,8 +38,10 @@ def test_qtype_table():
     assert moe.moe_qtype_info(L.QTYPE["q5_0"]) == (32, 22)
     assert moe.moe_qtype_info(L.QTYPE["q5_1"]) == (32, 24)
     assert moe.moe_qtype_info(L.QTYPE["q4_k"]) == (256, 144)  # one super-block
-    assert L.QTYPE == {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12}  # ggml's type numbers
-    for bad in (0, 1, 4, 5, 9, 10, 11, 13, 14, -1, 99):
+    assert moe.moe_qtype_info(L.QTYPE["q5_k"]) == (256, 176)
+    assert L.QTYPE == {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12,
+                       "q5_k": 13}  # ggml's type numbers
+    for bad in (0, 1, 4, 5, 9, 10, 11, 14, -1, 99):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_qtype_info(bad)
         assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"
@@ -54,10 +56,11 @@ def test_unsupported_qtype_leaves_outputs_untouched():
 
 @pytest.mark.parametrize("qt,H,I", [("q8_0", 256, 512), ("q8_0", 2048, 768), ("q4_0", 2048, 768),
                                     ("q4_0", 2048, 512), ("q4_0", 4096, 2048), ("q4_1", 2048, 768),
-                                    ("q5_0", 2048, 768), ("q5_1", 4096, 2048), ("q4_k", 2048, 768)])
+                                    ("q5_0", 2048, 768), ("q5_1", 4096, 2048), ("q4_k", 2048, 768),
+                                    ("q5_k", 2048, 768)])
 def test_slot_bytes_equal_ggml_bytes(qt, H, I):
-    if qt == "q4_k":  # 144 bytes per super-block of 256 weights
-        assert moe.moe_slot_bytes(L.QTYPE[qt], H, I) == 3 * H * I // 256 * 144
+    if qt in ("q4_k", "q5_k"):  # 144 / 176 bytes per super-block of 256 weights
+        assert moe.moe_slot_bytes(L.QTYPE[qt], H, I) == 3 * H * I // 256 * {"q4_k": 144, "q5_k": 176}[qt]
         return
     per_block = {"q8_0": 34, "q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24}[qt]
     assert moe.moe_slot_bytes(L.QTYPE[qt], H, I) == 3 * H * I // 32 * per_block
@@ -118,13 +121,35 @@ def _unpack_doc_layout_q4_k(rows, cols, packed):
     return out
 
 
-@pytest.mark.parametrize("qt", ["q8_0", "q4_0", "q4_1", "q5_0", "q5_1", "q4_k"])
+def _unpack_doc_layout_q5_k(rows, cols, packed):
+    """Read the documented Q5_K device groups back into ggml super-blocks:
+    per group 8 sub-blocks of 16 quant bytes (as in Q4_K), their 8 fifth-bit
+    words (bit l for element l), the 12 scale bytes, d, dmin; a ggml
+    super-block is d, dmin, scales, qh (bit j of byte l for element l of
+    sub-block j), then the nibbles as in Q4_K."""
+    out = np.empty((rows, cols // 256, 176), dtype=np.uint8)
+    for r in range(rows):
+        for g in range(cols // 256):
+            grp = packed[(r * (cols // 256) + g) * 176:(r * (cols // 256) + g + 1) * 176]
+            sb = out[r, g]
+            sb[0:2], sb[2:4], sb[4:16] = grp[172:174], grp[174:176], grp[160:172]
+            words = [int.from_bytes(bytes(grp[128 + 4 * b:132 + 4 * b]), "little") for b in range(8)]
+            sb[16:48] = [sum(((words[j] >> l) & 1) << j for j in range(8)) for l in range(32)]
+            codes = [[(grp[16 * b + (l % 16)] >> (4 * (l // 16))) & 15 for l in range(32)] for b in range(8)]
+            for i in range(4):
+                sb[48 + 32 * i:80 + 32 * i] = [codes[2 * i][l] | (codes[2 * i + 1][l] << 4) for l in range(32)]
+    return out
+
+
+@pytest.mark.parametrize("qt", ["q8_0", "q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q5_k"])
 def test_pack_expert_layout(qt):
     H, I = 512, 256
     rng = np.random.default_rng(1)
     quant = {"q8_0": gi.quantize_q8_0, "q4_0": gi.quantize_q4_0, "q4_1": gi.quantize_q4_1,
-             "q5_0": gi.quantize_q5_0, "q5_1": gi.quantize_q5_1, "q4_k": gi.quantize_q4_k}[qt]
-    unpack = _unpack_doc_layout_q4_k if qt == "q4_k" else (lambda r, c, p: _unpack_doc_layout(qt, r, c, p))
+             "q5_0": gi.quantize_q5_0, "q5_1": gi.quantize_q5_1, "q4_k": gi.quantize_q4_k,
+             "q5_k": gi.quantize_q5_k}[qt]
+    unpack = {"q4_k": _unpack_doc_layout_q4_k, "q5_k": _unpack_doc_layout_q5_k}.get(
+        qt, lambda r, c, p: _unpack_doc_layout(qt, r, c, p))
     g = quant(rng.standard_normal((I, H)).astype(np.float32))
     u = quant(rng.standard_normal((I, H)).astype(np.float32))
     d = quant(rng.standard_normal((H, I)).astype(np.float32))
@@ -170,7 +195,7 @@ def test_workspace_queries():
     args = L.moe_ffn_args(qtype=8, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, n_slots=128,
                           slot_bytes=moe.moe_slot_bytes(8, 2048, 768))
     assert moe.moe_expert_ffn_workspace_size(args) >= 16 * 8 * 768 * 4
-    bad = L.moe_ffn_args(qtype=13, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, slot_bytes=1)
+    bad = L.moe_ffn_args(qtype=14, H=2048, I=768, T=16, k=8, E=128, mode=0, x_dtype=0, slot_bytes=1)
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_expert_ffn_workspace_size(bad)
     assert ei.value.name == "MOE_ERR_UNSUPPORTED_QTYPE"

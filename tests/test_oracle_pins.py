@@ -240,6 +240,98 @@ def test_quantiser_error_bound_q4_k():
     assert (err <= 1.5 * step.max(axis=2)[..., None]).all()
 
 
+GOLDEN_Q5_K = os.path.join(os.path.dirname(__file__), "golden", "hand_superblock_q5_k.txt")
+
+
+def _golden_q5_k():
+    f = {}
+    for line in open(GOLDEN_Q5_K):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            f[k.strip()] = v.split()
+    return f
+
+
+def _hand_superblock_q5_k():
+    """The golden Q5_K super-block's bytes, built here from the field rules."""
+    f = _golden_q5_k()
+    b = [0x00, 0x3C, 0x00, 0x38] + [int(h, 16) for h in f["scales"]]
+    b += [1 << (l & 7) for l in range(32)]
+    for i in range(4):
+        b += [((l + i) & 15) | (((3 * l + i) & 15) << 4) for l in range(32)]
+    return np.array(b, dtype=np.uint8)
+
+
+def test_dequant_q5_k_hand_superblock():
+    """Hand-built Q5_K super-block: selected weights worked out by hand from
+    the format (golden file), fifth bits set and clear."""
+    f = _golden_q5_k()
+    blk = _hand_superblock_q5_k()
+    assert blk.shape == (176,)
+    sc, mn = oracle.q4_k_scales_mins(blk[4:16])
+    assert sc.tolist() == [int(v) for v in f["expected_scales"]]
+    assert mn.tolist() == [int(v) for v in f["expected_mins"]]
+    got = oracle.dequant("q5_k", blk[None, None, :])[0]
+    assert got.shape == (256,)
+    for item in f["weights"]:
+        idx, val = item.split(":")
+        assert got[int(idx)] == float(val), (idx, got[int(idx)], val)
+
+
+def test_dequant_q5_k_reduces_to_q4_k():
+    """With every fifth bit clear, a Q5_K super-block is the Q4_K one with
+    the same scale bytes and nibbles; with every bit set, each weight gains
+    16 * d * scale_j (its sub-block's scale)."""
+    rng = np.random.default_rng(17)
+    k4 = _hand_superblock_q4_k()
+    k4[4:16] = rng.integers(0, 256, 12)
+    k4[16:] = rng.integers(0, 256, 128)
+    k5 = np.concatenate([k4[:16], np.zeros(32, np.uint8), k4[16:]])
+    w4 = oracle.dequant("q4_k", k4[None, None, :])[0]
+    np.testing.assert_array_equal(oracle.dequant("q5_k", k5[None, None, :])[0], w4)
+    k5[16:48] = 0xFF
+    sc, _ = oracle.q4_k_scales_mins(k4[4:16])
+    want = w4 + np.repeat(16.0 * 1.0 * sc, 32)  # d = 1.0
+    np.testing.assert_array_equal(oracle.dequant("q5_k", k5[None, None, :])[0], want)
+
+
+def test_dequant_q5_k_brute_force():
+    """Every code 0..31 at every position of every sub-block, scale and min
+    codes over the 6-bit range, against the exact d * scale * q - dmin * min;
+    super-blocks packed by the harness packer."""
+    rng = np.random.default_rng(19)
+    for d_bits, m_bits in [(0x3C00, 0x3800), (0x2E66, 0x0001), (0x7BFF, 0x03FF)]:
+        dv, mv = Fraction(fp16_bits_to_float(d_bits)), Fraction(fp16_bits_to_float(m_bits))
+        for trial in range(4):
+            sc = rng.integers(0, 64, 8)
+            mn = rng.integers(0, 64, 8)
+            sc[trial % 8], mn[(trial + 5) % 8] = 63, 0
+            q = (np.arange(256).reshape(8, 32) * (2 * trial + 1) + trial) % 32
+            blk = gi.pack_q5_k(np.float32(fp16_bits_to_float(d_bits)), np.float32(fp16_bits_to_float(m_bits)),
+                               sc, mn, q)
+            assert blk.shape == (176,)
+            got = oracle.dequant("q5_k", blk[None, None, :])[0]
+            for j in range(8):
+                for l in range(32):
+                    want = dv * int(sc[j]) * int(q[j, l]) - mv * int(mn[j])
+                    assert Fraction(float(got[32 * j + l])) == want, (j, l)
+
+
+def test_quantiser_error_bound_q5_k():
+    """The harness Q5_K quantiser stays within about a step of its input,
+    and about half the Q4_K quantiser's error on the same weights."""
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    got = oracle.dequant("q5_k", gi.quantize_q5_k(w))
+    sb = w.reshape(6, 2, 8, 32).astype(np.float64)
+    step = (sb.max(axis=3) - np.minimum(sb.min(axis=3), 0)) / 31
+    err = np.abs(got - w).reshape(6, 2, 8, 32).max(axis=3)
+    assert (err <= 1.5 * step.max(axis=2)[..., None]).all()
+    e4 = np.abs(oracle.dequant("q4_k", gi.quantize_q4_k(w)) - w).mean()
+    assert np.abs(got - w).mean() < 0.7 * e4
+
+
 def test_dequant_layout_rows_and_blocks():
     """Blocks run along the input dimension; rows stack (shape [rows, nblk*32])."""
     rng = np.random.default_rng(3)
